@@ -1,0 +1,169 @@
+"""CPU oracle for absorbed MLA (test infrastructure only).
+
+Loads the plain C oracle (mla_oracle.c, float32 in/out, double accumulation)
+through ctypes.  Only the tests, the smoke check and the benchmark's CPU-baseline
+leg may import this package; the GPU library never does, and this package never
+imports the GPU library.
+
+Every function takes and returns numpy arrays in the layouts documented in
+mla_oracle.c.  The method follows the page "ik_llama.cpp MLA matrix absorption"
+(czykbl.com/news/93068), sections 1, 3, 4 and 5; the Q8_0 format follows its
+section 8.1 and the DeepSeek-V3 run of the KV-cache-rm page (trdm.cn/news/546512).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mla_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
+_u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
+
+
+def build(force: bool = False) -> str:
+    """Compile mla_oracle.c with gcc (OpenMP, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+                               "-std=c11", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        i, d, f = ctypes.c_int, ctypes.c_double, ctypes.c_float
+        L.orc_rope.argtypes = [_f32p, i, d, d, _f32p]
+        L.orc_absorb_q.argtypes = [i, i, i, i, d, _f32p, _f32p, _i32p, _f32p, i, _f32p]
+        L.orc_attention.argtypes = [i, i, i, d, _f32p, _i32p, i, _f32p, i, _f32p,
+                                    ctypes.c_void_p]
+        L.orc_out_proj.argtypes = [i, i, i, i, _f32p, _f32p, _f32p, i, ctypes.c_void_p, _f32p]
+        L.orc_mla_unabsorbed.argtypes = [i, i, i, i, i, i, d, d, _f32p, _f32p, _i32p, i, _f32p,
+                                         i, _f32p, _f32p, _f32p, ctypes.c_void_p, _f32p]
+        L.orc_half_to_float.argtypes = [ctypes.c_uint16]
+        L.orc_half_to_float.restype = f
+        L.orc_float_to_half.argtypes = [f]
+        L.orc_float_to_half.restype = ctypes.c_uint16
+        L.orc_q8_0_quantize.argtypes = [_f32p, ctypes.c_int64, i, _u8p]
+        L.orc_q8_0_dequantize.argtypes = [_u8p, ctypes.c_int64, i, _f32p]
+        L.orc_heads_per_chunk.argtypes = [i, d, i]
+        L.orc_heads_per_chunk.restype = i
+        _lib = L
+    return _lib
+
+
+def _c(a, dt=np.float32):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def rope(x, pos, base=10000.0):
+    """RoPE of one vector (adjacent pairs, angle pos * base^(-2i/dr))."""
+    x = _c(x)
+    y = np.empty_like(x)
+    lib().orc_rope(x, x.shape[-1], float(pos), float(base), y)
+    return y
+
+
+def absorb_q(dims, q_nope, q_rope, pos, wk_b):
+    """q_cat[t,h] = [wk_b[h] @ q_nope[t,h] | RoPE(q_rope[t,h], pos[t])]."""
+    q_nope, q_rope, wk_b, pos = _c(q_nope), _c(q_rope), _c(wk_b), _c(pos, np.int32)
+    T = q_nope.shape[0]
+    H, R, Dn, Dr = dims.n_head, dims.kv_lora_rank, dims.qk_nope, dims.qk_rope
+    q_cat = np.empty((T, H, R + Dr), dtype=np.float32)
+    lib().orc_absorb_q(H, R, Dn, Dr, float(dims.rope_base), q_nope, q_rope, pos, wk_b, T, q_cat)
+    return q_cat
+
+
+def attention(dims, q_cat, pos, cache_rows):
+    """Causal attention of q_cat [T,H,W] over cache rows [N,W]; returns (o_lat, lse)."""
+    q_cat, pos, cache_rows = _c(q_cat), _c(pos, np.int32), _c(cache_rows)
+    T, H, W = q_cat.shape
+    R = dims.kv_lora_rank
+    N = cache_rows.shape[0]
+    o = np.empty((T, H, R), dtype=np.float32)
+    lse = np.empty((T, H), dtype=np.float32)
+    lib().orc_attention(H, R, dims.qk_rope, float(dims.scale), q_cat, pos, T, cache_rows, N, o,
+                        lse.ctypes.data)
+    return o, lse
+
+
+def out_proj(dims, o_lat, wv_b, wo):
+    """Returns (v [T, H*Dv], out [T, D]): v = wv_b . o_lat per head, out = wo . v."""
+    o_lat, wv_b, wo = _c(o_lat), _c(wv_b), _c(wo)
+    T = o_lat.shape[0]
+    H, R, Dv, D = dims.n_head, dims.kv_lora_rank, dims.v_head, dims.d_model
+    v = np.empty((T, H * Dv), dtype=np.float32)
+    out = np.empty((T, D), dtype=np.float32)
+    lib().orc_out_proj(H, R, Dv, D, o_lat, wv_b, wo, T, v.ctypes.data, out)
+    return v, out
+
+
+def mla_unabsorbed(dims, q_nope, q_rope, pos, cache_rows, wk_b, wv_b, wo):
+    """Explicitly decompressed MLA (mode 0); returns (attn_v [T,H,Dv], out [T,D])."""
+    q_nope, q_rope, pos = _c(q_nope), _c(q_rope), _c(pos, np.int32)
+    cache_rows, wk_b, wv_b, wo = _c(cache_rows), _c(wk_b), _c(wv_b), _c(wo)
+    T = q_nope.shape[0]
+    H, R, Dn, Dr, Dv, D = (dims.n_head, dims.kv_lora_rank, dims.qk_nope, dims.qk_rope,
+                           dims.v_head, dims.d_model)
+    av = np.empty((T, H, Dv), dtype=np.float32)
+    out = np.empty((T, D), dtype=np.float32)
+    lib().orc_mla_unabsorbed(H, R, Dn, Dr, Dv, D, float(dims.scale), float(dims.rope_base),
+                             q_nope, q_rope, pos, T, cache_rows, cache_rows.shape[0], wk_b, wv_b,
+                             wo, av.ctypes.data, out)
+    return av, out
+
+
+def half_to_float(bits: int) -> float:
+    return float(lib().orc_half_to_float(int(bits)))
+
+
+def float_to_half(x: float) -> int:
+    return int(lib().orc_float_to_half(float(x)))
+
+
+def q8_0_row_bytes(width: int) -> int:
+    return width // 32 * 34
+
+
+def q8_0_quantize(x):
+    """Quantise rows [..., width] (width % 32 == 0) to Q8_0 bytes [..., width/32*34]."""
+    x = _c(x)
+    width = x.shape[-1]
+    assert width % 32 == 0
+    n_rows = x.size // width
+    out = np.empty(x.shape[:-1] + (q8_0_row_bytes(width),), dtype=np.uint8)
+    lib().orc_q8_0_quantize(x, n_rows, width, out)
+    return out
+
+
+def q8_0_dequantize(b, width):
+    b = _c(b, np.uint8)
+    n_rows = b.size // q8_0_row_bytes(width)
+    out = np.empty(b.shape[:-1] + (width,), dtype=np.float32)
+    lib().orc_q8_0_dequantize(b, n_rows, width, out)
+    return out
+
+
+def heads_per_chunk(n_head: int, size_mib: float, cap_mib: int) -> int:
+    return int(lib().orc_heads_per_chunk(int(n_head), float(size_mib), int(cap_mib)))
+
+
+def mla_absorbed(dims, q_nope, q_rope, pos, cache_rows, wk_b, wv_b, wo):
+    """The absorbed chain end to end; returns dict of q_cat, o_lat, lse, v, out."""
+    q_cat = absorb_q(dims, q_nope, q_rope, pos, wk_b)
+    o_lat, lse = attention(dims, q_cat, pos, cache_rows)
+    v, out = out_proj(dims, o_lat, wv_b, wo)
+    return {"q_cat": q_cat, "o_lat": o_lat, "lse": lse, "v": v, "out": out}
