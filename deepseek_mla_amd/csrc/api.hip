@@ -1,0 +1,267 @@
+// C-ABI entry points (include/mla.h): argument validation, work planning and dispatch.
+// Every check happens before the first launch; no call allocates device memory.
+#include <math.h>
+
+#include "common.h"
+
+using namespace mla;
+
+namespace {
+
+constexpr int NUM_CUS = 256;  // MI355X: 8 XCDs x 32 CUs
+
+bool dims_ok(const mla_dims *d) {
+    return d && d->n_head > 0 && d->kv_lora_rank > 0 && d->qk_nope > 0 && d->qk_rope > 0 &&
+           (d->qk_rope % 2) == 0 && d->v_head > 0 && d->d_model > 0 && isfinite(d->scale) &&
+           d->rope_base > 0.0f;
+}
+
+bool act_ok(int act) { return act == MLA_F32 || act == MLA_BF16; }
+
+// The bf16 attention kernels are specialised for the DeepSeek latent row [512 | 64].
+bool bf16_attn_dims(const mla_dims *d) { return d->kv_lora_rank == 512 && d->qk_rope == 64; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+hipStream_t as_stream(void *s) { return (hipStream_t)s; }
+
+constexpr int SIMT_SPLIT_GRAIN = 64;
+constexpr int MAX_SPLITS = 4096;  // the combine step keeps one weight per split in LDS
+constexpr int MFMA_SPLIT_GRAIN = 32;
+
+int auto_splits(const mla_dims *d, int kv, int B, int n_kv_max) {
+    if (kv == MLA_F32) {
+        int s = (n_kv_max + 255) / 256;
+        return s < 1 ? 1 : (s > 64 ? 64 : s);
+    }
+    const int hgroups = (d->n_head + 127) / 128;
+    const int per_seq = (B * hgroups);
+    int s = (NUM_CUS + per_seq - 1) / per_seq;
+    // at least 4 tiles of 32 keys per split
+    const int max_s = (n_kv_max + 127) / 128;
+    if (s > max_s) s = max_s;
+    return s < 1 ? 1 : s;
+}
+
+// split length (multiple of the kernel's key grain) and the resulting split count
+void split_plan(int kv, int n_kv_max, int n_splits, int *len, int *count) {
+    const int grain = kv == MLA_F32 ? SIMT_SPLIT_GRAIN : MFMA_SPLIT_GRAIN;
+    int L = (n_kv_max + n_splits - 1) / n_splits;
+    L = (L + grain - 1) / grain * grain;
+    *len = L;
+    *count = (n_kv_max + L - 1) / L;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char *mla_status_str(int status) {
+    switch (status) {
+    case MLA_OK: return "MLA_OK: success";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: shape or dtype not implemented";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime error";
+    default: return "unknown mla_status";
+    }
+}
+
+int32_t mla_q8_0_row_bytes(int32_t width) {
+    if (width <= 0 || width % 32) return -1;
+    return width / 32 * 34;
+}
+
+int32_t mla_heads_per_chunk(int32_t n_head, double size_mib, uint32_t cap_mib) {
+    if (n_head < 1) return n_head;
+    if (cap_mib == 0) return n_head;
+    double cap = cap_mib < 128 ? 128.0 : (double)cap_mib;
+    if (!(size_mib > cap)) return n_head;
+    int32_t heads = 1;
+    for (int32_t niter = 2; niter <= n_head; ++niter) {
+        if (n_head % niter == 0 && size_mib / niter <= cap) {
+            heads = n_head / niter;
+            break;
+        }
+    }
+    return heads;
+}
+
+int mla_absorb_q(const mla_dims *d, mla_dtype act, const void *q_nope, const void *q_rope,
+                 const int32_t *pos, const void *wk_b, void *q_cat, int32_t T, void *stream) {
+    if (!dims_ok(d) || !act_ok(act) || T < 0) return MLA_ERR_INVALID_ARG;
+    if (T == 0) return MLA_OK;
+    if (!q_nope || !q_rope || !pos || !wk_b || !q_cat) return MLA_ERR_INVALID_ARG;
+    const int H = d->n_head, R = d->kv_lora_rank, Dn = d->qk_nope, Dr = d->qk_rope;
+    const int W = R + Dr;
+    hipStream_t st = as_stream(stream);
+    hipError_t e;
+    if (act == MLA_F32) {
+        e = launch_gemm_nt_f32((const float *)q_nope, (const float *)wk_b, (float *)q_cat, T, R,
+                               Dn, (int64_t)H * Dn, Dn, (int64_t)H * W, H, Dn, (int64_t)R * Dn, W,
+                               st);
+        if (e == hipSuccess)
+            e = launch_rope_q<float>((const float *)q_rope, pos, (float *)q_cat, T, H, R, Dr,
+                                     d->rope_base, st);
+    } else {
+        if (Dn % 8) return MLA_ERR_UNSUPPORTED;
+        e = launch_gemm_nt_bf16((const bf16 *)q_nope, (const bf16 *)wk_b, (bf16 *)q_cat, T, R, Dn,
+                                (int64_t)H * Dn, Dn, (int64_t)H * W, H, Dn, (int64_t)R * Dn, W,
+                                st);
+        if (e == hipSuccess)
+            e = launch_rope_q<bf16>((const bf16 *)q_rope, pos, (bf16 *)q_cat, T, H, R, Dr,
+                                    d->rope_base, st);
+    }
+    return hip_status(e);
+}
+
+int mla_attn_prefill(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *q_cat,
+                     const int32_t *pos, int32_t T, const void *kv_cache, int32_t n_kv,
+                     void *o_lat, float *lse, uint32_t scratch_cap_mib, void *stream) {
+    if (!dims_ok(d) || !act_ok(act) || T < 0 || n_kv < 1) return MLA_ERR_INVALID_ARG;
+    if (kv != MLA_F32 && kv != MLA_BF16 && kv != MLA_Q8_0) return MLA_ERR_INVALID_ARG;
+    if (kv == MLA_Q8_0) return MLA_ERR_UNSUPPORTED;
+    if (kv != act) return MLA_ERR_INVALID_ARG;
+    if (T == 0) return MLA_OK;
+    if (!q_cat || !pos || !kv_cache || !o_lat) return MLA_ERR_INVALID_ARG;
+    const int H = d->n_head;
+    const double size_mib = (double)T * (double)n_kv * (double)H * 4.0 / (1024.0 * 1024.0);
+    const int hc = mla_heads_per_chunk(H, size_mib, scratch_cap_mib);
+    hipStream_t st = as_stream(stream);
+    if (act == MLA_F32) {
+        if (d->kv_lora_rank > 1024) return MLA_ERR_UNSUPPORTED;
+        for (int h0 = 0; h0 < H; h0 += hc) {
+            hipError_t e = launch_flash_simt_prefill(*d, (const float *)q_cat, pos, T,
+                                                     (const float *)kv_cache, n_kv, h0, hc,
+                                                     (float *)o_lat, lse, st);
+            if (e != hipSuccess) return MLA_ERR_HIP;
+        }
+        return MLA_OK;
+    }
+    if (!bf16_attn_dims(d)) return MLA_ERR_UNSUPPORTED;
+    if ((int64_t)T * hc > INT32_MAX / 2) return MLA_ERR_UNSUPPORTED;
+    return hip_status(launch_flash_prefill_bf16((const bf16 *)q_cat, pos, T, H,
+                                                (const bf16 *)kv_cache, n_kv, hc, d->scale,
+                                                (bf16 *)o_lat, lse, st));
+}
+
+int32_t mla_decode_auto_splits(const mla_dims *d, mla_dtype kv, int32_t B, int32_t n_kv_max) {
+    if (!dims_ok(d) || B < 1 || n_kv_max < 1) return 0;
+    return auto_splits(d, kv, B, n_kv_max);
+}
+
+size_t mla_decode_workspace_bytes(const mla_dims *d, int32_t B, int32_t n_kv_max,
+                                  int32_t n_splits) {
+    if (!dims_ok(d) || B < 1 || n_kv_max < 1 || n_splits < 0 || n_splits > MAX_SPLITS) return 0;
+    int S = n_splits;
+    if (S == 0) {
+        // the largest automatic choice over cache types
+        int a = auto_splits(d, MLA_F32, B, n_kv_max), b = auto_splits(d, MLA_BF16, B, n_kv_max);
+        S = a > b ? a : b;
+    }
+    if (S > n_kv_max) S = n_kv_max;
+    const size_t rows = (size_t)B * S * d->n_head;
+    return align256(rows * d->kv_lora_rank * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+int mla_attn_decode(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *q_cat,
+                    const void *kv_cache, int64_t kv_seq_stride_bytes, const int32_t *n_kv,
+                    int32_t B, int32_t n_kv_max, int32_t n_splits, void *o_lat, float *lse,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    if (!dims_ok(d) || !act_ok(act) || B < 0 || n_kv_max < 1 || n_splits < 0 ||
+        n_splits > MAX_SPLITS)
+        return MLA_ERR_INVALID_ARG;
+    if (kv != MLA_F32 && kv != MLA_BF16 && kv != MLA_Q8_0) return MLA_ERR_INVALID_ARG;
+    if (kv == MLA_F32 && act != MLA_F32) return MLA_ERR_INVALID_ARG;
+    if (kv != MLA_F32 && act != MLA_BF16) return MLA_ERR_INVALID_ARG;
+    if (B == 0) return MLA_OK;
+    if (!q_cat || !kv_cache || !n_kv || !o_lat || !workspace) return MLA_ERR_INVALID_ARG;
+    const int W = d->kv_lora_rank + d->qk_rope;
+    int64_t row_bytes;
+    if (kv == MLA_Q8_0) {
+        if (W % 32) return MLA_ERR_INVALID_ARG;
+        row_bytes = (int64_t)W / 32 * 34;
+    } else {
+        row_bytes = (int64_t)W * (kv == MLA_F32 ? 4 : 2);
+    }
+    if (B > 1 && kv_seq_stride_bytes < row_bytes * n_kv_max) return MLA_ERR_INVALID_ARG;
+    if (kv_seq_stride_bytes < 0 || (kv != MLA_Q8_0 && kv_seq_stride_bytes % 16) ||
+        (kv == MLA_Q8_0 && kv_seq_stride_bytes % 4))
+        return MLA_ERR_INVALID_ARG;
+    if (kv != MLA_F32 && !bf16_attn_dims(d)) return MLA_ERR_UNSUPPORTED;
+    if (kv == MLA_F32 && d->kv_lora_rank > 1024) return MLA_ERR_UNSUPPORTED;
+
+    int S = n_splits ? n_splits : auto_splits(d, kv, B, n_kv_max);
+    if (S > n_kv_max) S = n_kv_max;
+    int split_len, count;
+    split_plan(kv, n_kv_max, S, &split_len, &count);
+    if (workspace_bytes < mla_decode_workspace_bytes(d, B, n_kv_max, S)) return MLA_ERR_WORKSPACE;
+    const size_t rows = (size_t)B * count * d->n_head;
+    float *part_o = (float *)workspace;
+    float *part_lse = (float *)((char *)workspace + align256(rows * d->kv_lora_rank * sizeof(float)));
+    hipStream_t st = as_stream(stream);
+    hipError_t e;
+    if (kv == MLA_F32) {
+        e = launch_flash_simt_decode(*d, (const float *)q_cat, (const float *)kv_cache,
+                                     kv_seq_stride_bytes / 4, n_kv, n_kv_max, B, count, split_len,
+                                     part_o,
+                                     part_lse, st);
+        if (e == hipSuccess)
+            e = launch_combine<float>(part_o, part_lse, B, d->n_head, d->kv_lora_rank, count,
+                                      (float *)o_lat, lse, st);
+    } else {
+        e = launch_flash_decode_bf16((const bf16 *)q_cat, kv_cache, kv == MLA_Q8_0,
+                                     kv_seq_stride_bytes, n_kv, n_kv_max, B, d->n_head, count,
+                                     split_len,
+                                     d->scale, part_o, part_lse, st);
+        if (e == hipSuccess)
+            e = launch_combine<bf16>(part_o, part_lse, B, d->n_head, d->kv_lora_rank, count,
+                                     (bf16 *)o_lat, lse, st);
+    }
+    return hip_status(e);
+}
+
+int mla_out_proj(const mla_dims *d, mla_dtype act, const void *o_lat, const void *wv_b,
+                 const void *wo, void *v_scratch, void *out, int32_t T, void *stream) {
+    if (!dims_ok(d) || !act_ok(act) || T < 0) return MLA_ERR_INVALID_ARG;
+    if (T == 0) return MLA_OK;
+    if (!o_lat || !wv_b || !wo || !v_scratch || !out) return MLA_ERR_INVALID_ARG;
+    const int H = d->n_head, R = d->kv_lora_rank, Dv = d->v_head, D = d->d_model;
+    const int HDv = H * Dv;
+    hipStream_t st = as_stream(stream);
+    hipError_t e;
+    if (act == MLA_F32) {
+        e = launch_gemm_nt_f32((const float *)o_lat, (const float *)wv_b, (float *)v_scratch, T,
+                               Dv, R, (int64_t)H * R, R, HDv, H, R, (int64_t)Dv * R, Dv, st);
+        if (e == hipSuccess)
+            e = launch_gemm_nt_f32((const float *)v_scratch, (const float *)wo, (float *)out, T, D,
+                                   HDv, HDv, HDv, D, 1, 0, 0, 0, st);
+    } else {
+        if (R % 8 || Dv % 8) return MLA_ERR_UNSUPPORTED;
+        e = launch_gemm_nt_bf16((const bf16 *)o_lat, (const bf16 *)wv_b, (bf16 *)v_scratch, T, Dv,
+                                R, (int64_t)H * R, R, HDv, H, R, (int64_t)Dv * R, Dv, st);
+        if (e == hipSuccess)
+            e = launch_gemm_nt_bf16((const bf16 *)v_scratch, (const bf16 *)wo, (bf16 *)out, T, D,
+                                    HDv, HDv, HDv, D, 1, 0, 0, 0, st);
+    }
+    return hip_status(e);
+}
+
+int mla_quantize_q8_0(const float *x, void *rows, int64_t n_rows, int32_t width, void *stream) {
+    if (width <= 0 || width % 32 || n_rows < 0) return MLA_ERR_INVALID_ARG;
+    if (n_rows == 0) return MLA_OK;
+    if (!x || !rows) return MLA_ERR_INVALID_ARG;
+    return hip_status(launch_quantize_q8_0(x, (uint8_t *)rows, n_rows, width, as_stream(stream)));
+}
+
+int mla_dequant_q8_0(const void *rows, float *out, int64_t n_rows, int32_t width, void *stream) {
+    if (width <= 0 || width % 32 || n_rows < 0) return MLA_ERR_INVALID_ARG;
+    if (n_rows == 0) return MLA_OK;
+    if (!rows || !out) return MLA_ERR_INVALID_ARG;
+    return hip_status(launch_dequant_q8_0((const uint8_t *)rows, out, n_rows, width,
+                                          as_stream(stream)));
+}
+
+}  // extern "C"

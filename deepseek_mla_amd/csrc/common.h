@@ -1,0 +1,76 @@
+// Internal declarations shared by the HIP sources of the MLA library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+
+namespace mla {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
+__device__ __forceinline__ bf16 f2bf(float x) { return (bf16)x; }  // v_cvt_pk_bf16_f32 (RNE)
+
+template <typename T> __device__ __forceinline__ float ld_f(const T *p);
+template <> __device__ __forceinline__ float ld_f<float>(const float *p) { return *p; }
+template <> __device__ __forceinline__ float ld_f<bf16>(const bf16 *p) { return (float)*p; }
+template <typename T> __device__ __forceinline__ void st_f(T *p, float v);
+template <> __device__ __forceinline__ void st_f<float>(float *p, float v) { *p = v; }
+template <> __device__ __forceinline__ void st_f<bf16>(bf16 *p, float v) { *p = (bf16)v; }
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt_hi[15:14]).
+#define MLA_WAIT_VMCNT(n)                                                                      \
+    __builtin_amdgcn_s_waitcnt((((n)&0xF) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (0xF << 8)))
+
+// ---- launchers (implemented in the .hip sources; all return hipError_t of launch)
+
+// f32 / generic SIMT path
+hipError_t launch_gemm_nt_f32(const float *A, const float *B, float *C, int M, int N, int K,
+                              int64_t lda, int64_t ldb, int64_t ldc, int batch, int64_t sA,
+                              int64_t sB, int64_t sC, hipStream_t st);
+template <typename T>
+hipError_t launch_rope_q(const T *q_rope, const int32_t *pos, T *q_cat, int T_, int H, int R,
+                         int Dr, float base, hipStream_t st);
+hipError_t launch_flash_simt_prefill(const mla_dims &d, const float *q_cat, const int32_t *pos,
+                                     int T, const float *cache, int n_kv, int h0, int hc,
+                                     float *o_lat, float *lse, hipStream_t st);
+hipError_t launch_flash_simt_decode(const mla_dims &d, const float *q_cat, const float *cache,
+                                    int64_t seq_stride_elems, const int32_t *n_kv, int n_kv_max,
+                                    int B,
+                                    int n_splits, int split_len, float *part_o, float *part_lse,
+                                    hipStream_t st);
+template <typename OT>
+hipError_t launch_combine(const float *part_o, const float *part_lse, int B, int H, int R,
+                          int n_splits, OT *o_lat, float *lse, hipStream_t st);
+hipError_t launch_quantize_q8_0(const float *x, uint8_t *rows, int64_t n_rows, int width,
+                                hipStream_t st);
+hipError_t launch_dequant_q8_0(const uint8_t *rows, float *out, int64_t n_rows, int width,
+                               hipStream_t st);
+
+// bf16 MFMA path
+hipError_t launch_gemm_nt_bf16(const bf16 *A, const bf16 *B, bf16 *C, int M, int N, int K,
+                               int64_t lda, int64_t ldb, int64_t ldc, int batch, int64_t sA,
+                               int64_t sB, int64_t sC, hipStream_t st);
+hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int T, int H,
+                                     const bf16 *cache, int n_kv, int hc, float scale,
+                                     bf16 *o_lat, float *lse, hipStream_t st);
+hipError_t launch_flash_decode_bf16(const bf16 *q_cat, const void *cache, int cache_q8,
+                                    int64_t seq_stride_bytes, const int32_t *n_kv, int n_kv_max,
+                                    int B, int H,
+                                    int n_splits, int split_len, float scale, float *part_o,
+                                    float *part_lse, hipStream_t st);
+
+}  // namespace mla

@@ -1,0 +1,516 @@
+// Fused flash-MLA attention on the latent cache, gfx950 (CDNA4) bf16 matrix cores.
+//
+// Method (page "ik_llama.cpp MLA matrix absorption", sections 4 and 5): every head
+// attends to the same latent rows [c_kv (512) | k_rope (64)], with score
+//   s_j = scale * (q_lat . c_kv[j] + q_rope' . k_rope[j])
+// and output o_lat = softmax(s) . c_kv -- one KV head shared by all query rows.
+//
+// Work decomposition.  A workgroup owns 32*NW query rows (flattened (token, head)
+// pairs in prefill, the heads of one sequence in decode); wave w owns 32 of them.
+// The workgroup streams the cache in tiles of 32 rows; each tile is read from HBM
+// once into LDS and used by every wave, i.e. by all of the workgroup's rows.
+//   S^T[key][row] = K_tile (32x576, LDS) x Q^T (576x32, registers)   36 MFMA 32x32x16
+//   O^T[col][row] += V^T (512x32, LDS via ds_read_b64_tr_b16) x P^T   32 MFMA 32x32x16
+// Computing the transposed products puts one query row in each lane (lanes l and
+// l^32 share a row), so the softmax statistics and the output rescale are lane-local.
+// The same LDS tile serves as K (all 576 columns) and as V (first 512).
+//
+// Online softmax (FlashAttention-2 recurrence, KV-cache page section 3.3) in the
+// base-2 domain with a frozen maximum: a row's reference max m is taken from its first
+// visible tile and never raised in place, so the 512-wide fp32 output accumulator is
+// only ever touched by MFMA inside the key loop (no rescale).  Weights exp2(s - m) may
+// exceed 1; they stay finite while s - m <= 64 (fp32/bf16 range is 2^128).  A row
+// whose score exceeds m + 64 is marked, keeps tracking its true max for the rest of
+// the pass, and the workgroup repeats the pass once with the marked rows starting
+// from their true max (unmarked rows recompute bit-identical values).
+//
+// LDS tile layout: row k (1152 B = 72 chunks of 16 B), logical chunk c stored at
+// chunk c ^ swz(k), swz(k) = (k & 7) ^ ((k >> 3) & 1): conflict-free for the
+// 16-byte K-fragment reads of 16 consecutive rows.
+#include "common.h"
+
+namespace mla {
+
+namespace fl {
+constexpr int R = 512, DR = 64, W = 576;
+constexpr int RB = W * 2;         // 1152 bytes per bf16 row
+constexpr int WCH = W / 8;        // 72 chunks of 16 B per row
+constexpr int NK = 32;            // keys per tile
+constexpr int TILE_CH = NK * WCH;           // 2304 chunks
+constexpr int TILE_BYTES = TILE_CH * 16;    // 36864 B
+constexpr int Q8_RB = W / 32 * 34;          // 612 B per Q8_0 row
+constexpr int Q8_TILE_BYTES = NK * Q8_RB;   // 19584 B, 16-B aligned for aligned tiles
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float FREEZE_LIMIT = 64.0f;  // log2 units a score may exceed the frozen max by
+}  // namespace fl
+
+__device__ __forceinline__ int fswz(int k) { return (k & 7) ^ ((k >> 3) & 1); }
+
+__device__ __forceinline__ bf16x8 tr_pair(const uint8_t MLA_LDS *p0, const uint8_t MLA_LDS *p1) {
+    s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS *)p0);
+    s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS *)p1);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Issue the async copy of one bf16 tile (32 rows starting at key0; rows past `last`
+// re-read row `last`, they are masked out of the softmax) into LDS stage `dst`.
+template <int NW>
+__device__ __forceinline__ void issue_tile_bf16(const uint8_t *__restrict__ rows, int key0,
+                                                int last, uint8_t MLA_LDS *dst) {
+    constexpr int NI = fl::TILE_CH / (64 * NW);  // instructions per wave
+    static_assert(fl::TILE_CH % (64 * NW) == 0, "tile chunks must split evenly over waves");
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    // rows past `last` are clamped; offsets stay below 2^31 for caches < 2 GiB per call
+    const uint8_t *base = rows + (int64_t)key0 * fl::RB;
+    const int lim = last - key0;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int P = (w * NI + i) * 64 + l;  // physical chunk in the tile
+        const int k = P / fl::WCH;
+        const int c = (P % fl::WCH) ^ fswz(k);
+        const uint32_t off = (uint32_t)(min(k, lim) * fl::RB + c * 16);
+        __builtin_amdgcn_global_load_lds((const void *)(base + off),
+                                         (void MLA_LDS *)(dst + (w * NI + i) * 1024), 16, 0, 0);
+    }
+}
+
+// Issue the async copy of the raw Q8_0 bytes of a 32-row tile into LDS, one dword per
+// lane (612-byte rows are dword aligned, not 16-byte aligned).  Dwords past the
+// sequence's last row re-read its final dword; the dequant pass zeroes those rows.
+// 80 instructions of 64 dwords cover the 4896-dword tile; the stage holds 20480 B.
+constexpr int Q8_RAW_DW = fl::Q8_TILE_BYTES / 4;      // 4896
+constexpr int Q8_RAW_INST = (Q8_RAW_DW + 63) / 64 + 3; // 80 (rounded up to a multiple of 4)
+constexpr int Q8_RAW_STAGE = Q8_RAW_INST * 256;        // 20480 B
+static_assert(Q8_RAW_INST * 64 >= Q8_RAW_DW, "raw tile coverage");
+
+template <int NW>
+__device__ __forceinline__ void issue_tile_q8(const uint8_t *__restrict__ rows, int key0,
+                                              int n_rows, uint8_t MLA_LDS *dst) {
+    static_assert(Q8_RAW_INST % NW == 0, "raw copies must split evenly over waves");
+    constexpr int NI = Q8_RAW_INST / NW;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const uint32_t *src = (const uint32_t *)rows;
+    const int64_t base = (int64_t)key0 * (fl::Q8_RB / 4);
+    const int64_t last = (int64_t)n_rows * (fl::Q8_RB / 4) - 1;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int inst = w * NI + i;
+        int64_t g = base + inst * 64 + l;
+        if (g > last) g = last;
+        __builtin_amdgcn_global_load_lds((const void *)(src + g),
+                                         (void MLA_LDS *)(dst + inst * 256), 4, 0, 0);
+    }
+}
+
+// Number of async-copy instructions a wave issues per Q8_0 tile (for vmcnt waits).
+template <int NW> __host__ __device__ constexpr int q8_inst_per_wave() {
+    return Q8_RAW_INST / NW;
+}
+
+// Dequantise the raw Q8_0 tile (LDS) into the bf16 tile layout (LDS).  Task = (row,
+// block of 32 values); rows with key0 + k >= n_rows are written as zeros.
+template <int NW>
+__device__ __forceinline__ void dequant_tile_q8(const uint8_t MLA_LDS *raw, int key0, int n_rows,
+                                                uint8_t MLA_LDS *dst) {
+    constexpr int NB = fl::W / 32;  // 18 blocks per row
+    for (int task = threadIdx.x; task < fl::NK * NB; task += 64 * NW) {
+        const int k = task / NB, b = task % NB;
+        const int off = k * fl::Q8_RB + b * 34;       // block start, 2-byte aligned
+        const int a0 = off & ~3, sh = (off & 2) * 8;  // dword-aligned window
+        uint32_t wv[10];
+#pragma unroll
+        for (int i = 0; i < 10; ++i) {
+            const int o = a0 + 4 * i;
+            wv[i] = (o < fl::Q8_TILE_BYTES) ? *(const uint32_t MLA_LDS *)(raw + o) : 0u;
+        }
+        // bytes starting at `off`: shift the window right by sh bits
+        uint32_t bb[9];
+#pragma unroll
+        for (int i = 0; i < 9; ++i)
+            bb[i] = sh ? ((wv[i] >> 16) | (wv[i + 1] << 16)) : wv[i];
+        const bool valid = (key0 + k) < n_rows;
+        const float d = valid ? (float)__builtin_bit_cast(_Float16, (uint16_t)(bb[0] & 0xFFFF)) : 0.0f;
+        // codes: bytes 2..33 of the block = bb[0]>>16 .. bb[8]&0xFFFF
+        bf16 v[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int byte = 2 + i;
+            const uint32_t word = bb[byte >> 2];
+            const int8_t q = (int8_t)((word >> ((byte & 3) * 8)) & 0xFF);
+            v[i] = f2bf(d * (float)q);
+        }
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int c = b * 4 + qq;
+            uint8_t MLA_LDS *p = dst + k * fl::RB + ((c ^ fswz(k)) * 16);
+            bf16x8 t;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t[e] = v[qq * 8 + e];
+            *(bf16x8 MLA_LDS *)p = t;
+        }
+    }
+}
+
+// Per-wave attention state and the tile computation.
+struct WaveState {
+    bf16x8 q[36];     // Q^T fragments: lane l holds row l%32, dims kk*16 + (l/32)*8 .. +7
+    f32x16 o[16];     // O^T accumulators: block nb covers latent columns nb*32 .. nb*32+31
+    float m;          // frozen reference max of the row (scaled, log2 domain)
+    float lsum;       // this lane's share of the softmax denominator
+    bool bad;         // a score exceeded m + FREEZE_LIMIT: this pass is discarded
+};
+
+// One tile: keys key0 .. key0+31 in LDS stage `t`.  Keys with index > lim are masked.
+__device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t MLA_LDS *t, int key0,
+                                            int lim, float sc) {
+    const int l = threadIdx.x & 63;
+    const int hi = l >> 5;
+// ---- S^T = K Q^T.  Chunk (2kk + hi) ^ swz(k) = 8*(kk/4) + ((2*(kk%4) + hi) ^ swz(k)):
+    // four lane-dependent bases plus compile-time offsets.
+    f32x16 s, s1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        s[e] = 0.0f;
+        s1[e] = 0.0f;
+    }
+    {
+        const int k = l & 31;
+        const int sw = fswz(k);
+        const uint8_t MLA_LDS *rowp = t + k * fl::RB;
+        const uint8_t MLA_LDS *kb[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) kb[b] = rowp + (((2 * b + hi) ^ sw) * 16);
+#pragma unroll
+        for (int kk = 0; kk < 36; kk += 2) {
+            const bf16x8 a0 = *(const bf16x8 MLA_LDS *)(kb[kk & 3] + (kk >> 2) * 128);
+            const bf16x8 a1 = *(const bf16x8 MLA_LDS *)(kb[(kk + 1) & 3] + ((kk + 1) >> 2) * 128);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, st.q[kk], s, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, st.q[kk + 1], s1, 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] += s1[e];
+    // ---- softmax: lane holds row l%32, keys (e/4)*8 + hi*4 + e%4
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int key = key0 + (e >> 2) * 8 + hi * 4 + (e & 3);
+        float v = s[e] * sc;
+        v = (key <= lim) ? v : -INFINITY;
+        s[e] = v;
+        tmax = fmaxf(tmax, v);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    if (st.m == -INFINITY) {
+        st.m = tmax;  // first visible keys of this row (o and lsum are still zero)
+    } else if (tmax > st.m + fl::FREEZE_LIMIT || st.bad) {
+        st.bad = true;
+        st.m = fmaxf(st.m, tmax);  // track the true max for the repeated pass
+    }
+    const float mu = (st.m == -INFINITY) ? 0.0f : st.m;
+    bf16x8 p[2];
+    float psum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const bf16 pb = f2bf(__builtin_amdgcn_exp2f(s[e] - mu));
+        p[e >> 3][e & 7] = pb;
+        psum += bf2f(pb);
+    }
+    st.lsum += psum;
+    // ---- O^T += V^T P^T  (two k-steps of 16 keys, 16 column blocks of 32)
+    const int G = l >> 4, lam = l & 15;
+    const int kin = (G >> 1) * 4 + (lam >> 2);            // key within an 8-key group
+    const int colb = (G & 1) * 16 + 4 * (lam & 3);         // column within a 32-column block
+    // rows ks*16 + kin have swizzle kin, rows ks*16 + 8 + kin have swizzle kin ^ 1.
+    // Chunk (4nb + c3) ^ sw = 8*(nb/2) + ((4*(nb%2) + c3) ^ sw): bases per (row half, nb%2).
+    const int sw0 = fswz(kin), sw1 = fswz(kin + 8);
+    const int c3 = colb >> 3, cb = (colb & 7) * 2;
+    const uint8_t MLA_LDS *r0 = t + kin * fl::RB;
+    const uint8_t MLA_LDS *r1 = r0 + 8 * fl::RB;
+    const uint8_t MLA_LDS *vb[2][2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        vb[0][par] = r0 + (((4 * par + c3) ^ sw0) * 16) + cb;
+        vb[1][par] = r1 + (((4 * par + c3) ^ sw1) * 16) + cb;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) {
+            const int off = ks * 16 * fl::RB + (nb >> 1) * 128;
+            const bf16x8 a = tr_pair(vb[0][nb & 1] + off, vb[1][nb & 1] + off);
+            st.o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[ks], st.o[nb], 0, 0, 0);
+        }
+    }
+}
+
+// Rows that are not valid load a valid row's query instead (their keys are all masked,
+// so their scores never reach the softmax).
+__device__ __forceinline__ void load_q(WaveState &st, const bf16 *__restrict__ qrow) {
+    const int hi = (threadIdx.x & 63) >> 5;
+    const bf16 *p = qrow + hi * 8;
+#pragma unroll
+    for (int kk = 0; kk < 36; ++kk) st.q[kk] = *(const bf16x8 *)(p + kk * 16);
+}
+
+__device__ __forceinline__ void init_acc(WaveState &st, float m0) {
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st.o[nb][e] = 0.0f;
+    st.m = m0;
+    st.lsum = 0.0f;
+    st.bad = false;
+}
+
+// Stream keys [kbeg, kend) of `rows` (bf16 or Q8_0) through LDS and attend every tile.
+template <int NW, int NS, bool Q8>
+__device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
+                                            const uint8_t *__restrict__ rows, int n_rows,
+                                            int kbeg, int kend, int lim, float sc) {
+    if (kend <= kbeg) return;
+    const int ntiles = (kend - kbeg + fl::NK - 1) / fl::NK;
+    if constexpr (!Q8) {
+        constexpr int PER = fl::TILE_CH / (64 * NW);
+        const int last = n_rows - 1;
+#pragma unroll
+        for (int s = 0; s < NS - 1; ++s)
+            if (s < ntiles) issue_tile_bf16<NW>(rows, kbeg + s * fl::NK, last, lds + s * fl::TILE_BYTES);
+        for (int ti = 0; ti < ntiles; ++ti) {
+            // wait until this wave's copies for tile ti landed
+            const int after = min(NS - 2, ntiles - 1 - ti);  // tiles issued after ti
+            if (after >= 2) {
+                MLA_WAIT_VMCNT(2 * PER);
+            } else if (after == 1) {
+                MLA_WAIT_VMCNT(PER);
+            } else {
+                MLA_WAIT_VMCNT(0);
+            }
+            __syncthreads();
+            const int nx = ti + NS - 1;
+            if (nx < ntiles)
+                issue_tile_bf16<NW>(rows, kbeg + nx * fl::NK, last, lds + (nx % NS) * fl::TILE_BYTES);
+            attend_tile(st, lds + (ti % NS) * fl::TILE_BYTES, kbeg + ti * fl::NK, lim, sc);
+        }
+        __syncthreads();
+    } else {
+        // raw Q8_0 stages (2) after the bf16 stages (2)
+        uint8_t MLA_LDS *raw = lds + 2 * fl::TILE_BYTES;  // two raw stages of Q8_RAW_STAGE
+        constexpr int PER = q8_inst_per_wave<NW>();
+        (void)PER;
+        issue_tile_q8<NW>(rows, kbeg, n_rows, raw);
+        if (ntiles > 1) issue_tile_q8<NW>(rows, kbeg + fl::NK, n_rows, raw + Q8_RAW_STAGE);
+        if (ntiles > 1) {
+            MLA_WAIT_VMCNT(PER);
+        } else {
+            MLA_WAIT_VMCNT(0);
+        }
+        __syncthreads();
+        dequant_tile_q8<NW>(raw, kbeg, n_rows, lds);
+        __syncthreads();
+        for (int ti = 0; ti < ntiles; ++ti) {
+            if (ti + 2 < ntiles)
+                issue_tile_q8<NW>(rows, kbeg + (ti + 2) * fl::NK, n_rows,
+                                  raw + (ti % 2) * Q8_RAW_STAGE);
+            attend_tile(st, lds + (ti % 2) * fl::TILE_BYTES, kbeg + ti * fl::NK, lim, sc);
+            if (ti + 1 < ntiles) {
+                if (ti + 2 < ntiles) {
+                    MLA_WAIT_VMCNT(PER);
+                } else {
+                    MLA_WAIT_VMCNT(0);
+                }
+                __syncthreads();
+                dequant_tile_q8<NW>(raw + ((ti + 1) % 2) * Q8_RAW_STAGE, kbeg + (ti + 1) * fl::NK,
+                                    n_rows, lds + ((ti + 1) % 2) * fl::TILE_BYTES);
+                __syncthreads();
+            }
+        }
+    }
+}
+
+// Runs the key stream for the workgroup, repeating it once if any row was marked.
+template <int NW, int NS, bool Q8>
+__device__ __forceinline__ void attend_range(WaveState &st, uint8_t MLA_LDS *lds, int *flag,
+                                             const uint8_t *__restrict__ rows, int n_rows,
+                                             int kbeg, int kend, int lim, float sc) {
+    float m0 = -INFINITY;
+    for (int pass = 0; pass < 2; ++pass) {
+        init_acc(st, m0);
+        stream_keys<NW, NS, Q8>(st, lds, rows, n_rows, kbeg, kend, lim, sc);
+        if (threadIdx.x == 0) *flag = 0;
+        __syncthreads();
+        if (__builtin_amdgcn_ballot_w64(st.bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1);
+        __syncthreads();
+        const int again = *flag;
+        __syncthreads();
+        if (!again) break;
+        m0 = st.m;  // marked rows: their true max; others: unchanged reference
+    }
+}
+
+// Final normalisation.  Returns lse (natural log) for this lane's row; writes o / l into
+// the caller's store functor per 4 consecutive columns.
+template <typename Store>
+__device__ __forceinline__ float finish(WaveState &st, Store store) {
+    const int l = threadIdx.x & 63, hi = l >> 5;
+    const float lt = st.lsum + __shfl_xor(st.lsum, 32);
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int col = nb * 32 + g * 8 + hi * 4;
+            store(col, st.o[nb][g * 4 + 0] * inv, st.o[nb][g * 4 + 1] * inv,
+                  st.o[nb][g * 4 + 2] * inv, st.o[nb][g * 4 + 3] * inv);
+        }
+    return lt > 0.0f ? (st.m + __log2f(lt)) * fl::LN2 : -INFINITY;
+}
+
+constexpr int PF_NW = 4, PF_NS = 4;
+
+// Prefill.  Rows are the flattened (token, head-in-chunk) pairs of all head chunks:
+// block -> (chunk, group of 128 rows), heavy (late) groups first, consecutive groups
+// on the same XCD so that co-running workgroups stream the same cache rows.
+__global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
+    const bf16 *__restrict__ q_cat, const int32_t *__restrict__ pos, int T, int H,
+    const uint8_t *__restrict__ cache, int n_kv, int hc, int n_groups, int n_chunks, float sc,
+    bf16 *__restrict__ o_lat, float *__restrict__ lse) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+    uint8_t MLA_LDS *lds = (uint8_t MLA_LDS *)lds_raw;
+    __shared__ int kmax_sh, flag_sh;
+    const int total = n_groups * n_chunks;
+    // XCD-aware bijection: blocks bid, bid+8, ... run on one XCD; give each XCD a
+    // contiguous range of logical indices.
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, kx = bid >> 3;
+    const int q = total >> 3, rem = total & 7;
+    const int logical = xcd * q + min(xcd, rem) + kx;
+    const int g2 = total - 1 - logical;  // heavy first
+    const int chunk = g2 / n_groups, grp = g2 % n_groups;
+
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int rows_total = T * hc;
+    const int r = grp * (32 * PF_NW) + w * 32 + (l & 31);
+    const bool valid = r < rows_total;
+    const int t = valid ? r / hc : 0;
+    const int h = chunk * hc + (valid ? r % hc : 0);
+    int lim = -1;
+    if (valid) lim = min(pos[t], n_kv - 1);
+
+    if (threadIdx.x == 0) kmax_sh = -1;
+    __syncthreads();
+    {
+        // max visible key over the group's rows
+        int v = lim;
+        for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+        if (l == 0) atomicMax(&kmax_sh, v);
+    }
+    WaveState st;
+    load_q(st, q_cat + ((int64_t)t * H + h) * fl::W);
+    __syncthreads();
+    const int kend = kmax_sh + 1;
+    attend_range<PF_NW, PF_NS, false>(st, lds, &flag_sh, cache, n_kv, 0, kend, lim, sc);
+    bf16 *dst = o_lat + ((int64_t)t * H + h) * fl::R;
+    const float ls = finish(st, [&](int col, float a, float b, float c, float d) {
+        if (valid) {
+            bf16x4 v = {f2bf(a), f2bf(b), f2bf(c), f2bf(d)};
+            *(bf16x4 *)(dst + col) = v;
+        }
+    });
+    if (lse && valid && l < 32) lse[(int64_t)t * H + h] = ls;
+}
+
+hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int T, int H,
+                                     const bf16 *cache, int n_kv, int hc, float scale,
+                                     bf16 *o_lat, float *lse, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    const int rows = T * hc;
+    const int n_groups = (rows + 32 * PF_NW - 1) / (32 * PF_NW);
+    const int n_chunks = H / hc;
+    const size_t shm = (size_t)PF_NS * fl::TILE_BYTES;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)flash_prefill_bf16_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(flash_prefill_bf16_kernel, dim3(n_groups * n_chunks), dim3(64 * PF_NW), shm,
+                       st, q_cat, pos, T, H, (const uint8_t *)cache, n_kv, hc, n_groups, n_chunks,
+                       scale * fl::LOG2E, o_lat, lse);
+    return hipGetLastError();
+}
+
+constexpr int DC_NW = 4, DC_NS = 4;
+
+// Decode partials.  Block (split s, sequence b, head group hg); rows = heads
+// hg*128 .. +127 of sequence b; keys [s*split_len, min((s+1)*split_len, n_kv[b])).
+template <bool Q8>
+__global__ __launch_bounds__(64 * DC_NW, 1) void flash_decode_kernel(
+    const bf16 *__restrict__ q_cat, int H, const uint8_t *__restrict__ cache,
+    int64_t seq_stride, const int32_t *__restrict__ n_kv, int n_kv_max, int n_splits,
+    int split_len, float sc, float *__restrict__ part_o, float *__restrict__ part_lse) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+    uint8_t MLA_LDS *lds = (uint8_t MLA_LDS *)lds_raw;
+    const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int h = hg * (32 * DC_NW) + w * 32 + (l & 31);
+    const bool valid = h < H;
+    const int nk = min(n_kv[b], n_kv_max);  // rows past n_kv_max are never read
+    const int k0 = s * split_len;
+    const int k1 = min(k0 + split_len, nk);
+    WaveState st;
+    load_q(st, q_cat + ((int64_t)b * H + (valid ? h : 0)) * fl::W);
+    const uint8_t *rows = cache + b * seq_stride;
+    __shared__ int flag_sh;
+    attend_range<DC_NW, DC_NS, Q8>(st, lds, &flag_sh, rows, nk, k0, k1, k1 - 1, sc);
+    const int64_t pi = ((int64_t)b * n_splits + s) * H + h;
+    float *dst = part_o + pi * fl::R;
+    const float ls = finish(st, [&](int col, float a, float b_, float c, float d) {
+        if (valid) {
+            f32x4 v = {a, b_, c, d};
+            *(f32x4 *)(dst + col) = v;
+        }
+    });
+    if (valid && l < 32) part_lse[pi] = ls;
+}
+
+hipError_t launch_flash_decode_bf16(const bf16 *q_cat, const void *cache, int cache_q8,
+                                    int64_t seq_stride_bytes, const int32_t *n_kv, int n_kv_max,
+                                    int B, int H,
+                                    int n_splits, int split_len, float scale, float *part_o,
+                                    float *part_lse, hipStream_t st) {
+    const int hgroups = (H + 32 * DC_NW - 1) / (32 * DC_NW);
+    dim3 grid(n_splits, B, hgroups);
+    if (cache_q8) {
+        const size_t shm = 2 * (size_t)fl::TILE_BYTES + 2 * (size_t)Q8_RAW_STAGE;
+        static bool attr_set = false;
+        if (!attr_set) {
+            hipError_t e = hipFuncSetAttribute((const void *)flash_decode_kernel<true>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+        hipLaunchKernelGGL(flash_decode_kernel<true>, grid, dim3(64 * DC_NW), shm, st, q_cat, H,
+                           (const uint8_t *)cache, seq_stride_bytes, n_kv, n_kv_max, n_splits, split_len,
+                           scale * fl::LOG2E, part_o, part_lse);
+    } else {
+        const size_t shm = (size_t)DC_NS * fl::TILE_BYTES;
+        static bool attr_set = false;
+        if (!attr_set) {
+            hipError_t e = hipFuncSetAttribute((const void *)flash_decode_kernel<false>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+        hipLaunchKernelGGL(flash_decode_kernel<false>, grid, dim3(64 * DC_NW), shm, st, q_cat, H,
+                           (const uint8_t *)cache, seq_stride_bytes, n_kv, n_kv_max, n_splits, split_len,
+                           scale * fl::LOG2E, part_o, part_lse);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,367 @@
+// Generic (non-MFMA) kernels: the float32 path for any layer dims, the RoPE part of
+// query absorption, the split-KV log-sum-exp combine, and Q8_0 (de)quantisation.
+#include "common.h"
+
+#include <math.h>
+
+namespace mla {
+
+// ---------------------------------------------------------------- NT GEMM (f32)
+// C[b][m][n] = sum_k A[b][m][k] * B[b][n][k]; 64x64 tiles, 256 threads, 4x4 outputs
+// per thread, K staged through LDS in steps of 16.
+constexpr int SG_TM = 64, SG_TN = 64, SG_TK = 16;
+
+__global__ __launch_bounds__(256) void gemm_nt_f32_kernel(const float *__restrict__ A,
+                                                          const float *__restrict__ B,
+                                                          float *__restrict__ C, int M, int N,
+                                                          int K, int64_t lda, int64_t ldb,
+                                                          int64_t ldc, int64_t sA, int64_t sB,
+                                                          int64_t sC) {
+    __shared__ float As[SG_TK][SG_TM + 4];
+    __shared__ float Bs[SG_TK][SG_TN + 4];
+    const int bz = blockIdx.z;
+    A += bz * sA;
+    B += bz * sB;
+    C += bz * sC;
+    const int m0 = blockIdx.y * SG_TM, n0 = blockIdx.x * SG_TN;
+    const int tid = threadIdx.x;
+    const int tm = (tid / 16) * 4, tn = (tid % 16) * 4;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < K; k0 += SG_TK) {
+        for (int e = tid; e < SG_TM * SG_TK; e += 256) {
+            int r = e / SG_TK, kk = e % SG_TK;
+            int gm = m0 + r, gk = k0 + kk;
+            As[kk][r] = (gm < M && gk < K) ? A[gm * lda + gk] : 0.0f;
+            int gn = n0 + r;
+            Bs[kk][r] = (gn < N && gk < K) ? B[gn * ldb + gk] : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < SG_TK; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a[i] = As[kk][tm + i];
+                b[i] = Bs[kk][tn + i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int gm = m0 + tm + i, gn = n0 + tn + j;
+            if (gm < M && gn < N) C[gm * ldc + gn] = acc[i][j];
+        }
+}
+
+hipError_t launch_gemm_nt_f32(const float *A, const float *B, float *C, int M, int N, int K,
+                              int64_t lda, int64_t ldb, int64_t ldc, int batch, int64_t sA,
+                              int64_t sB, int64_t sC, hipStream_t st) {
+    if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
+    dim3 grid((N + SG_TN - 1) / SG_TN, (M + SG_TM - 1) / SG_TM, batch);
+    hipLaunchKernelGGL(gemm_nt_f32_kernel, grid, dim3(256), 0, st, A, B, C, M, N, K, lda, ldb,
+                       ldc, sA, sB, sC);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ query RoPE
+// q_cat[t][h][R + 2i .. R + 2i+1] = rotation of (q_rope[t][h][2i], q_rope[t][h][2i+1]) by
+// pos[t] * base^(-2i/Dr).  Angles, sines and cosines in double; one block per token.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_q_kernel(const T *__restrict__ q_rope,
+                                                     const int32_t *__restrict__ pos,
+                                                     T *__restrict__ q_cat, int H, int R, int Dr,
+                                                     float base) {
+    extern __shared__ double cs[];  // [Dr/2][2]
+    const int t = blockIdx.x;
+    const int half = Dr / 2;
+    const double p = (double)pos[t];
+    for (int i = threadIdx.x; i < half; i += blockDim.x) {
+        double theta = pow((double)base, -2.0 * (double)i / (double)Dr);
+        double ang = p * theta;
+        cs[2 * i] = cos(ang);
+        cs[2 * i + 1] = sin(ang);
+    }
+    __syncthreads();
+    const int W = R + Dr;
+    for (int e = threadIdx.x; e < H * half; e += blockDim.x) {
+        int h = e / half, i = e % half;
+        const T *src = q_rope + ((int64_t)t * H + h) * Dr + 2 * i;
+        double a = (double)ld_f(src), b = (double)ld_f(src + 1);
+        double c = cs[2 * i], s = cs[2 * i + 1];
+        T *dst = q_cat + ((int64_t)t * H + h) * W + R + 2 * i;
+        st_f(dst, (float)(a * c - b * s));
+        st_f(dst + 1, (float)(a * s + b * c));
+    }
+}
+
+template <typename T>
+hipError_t launch_rope_q(const T *q_rope, const int32_t *pos, T *q_cat, int T_, int H, int R,
+                         int Dr, float base, hipStream_t st) {
+    if (T_ <= 0) return hipSuccess;
+    size_t shm = sizeof(double) * (size_t)Dr;
+    hipLaunchKernelGGL(rope_q_kernel<T>, dim3(T_), dim3(256), shm, st, q_rope, pos, q_cat, H, R,
+                       Dr, base);
+    return hipGetLastError();
+}
+template hipError_t launch_rope_q<float>(const float *, const int32_t *, float *, int, int, int,
+                                         int, float, hipStream_t);
+template hipError_t launch_rope_q<bf16>(const bf16 *, const int32_t *, bf16 *, int, int, int,
+                                        int, float, hipStream_t);
+
+// ------------------------------------------------------- SIMT flash attention (f32)
+// One wave per (query row, head).  Keys are taken 64 at a time: lane i scores key
+// j0+i (dot product over the W-wide row against the query held in LDS), the wave
+// updates a running max / sum (online softmax), and each lane accumulates output
+// columns lane, lane+64, ... of the latent weighted sum.
+constexpr int SF_WAVES = 4;
+constexpr int SF_MAXR = 16;  // R <= 64 * SF_MAXR
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Attends query row q (W floats in LDS) over cache rows [k0, k1) (row stride W).
+// Returns normalised output in o[] (lane's columns) and lse (natural log; -inf if
+// the range is empty).
+__device__ void simt_attend(const float *qs, const float *__restrict__ rows, int k0, int k1,
+                            int R, int W, float scale, float *o, float &lse_out) {
+    const int lane = threadIdx.x & 63;
+    const int nc = (R + 63) / 64;
+    float m = -INFINITY, l = 0.0f;
+    for (int c = 0; c < SF_MAXR; ++c) o[c] = 0.0f;
+    for (int j0 = k0; j0 < k1; j0 += 64) {
+        const int j = j0 + lane;
+        float s = -INFINITY;
+        if (j < k1) {
+            const float *row = rows + (int64_t)j * W;
+            float acc = 0.0f;
+            for (int e = 0; e < W; ++e) acc = fmaf(qs[e], row[e], acc);
+            s = acc * scale;
+        }
+        const float cmax = wave_max(s);
+        const float mnew = fmaxf(m, cmax);
+        const float alpha = (m == -INFINITY) ? 0.0f : expf(m - mnew);
+        const float p = (j < k1) ? expf(s - mnew) : 0.0f;
+        l = l * alpha + wave_sum(p);
+        for (int c = 0; c < SF_MAXR; ++c) o[c] *= alpha;
+        m = mnew;
+        const int cnt = min(64, k1 - j0);
+        for (int i = 0; i < cnt; ++i) {
+            const float pi = __shfl(p, i);
+            const float *row = rows + (int64_t)(j0 + i) * W;
+            for (int c = 0; c < nc; ++c) {
+                int col = c * 64 + lane;
+                if (col < R) o[c] = fmaf(pi, row[col], o[c]);
+            }
+        }
+    }
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    for (int c = 0; c < SF_MAXR; ++c) o[c] *= inv;
+    lse_out = l > 0.0f ? m + logf(l) : -INFINITY;
+}
+
+__global__ __launch_bounds__(256) void flash_simt_prefill_kernel(
+    const float *__restrict__ q_cat, const int32_t *__restrict__ pos, int T, int H, int R, int W,
+    const float *__restrict__ cache, int n_kv, int h0, int hc, float scale,
+    float *__restrict__ o_lat, float *__restrict__ lse) {
+    extern __shared__ float qsh[];  // [SF_WAVES][W]
+    const int w = threadIdx.x / 64, lane = threadIdx.x & 63;
+    const int row = blockIdx.x * SF_WAVES + w;  // flattened (t, head-in-chunk)
+    if (row >= T * hc) return;
+    const int t = row / hc, h = h0 + row % hc;
+    float *qs = qsh + w * W;
+    const float *q = q_cat + ((int64_t)t * H + h) * W;
+    for (int e = lane; e < W; e += 64) qs[e] = q[e];
+    __builtin_amdgcn_wave_barrier();
+    int k1 = min(pos[t] + 1, n_kv);
+    if (k1 < 0) k1 = 0;
+    float o[SF_MAXR], ls;
+    simt_attend(qs, cache, 0, k1, R, W, scale, o, ls);
+    float *dst = o_lat + ((int64_t)t * H + h) * R;
+    for (int c = 0; c < SF_MAXR; ++c) {
+        int col = c * 64 + lane;
+        if (col < R) dst[col] = o[c];
+    }
+    if (lse && lane == 0) lse[(int64_t)t * H + h] = ls;
+}
+
+hipError_t launch_flash_simt_prefill(const mla_dims &d, const float *q_cat, const int32_t *pos,
+                                     int T, const float *cache, int n_kv, int h0, int hc,
+                                     float *o_lat, float *lse, hipStream_t st) {
+    const int W = d.kv_lora_rank + d.qk_rope;
+    const int rows = T * hc;
+    if (rows <= 0) return hipSuccess;
+    dim3 grid((rows + SF_WAVES - 1) / SF_WAVES);
+    hipLaunchKernelGGL(flash_simt_prefill_kernel, grid, dim3(64 * SF_WAVES),
+                       sizeof(float) * SF_WAVES * W, st, q_cat, pos, T, d.n_head,
+                       d.kv_lora_rank, W, cache, n_kv, h0, hc, d.scale, o_lat, lse);
+    return hipGetLastError();
+}
+
+// Decode partials: block (row group, split, sequence).  part_o [B][S][H][R] (normalised
+// within the split), part_lse [B][S][H].
+__global__ __launch_bounds__(256) void flash_simt_decode_kernel(
+    const float *__restrict__ q_cat, int H, int R, int W, const float *__restrict__ cache,
+    int64_t seq_stride, const int32_t *__restrict__ n_kv, int n_kv_max, int n_splits,
+    int split_len, float scale, float *__restrict__ part_o, float *__restrict__ part_lse) {
+    extern __shared__ float qsh[];
+    const int w = threadIdx.x / 64, lane = threadIdx.x & 63;
+    const int h = blockIdx.x * SF_WAVES + w;
+    const int s = blockIdx.y, b = blockIdx.z;
+    if (h >= H) return;
+    float *qs = qsh + w * W;
+    const float *q = q_cat + ((int64_t)b * H + h) * W;
+    for (int e = lane; e < W; e += 64) qs[e] = q[e];
+    __builtin_amdgcn_wave_barrier();
+    const int nk = min(n_kv[b], n_kv_max);  // rows past n_kv_max are never read
+    const int k0 = s * split_len, k1 = min(k0 + split_len, nk);
+    float o[SF_MAXR], ls;
+    simt_attend(qs, cache + b * seq_stride, k0, max(k0, k1), R, W, scale, o, ls);
+    const int64_t pi = ((int64_t)b * n_splits + s) * H + h;
+    float *dst = part_o + pi * R;
+    for (int c = 0; c < SF_MAXR; ++c) {
+        int col = c * 64 + lane;
+        if (col < R) dst[col] = o[c];
+    }
+    if (lane == 0) part_lse[pi] = ls;
+}
+
+hipError_t launch_flash_simt_decode(const mla_dims &d, const float *q_cat, const float *cache,
+                                    int64_t seq_stride_elems, const int32_t *n_kv, int n_kv_max,
+                                    int B,
+                                    int n_splits, int split_len, float *part_o, float *part_lse,
+                                    hipStream_t st) {
+    const int W = d.kv_lora_rank + d.qk_rope;
+    dim3 grid((d.n_head + SF_WAVES - 1) / SF_WAVES, n_splits, B);
+    hipLaunchKernelGGL(flash_simt_decode_kernel, grid, dim3(64 * SF_WAVES),
+                       sizeof(float) * SF_WAVES * W, st, q_cat, d.n_head, d.kv_lora_rank, W,
+                       cache, seq_stride_elems, n_kv, n_kv_max, n_splits, split_len, d.scale, part_o,
+                       part_lse);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ split-KV combine
+// lse = log sum_s exp(lse_s); o = sum_s exp(lse_s - lse) o_s.  One block per (b, h);
+// splits with lse_s = -inf contribute nothing.
+template <typename OT>
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ part_o,
+                                                      const float *__restrict__ part_lse, int H,
+                                                      int R, int S, OT *__restrict__ o_lat,
+                                                      float *__restrict__ lse) {
+    extern __shared__ float wsh[];  // [S]
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh % H;
+    float mx = -INFINITY;
+    for (int s = 0; s < S; ++s) mx = fmaxf(mx, part_lse[((int64_t)b * S + s) * H + h]);
+    float sum = 0.0f;
+    for (int s = threadIdx.x; s < S; s += blockDim.x) {
+        float ls = part_lse[((int64_t)b * S + s) * H + h];
+        wsh[s] = (mx == -INFINITY) ? 0.0f : expf(ls - mx);
+    }
+    __syncthreads();
+    for (int s = 0; s < S; ++s) sum += wsh[s];
+    const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
+    for (int c = threadIdx.x; c < R; c += blockDim.x) {
+        float acc = 0.0f;
+        for (int s = 0; s < S; ++s) {
+            float wgt = wsh[s];
+            if (wgt != 0.0f) acc = fmaf(wgt, part_o[(((int64_t)b * S + s) * H + h) * R + c], acc);
+        }
+        st_f(o_lat + ((int64_t)b * H + h) * R + c, acc * inv);
+    }
+    if (lse && threadIdx.x == 0) lse[(int64_t)b * H + h] = sum > 0.0f ? mx + logf(sum) : -INFINITY;
+}
+
+template <typename OT>
+hipError_t launch_combine(const float *part_o, const float *part_lse, int B, int H, int R,
+                          int n_splits, OT *o_lat, float *lse, hipStream_t st) {
+    hipLaunchKernelGGL(combine_kernel<OT>, dim3(B * H), dim3(256), sizeof(float) * n_splits, st,
+                       part_o, part_lse, H, R, n_splits, o_lat, lse);
+    return hipGetLastError();
+}
+template hipError_t launch_combine<float>(const float *, const float *, int, int, int, int,
+                                          float *, float *, hipStream_t);
+template hipError_t launch_combine<bf16>(const float *, const float *, int, int, int, int, bf16 *,
+                                         float *, hipStream_t);
+
+// ------------------------------------------------------------------------ Q8_0
+// One thread per 32-value block.  Block layout: binary16 scale (little endian) then
+// 32 int8 codes; blocks are 34 bytes, so scales sit at 2-byte alignment.
+__global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float *__restrict__ x,
+                                                            uint8_t *__restrict__ rows,
+                                                            int64_t n_blocks, int nb_row,
+                                                            int width) {
+    const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (blk >= n_blocks) return;
+    const int64_t r = blk / nb_row;
+    const int b = (int)(blk % nb_row);
+    const float *v = x + r * width + (int64_t)b * 32;
+    float amax = 0.0f;
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const float d = amax / 127.0f;
+    const _Float16 hd = (_Float16)d;
+    uint8_t *out = rows + r * (int64_t)nb_row * 34 + (int64_t)b * 34;
+    *(uint16_t *)out = __builtin_bit_cast(uint16_t, hd);
+    for (int i = 0; i < 32; i += 2) {
+        int q0 = 0, q1 = 0;
+        if (d != 0.0f) {
+            q0 = (int)fminf(fmaxf(roundf(v[i] / d), -127.0f), 127.0f);
+            q1 = (int)fminf(fmaxf(roundf(v[i + 1] / d), -127.0f), 127.0f);
+        }
+        *(uint16_t *)(out + 2 + i) = (uint16_t)((q0 & 0xFF) | ((q1 & 0xFF) << 8));
+    }
+}
+
+__global__ __launch_bounds__(256) void dequant_q8_0_kernel(const uint8_t *__restrict__ rows,
+                                                           float *__restrict__ out,
+                                                           int64_t n_blocks, int nb_row,
+                                                           int width) {
+    const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (blk >= n_blocks) return;
+    const int64_t r = blk / nb_row;
+    const int b = (int)(blk % nb_row);
+    const uint8_t *in = rows + r * (int64_t)nb_row * 34 + (int64_t)b * 34;
+    const float d = (float)__builtin_bit_cast(_Float16, *(const uint16_t *)in);
+    float *o = out + r * width + (int64_t)b * 32;
+    for (int i = 0; i < 32; i += 2) {
+        uint16_t pr = *(const uint16_t *)(in + 2 + i);
+        o[i] = d * (float)(int8_t)(pr & 0xFF);
+        o[i + 1] = d * (float)(int8_t)(pr >> 8);
+    }
+}
+
+hipError_t launch_quantize_q8_0(const float *x, uint8_t *rows, int64_t n_rows, int width,
+                                hipStream_t st) {
+    const int nb = width / 32;
+    const int64_t n = n_rows * nb;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(quantize_q8_0_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       x, rows, n, nb, width);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_q8_0(const uint8_t *rows, float *out, int64_t n_rows, int width,
+                               hipStream_t st) {
+    const int nb = width / 32;
+    const int64_t n = n_rows * nb;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(dequant_q8_0_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       rows, out, n, nb, width);
+    return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,168 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) absorbed Multi-head Latent Attention library.
+ *
+ * The four calls follow the order in which the page "ik_llama.cpp MLA matrix
+ * absorption" (czykbl.com/news/93068) applies the absorbed method, section 4:
+ * project q_nope through wk_b into the latent space (mla_absorb_q), attend
+ * directly on the latent cache (mla_attn_prefill / mla_attn_decode), then
+ * decompress late through wv_b and apply wo (mla_out_proj).
+ *
+ * Conventions for every call
+ *   - Pointers are device pointers unless stated otherwise.  The caller owns every
+ *     buffer (weights, cache, activations, outputs, workspace); the library never
+ *     allocates on these paths and never frees caller memory.
+ *   - Tensors are dense, row-major, innermost dimension last.  Element type is given
+ *     by the mla_dtype arguments.  Device pointers must be 16-byte aligned.
+ *   - Launches are asynchronous on `stream` (a hipStream_t; NULL = default stream).
+ *     Nothing synchronises.
+ *   - Every call validates its arguments before launching anything and returns an
+ *     mla_status; nothing aborts or exits.  A shape or dtype a kernel does not
+ *     implement returns MLA_ERR_UNSUPPORTED: no call silently switches to another
+ *     path.  A HIP launch error returns MLA_ERR_HIP.
+ *
+ * Notation: H heads, R = kv_lora_rank, Dn = qk_nope, Dr = qk_rope, Dv = v_head,
+ * D = d_model, W = R + Dr (latent cache row width), T query tokens, N cached rows.
+ *
+ * Data types
+ *   MLA_F32  : activations, weights, cache and o_lat in float32 (any dims).
+ *   MLA_BF16 : activations, weights, cache and o_lat in bfloat16, float32
+ *              accumulation; attention kernels need R = 512, Dr = 64 (the
+ *              DeepSeek latent shape: K 576 / V 512 / rope 64, page "ik_llama.cpp
+ *              PR #394", section 3.1).
+ *   MLA_Q8_0 : cache only (attention decode): each 32-value run of a row is a
+ *              34-byte block {binary16 scale d (little endian), int8 q[32]},
+ *              value = d * q.  A 576-wide row is 612 bytes.  Activations bf16.
+ *   lse outputs are always float32.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, odd Dr, bad dtype combination */
+    MLA_ERR_UNSUPPORTED = -2, /* valid request that no kernel implements (see each call) */
+    MLA_ERR_WORKSPACE = -3,   /* decode workspace smaller than mla_decode_workspace_bytes() */
+    MLA_ERR_HIP = -4          /* the HIP runtime reported an error on launch */
+} mla_status;
+
+typedef enum mla_dtype { MLA_F32 = 0, MLA_BF16 = 1, MLA_Q8_0 = 2 } mla_dtype;
+
+/* Layer dimensions.  scale multiplies the score (DeepSeek: 1/sqrt(Dn + Dr));
+ * rope_base is the RoPE frequency base (10000). */
+typedef struct mla_dims {
+    int32_t n_head, kv_lora_rank, qk_nope, qk_rope, v_head, d_model;
+    float scale;
+    float rope_base;
+} mla_dims;
+
+/* K absorption and query RoPE (absorption page, sections 3 and 4).
+ *   q_cat[t][h][0:R]  = sum_d wk_b[h][l][d] * q_nope[t][h][d]   (q_lat; the
+ *                       mul_mat(wk_b, q_nope) of section 4)
+ *   q_cat[t][h][R:W]  = RoPE(q_rope[t][h], pos[t])  -- RoPE is not absorbable
+ *                       (section 3): adjacent pairs (x[2i], x[2i+1]) rotated by
+ *                       pos * rope_base^(-2i/Dr), angles in double precision.
+ * q_nope [T][H][Dn], q_rope [T][H][Dr] (pre-RoPE), pos [T] int32 (device),
+ * wk_b [H][R][Dn] (the split layout ggml {Dn,R,H} of the PR #394 page, section
+ * 3.2), q_cat [T][H][W].  All of dtype act (MLA_F32 or MLA_BF16).
+ * T == 0 is a no-op.  Errors: INVALID_ARG for nulls, T < 0, odd Dr, act Q8_0. */
+int mla_absorb_q(const mla_dims *dims, mla_dtype act, const void *q_nope, const void *q_rope,
+                 const int32_t *pos, const void *wk_b, void *q_cat, int32_t T, void *stream);
+
+/* Causal attention on the latent cache (absorption page, sections 4 and 5).
+ * For each query t and head h, key row j is visible iff j <= pos[t] and j < n_kv:
+ *   s_j   = scale * (q_cat[t][h][0:R] . c_kv[j] + q_cat[t][h][R:W] . k_rope[j])
+ *           (the two-term "move elision" score over the row's adjacent parts)
+ *   o_lat[t][h] = sum_j softmax(s)_j * c_kv[j]       (the latent weighted sum)
+ *   lse[t][h]   = log sum_j exp(s_j)                 (natural log)
+ * Rows with no visible key get o_lat = 0 and lse = -inf.
+ * q_cat [T][H][W] (act), pos [T] int32, kv_cache [n_kv][W] (kv dtype; row j holds the
+ * token at position j, k_rope stored post-RoPE), o_lat [T][H][R] (act), lse [T][H]
+ * float32 or NULL.
+ * scratch_cap_mib is the -amb analogue (absorption page, section 8.3): with
+ * size = T * n_kv * H * 4 bytes (the K x Q intermediate an unfused path would hold),
+ * heads are processed in chunks of mla_heads_per_chunk(H, size, cap) heads.  0 means
+ * unlimited; a value in (0, 128) is raised to 128.  The fused kernel holds no such
+ * intermediate, so the cap only changes the work decomposition: results are
+ * bitwise identical for every cap.
+ * Supported: act == kv == MLA_F32 (any dims), act == kv == MLA_BF16 (R 512, Dr 64).
+ * Errors: INVALID_ARG (nulls, T < 0, n_kv < 1, dtype mix), UNSUPPORTED (Q8_0 cache,
+ * bf16 with other R/Dr). */
+int mla_attn_prefill(const mla_dims *dims, mla_dtype act, mla_dtype kv, const void *q_cat,
+                     const int32_t *pos, int32_t T, const void *kv_cache, int32_t n_kv,
+                     void *o_lat, float *lse, uint32_t scratch_cap_mib, void *stream);
+
+/* Heads per chunk for the -amb rule (absorption page, section 8.3): if
+ * size_mib > cap, the smallest niter >= 2 with n_head % niter == 0 and
+ * size_mib / niter <= cap gives n_head / niter heads per chunk (1 if none does);
+ * cap 0 = unlimited, cap in (0,128) -> 128.  Host-only, never fails (returns
+ * n_head for n_head < 1). */
+int32_t mla_heads_per_chunk(int32_t n_head, double size_mib, uint32_t cap_mib);
+
+/* Workspace bytes mla_attn_decode needs for B sequences of up to n_kv_max rows
+ * with n_splits key splits per sequence (0 = the automatic choice).  Returns 0
+ * for invalid arguments.  Host-only. */
+size_t mla_decode_workspace_bytes(const mla_dims *dims, int32_t B, int32_t n_kv_max,
+                                  int32_t n_splits);
+
+/* The split count mla_attn_decode uses for n_splits == 0.  Host-only. */
+int32_t mla_decode_auto_splits(const mla_dims *dims, mla_dtype kv, int32_t B, int32_t n_kv_max);
+
+/* One decode step per sequence (absorption page, section 8: a separate kernel for
+ * token generation).  Sequence b has n_kv[b] cache rows, its new token is already
+ * appended, so its query (position n_kv[b]-1) sees every row.  The key range
+ * [0, n_kv_max) is cut into n_splits contiguous splits; each split computes a
+ * partial (o_s, lse_s) of the attention above over its rows, and a combine step
+ * merges them:  lse = log sum_s exp(lse_s),  o_lat = sum_s exp(lse_s - lse) o_s.
+ * Splits with no row contribute nothing (lse_s = -inf).
+ * q_cat [B][H][W] (act); kv_cache: sequence b's rows start at byte offset
+ * b * kv_seq_stride_bytes (rows of W values for F32/BF16, of W/32*34 bytes for
+ * Q8_0); n_kv [B] int32 on the device, each in [1, n_kv_max]; o_lat [B][H][R] (act);
+ * lse [B][H] float32 or NULL; workspace of at least
+ * mla_decode_workspace_bytes(dims, B, n_kv_max, n_splits) bytes (device, 16-byte
+ * aligned), contents need not be initialised.
+ * Supported: act == kv == MLA_F32 (any dims); act == MLA_BF16 with kv MLA_BF16 or
+ * MLA_Q8_0 (R 512, Dr 64).
+ * Errors: INVALID_ARG, WORKSPACE, UNSUPPORTED as above. */
+int mla_attn_decode(const mla_dims *dims, mla_dtype act, mla_dtype kv, const void *q_cat,
+                    const void *kv_cache, int64_t kv_seq_stride_bytes, const int32_t *n_kv,
+                    int32_t B, int32_t n_kv_max, int32_t n_splits, void *o_lat, float *lse,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Late V decompression and output projection (absorption page, section 4):
+ *   v[t][h*Dv + d] = sum_l wv_b[h][d][l] * o_lat[t][h][l]     (einsum bhqc,hdc->bhqd)
+ *   out[t][e]      = sum_k wo[e][k] * v[t][k]                  (einsum hdD,bhqd->bqD)
+ * o_lat [T][H][R], wv_b [H][Dv][R] (ggml {R,Dv,H} of the PR #394 page, section 3.2),
+ * wo [D][H*Dv] (heads concatenated as reshape_2d(n_embd_head_v*n_head)),
+ * v_scratch [T][H*Dv] (caller-owned; holds v afterwards), out [T][D]; all act.
+ * Errors: INVALID_ARG (nulls, T < 0, act Q8_0). */
+int mla_out_proj(const mla_dims *dims, mla_dtype act, const void *o_lat, const void *wv_b,
+                 const void *wo, void *v_scratch, void *out, int32_t T, void *stream);
+
+/* Q8_0 helpers (the 8-bit latent cache of the absorption page, section 8.1).
+ * mla_quantize_q8_0: rows [n_rows][width] float32 -> Q8_0 bytes; per 32-block
+ *   amax = max|x|, d = amax/127 (float32), q = round-half-away(x/d) clamped to
+ *   [-127,127] (0 when d == 0), stored scale binary16(d) rounded to nearest even.
+ * mla_dequant_q8_0: Q8_0 bytes -> float32, value = float(d) * q (exact).
+ * width must be a positive multiple of 32 (else INVALID_ARG). */
+int mla_quantize_q8_0(const float *x, void *rows, int64_t n_rows, int32_t width, void *stream);
+int mla_dequant_q8_0(const void *rows, float *out, int64_t n_rows, int32_t width, void *stream);
+
+/* Bytes of one Q8_0 row of `width` values (width/32*34), or -1 if width is not a
+ * positive multiple of 32.  Host-only. */
+int32_t mla_q8_0_row_bytes(int32_t width);
+
+/* Static description of a status code.  Host-only. */
+const char *mla_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

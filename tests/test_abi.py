@@ -1,0 +1,87 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol include/mla.h declares,
+and rejects invalid arguments with status codes before touching the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from deepseek_mla_amd import mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "mla.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text))
+
+
+def test_exports_match_header():
+    declared = header_functions()
+    assert declared == set(mla.EXPORTS)
+    out = subprocess.check_output(["nm", "-D", "--defined-only", mla.LIB_PATH]).decode()
+    exported = set(re.findall(r" T (mla_[a-z0-9_]+)$", out, flags=re.M))
+    assert declared <= exported
+    L = mla.lib()
+    for name in declared:
+        assert getattr(L, name) is not None
+
+
+def tiny():
+    return mla.mla_dims(4, 64, 32, 16, 32, 128, 0.144, 10000.0)
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4):
+        assert mla.status_str(s).startswith("MLA_")
+    assert "unknown" in mla.status_str(7)
+
+
+def test_invalid_arguments_rejected_without_gpu():
+    L = mla.lib()
+    d = tiny()
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    bad = mla.mla_dims(4, 64, 32, 15, 32, 128, 0.1, 10000.0)  # odd rope dim
+    assert L.mla_absorb_q(None, 0, p, p, p, p, p, 4, None) == mla.ERR_INVALID_ARG
+    assert L.mla_absorb_q(ctypes.byref(bad), 0, p, p, p, p, p, 4, None) == mla.ERR_INVALID_ARG
+    assert L.mla_absorb_q(ctypes.byref(d), 0, None, p, p, p, p, 4, None) == mla.ERR_INVALID_ARG
+    assert L.mla_absorb_q(ctypes.byref(d), 2, p, p, p, p, p, 4, None) == mla.ERR_INVALID_ARG
+    assert L.mla_absorb_q(ctypes.byref(d), 0, p, p, p, p, p, -1, None) == mla.ERR_INVALID_ARG
+    assert L.mla_absorb_q(ctypes.byref(d), 0, None, None, None, None, None, 0, None) == mla.OK
+    # prefill: Q8_0 cache unsupported, bf16 needs the 512/64 latent row, dtype mix invalid
+    assert L.mla_attn_prefill(ctypes.byref(d), 1, 2, p, p, 4, p, 8, p, None, 0, None) == \
+        mla.ERR_UNSUPPORTED
+    assert L.mla_attn_prefill(ctypes.byref(d), 1, 1, p, p, 4, p, 8, p, None, 0, None) == \
+        mla.ERR_UNSUPPORTED
+    assert L.mla_attn_prefill(ctypes.byref(d), 0, 1, p, p, 4, p, 8, p, None, 0, None) == \
+        mla.ERR_INVALID_ARG
+    assert L.mla_attn_prefill(ctypes.byref(d), 0, 0, p, p, 4, p, 0, p, None, 0, None) == \
+        mla.ERR_INVALID_ARG
+    # decode: workspace too small; Q8_0 needs a width multiple of 32 (tiny rows are 80 wide)
+    ws = mla.mla_decode_workspace_bytes(d, 2, 100, 3)
+    assert ws > 0
+    assert L.mla_attn_decode(ctypes.byref(d), 0, 0, p, p, 80 * 4 * 100, p, 2, 100, 3, p, None,
+                             p, ws - 1, None) == mla.ERR_WORKSPACE
+    assert L.mla_attn_decode(ctypes.byref(d), 1, 2, p, p, 4000, p, 2, 100, 3, p, None, p, ws,
+                             None) == mla.ERR_INVALID_ARG
+    assert L.mla_attn_decode(ctypes.byref(d), 0, 0, p, p, 16, p, 2, 100, 3, p, None, p, ws,
+                             None) == mla.ERR_INVALID_ARG  # stride shorter than a sequence
+    assert L.mla_out_proj(ctypes.byref(d), 0, p, p, p, None, p, 3, None) == mla.ERR_INVALID_ARG
+    assert L.mla_quantize_q8_0(p, p, 3, 80, None) == mla.ERR_INVALID_ARG
+    assert L.mla_dequant_q8_0(p, p, 3, 0, None) == mla.ERR_INVALID_ARG
+
+
+def test_host_helpers():
+    assert mla.mla_q8_0_row_bytes(576) == 612
+    assert mla.mla_q8_0_row_bytes(80) == -1
+    assert mla.mla_heads_per_chunk(128, 131072.0, 8192) == 8
+    assert mla.mla_heads_per_chunk(128, 4096.0, 256) == 8
+    assert mla.mla_heads_per_chunk(128, 4096.0, 100) == 4
+    assert mla.mla_heads_per_chunk(128, 4096.0, 0) == 128
+    assert mla.mla_heads_per_chunk(7, 1000.0, 128) == 1
+    v3 = mla.mla_dims(128, 512, 128, 64, 128, 7168, 0.0722, 10000.0)
+    s = mla.mla_decode_auto_splits(v3, mla.BF16, 1, 32768)
+    assert s >= 1
+    assert mla.mla_decode_workspace_bytes(v3, 1, 32768, s) >= s * 128 * 513 * 4
