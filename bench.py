@@ -1,0 +1,233 @@
+"""Benchmark: one absorbed-MLA layer step on one MI355X.
+
+A step is the whole path on one batch of synthetic input already resident in HBM:
+mla_absorb_q -> mla_attn_prefill (or mla_attn_decode) -> mla_out_proj.
+
+Default workload (the headline line): the DeepSeek-Lite-shaped prefill layer
+(16 heads, kv_lora_rank 512, rope 64, nope 128, v 128, d_model 2048; 2048 causal
+tokens over a 2048-row bf16 latent cache).  `value` is the step's algorithmic FLOP
+count (absorption GEMM + two-term attention + latent weighted sum + wv_b + wo, a
+multiply-add counted as 2 FLOP; attention priced per visible (query, key) pair as
+in the absorption page's section 7 table) divided by the step's wall time.
+
+The V3-shaped configurations run as extra entries under "workloads" (decode ones
+report latent-cache GB/s of the attention kernels, prefill ones TFLOP/s); each entry
+carries its own roofline object.  Decode timing rotates through several copies of
+the latent cache so that the 256 MB last-level cache cannot hold it between steps.
+
+`cpu_baseline` times the CPU oracle (test infrastructure) on a bounded sample of the
+same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def step_flops(w, pos) -> dict:
+    from deepseek_mla_amd import accounting
+    d = w.dims
+    Q = len(pos)
+    H, R, Dn, Dv, D = d.n_head, d.kv_lora_rank, d.qk_nope, d.v_head, d.d_model
+    n_kv = w.n_kv
+    if w.kind == "decode":
+        attn = w.n_seq * n_kv * accounting.absorbed_flops_per_pair(d)
+    else:
+        attn = accounting.attention_flops(d, pos, n_kv)
+    return {"absorb": 2 * Q * H * R * Dn, "attention": attn,
+            "out_proj": 2 * Q * H * Dv * R + 2 * Q * D * H * Dv}
+
+
+def attention_bytes(w) -> int:
+    """Decode: latent rows of every sequence + q_cat and o_lat of every head (bf16)."""
+    from deepseek_mla_amd import accounting
+    d = w.dims
+    W = d.kv_lora_rank + d.qk_rope
+    row = accounting.q8_0_row_bytes(W) if w.mode == "q8_0" else W * 2
+    return accounting.decode_bytes(d, w.n_kv, w.n_seq, row)
+
+
+def time_workload(w, steps, warmup, copies=1):
+    import torch
+    from deepseek_mla_amd import layer, synth
+    x = synth.generate_workload(w)
+    L = layer.for_workload(w, x, cache_copies=copies)
+    del x
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        L.step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        e = ev[i]
+        e[0].record(stream)
+        L.absorb()
+        e[1].record(stream)
+        L.attend()
+        e[2].record(stream)
+        L.project()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    parts = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                      for e in ev])
+    res = {"ms_per_step": wall * 1e3, "absorb_ms": float(parts[:, 0].mean()),
+           "attention_ms": float(parts[:, 1].mean()), "out_proj_ms": float(parts[:, 2].mean()),
+           "attention_ms_min": float(parts[:, 1].min())}
+    pos = L.pos.cpu().numpy()
+    del L
+    torch.cuda.empty_cache()
+    return res, pos
+
+
+def cpu_baseline(w, max_queries):
+    """Oracle (absorb + attention + out_proj) on a bounded sample of the workload."""
+    import oracle
+    from deepseek_mla_amd import accounting, synth
+    x = synth.generate_workload(w)
+    d = w.dims
+    if w.kind == "prefill":
+        sel = np.unique(np.linspace(0, w.T - 1, min(max_queries, w.T)).astype(int))
+        seqs = [(0, sel)]
+        sample = f"{len(sel)} of {w.T} query tokens (evenly spaced), all {d.n_head} heads"
+    else:
+        nseq = min(w.n_seq, max(1, max_queries))
+        seqs = [(b, np.array([b])) for b in range(nseq)]
+        sample = f"{nseq} of {w.n_seq} sequences, all {d.n_head} heads, all {w.n_kv} rows"
+    fl = 0
+    dt = 0.0
+    nbytes = 0
+    for b, sel in seqs:
+        rows = synth.cache_rows(x["c_kv"][b], x["k_rope"][b])
+        if w.mode == "q8_0":
+            rows = oracle.q8_0_dequantize(oracle.q8_0_quantize(rows), rows.shape[-1])
+        t0 = time.perf_counter()
+        oracle.mla_absorbed(d, x["q_nope"][sel], x["q_rope"][sel], x["pos"][sel], rows,
+                            x["wk_b"], x["wv_b"], x["wo"])
+        dt += time.perf_counter() - t0
+        f = step_flops(w, x["pos"][sel])
+        if w.kind == "decode":
+            f["attention"] = accounting.absorbed_flops_per_pair(d) * w.n_kv
+        fl += f["attention"] if w.kind == "decode" else sum(f.values())
+        nbytes += attention_bytes(w) // w.n_seq
+    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
+    if w.kind == "prefill":
+        return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "sample": sample + "; full step (absorb, attention, out_proj)", "seconds": dt}
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": sample + "; full step, bytes = latent rows + q_cat + o_lat", "seconds": dt}
+
+
+def run_one(name, steps, warmup, with_cpu):
+    from deepseek_mla_amd import synth
+    w = synth.WORKLOADS[name]
+    copies = 1
+    if w.kind == "decode":
+        # rotate caches so that the 256 MB last-level cache holds none of them between steps
+        per = attention_bytes(w)
+        copies = max(1, min(16, int(np.ceil(600e6 / per))))
+    log(f"[bench] {name}: {steps} steps after {warmup} warmup, cache copies {copies}")
+    res, pos = time_workload(w, steps, warmup, copies)
+    fl = step_flops(w, pos)
+    total = sum(fl.values())
+    entry = {"workload": name, "ms_per_step": res["ms_per_step"],
+             "kernel_ms": {k: res[k] for k in ("absorb_ms", "attention_ms", "out_proj_ms")},
+             "step_tflops": total / (res["ms_per_step"] * 1e-3) / 1e12}
+    if w.kind == "prefill":
+        ach = fl["attention"] / (res["attention_ms"] * 1e-3) / 1e12
+        entry["value"] = entry["step_tflops"]
+        entry["unit"] = "TFLOP/s"
+        entry["attention_tflops"] = ach
+        entry["roofline"] = {"kernel": "flash_prefill_bf16_kernel", "bound": "mfma",
+                             "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": ach / BF16_PEAK_TFLOPS, "traffic": None,
+                             "per_launch": f"{fl['attention']} FLOP = visible pairs x "
+                                           f"{2 * (2 * w.dims.kv_lora_rank + w.dims.qk_rope)}"
+                                           f" x {w.dims.n_head} heads"}
+    else:
+        nbytes = attention_bytes(w)
+        ach = nbytes / (res["attention_ms"] * 1e-3) / 1e9
+        entry["value"] = ach
+        entry["unit"] = "GB/s"
+        entry["attention_tflops"] = fl["attention"] / (res["attention_ms"] * 1e-3) / 1e12
+        entry["roofline"] = {"kernel": "flash_decode_kernel + combine_kernel", "bound": "hbm",
+                             "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                             "mfma_frac": entry["attention_tflops"] / BF16_PEAK_TFLOPS,
+                             "per_launch": f"{nbytes} B = {w.n_seq} x ({w.n_kv} latent rows + "
+                                           f"q_cat + o_lat of {w.dims.n_head} heads)"}
+    if with_cpu:
+        t0 = time.perf_counter()
+        mq = {"lite_prefill": 2048, "v3_long_prefill": 8, "v3_decode": 1, "v3_decode_q8": 1,
+              "tiny_f32": 16}[name]
+        entry["cpu_baseline"] = cpu_baseline(w, mq)
+        log(f"[bench] {name}: cpu baseline {time.perf_counter() - t0:.1f}s")
+    log(f"[bench] {name}: {json.dumps(entry)}")
+    return entry
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="lite_prefill")
+    ap.add_argument("--extra", default="v3_decode,v3_long_prefill,v3_decode_q8",
+                    help="comma-separated extra workloads reported under 'workloads' ('' = none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the design for sharding is described in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from deepseek_mla_amd import mla
+    mla.lib()
+    main_entry = run_one(args.workload, args.steps, args.warmup, not args.no_cpu_baseline)
+    extras = []
+    for name in [n for n in args.extra.split(",") if n and n != args.workload]:
+        steps = max(3, args.steps // 2) if "long" in name else args.steps
+        extras.append(run_one(name, steps, args.warmup, not args.no_cpu_baseline))
+    from deepseek_mla_amd import synth
+    w = synth.WORKLOADS[args.workload]
+    line = {
+        "metric": "MLA attention TFLOP/s (prefill) and latent-cache GB/s (decode), 1 MI355X",
+        "value": main_entry["value"], "unit": main_entry["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_entry["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.mode != "f32" else "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "n_head": w.dims.n_head,
+                   "kv_lora_rank": w.dims.kv_lora_rank, "qk_rope": w.dims.qk_rope,
+                   "qk_nope": w.dims.qk_nope, "v_head": w.dims.v_head,
+                   "d_model": w.dims.d_model, "query_tokens": w.n_query, "n_kv": w.n_kv,
+                   "cache": w.mode, "flop_count": "absorb + attention + out_proj per step"},
+        "roofline": main_entry["roofline"],
+        "kernel_ms": main_entry["kernel_ms"],
+        "attention_tflops": main_entry.get("attention_tflops"),
+        "workloads": extras,
+    }
+    if "cpu_baseline" in main_entry:
+        line["cpu_baseline"] = main_entry["cpu_baseline"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -183,12 +183,22 @@ __device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t MLA_LDS
         const uint8_t MLA_LDS *kb[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) kb[b] = rowp + (((2 * b + hi) ^ sw) * 16);
+        // software pipeline: the fragment for step kk+QK_AHEAD is requested right after the
+        // MFMA of step kk, so LDS latency overlaps QK_AHEAD matrix operations.
+        constexpr int QK_AHEAD = 4;
+        bf16x8 a[QK_AHEAD];
 #pragma unroll
-        for (int kk = 0; kk < 36; kk += 2) {
-            const bf16x8 a0 = *(const bf16x8 MLA_LDS *)(kb[kk & 3] + (kk >> 2) * 128);
-            const bf16x8 a1 = *(const bf16x8 MLA_LDS *)(kb[(kk + 1) & 3] + ((kk + 1) >> 2) * 128);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, st.q[kk], s, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, st.q[kk + 1], s1, 0, 0, 0);
+        for (int kk = 0; kk < QK_AHEAD; ++kk)
+            a[kk] = *(const bf16x8 MLA_LDS *)(kb[kk & 3] + (kk >> 2) * 128);
+#pragma unroll
+        for (int kk = 0; kk < 36; ++kk) {
+            if (kk & 1)
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk % QK_AHEAD], st.q[kk], s1, 0, 0, 0);
+            else
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk % QK_AHEAD], st.q[kk], s, 0, 0, 0);
+            const int nk = kk + QK_AHEAD;
+            if (nk < 36) a[kk % QK_AHEAD] = *(const bf16x8 MLA_LDS *)(kb[nk & 3] + (nk >> 2) * 128);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll
@@ -236,14 +246,23 @@ __device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t MLA_LDS
         vb[0][par] = r0 + (((4 * par + c3) ^ sw0) * 16) + cb;
         vb[1][par] = r1 + (((4 * par + c3) ^ sw1) * 16) + cb;
     }
+    // 32 steps (ks, nb) with the same read-ahead ring as the score loop
+    constexpr int PV_AHEAD = 4;
+    auto vaddr = [&](int i, int half) {
+        const int ks = i >> 4, nb = i & 15;
+        return vb[half][nb & 1] + ks * 16 * fl::RB + (nb >> 1) * 128;
+    };
+    bf16x8 va[PV_AHEAD];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int i = 0; i < PV_AHEAD; ++i) va[i] = tr_pair(vaddr(i, 0), vaddr(i, 1));
 #pragma unroll
-        for (int nb = 0; nb < 16; ++nb) {
-            const int off = ks * 16 * fl::RB + (nb >> 1) * 128;
-            const bf16x8 a = tr_pair(vb[0][nb & 1] + off, vb[1][nb & 1] + off);
-            st.o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[ks], st.o[nb], 0, 0, 0);
-        }
+    for (int i = 0; i < 32; ++i) {
+        const int ks = i >> 4, nb = i & 15;
+        st.o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % PV_AHEAD], p[ks], st.o[nb], 0, 0,
+                                                           0);
+        const int ni = i + PV_AHEAD;
+        if (ni < 32) va[i % PV_AHEAD] = tr_pair(vaddr(ni, 0), vaddr(ni, 1));
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 

@@ -255,41 +255,70 @@ hipError_t launch_flash_simt_decode(const mla_dims &d, const float *q_cat, const
 }
 
 // ------------------------------------------------------------ split-KV combine
-// lse = log sum_s exp(lse_s); o = sum_s exp(lse_s - lse) o_s.  One block per (b, h);
-// splits with lse_s = -inf contribute nothing.
+// lse = log sum_s exp(lse_s); o = sum_s exp(lse_s - lse) o_s.  Block (b*H + h, column
+// slice of CB columns); splits with lse_s = -inf contribute nothing.  The split weights
+// are computed once per block into LDS; each thread then accumulates one column over
+// all splits (loads coalesced across the block, 8 splits in flight).
+constexpr int CB = 128;
+
 template <typename OT>
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ part_o,
-                                                      const float *__restrict__ part_lse, int H,
-                                                      int R, int S, OT *__restrict__ o_lat,
-                                                      float *__restrict__ lse) {
-    extern __shared__ float wsh[];  // [S]
+__global__ __launch_bounds__(CB) void combine_kernel(const float *__restrict__ part_o,
+                                                     const float *__restrict__ part_lse, int H,
+                                                     int R, int S, OT *__restrict__ o_lat,
+                                                     float *__restrict__ lse) {
+    extern __shared__ float wsh[];  // [S] weights, then [CB] reduction scratch
+    float *red = wsh + S;
     const int bh = blockIdx.x;
     const int b = bh / H, h = bh % H;
+    const int tid = threadIdx.x;
+    const float *pl = part_lse + (int64_t)b * S * H + h;
     float mx = -INFINITY;
-    for (int s = 0; s < S; ++s) mx = fmaxf(mx, part_lse[((int64_t)b * S + s) * H + h]);
-    float sum = 0.0f;
-    for (int s = threadIdx.x; s < S; s += blockDim.x) {
-        float ls = part_lse[((int64_t)b * S + s) * H + h];
-        wsh[s] = (mx == -INFINITY) ? 0.0f : expf(ls - mx);
-    }
+    for (int s = tid; s < S; s += CB) mx = fmaxf(mx, pl[(int64_t)s * H]);
+    red[tid] = mx;
     __syncthreads();
-    for (int s = 0; s < S; ++s) sum += wsh[s];
-    const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
-    for (int c = threadIdx.x; c < R; c += blockDim.x) {
-        float acc = 0.0f;
-        for (int s = 0; s < S; ++s) {
-            float wgt = wsh[s];
-            if (wgt != 0.0f) acc = fmaf(wgt, part_o[(((int64_t)b * S + s) * H + h) * R + c], acc);
-        }
-        st_f(o_lat + ((int64_t)b * H + h) * R + c, acc * inv);
+    for (int o = CB / 2; o > 0; o >>= 1) {
+        if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+        __syncthreads();
     }
-    if (lse && threadIdx.x == 0) lse[(int64_t)b * H + h] = sum > 0.0f ? mx + logf(sum) : -INFINITY;
+    mx = red[0];
+    __syncthreads();
+    float sum = 0.0f;
+    for (int s = tid; s < S; s += CB) {
+        const float wgt = (mx == -INFINITY) ? 0.0f : expf(pl[(int64_t)s * H] - mx);
+        wsh[s] = wgt;
+        sum += wgt;
+    }
+    red[tid] = sum;
+    __syncthreads();
+    for (int o = CB / 2; o > 0; o >>= 1) {
+        if (tid < o) red[tid] += red[tid + o];
+        __syncthreads();
+    }
+    sum = red[0];
+    const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
+    const int c = blockIdx.y * CB + tid;
+    if (c < R) {
+        const float *po = part_o + ((int64_t)b * S * H + h) * R + c;
+        const int64_t stride = (int64_t)H * R;
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        int s = 0;
+        for (; s + 8 <= S; s += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[u] = fmaf(wsh[s + u], po[(int64_t)(s + u) * stride], acc[u]);
+        }
+        for (; s < S; ++s) acc[0] = fmaf(wsh[s], po[(int64_t)s * stride], acc[0]);
+        const float tot = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+        st_f(o_lat + ((int64_t)b * H + h) * R + c, tot * inv);
+    }
+    if (lse && blockIdx.y == 0 && tid == 0)
+        lse[(int64_t)b * H + h] = sum > 0.0f ? mx + logf(sum) : -INFINITY;
 }
 
 template <typename OT>
 hipError_t launch_combine(const float *part_o, const float *part_lse, int B, int H, int R,
                           int n_splits, OT *o_lat, float *lse, hipStream_t st) {
-    hipLaunchKernelGGL(combine_kernel<OT>, dim3(B * H), dim3(256), sizeof(float) * n_splits, st,
+    dim3 grid(B * H, (R + CB - 1) / CB);
+    hipLaunchKernelGGL(combine_kernel<OT>, grid, dim3(CB), sizeof(float) * (n_splits + CB), st,
                        part_o, part_lse, H, R, n_splits, o_lat, lse);
     return hipGetLastError();
 }

@@ -28,7 +28,8 @@ class LayerStep:
     """
 
     def __init__(self, dims: synth.Dims, mode: str, kind: str, inputs: dict, n_kv: int,
-                 scratch_cap_mib: int = 0, n_splits: int = 0, device="cuda"):
+                 scratch_cap_mib: int = 0, n_splits: int = 0, cache_copies: int = 1,
+                 device="cuda"):
         self.dims, self.mode, self.kind = dims, mode, kind
         self.act, self.kv = _MODE[mode]
         self.cdims = mla.make_dims(dims)
@@ -61,6 +62,10 @@ class LayerStep:
             rows = np.concatenate([inputs["c_kv"], inputs["k_rope"]], axis=-1)
             self.cache = _dev(rows, tdt, device)
             self.row_bytes = W * (4 if mode == "f32" else 2)
+        # identical copies of the cache, used in rotation (keeps timing honest when the
+        # cache would otherwise stay resident in the last-level cache between steps)
+        self.caches = [self.cache] + [self.cache.clone() for _ in range(cache_copies - 1)]
+        self._ci = 0
         self.q_cat = torch.empty((self.T, H, W), dtype=tdt, device=device)
         self.o_lat = torch.empty((self.T, H, R), dtype=tdt, device=device)
         self.lse = torch.empty((self.T, H), dtype=torch.float32, device=device)
@@ -77,6 +82,8 @@ class LayerStep:
                          self.q_cat, self.T, stream)
 
     def attend(self, stream=None):
+        self.cache = self.caches[self._ci]
+        self._ci = (self._ci + 1) % len(self.caches)
         if self.kind == "prefill":
             mla.mla_attn_prefill(self.cdims, self.act, self.kv, self.q_cat, self.pos, self.T,
                                  self.cache, self.n_kv, self.o_lat, self.lse,

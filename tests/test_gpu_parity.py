@@ -1,7 +1,10 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
-Tolerance (for each output X): max |X_gpu - X_oracle| <= tol * rms(X_oracle), with
-tol = 1e-4 in float32 mode and 2e-2 in bf16 / Q8_0 mode.  Inputs are the same seeded
+Tolerance (for each output row x, i.e. one query's vector along the last axis):
+max |x_gpu - x_oracle| <= tol * rms(x_oracle), with tol = 1e-4 in float32 mode and
+2e-2 in bf16 / Q8_0 mode; outputs stored in bf16 are
+additionally allowed half a bf16 ulp of the exact value (the rounding of the stored
+result itself).  lse (always float32) is compared in absolute terms against tol.  Inputs are the same seeded
 values on both sides (bf16-rounded, or Q8_0 bytes produced by the oracle's quantiser,
 before either side sees them).  Q8_0 (de)quantisation is compared bit for bit.
 """
@@ -12,12 +15,13 @@ import pytest
 
 import oracle
 from deepseek_mla_amd import synth
+from oracle import compare
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-TOL = {"f32": 1e-4, "bf16": 2e-2, "q8_0": 2e-2}
+TOL = compare.TOL
 
 
 @pytest.fixture(scope="module")
@@ -33,6 +37,10 @@ def rel_err(a, b):
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     return float(np.abs(a - b).max() / max(np.sqrt((b ** 2).mean()), 1e-30))
+
+
+def rel_err_stored(g, r, mode):
+    return compare.row_error(g, r, mode)
 
 
 def report(name, err, tol):
@@ -57,7 +65,7 @@ def check_stages(got, ref, mode, sel=None, stages=("q_cat", "o_lat", "lse", "out
             err = float(np.abs(g - r).max())
             report(k + " (abs)", err, tol)
         else:
-            report(k, rel_err(g, r), tol)
+            report(k, rel_err_stored(g, r, mode), tol)
 
 
 def small_prefill(dims, mode, T, N, seed, pos):
@@ -169,7 +177,8 @@ def test_bf16_prefill_chunked_vs_unchunked_bitwise(dev):
     # and sampled rows against the oracle
     sel = np.array([0, 1, 511, 1022, 1023])
     ref = oracle_chain(d, x, rows, qsel=sel)
-    report("o_lat (sampled)", rel_err(o0.float().cpu().numpy()[sel], ref["o_lat"]), 2e-2)
+    report("o_lat (sampled)", rel_err_stored(o0.float().cpu().numpy()[sel], ref["o_lat"], "bf16"),
+           2e-2)
 
 
 def test_bf16_prefill_causal_perturbation(dev):
@@ -215,7 +224,7 @@ def test_bf16_prefill_score_jump_repass(dev):
     torch.cuda.synchronize()
     s_max = (d.scale * rows[250].astype(np.float64) @ q[3, 5].astype(np.float64))
     assert s_max > 60.0  # far beyond the frozen max's 44-nat margin
-    report("o_lat", rel_err(o.float().cpu().numpy(), ro), 2e-2)
+    report("o_lat", rel_err_stored(o.float().cpu().numpy(), ro, "bf16"), 2e-2)
     report("lse (abs)", float(np.abs(lse.cpu().numpy() - rl).max()), 2e-2)
 
 
@@ -256,7 +265,8 @@ def test_decode_splits(dev, mode):
         torch.cuda.synchronize()
         for b in range(2):
             print(f" splits={ns} seq={b}")
-            report("o_lat", rel_err(o[b].float().cpu().numpy(), ref[b][0][0]), TOL[mode])
+            report("o_lat", rel_err_stored(o[b].float().cpu().numpy(), ref[b][0][0], mode),
+                   TOL[mode])
             report("lse (abs)", float(np.abs(lse[b].cpu().numpy() - ref[b][1][0]).max()), TOL[mode])
 
 
@@ -321,10 +331,10 @@ def test_v3_decode_q8_sampled_heads(dev):
     d = w.dims
     heads = np.arange(0, 128, 8)
     qc = oracle.absorb_q(d, x["q_nope"], x["q_rope"], x["pos"], x["wk_b"])
-    report("q_cat", rel_err(got["q_cat"], qc), 2e-2)
+    report("q_cat", rel_err_stored(got["q_cat"], qc, "q8_0"), 2e-2)
     for b in range(w.n_seq):
         rows = synth.cache_rows(x["c_kv"][b], x["k_rope"][b])
         rows = oracle.q8_0_dequantize(oracle.q8_0_quantize(rows), 576)
         ro, rl = oracle.attention(d, qc[b:b + 1][:, heads], x["pos"][b:b + 1], rows)
-        report(f"o_lat seq {b}", rel_err(got["o_lat"][b][heads], ro[0]), 2e-2)
+        report(f"o_lat seq {b}", rel_err_stored(got["o_lat"][b][heads], ro[0], "q8_0"), 2e-2)
         report(f"lse seq {b} (abs)", float(np.abs(got["lse"][b][heads] - rl[0]).max()), 2e-2)
