@@ -165,17 +165,14 @@ struct WaveState {
 
 // One tile: keys key0 .. key0+31 in LDS stage `t`.  Keys with index > lim are masked.
 __device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t MLA_LDS *t, int key0,
-                                            int lim, float sc) {
+                                            int lim, int wave_lim_min, float sc) {
     const int l = threadIdx.x & 63;
     const int hi = l >> 5;
 // ---- S^T = K Q^T.  Chunk (2kk + hi) ^ swz(k) = 8*(kk/4) + ((2*(kk%4) + hi) ^ swz(k)):
     // four lane-dependent bases plus compile-time offsets.
-    f32x16 s, s1;
+    f32x16 s;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        s[e] = 0.0f;
-        s1[e] = 0.0f;
-    }
+    for (int e = 0; e < 16; ++e) s[e] = 0.0f;
     {
         const int k = l & 31;
         const int sw = fswz(k);
@@ -184,7 +181,8 @@ __device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t MLA_LDS
 #pragma unroll
         for (int b = 0; b < 4; ++b) kb[b] = rowp + (((2 * b + hi) ^ sw) * 16);
         // software pipeline: the fragment for step kk+QK_AHEAD is requested right after the
-        // MFMA of step kk, so LDS latency overlaps QK_AHEAD matrix operations.
+        // MFMA of step kk, so LDS latency overlaps QK_AHEAD matrix operations.  One
+        // accumulator chain: dependent 32x32x16 MFMAs issue at the independent rate.
         constexpr int QK_AHEAD = 4;
         bf16x8 a[QK_AHEAD];
 #pragma unroll
@@ -192,42 +190,39 @@ __device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t MLA_LDS
             a[kk] = *(const bf16x8 MLA_LDS *)(kb[kk & 3] + (kk >> 2) * 128);
 #pragma unroll
         for (int kk = 0; kk < 36; ++kk) {
-            if (kk & 1)
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk % QK_AHEAD], st.q[kk], s1, 0, 0, 0);
-            else
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk % QK_AHEAD], st.q[kk], s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk % QK_AHEAD], st.q[kk], s, 0, 0, 0);
             const int nk = kk + QK_AHEAD;
             if (nk < 36) a[kk % QK_AHEAD] = *(const bf16x8 MLA_LDS *)(kb[nk & 3] + (nk >> 2) * 128);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] += s1[e];
-    // ---- softmax: lane holds row l%32, keys (e/4)*8 + hi*4 + e%4
+    // ---- softmax: lane holds row l%32, keys (e/4)*8 + hi*4 + e%4.  Masking is only
+    // needed on tiles that reach past some row's last visible key (wave-uniform test).
     float tmax = -INFINITY;
+    if (key0 + fl::NK - 1 > wave_lim_min) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int key = key0 + (e >> 2) * 8 + hi * 4 + (e & 3);
-        float v = s[e] * sc;
-        v = (key <= lim) ? v : -INFINITY;
-        s[e] = v;
-        tmax = fmaxf(tmax, v);
+        for (int e = 0; e < 16; ++e) {
+            const int key = key0 + (e >> 2) * 8 + hi * 4 + (e & 3);
+            s[e] = (key <= lim) ? s[e] : -INFINITY;
+        }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+#pragma unroll
+    for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[e]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sc;  // sc > 0: max of scaled = scaled max
     if (st.m == -INFINITY) {
         st.m = tmax;  // first visible keys of this row (o and lsum are still zero)
     } else if (tmax > st.m + fl::FREEZE_LIMIT || st.bad) {
         st.bad = true;
         st.m = fmaxf(st.m, tmax);  // track the true max for the repeated pass
     }
-    const float mu = (st.m == -INFINITY) ? 0.0f : st.m;
+    const float nmu = (st.m == -INFINITY) ? 0.0f : -st.m;
     bf16x8 p[2];
     float psum = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-        const bf16 pb = f2bf(__builtin_amdgcn_exp2f(s[e] - mu));
-        p[e >> 3][e & 7] = pb;
-        psum += bf2f(pb);
+        const float pe = __builtin_amdgcn_exp2f(fmaf(s[e], sc, nmu));  // masked: exp2(-inf) = 0
+        psum += pe;
+        p[e >> 3][e & 7] = f2bf(pe);
     }
     st.lsum += psum;
     // ---- O^T += V^T P^T  (two k-steps of 16 keys, 16 column blocks of 32)
@@ -292,6 +287,9 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
                                             int kbeg, int kend, int lim, float sc) {
     if (kend <= kbeg) return;
     const int ntiles = (kend - kbeg + fl::NK - 1) / fl::NK;
+    int wlim = lim;  // smallest last-visible key over the wave's rows
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wlim = min(wlim, __shfl_xor(wlim, o));
     if constexpr (!Q8) {
         constexpr int PER = fl::TILE_CH / (64 * NW);
         const int last = n_rows - 1;
@@ -312,7 +310,7 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             const int nx = ti + NS - 1;
             if (nx < ntiles)
                 issue_tile_bf16<NW>(rows, kbeg + nx * fl::NK, last, lds + (nx % NS) * fl::TILE_BYTES);
-            attend_tile(st, lds + (ti % NS) * fl::TILE_BYTES, kbeg + ti * fl::NK, lim, sc);
+            attend_tile(st, lds + (ti % NS) * fl::TILE_BYTES, kbeg + ti * fl::NK, lim, wlim, sc);
         }
         __syncthreads();
     } else {
@@ -334,7 +332,7 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             if (ti + 2 < ntiles)
                 issue_tile_q8<NW>(rows, kbeg + (ti + 2) * fl::NK, n_rows,
                                   raw + (ti % 2) * Q8_RAW_STAGE);
-            attend_tile(st, lds + (ti % 2) * fl::TILE_BYTES, kbeg + ti * fl::NK, lim, sc);
+            attend_tile(st, lds + (ti % 2) * fl::TILE_BYTES, kbeg + ti * fl::NK, lim, wlim, sc);
             if (ti + 1 < ntiles) {
                 if (ti + 2 < ntiles) {
                     MLA_WAIT_VMCNT(PER);
