@@ -34,6 +34,26 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
+# HBM bytes per launch of the dominant kernel(s), from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# passes scaled by a 512 MiB copy (fetch x2.0, write x1.0); the summaries and commands are
+# in profiles/.  Valid only for the kernel source they were taken on (sha256 prefix).
+TRAFFIC = {
+    "src": ("deepseek_mla_amd/csrc/flash_mfma.hip", "ccf41e0558d589da"),
+    "lite_prefill": 61.55e6 + 47.32e6,
+    "v3_long_prefill": 10187.41e6 + 1514.14e6,
+    "v3_decode": (51.78e6 + 81.73e6) + (68.20e6 + 0.14e6),       # partial kernel + combine
+    "v3_decode_q8": (279.56e6 + 100.53e6) + (68.20e6 + 0.54e6),  # partial kernel + combine
+}
+
+
+def measured_traffic(name):
+    import hashlib
+    path, sha = TRAFFIC["src"]
+    with open(os.path.join(ROOT, path), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != sha:
+            return None  # kernel changed since the counters were taken
+    return TRAFFIC.get(name)
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -157,7 +177,7 @@ def run_one(name, steps, warmup, with_cpu):
         entry["attention_tflops"] = ach
         entry["roofline"] = {"kernel": "flash_prefill_bf16_kernel", "bound": "mfma",
                              "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": ach / BF16_PEAK_TFLOPS, "traffic": None,
+                             "frac": ach / BF16_PEAK_TFLOPS, "traffic": measured_traffic(name),
                              "per_launch": f"{fl['attention']} FLOP = visible pairs x "
                                            f"{2 * (2 * w.dims.kv_lora_rank + w.dims.qk_rope)}"
                                            f" x {w.dims.n_head} heads"}
@@ -169,7 +189,7 @@ def run_one(name, steps, warmup, with_cpu):
         entry["attention_tflops"] = fl["attention"] / (res["attention_ms"] * 1e-3) / 1e12
         entry["roofline"] = {"kernel": "flash_decode_kernel + combine_kernel", "bound": "hbm",
                              "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                             "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(name),
                              "mfma_frac": entry["attention_tflops"] / BF16_PEAK_TFLOPS,
                              "per_launch": f"{nbytes} B = {w.n_seq} x ({w.n_kv} latent rows + "
                                            f"q_cat + o_lat of {w.dims.n_head} heads)"}
@@ -192,6 +212,8 @@ def main():
     ap.add_argument("--extra", default="v3_decode,v3_long_prefill,v3_decode_q8",
                     help="comma-separated extra workloads reported under 'workloads' ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -199,6 +221,16 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        n = 512 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return
     from deepseek_mla_amd import mla
     mla.lib()
     main_entry = run_one(args.workload, args.steps, args.warmup, not args.no_cpu_baseline)
