@@ -82,11 +82,11 @@ def attention_bytes(w) -> int:
     return accounting.decode_bytes(d, w.n_kv, w.n_seq, row)
 
 
-def time_workload(w, steps, warmup, copies=1):
+def time_workload(w, steps, warmup, copies=1, n_splits=0):
     import torch
     from deepseek_mla_amd import layer, synth
     x = synth.generate_workload(w)
-    L = layer.for_workload(w, x, cache_copies=copies)
+    L = layer.for_workload(w, x, cache_copies=copies, n_splits=n_splits)
     del x
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -155,7 +155,7 @@ def cpu_baseline(w, max_queries):
             "sample": sample + "; full step, bytes = latent rows + q_cat + o_lat", "seconds": dt}
 
 
-def run_one(name, steps, warmup, with_cpu):
+def run_one(name, steps, warmup, with_cpu, n_splits=0):
     from deepseek_mla_amd import synth
     w = synth.WORKLOADS[name]
     copies = 1
@@ -164,7 +164,7 @@ def run_one(name, steps, warmup, with_cpu):
         per = attention_bytes(w)
         copies = max(1, min(16, int(np.ceil(600e6 / per))))
     log(f"[bench] {name}: {steps} steps after {warmup} warmup, cache copies {copies}")
-    res, pos = time_workload(w, steps, warmup, copies)
+    res, pos = time_workload(w, steps, warmup, copies, n_splits)
     fl = step_flops(w, pos)
     total = sum(fl.values())
     entry = {"workload": name, "ms_per_step": res["ms_per_step"],
@@ -212,6 +212,8 @@ def main():
     ap.add_argument("--extra", default="v3_decode,v3_long_prefill,v3_decode_q8",
                     help="comma-separated extra workloads reported under 'workloads' ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="decode key splits per sequence (0 = the library's automatic choice)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -233,11 +235,12 @@ def main():
         return
     from deepseek_mla_amd import mla
     mla.lib()
-    main_entry = run_one(args.workload, args.steps, args.warmup, not args.no_cpu_baseline)
+    main_entry = run_one(args.workload, args.steps, args.warmup, not args.no_cpu_baseline,
+                         args.splits)
     extras = []
     for name in [n for n in args.extra.split(",") if n and n != args.workload]:
         steps = max(3, args.steps // 2) if "long" in name else args.steps
-        extras.append(run_one(name, steps, args.warmup, not args.no_cpu_baseline))
+        extras.append(run_one(name, steps, args.warmup, not args.no_cpu_baseline, args.splits))
     from deepseek_mla_amd import synth
     w = synth.WORKLOADS[args.workload]
     line = {

@@ -163,6 +163,7 @@ size_t mla_decode_workspace_bytes(const mla_dims *d, int32_t B, int32_t n_kv_max
     }
     if (S > n_kv_max) S = n_kv_max;
     const size_t rows = (size_t)B * S * d->n_head;
+    // partial outputs: float32 on the float32 path, bfloat16 otherwise; sized for the larger
     return align256(rows * d->kv_lora_rank * sizeof(float)) + align256(rows * sizeof(float));
 }
 
@@ -199,26 +200,25 @@ int mla_attn_decode(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *
     split_plan(kv, n_kv_max, S, &split_len, &count);
     if (workspace_bytes < mla_decode_workspace_bytes(d, B, n_kv_max, S)) return MLA_ERR_WORKSPACE;
     const size_t rows = (size_t)B * count * d->n_head;
-    float *part_o = (float *)workspace;
-    float *part_lse = (float *)((char *)workspace + align256(rows * d->kv_lora_rank * sizeof(float)));
+    const size_t po_elem = kv == MLA_F32 ? sizeof(float) : sizeof(bf16);
+    void *part_o = workspace;
+    float *part_lse = (float *)((char *)workspace + align256(rows * d->kv_lora_rank * po_elem));
     hipStream_t st = as_stream(stream);
     hipError_t e;
     if (kv == MLA_F32) {
         e = launch_flash_simt_decode(*d, (const float *)q_cat, (const float *)kv_cache,
                                      kv_seq_stride_bytes / 4, n_kv, n_kv_max, B, count, split_len,
-                                     part_o,
-                                     part_lse, st);
+                                     (float *)part_o, part_lse, st);
         if (e == hipSuccess)
-            e = launch_combine<float>(part_o, part_lse, B, d->n_head, d->kv_lora_rank, count,
-                                      (float *)o_lat, lse, st);
+            e = launch_combine<float, float>((const float *)part_o, part_lse, B, d->n_head,
+                                             d->kv_lora_rank, count, (float *)o_lat, lse, st);
     } else {
         e = launch_flash_decode_bf16((const bf16 *)q_cat, kv_cache, kv == MLA_Q8_0,
                                      kv_seq_stride_bytes, n_kv, n_kv_max, B, d->n_head, count,
-                                     split_len,
-                                     d->scale, part_o, part_lse, st);
+                                     split_len, d->scale, (bf16 *)part_o, part_lse, st);
         if (e == hipSuccess)
-            e = launch_combine<bf16>(part_o, part_lse, B, d->n_head, d->kv_lora_rank, count,
-                                     (bf16 *)o_lat, lse, st);
+            e = launch_combine<bf16, bf16>((const bf16 *)part_o, part_lse, B, d->n_head,
+                                           d->kv_lora_rank, count, (bf16 *)o_lat, lse, st);
     }
     return hip_status(e);
 }

@@ -52,8 +52,8 @@ hipError_t launch_flash_simt_decode(const mla_dims &d, const float *q_cat, const
                                     int B,
                                     int n_splits, int split_len, float *part_o, float *part_lse,
                                     hipStream_t st);
-template <typename OT>
-hipError_t launch_combine(const float *part_o, const float *part_lse, int B, int H, int R,
+template <typename PT, typename OT>
+hipError_t launch_combine(const PT *part_o, const float *part_lse, int B, int H, int R,
                           int n_splits, OT *o_lat, float *lse, hipStream_t st);
 hipError_t launch_quantize_q8_0(const float *x, uint8_t *rows, int64_t n_rows, int width,
                                 hipStream_t st);
@@ -70,7 +70,7 @@ hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int 
 hipError_t launch_flash_decode_bf16(const bf16 *q_cat, const void *cache, int cache_q8,
                                     int64_t seq_stride_bytes, const int32_t *n_kv, int n_kv_max,
                                     int B, int H,
-                                    int n_splits, int split_len, float scale, float *part_o,
+                                    int n_splits, int split_len, float scale, bf16 *part_o,
                                     float *part_lse, hipStream_t st);
 
 }  // namespace mla

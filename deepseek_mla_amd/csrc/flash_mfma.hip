@@ -47,6 +47,17 @@ constexpr float FREEZE_LIMIT = 64.0f;  // log2 units a score may exceed the froz
 
 __device__ __forceinline__ int fswz(int k) { return (k & 7) ^ ((k >> 3) & 1); }
 
+// Lanes l and l^32 hold the same query row; these combine the pair (ds_bpermute).
+// Both halves compute (x[l % 32] op x[32 + l % 32]), so the results are bit-identical.
+__device__ __forceinline__ float pair_max(float x) {
+    const float y = __shfl_xor(x, 32);
+    return (threadIdx.x & 32) ? fmaxf(y, x) : fmaxf(x, y);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const float y = __shfl_xor(x, 32);
+    return (threadIdx.x & 32) ? y + x : x + y;
+}
+
 __device__ __forceinline__ bf16x8 tr_pair(const uint8_t MLA_LDS *p0, const uint8_t MLA_LDS *p1) {
     s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS *)p0);
     s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS *)p1);
@@ -62,7 +73,13 @@ __device__ __forceinline__ void issue_tile_bf16(const uint8_t *__restrict__ rows
                                                 int last, uint8_t MLA_LDS *dst) {
     constexpr int NI = fl::TILE_CH / (64 * NW);  // instructions per wave
     static_assert(fl::TILE_CH % (64 * NW) == 0, "tile chunks must split evenly over waves");
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // The lane index is made opaque so that the per-lane offsets below are recomputed at
+    // each call (a few integer ops) instead of being hoisted, kept and spilled: a scratch
+    // reload is a vector-memory load, and waiting for it would also wait for every
+    // earlier tile copy.
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));
     // rows past `last` are clamped; offsets stay below 2^31 for caches < 2 GiB per call
     const uint8_t *base = rows + (int64_t)key0 * fl::RB;
     const int lim = last - key0;
@@ -71,7 +88,8 @@ __device__ __forceinline__ void issue_tile_bf16(const uint8_t *__restrict__ rows
         const int P = (w * NI + i) * 64 + l;  // physical chunk in the tile
         const int k = P / fl::WCH;
         const int c = (P % fl::WCH) ^ fswz(k);
-        const uint32_t off = (uint32_t)(min(k, lim) * fl::RB + c * 16);
+        uint32_t off = (uint32_t)(min(k, lim) * fl::RB + c * 16);
+        asm volatile("" : "+v"(off));  // keep (uniform base) + (32-bit lane offset) addressing
         __builtin_amdgcn_global_load_lds((const void *)(base + off),
                                          (void MLA_LDS *)(dst + (w * NI + i) * 1024), 16, 0, 0);
     }
@@ -91,16 +109,19 @@ __device__ __forceinline__ void issue_tile_q8(const uint8_t *__restrict__ rows, 
                                               int n_rows, uint8_t MLA_LDS *dst) {
     static_assert(Q8_RAW_INST % NW == 0, "raw copies must split evenly over waves");
     constexpr int NI = Q8_RAW_INST / NW;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const uint32_t *src = (const uint32_t *)rows;
-    const int64_t base = (int64_t)key0 * (fl::Q8_RB / 4);
-    const int64_t last = (int64_t)n_rows * (fl::Q8_RB / 4) - 1;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w >= NW) return;  // only waves 0 .. NW-1 copy
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));  // recompute offsets per call (see issue_tile_bf16)
+    // tile-relative dword index of the sequence's last dword (uniform, 32-bit)
+    const int64_t rem = (int64_t)(n_rows - key0) * (fl::Q8_RB / 4) - 1;
+    const int last_rel = (int)(rem < Q8_RAW_INST * 64 ? rem : Q8_RAW_INST * 64);
+    const uint8_t *gbase = rows + (int64_t)key0 * fl::Q8_RB;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int inst = w * NI + i;
-        int64_t g = base + inst * 64 + l;
-        if (g > last) g = last;
-        __builtin_amdgcn_global_load_lds((const void *)(src + g),
+        const uint32_t off = (uint32_t)min(inst * 64 + l, last_rel) * 4u;
+        __builtin_amdgcn_global_load_lds((const void *)(gbase + off),
                                          (void MLA_LDS *)(dst + inst * 256), 4, 0, 0);
     }
 }
@@ -208,7 +229,7 @@ __device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t MLA_LDS
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[e]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sc;  // sc > 0: max of scaled = scaled max
+    tmax = pair_max(tmax) * sc;  // sc > 0: max of scaled = scaled max
     if (st.m == -INFINITY) {
         st.m = tmax;  // first visible keys of this row (o and lsum are still zero)
     } else if (tmax > st.m + fl::FREEZE_LIMIT || st.bad) {
@@ -284,12 +305,9 @@ __device__ __forceinline__ void init_acc(WaveState &st, float m0) {
 template <int NW, int NS, bool Q8>
 __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
                                             const uint8_t *__restrict__ rows, int n_rows,
-                                            int kbeg, int kend, int lim, float sc) {
+                                            int kbeg, int kend, int lim, int wlim, float sc) {
     if (kend <= kbeg) return;
     const int ntiles = (kend - kbeg + fl::NK - 1) / fl::NK;
-    int wlim = lim;  // smallest last-visible key over the wave's rows
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) wlim = min(wlim, __shfl_xor(wlim, o));
     if constexpr (!Q8) {
         constexpr int PER = fl::TILE_CH / (64 * NW);
         const int last = n_rows - 1;
@@ -352,11 +370,11 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
 template <int NW, int NS, bool Q8>
 __device__ __forceinline__ void attend_range(WaveState &st, uint8_t MLA_LDS *lds, int *flag,
                                              const uint8_t *__restrict__ rows, int n_rows,
-                                             int kbeg, int kend, int lim, float sc) {
+                                             int kbeg, int kend, int lim, int wlim, float sc) {
     float m0 = -INFINITY;
     for (int pass = 0; pass < 2; ++pass) {
         init_acc(st, m0);
-        stream_keys<NW, NS, Q8>(st, lds, rows, n_rows, kbeg, kend, lim, sc);
+        stream_keys<NW, NS, Q8>(st, lds, rows, n_rows, kbeg, kend, lim, wlim, sc);
         if (threadIdx.x == 0) *flag = 0;
         __syncthreads();
         if (__builtin_amdgcn_ballot_w64(st.bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1);
@@ -373,7 +391,7 @@ __device__ __forceinline__ void attend_range(WaveState &st, uint8_t MLA_LDS *lds
 template <typename Store>
 __device__ __forceinline__ float finish(WaveState &st, Store store) {
     const int l = threadIdx.x & 63, hi = l >> 5;
-    const float lt = st.lsum + __shfl_xor(st.lsum, 32);
+    const float lt = pair_sum(st.lsum);
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
 #pragma unroll
     for (int nb = 0; nb < 16; ++nb)
@@ -397,7 +415,7 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
     bf16 *__restrict__ o_lat, float *__restrict__ lse) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     uint8_t MLA_LDS *lds = (uint8_t MLA_LDS *)lds_raw;
-    __shared__ int kmax_sh, flag_sh;
+    __shared__ int kmax_sh, flag_sh, wmin_sh[PF_NW];
     const int total = n_groups * n_chunks;
     // XCD-aware bijection: blocks bid, bid+8, ... run on one XCD; give each XCD a
     // contiguous range of logical indices.
@@ -417,19 +435,18 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
     int lim = -1;
     if (valid) lim = min(pos[t], n_kv - 1);
 
+    // key range of the group (max) and of each wave (min of the rows' last visible key)
+    if (threadIdx.x < PF_NW) wmin_sh[threadIdx.x] = INT32_MAX;
     if (threadIdx.x == 0) kmax_sh = -1;
     __syncthreads();
-    {
-        // max visible key over the group's rows
-        int v = lim;
-        for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-        if (l == 0) atomicMax(&kmax_sh, v);
-    }
+    atomicMax(&kmax_sh, lim);
+    atomicMin(&wmin_sh[w], lim);
     WaveState st;
     load_q(st, q_cat + ((int64_t)t * H + h) * fl::W);
     __syncthreads();
     const int kend = kmax_sh + 1;
-    attend_range<PF_NW, PF_NS, false>(st, lds, &flag_sh, cache, n_kv, 0, kend, lim, sc);
+    attend_range<PF_NW, PF_NS, false>(st, lds, &flag_sh, cache, n_kv, 0, kend, lim, wmin_sh[w],
+                                      sc);
     bf16 *dst = o_lat + ((int64_t)t * H + h) * fl::R;
     const float ls = finish(st, [&](int col, float a, float b, float c, float d) {
         if (valid) {
@@ -469,7 +486,7 @@ template <bool Q8>
 __global__ __launch_bounds__(64 * DC_NW, 1) void flash_decode_kernel(
     const bf16 *__restrict__ q_cat, int H, const uint8_t *__restrict__ cache,
     int64_t seq_stride, const int32_t *__restrict__ n_kv, int n_kv_max, int n_splits,
-    int split_len, float sc, float *__restrict__ part_o, float *__restrict__ part_lse) {
+    int split_len, float sc, bf16 *__restrict__ part_o, float *__restrict__ part_lse) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     uint8_t MLA_LDS *lds = (uint8_t MLA_LDS *)lds_raw;
     const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
@@ -483,13 +500,13 @@ __global__ __launch_bounds__(64 * DC_NW, 1) void flash_decode_kernel(
     load_q(st, q_cat + ((int64_t)b * H + (valid ? h : 0)) * fl::W);
     const uint8_t *rows = cache + b * seq_stride;
     __shared__ int flag_sh;
-    attend_range<DC_NW, DC_NS, Q8>(st, lds, &flag_sh, rows, nk, k0, k1, k1 - 1, sc);
+    attend_range<DC_NW, DC_NS, Q8>(st, lds, &flag_sh, rows, nk, k0, k1, k1 - 1, k1 - 1, sc);
     const int64_t pi = ((int64_t)b * n_splits + s) * H + h;
-    float *dst = part_o + pi * fl::R;
+    bf16 *dst = part_o + pi * fl::R;
     const float ls = finish(st, [&](int col, float a, float b_, float c, float d) {
         if (valid) {
-            f32x4 v = {a, b_, c, d};
-            *(f32x4 *)(dst + col) = v;
+            bf16x4 v = {f2bf(a), f2bf(b_), f2bf(c), f2bf(d)};
+            *(bf16x4 *)(dst + col) = v;
         }
     });
     if (valid && l < 32) part_lse[pi] = ls;
@@ -498,7 +515,7 @@ __global__ __launch_bounds__(64 * DC_NW, 1) void flash_decode_kernel(
 hipError_t launch_flash_decode_bf16(const bf16 *q_cat, const void *cache, int cache_q8,
                                     int64_t seq_stride_bytes, const int32_t *n_kv, int n_kv_max,
                                     int B, int H,
-                                    int n_splits, int split_len, float scale, float *part_o,
+                                    int n_splits, int split_len, float scale, bf16 *part_o,
                                     float *part_lse, hipStream_t st) {
     const int hgroups = (H + 32 * DC_NW - 1) / (32 * DC_NW);
     dim3 grid(n_splits, B, hgroups);

@@ -255,77 +255,110 @@ hipError_t launch_flash_simt_decode(const mla_dims &d, const float *q_cat, const
 }
 
 // ------------------------------------------------------------ split-KV combine
-// lse = log sum_s exp(lse_s); o = sum_s exp(lse_s - lse) o_s.  Block (b*H + h, column
-// slice of CB columns); splits with lse_s = -inf contribute nothing.  The split weights
-// are computed once per block into LDS; each thread then accumulates one column over
-// all splits (loads coalesced across the block, 8 splits in flight).
-constexpr int CB = 128;
+// lse = log sum_s exp(lse_s); o = sum_s exp(lse_s - lse) o_s (partials o_s float32 on the
+// float32 path, bfloat16 on the bf16 / Q8_0 path).  Splits with lse_s = -inf contribute
+// nothing.  Block (b*H + h, slice of CB_COLS columns) of CB_T threads: thread
+// (phase, group) accumulates 8 adjacent columns over splits phase, phase + CB_PH, ...
+// (one 16- or 32-byte load per split, several in flight), the phases are then summed
+// through LDS in a fixed order.
+constexpr int CB_T = 256, CB_COLS = 128, CB_GROUPS = CB_COLS / 8, CB_PH = CB_T / CB_GROUPS;
 
-template <typename OT>
-__global__ __launch_bounds__(CB) void combine_kernel(const float *__restrict__ part_o,
-                                                     const float *__restrict__ part_lse, int H,
-                                                     int R, int S, OT *__restrict__ o_lat,
-                                                     float *__restrict__ lse) {
-    extern __shared__ float wsh[];  // [S] weights, then [CB] reduction scratch
+template <typename PT> struct Vec8;
+template <> struct Vec8<float> {
+    static __device__ __forceinline__ void load(const float *p, float *v) {
+        const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
+        for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+    }
+};
+template <> struct Vec8<bf16> {
+    static __device__ __forceinline__ void load(const bf16 *p, float *v) {
+        const bf16x8 a = *(const bf16x8 *)p;
+        for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
+    }
+};
+
+template <typename PT, typename OT>
+__global__ __launch_bounds__(CB_T) void combine_kernel(const PT *__restrict__ part_o,
+                                                       const float *__restrict__ part_lse, int H,
+                                                       int R, int S, OT *__restrict__ o_lat,
+                                                       float *__restrict__ lse) {
+    extern __shared__ float wsh[];  // [S] weights | [CB_T] reduction | [CB_PH][CB_COLS] sums
     float *red = wsh + S;
+    float *acc_sh = red + CB_T;
     const int bh = blockIdx.x;
     const int b = bh / H, h = bh % H;
     const int tid = threadIdx.x;
     const float *pl = part_lse + (int64_t)b * S * H + h;
     float mx = -INFINITY;
-    for (int s = tid; s < S; s += CB) mx = fmaxf(mx, pl[(int64_t)s * H]);
+    for (int s = tid; s < S; s += CB_T) mx = fmaxf(mx, pl[(int64_t)s * H]);
     red[tid] = mx;
     __syncthreads();
-    for (int o = CB / 2; o > 0; o >>= 1) {
+    for (int o = CB_T / 2; o > 0; o >>= 1) {
         if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
         __syncthreads();
     }
     mx = red[0];
     __syncthreads();
     float sum = 0.0f;
-    for (int s = tid; s < S; s += CB) {
+    for (int s = tid; s < S; s += CB_T) {
         const float wgt = (mx == -INFINITY) ? 0.0f : expf(pl[(int64_t)s * H] - mx);
         wsh[s] = wgt;
         sum += wgt;
     }
     red[tid] = sum;
     __syncthreads();
-    for (int o = CB / 2; o > 0; o >>= 1) {
+    for (int o = CB_T / 2; o > 0; o >>= 1) {
         if (tid < o) red[tid] += red[tid + o];
         __syncthreads();
     }
     sum = red[0];
     const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
-    const int c = blockIdx.y * CB + tid;
-    if (c < R) {
-        const float *po = part_o + ((int64_t)b * S * H + h) * R + c;
+    const int grp = tid % CB_GROUPS, ph = tid / CB_GROUPS;
+    const int c0 = blockIdx.y * CB_COLS + grp * 8;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (c0 < R) {
+        const PT *po = part_o + ((int64_t)b * S * H + h) * R + c0;
         const int64_t stride = (int64_t)H * R;
-        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        int s = 0;
-        for (; s + 8 <= S; s += 8) {
+#pragma unroll 4
+        for (int s = ph; s < S; s += CB_PH) {
+            float v[8];
+            if (R % 8 == 0) {  // rows of 8-column groups: aligned vector loads, no overrun
+                Vec8<PT>::load(po + (int64_t)s * stride, v);
+            } else {
+                for (int i = 0; i < 8; ++i)
+                    v[i] = (c0 + i < R) ? ld_f(po + (int64_t)s * stride + i) : 0.0f;
+            }
+            const float wgt = wsh[s];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) acc[u] = fmaf(wsh[s + u], po[(int64_t)(s + u) * stride], acc[u]);
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt, v[i], acc[i]);
         }
-        for (; s < S; ++s) acc[0] = fmaf(wsh[s], po[(int64_t)s * stride], acc[0]);
-        const float tot = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-        st_f(o_lat + ((int64_t)b * H + h) * R + c, tot * inv);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc_sh[ph * CB_COLS + grp * 8 + i] = acc[i];
+    __syncthreads();
+    if (tid < CB_COLS) {
+        const int c = blockIdx.y * CB_COLS + tid;
+        float tot = 0.0f;
+        for (int p = 0; p < CB_PH; ++p) tot += acc_sh[p * CB_COLS + tid];
+        if (c < R) st_f(o_lat + ((int64_t)b * H + h) * R + c, tot * inv);
     }
     if (lse && blockIdx.y == 0 && tid == 0)
         lse[(int64_t)b * H + h] = sum > 0.0f ? mx + logf(sum) : -INFINITY;
 }
 
-template <typename OT>
-hipError_t launch_combine(const float *part_o, const float *part_lse, int B, int H, int R,
+template <typename PT, typename OT>
+hipError_t launch_combine(const PT *part_o, const float *part_lse, int B, int H, int R,
                           int n_splits, OT *o_lat, float *lse, hipStream_t st) {
-    dim3 grid(B * H, (R + CB - 1) / CB);
-    hipLaunchKernelGGL(combine_kernel<OT>, grid, dim3(CB), sizeof(float) * (n_splits + CB), st,
-                       part_o, part_lse, H, R, n_splits, o_lat, lse);
+    dim3 grid(B * H, (R + CB_COLS - 1) / CB_COLS);
+    const size_t shm = sizeof(float) * (n_splits + CB_T + CB_PH * CB_COLS);
+    hipLaunchKernelGGL((combine_kernel<PT, OT>), grid, dim3(CB_T), shm, st, part_o, part_lse, H,
+                       R, n_splits, o_lat, lse);
     return hipGetLastError();
 }
-template hipError_t launch_combine<float>(const float *, const float *, int, int, int, int,
-                                          float *, float *, hipStream_t);
-template hipError_t launch_combine<bf16>(const float *, const float *, int, int, int, int, bf16 *,
-                                         float *, hipStream_t);
+template hipError_t launch_combine<float, float>(const float *, const float *, int, int, int, int,
+                                                 float *, float *, hipStream_t);
+template hipError_t launch_combine<bf16, bf16>(const bf16 *, const float *, int, int, int, int,
+                                               bf16 *, float *, hipStream_t);
 
 // ------------------------------------------------------------------------ Q8_0
 // One thread per 32-value block.  Block layout: binary16 scale (little endian) then
