@@ -24,9 +24,12 @@
 // the pass, and the workgroup repeats the pass once with the marked rows starting
 // from their true max (unmarked rows recompute bit-identical values).
 //
-// LDS tile layout: row k (1152 B = 72 chunks of 16 B), logical chunk c stored at
-// chunk c ^ swz(k), swz(k) = (k & 7) ^ ((k >> 3) & 1): conflict-free for the
-// 16-byte K-fragment reads of 16 consecutive rows.
+// LDS tile layout (32 keys, 38912 B).  The latent part (512 bf16 = 64 chunks of 16 B per
+// key) sits in rows of pitch 1088 B, logical chunk c at chunk c ^ mask_a(k); the rope part
+// (64 bf16 = 8 chunks) follows in rows of 128 B, chunk c at c ^ mask_b(k).  One copy
+// instruction then moves one whole latent row (uniform global address, lane-contiguous
+// LDS), and both the 16-byte K-fragment reads and the transposing V reads are free of
+// bank conflicts (see mask_a and mask_b).
 #include "common.h"
 
 namespace mla {
@@ -36,8 +39,10 @@ constexpr int R = 512, DR = 64, W = 576;
 constexpr int RB = W * 2;         // 1152 bytes per bf16 row
 constexpr int WCH = W / 8;        // 72 chunks of 16 B per row
 constexpr int NK = 32;            // keys per tile
-constexpr int TILE_CH = NK * WCH;           // 2304 chunks
-constexpr int TILE_BYTES = TILE_CH * 16;    // 36864 B
+constexpr int PA = 1088;                    // latent row pitch: 1024 B + 64 B pad
+constexpr int A_BYTES = NK * PA;            // 34816 B
+constexpr int PB = 128;                     // rope row pitch
+constexpr int TILE_BYTES = A_BYTES + NK * PB;  // 38912 B
 constexpr int Q8_RB = W / 32 * 34;          // 612 B per Q8_0 row
 constexpr int Q8_TILE_BYTES = NK * Q8_RB;   // 19584 B, 16-B aligned for aligned tiles
 constexpr float LOG2E = 1.4426950408889634f;
@@ -45,7 +50,25 @@ constexpr float LN2 = 0.6931471805599453f;
 constexpr float FREEZE_LIMIT = 64.0f;  // log2 units a score may exceed the frozen max by
 }  // namespace fl
 
-__device__ __forceinline__ int fswz(int k) { return (k & 7) ^ ((k >> 3) & 1); }
+// LDS has 64 banks of 4 B, i.e. 16 groups of 16 B.
+// Latent rows: the pitch of 1088 B moves row k by 4k groups and the mask XORs the low
+// two chunk bits with (k >> 2) & 3, so
+//  - 16 consecutive rows read at one logical chunk (K fragments, 16 lanes per cycle)
+//    land in 16 distinct groups: 4 * (k & 3) picks the high part, the mask the low part;
+//  - a ds_read_b64_tr_b16 half-wave reads 4 consecutive rows (one mask value) x 4
+//    chunks: the rows pick distinct high parts, the chunks distinct low parts.
+__device__ __forceinline__ int mask_a(int k) { return (k >> 2) & 3; }
+// Rope rows (128 B = half a bank row): even and odd rows take the two halves, and bits
+// (k1, k2, k3) of the row index as bits (2, 1, 0) of the mask spread 8 even (odd) rows
+// over the 8 groups of their half.
+__device__ __forceinline__ int mask_b(int k) {
+    return (((k >> 1) & 1) << 2) | (((k >> 2) & 1) << 1) | ((k >> 3) & 1);
+}
+// Byte offset of logical chunk c (0 .. 71) of key k in a tile.
+__device__ __forceinline__ int tile_off(int k, int c) {
+    return c < 64 ? k * fl::PA + ((c ^ mask_a(k)) * 16)
+                  : fl::A_BYTES + k * fl::PB + (((c - 64) ^ mask_b(k)) * 16);
+}
 
 // Lanes l and l^32 hold the same query row; these combine the pair (ds_bpermute).
 // Both halves compute (x[l % 32] op x[32 + l % 32]), so the results are bit-identical.
@@ -66,33 +89,45 @@ __device__ __forceinline__ bf16x8 tr_pair(const uint8_t MLA_LDS *p0, const uint8
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// Issue the async copy of one bf16 tile (32 rows starting at key0; rows past `last`
-// re-read row `last`, they are masked out of the softmax) into LDS stage `dst`.
+// Async copy of one bf16 tile (32 keys from key0; keys past `last` re-read key `last`,
+// they are masked out of the softmax) into LDS stage `dst`.  Part i (0 .. 8) of wave w:
+// parts 0..7 copy the latent row 8w + i (one instruction, uniform source row), part 8
+// copies the rope rows 8w .. 8w+7 (one instruction).
+template <int NW>
+__device__ __forceinline__ void issue_chunk_bf16(const uint8_t *__restrict__ rows, int key0,
+                                                 int last, uint8_t MLA_LDS *dst, int i) {
+    static_assert(NW == 4, "one latent row per instruction: 8 rows and one rope part per wave");
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // The lane index is made opaque so that the per-lane offsets below are recomputed at
+    // each call (one or two integer ops) instead of being hoisted, kept and spilled: a
+    // scratch reload is a vector-memory load, and waiting for it would also wait for
+    // every earlier tile copy.
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));
+    if (i < 8) {
+        const int k = w * 8 + i;
+        const uint8_t *src = rows + (int64_t)min(key0 + k, last) * fl::RB;
+        uint32_t off = (uint32_t)((l ^ mask_a(k)) * 16);
+        asm volatile("" : "+v"(off));  // keep (uniform base) + (32-bit lane offset) addressing
+        __builtin_amdgcn_global_load_lds((const void *)(src + off),
+                                         (void MLA_LDS *)(dst + k * fl::PA), 16, 0, 0);
+    } else {
+        // rows past `last` are clamped per lane; offsets stay below 32 rows
+        const int k = w * 8 + (l >> 3);
+        const int kr = min(k, last - key0);
+        uint32_t off = (uint32_t)(kr * fl::RB + fl::R * 2 + (((l & 7) ^ mask_b(k)) * 16));
+        asm volatile("" : "+v"(off));
+        __builtin_amdgcn_global_load_lds((const void *)(rows + (int64_t)key0 * fl::RB + off),
+                                         (void MLA_LDS *)(dst + fl::A_BYTES + w * 1024), 16, 0,
+                                         0);
+    }
+}
+
 template <int NW>
 __device__ __forceinline__ void issue_tile_bf16(const uint8_t *__restrict__ rows, int key0,
                                                 int last, uint8_t MLA_LDS *dst) {
-    constexpr int NI = fl::TILE_CH / (64 * NW);  // instructions per wave
-    static_assert(fl::TILE_CH % (64 * NW) == 0, "tile chunks must split evenly over waves");
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // The lane index is made opaque so that the per-lane offsets below are recomputed at
-    // each call (a few integer ops) instead of being hoisted, kept and spilled: a scratch
-    // reload is a vector-memory load, and waiting for it would also wait for every
-    // earlier tile copy.
-    int l = threadIdx.x & 63;
-    asm volatile("" : "+v"(l));
-    // rows past `last` are clamped; offsets stay below 2^31 for caches < 2 GiB per call
-    const uint8_t *base = rows + (int64_t)key0 * fl::RB;
-    const int lim = last - key0;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int P = (w * NI + i) * 64 + l;  // physical chunk in the tile
-        const int k = P / fl::WCH;
-        const int c = (P % fl::WCH) ^ fswz(k);
-        uint32_t off = (uint32_t)(min(k, lim) * fl::RB + c * 16);
-        asm volatile("" : "+v"(off));  // keep (uniform base) + (32-bit lane offset) addressing
-        __builtin_amdgcn_global_load_lds((const void *)(base + off),
-                                         (void MLA_LDS *)(dst + (w * NI + i) * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < 9; ++i) issue_chunk_bf16<NW>(rows, key0, last, dst, i);
 }
 
 // Issue the async copy of the raw Q8_0 bytes of a 32-row tile into LDS, one dword per
@@ -166,7 +201,7 @@ __device__ __forceinline__ void dequant_tile_q8(const uint8_t MLA_LDS *raw, int 
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
             const int c = b * 4 + qq;
-            uint8_t MLA_LDS *p = dst + k * fl::RB + ((c ^ fswz(k)) * 16);
+            uint8_t MLA_LDS *p = dst + tile_off(k, c);
             bf16x8 t;
 #pragma unroll
             for (int e = 0; e < 8; ++e) t[e] = v[qq * 8 + e];
@@ -184,23 +219,36 @@ struct WaveState {
     bool bad;         // a score exceeded m + FREEZE_LIMIT: this pass is discarded
 };
 
+struct NoPrefetch {
+    __device__ __forceinline__ void operator()(int) const {}
+};
+
 // One tile: keys key0 .. key0+31 in LDS stage `t`.  Keys with index > lim are masked.
+// pf(i), i = 0 .. 8, issues part i of the next tile's copy; calls are spread over the
+// score MFMAs so their address arithmetic overlaps matrix work.
+template <typename Pf>
 __device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t MLA_LDS *t, int key0,
-                                            int lim, int wave_lim_min, float sc) {
+                                            int lim, int wave_lim_min, float sc, Pf pf) {
     const int l = threadIdx.x & 63;
     const int hi = l >> 5;
-// ---- S^T = K Q^T.  Chunk (2kk + hi) ^ swz(k) = 8*(kk/4) + ((2*(kk%4) + hi) ^ swz(k)):
-    // four lane-dependent bases plus compile-time offsets.
+    // ---- S^T = K Q^T.  Latent chunk 2kk + hi (kk < 32) is stored at
+    // 4*(kk/2) + ((2*(kk%2) + hi) ^ mask_a(k)): two lane-dependent bases plus compile-time
+    // offsets; the four rope chunks (kk = 32 .. 35) take one address each.
     f32x16 s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.0f;
     {
         const int k = l & 31;
-        const int sw = fswz(k);
-        const uint8_t MLA_LDS *rowp = t + k * fl::RB;
-        const uint8_t MLA_LDS *kb[4];
+        const int ma = mask_a(k), mb = mask_b(k);
+        const uint8_t MLA_LDS *rowa = t + k * fl::PA;
+        const uint8_t MLA_LDS *rowb = t + fl::A_BYTES + k * fl::PB;
+        const uint8_t MLA_LDS *kb[2];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) kb[b] = rowp + (((2 * b + hi) ^ sw) * 16);
+        for (int b = 0; b < 2; ++b) kb[b] = rowa + (((2 * b + hi) ^ ma) * 16);
+        auto kaddr = [&](int kk) -> const uint8_t MLA_LDS * {
+            return kk < 32 ? kb[kk & 1] + (kk >> 1) * 64
+                           : rowb + (((2 * (kk - 32) + hi) ^ mb) * 16);
+        };
         // software pipeline: the fragment for step kk+QK_AHEAD is requested right after the
         // MFMA of step kk, so LDS latency overlaps QK_AHEAD matrix operations.  One
         // accumulator chain: dependent 32x32x16 MFMAs issue at the independent rate.
@@ -208,15 +256,35 @@ __device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t MLA_LDS
         bf16x8 a[QK_AHEAD];
 #pragma unroll
         for (int kk = 0; kk < QK_AHEAD; ++kk)
-            a[kk] = *(const bf16x8 MLA_LDS *)(kb[kk & 3] + (kk >> 2) * 128);
+            a[kk] = *(const bf16x8 MLA_LDS *)kaddr(kk);
 #pragma unroll
         for (int kk = 0; kk < 36; ++kk) {
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk % QK_AHEAD], st.q[kk], s, 0, 0, 0);
             const int nk = kk + QK_AHEAD;
-            if (nk < 36) a[kk % QK_AHEAD] = *(const bf16x8 MLA_LDS *)(kb[nk & 3] + (nk >> 2) * 128);
+            if (nk < 36) a[kk % QK_AHEAD] = *(const bf16x8 MLA_LDS *)kaddr(nk);
+            if ((kk & 3) == 1) pf(kk >> 2);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    // ---- V^T fragment addressing; the first PV_AHEAD reads are issued before the softmax
+    const int G = l >> 4, lam = l & 15;
+    const int kin = (G >> 1) * 4 + (lam >> 2);            // key within an 8-key group
+    const int colb = (G & 1) * 16 + 4 * (lam & 3);         // column within a 32-column block
+    // Row ks*16 + half*8 + kin has mask mask_a(half*8 + kin); chunk 4nb + c3 (c3 < 4) is
+    // stored at 4nb + (c3 ^ mask): one base per row half plus compile-time offsets.
+    const int c3 = colb >> 3, cb = (colb & 7) * 2;
+    const uint8_t MLA_LDS *vb[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+        vb[half] = t + (half * 8 + kin) * fl::PA + ((c3 ^ mask_a(half * 8 + kin)) * 16) + cb;
+    constexpr int PV_AHEAD = 4;
+    auto vaddr = [&](int i, int half) {
+        const int ks = i >> 4, nb = i & 15;
+        return vb[half] + ks * 16 * fl::PA + nb * 64;
+    };
+    bf16x8 va[PV_AHEAD];
+#pragma unroll
+    for (int i = 0; i < PV_AHEAD; ++i) va[i] = tr_pair(vaddr(i, 0), vaddr(i, 1));
     // ---- softmax: lane holds row l%32, keys (e/4)*8 + hi*4 + e%4.  Masking is only
     // needed on tiles that reach past some row's last visible key (wave-uniform test).
     float tmax = -INFINITY;
@@ -237,40 +305,18 @@ __device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t MLA_LDS
         st.m = fmaxf(st.m, tmax);  // track the true max for the repeated pass
     }
     const float nmu = (st.m == -INFINITY) ? 0.0f : -st.m;
+    // weights of the first 16 keys now; those of the second 16 while the first PV k-step
+    // runs (one element per MFMA)
     bf16x8 p[2];
     float psum = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < 8; ++e) {
         const float pe = __builtin_amdgcn_exp2f(fmaf(s[e], sc, nmu));  // masked: exp2(-inf) = 0
         psum += pe;
-        p[e >> 3][e & 7] = f2bf(pe);
+        p[0][e] = f2bf(pe);
     }
-    st.lsum += psum;
-    // ---- O^T += V^T P^T  (two k-steps of 16 keys, 16 column blocks of 32)
-    const int G = l >> 4, lam = l & 15;
-    const int kin = (G >> 1) * 4 + (lam >> 2);            // key within an 8-key group
-    const int colb = (G & 1) * 16 + 4 * (lam & 3);         // column within a 32-column block
-    // rows ks*16 + kin have swizzle kin, rows ks*16 + 8 + kin have swizzle kin ^ 1.
-    // Chunk (4nb + c3) ^ sw = 8*(nb/2) + ((4*(nb%2) + c3) ^ sw): bases per (row half, nb%2).
-    const int sw0 = fswz(kin), sw1 = fswz(kin + 8);
-    const int c3 = colb >> 3, cb = (colb & 7) * 2;
-    const uint8_t MLA_LDS *r0 = t + kin * fl::RB;
-    const uint8_t MLA_LDS *r1 = r0 + 8 * fl::RB;
-    const uint8_t MLA_LDS *vb[2][2];
-#pragma unroll
-    for (int par = 0; par < 2; ++par) {
-        vb[0][par] = r0 + (((4 * par + c3) ^ sw0) * 16) + cb;
-        vb[1][par] = r1 + (((4 * par + c3) ^ sw1) * 16) + cb;
-    }
-    // 32 steps (ks, nb) with the same read-ahead ring as the score loop
-    constexpr int PV_AHEAD = 4;
-    auto vaddr = [&](int i, int half) {
-        const int ks = i >> 4, nb = i & 15;
-        return vb[half][nb & 1] + ks * 16 * fl::RB + (nb >> 1) * 128;
-    };
-    bf16x8 va[PV_AHEAD];
-#pragma unroll
-    for (int i = 0; i < PV_AHEAD; ++i) va[i] = tr_pair(vaddr(i, 0), vaddr(i, 1));
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- O^T += V^T P^T: 32 steps (ks, nb) with the same read-ahead ring
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
         const int ks = i >> 4, nb = i & 15;
@@ -278,8 +324,14 @@ __device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t MLA_LDS
                                                            0);
         const int ni = i + PV_AHEAD;
         if (ni < 32) va[i % PV_AHEAD] = tr_pair(vaddr(ni, 0), vaddr(ni, 1));
+        if (i < 8) {
+            const float pe = __builtin_amdgcn_exp2f(fmaf(s[8 + i], sc, nmu));
+            psum += pe;
+            p[1][i] = f2bf(pe);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
+    st.lsum += psum;
 }
 
 // Rows that are not valid load a valid row's query instead (their keys are all masked,
@@ -309,7 +361,7 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
     if (kend <= kbeg) return;
     const int ntiles = (kend - kbeg + fl::NK - 1) / fl::NK;
     if constexpr (!Q8) {
-        constexpr int PER = fl::TILE_CH / (64 * NW);
+        constexpr int PER = 9;  // copy instructions per wave per tile (issue_chunk_bf16)
         const int last = n_rows - 1;
 #pragma unroll
         for (int s = 0; s < NS - 1; ++s)
@@ -326,9 +378,14 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             }
             __syncthreads();
             const int nx = ti + NS - 1;
-            if (nx < ntiles)
-                issue_tile_bf16<NW>(rows, kbeg + nx * fl::NK, last, lds + (nx % NS) * fl::TILE_BYTES);
-            attend_tile(st, lds + (ti % NS) * fl::TILE_BYTES, kbeg + ti * fl::NK, lim, wlim, sc);
+            uint8_t MLA_LDS *ndst = lds + (nx % NS) * fl::TILE_BYTES;
+            const int nkey0 = kbeg + nx * fl::NK;
+            const bool more = nx < ntiles;
+            auto pf = [&](int i) {
+                if (more) issue_chunk_bf16<NW>(rows, nkey0, last, ndst, i);
+            };
+            attend_tile(st, lds + (ti % NS) * fl::TILE_BYTES, kbeg + ti * fl::NK, lim, wlim, sc,
+                        pf);
         }
         __syncthreads();
     } else {
@@ -350,7 +407,8 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             if (ti + 2 < ntiles)
                 issue_tile_q8<NW>(rows, kbeg + (ti + 2) * fl::NK, n_rows,
                                   raw + (ti % 2) * Q8_RAW_STAGE);
-            attend_tile(st, lds + (ti % 2) * fl::TILE_BYTES, kbeg + ti * fl::NK, lim, wlim, sc);
+            attend_tile(st, lds + (ti % 2) * fl::TILE_BYTES, kbeg + ti * fl::NK, lim, wlim, sc,
+                        NoPrefetch{});
             if (ti + 1 < ntiles) {
                 if (ti + 2 < ntiles) {
                     MLA_WAIT_VMCNT(PER);
