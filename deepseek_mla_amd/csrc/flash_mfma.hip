@@ -89,6 +89,31 @@ __device__ __forceinline__ bf16x8 tr_pair(const uint8_t MLA_LDS *p0, const uint8
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// One LDS-direct copy instruction: lane l moves 16 bytes from sbase + voff (sbase uniform)
+// to LDS address lds_addr + 16*l (lds_addr uniform, through M0).  Written as inline asm so
+// that the compiler's LDS wait tracking does not see it: the compiler follows the builtin
+// form with a wait for every outstanding LDS read, which would drain the read rings of the
+// tile loop.  Completion is tracked by hand: a vmcnt wait and a barrier precede every read
+// of a copied tile, and no other vector-memory instruction is issued in the tile loop.
+__device__ __forceinline__ void lds_copy16(const uint8_t *sbase, uint32_t voff,
+                                           uint32_t lds_addr) {
+    const uint64_t a = (uint64_t)sbase;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint64_t su = ((uint64_t)hi << 32) | lo;
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(su), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+        : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const uint8_t MLA_LDS *p) {
+    return (uint32_t)(uintptr_t)p;
+}
+
 // Async copy of one bf16 tile (32 keys from key0; keys past `last` re-read key `last`,
 // they are masked out of the softmax) into LDS stage `dst`.  Part i (0 .. 8) of wave w:
 // parts 0..7 copy the latent row 8w + i (one instruction, uniform source row), part 8
@@ -98,28 +123,18 @@ __device__ __forceinline__ void issue_chunk_bf16(const uint8_t *__restrict__ row
                                                  int last, uint8_t MLA_LDS *dst, int i) {
     static_assert(NW == 4, "one latent row per instruction: 8 rows and one rope part per wave");
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // The lane index is made opaque so that the per-lane offsets below are recomputed at
-    // each call (one or two integer ops) instead of being hoisted, kept and spilled: a
-    // scratch reload is a vector-memory load, and waiting for it would also wait for
-    // every earlier tile copy.
-    int l = threadIdx.x & 63;
-    asm volatile("" : "+v"(l));
+    const int l = threadIdx.x & 63;
     if (i < 8) {
         const int k = w * 8 + i;
         const uint8_t *src = rows + (int64_t)min(key0 + k, last) * fl::RB;
-        uint32_t off = (uint32_t)((l ^ mask_a(k)) * 16);
-        asm volatile("" : "+v"(off));  // keep (uniform base) + (32-bit lane offset) addressing
-        __builtin_amdgcn_global_load_lds((const void *)(src + off),
-                                         (void MLA_LDS *)(dst + k * fl::PA), 16, 0, 0);
+        lds_copy16(src, (uint32_t)((l ^ mask_a(k)) * 16), lds_u32(dst + k * fl::PA));
     } else {
         // rows past `last` are clamped per lane; offsets stay below 32 rows
         const int k = w * 8 + (l >> 3);
         const int kr = min(k, last - key0);
-        uint32_t off = (uint32_t)(kr * fl::RB + fl::R * 2 + (((l & 7) ^ mask_b(k)) * 16));
-        asm volatile("" : "+v"(off));
-        __builtin_amdgcn_global_load_lds((const void *)(rows + (int64_t)key0 * fl::RB + off),
-                                         (void MLA_LDS *)(dst + fl::A_BYTES + w * 1024), 16, 0,
-                                         0);
+        lds_copy16(rows + (int64_t)key0 * fl::RB,
+                   (uint32_t)(kr * fl::RB + fl::R * 2 + (((l & 7) ^ mask_b(k)) * 16)),
+                   lds_u32(dst + fl::A_BYTES + w * 1024));
     }
 }
 
@@ -219,119 +234,173 @@ struct WaveState {
     bool bad;         // a score exceeded m + FREEZE_LIMIT: this pass is discarded
 };
 
-struct NoPrefetch {
-    __device__ __forceinline__ void operator()(int) const {}
-};
-
-// One tile: keys key0 .. key0+31 in LDS stage `t`.  Keys with index > lim are masked.
-// pf(i), i = 0 .. 8, issues part i of the next tile's copy; calls are spread over the
-// score MFMAs so their address arithmetic overlaps matrix work.
-template <typename Pf>
-__device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t MLA_LDS *t, int key0,
-                                            int lim, int wave_lim_min, float sc, Pf pf) {
-    const int l = threadIdx.x & 63;
-    const int hi = l >> 5;
-    // ---- S^T = K Q^T.  Latent chunk 2kk + hi (kk < 32) is stored at
-    // 4*(kk/2) + ((2*(kk%2) + hi) ^ mask_a(k)): two lane-dependent bases plus compile-time
-    // offsets; the four rope chunks (kk = 32 .. 35) take one address each.
+// Score product S^T = K Q^T of the tile in stage t: 36 MFMAs on one accumulator chain.
+// Step kk requests the K fragment of step kk + QK_AHEAD right after its MFMA, so LDS
+// latency overlaps matrix work; fill(kk) places other work (the previous tile's softmax,
+// copy issue) between the MFMAs.  Latent chunk 2kk + hi (kk < 32) is stored at
+// 4*(kk/2) + ((2*(kk%2) + hi) ^ mask_a(k)): two lane-dependent bases plus compile-time
+// offsets; the four rope chunks (kk = 32 .. 35) take one address each.
+template <typename Fill>
+__device__ __forceinline__ f32x16 score_tile(const WaveState &st, const uint8_t MLA_LDS *t,
+                                             Fill fill) {
+    const int l = threadIdx.x & 63, hi = l >> 5;
+    const int k = l & 31;
+    const int ma = mask_a(k), mb = mask_b(k);
+    const uint8_t MLA_LDS *rowa = t + k * fl::PA;
+    const uint8_t MLA_LDS *rowb = t + fl::A_BYTES + k * fl::PB;
+    const uint8_t MLA_LDS *kb[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) kb[b] = rowa + (((2 * b + hi) ^ ma) * 16);
+    auto kaddr = [&](int kk) -> const uint8_t MLA_LDS * {
+        return kk < 32 ? kb[kk & 1] + (kk >> 1) * 64 : rowb + (((2 * (kk - 32) + hi) ^ mb) * 16);
+    };
     f32x16 s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.0f;
-    {
-        const int k = l & 31;
-        const int ma = mask_a(k), mb = mask_b(k);
-        const uint8_t MLA_LDS *rowa = t + k * fl::PA;
-        const uint8_t MLA_LDS *rowb = t + fl::A_BYTES + k * fl::PB;
-        const uint8_t MLA_LDS *kb[2];
+    constexpr int QK_AHEAD = 4;
+    bf16x8 a[QK_AHEAD];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) kb[b] = rowa + (((2 * b + hi) ^ ma) * 16);
-        auto kaddr = [&](int kk) -> const uint8_t MLA_LDS * {
-            return kk < 32 ? kb[kk & 1] + (kk >> 1) * 64
-                           : rowb + (((2 * (kk - 32) + hi) ^ mb) * 16);
-        };
-        // software pipeline: the fragment for step kk+QK_AHEAD is requested right after the
-        // MFMA of step kk, so LDS latency overlaps QK_AHEAD matrix operations.  One
-        // accumulator chain: dependent 32x32x16 MFMAs issue at the independent rate.
-        constexpr int QK_AHEAD = 4;
-        bf16x8 a[QK_AHEAD];
+    for (int kk = 0; kk < QK_AHEAD; ++kk) a[kk] = *(const bf16x8 MLA_LDS *)kaddr(kk);
 #pragma unroll
-        for (int kk = 0; kk < QK_AHEAD; ++kk)
-            a[kk] = *(const bf16x8 MLA_LDS *)kaddr(kk);
-#pragma unroll
-        for (int kk = 0; kk < 36; ++kk) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk % QK_AHEAD], st.q[kk], s, 0, 0, 0);
-            const int nk = kk + QK_AHEAD;
-            if (nk < 36) a[kk % QK_AHEAD] = *(const bf16x8 MLA_LDS *)kaddr(nk);
-            if ((kk & 3) == 1) pf(kk >> 2);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    for (int kk = 0; kk < 36; ++kk) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk % QK_AHEAD], st.q[kk], s, 0, 0, 0);
+        const int nk = kk + QK_AHEAD;
+        if (nk < 36) a[kk % QK_AHEAD] = *(const bf16x8 MLA_LDS *)kaddr(nk);
+        fill(kk);
+        __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- V^T fragment addressing; the first PV_AHEAD reads are issued before the softmax
-    const int G = l >> 4, lam = l & 15;
-    const int kin = (G >> 1) * 4 + (lam >> 2);            // key within an 8-key group
-    const int colb = (G & 1) * 16 + 4 * (lam & 3);         // column within a 32-column block
-    // Row ks*16 + half*8 + kin has mask mask_a(half*8 + kin); chunk 4nb + c3 (c3 < 4) is
-    // stored at 4nb + (c3 ^ mask): one base per row half plus compile-time offsets.
-    const int c3 = colb >> 3, cb = (colb & 7) * 2;
-    const uint8_t MLA_LDS *vb[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-        vb[half] = t + (half * 8 + kin) * fl::PA + ((c3 ^ mask_a(half * 8 + kin)) * 16) + cb;
-    constexpr int PV_AHEAD = 4;
-    auto vaddr = [&](int i, int half) {
-        const int ks = i >> 4, nb = i & 15;
-        return vb[half] + ks * 16 * fl::PA + nb * 64;
-    };
-    bf16x8 va[PV_AHEAD];
-#pragma unroll
-    for (int i = 0; i < PV_AHEAD; ++i) va[i] = tr_pair(vaddr(i, 0), vaddr(i, 1));
-    // ---- softmax: lane holds row l%32, keys (e/4)*8 + hi*4 + e%4.  Masking is only
-    // needed on tiles that reach past some row's last visible key (wave-uniform test).
-    float tmax = -INFINITY;
-    if (key0 + fl::NK - 1 > wave_lim_min) {
+    return s;
+}
+
+// Softmax set-up for the raw scores s of keys key0 .. key0+31 (lane: row l%32, keys
+// (e/4)*8 + hi*4 + e%4); keys past lim are masked.  The row's reference max is frozen at
+// its first visible tile, so the tile max is only needed while some row of the wave has
+// no reference yet or is marked (wave-uniform branch).  Returns the exponent offset -m.
+__device__ __forceinline__ float softmax_prep(WaveState &st, f32x16 &s, int key0, int lim,
+                                              int wave_lim_min, float sc) {
+    const int hi = (threadIdx.x & 63) >> 5;
+    if (key0 + fl::NK - 1 > wave_lim_min) {  // masking only where some row ends in the tile
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int key = key0 + (e >> 2) * 8 + hi * 4 + (e & 3);
             s[e] = (key <= lim) ? s[e] : -INFINITY;
         }
     }
+    if (__builtin_amdgcn_ballot_w64((st.m == -INFINITY && key0 <= lim) || st.bad)) {
+        float tmax = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[e]);
-    tmax = pair_max(tmax) * sc;  // sc > 0: max of scaled = scaled max
-    if (st.m == -INFINITY) {
-        st.m = tmax;  // first visible keys of this row (o and lsum are still zero)
-    } else if (tmax > st.m + fl::FREEZE_LIMIT || st.bad) {
-        st.bad = true;
-        st.m = fmaxf(st.m, tmax);  // track the true max for the repeated pass
+        for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[e]);
+        tmax = pair_max(tmax) * sc;  // sc > 0: max of scaled = scaled max
+        if (st.m == -INFINITY) {
+            st.m = tmax;  // first visible keys of this row (o and lsum are still zero)
+        } else if (tmax > st.m + fl::FREEZE_LIMIT || st.bad) {
+            st.bad = true;
+            st.m = fmaxf(st.m, tmax);  // track the true max for the repeated pass
+        }
     }
-    const float nmu = (st.m == -INFINITY) ? 0.0f : -st.m;
-    // weights of the first 16 keys now; those of the second 16 while the first PV k-step
-    // runs (one element per MFMA)
-    bf16x8 p[2];
-    float psum = 0.0f;
+    return (st.m == -INFINITY) ? 0.0f : -st.m;
+}
+
+// Overflow test of the frozen max.  A weight above 2^FREEZE_LIMIT makes this lane's tile
+// sum exceed it, so the exact test (tile max against m + FREEZE_LIMIT, as in
+// softmax_prep) only runs when some lane's sum does.
+__device__ __forceinline__ void softmax_check(WaveState &st, const f32x16 &s, float psum,
+                                              float sc) {
+    if (__builtin_amdgcn_ballot_w64(!(psum <= 0x1p64f))) {
+        float tmax = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(fmaf(s[e], sc, nmu));  // masked: exp2(-inf) = 0
-        psum += pe;
-        p[0][e] = f2bf(pe);
+        for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[e]);
+        tmax = pair_max(tmax) * sc;
+        if (st.m != -INFINITY && tmax > st.m + fl::FREEZE_LIMIT) {
+            st.bad = true;
+            st.m = fmaxf(st.m, tmax);
+        }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- O^T += V^T P^T: 32 steps (ks, nb) with the same read-ahead ring
+}
+static_assert(fl::FREEZE_LIMIT == 64.0f, "softmax_check compares against 2^64");
+
+// V^T fragment addressing of the tile in stage t for O^T += V^T P^T.  Lane: key
+// kin + 8*half (+16 ks) and 4 columns at colb of each 32-column block.  Row
+// ks*16 + half*8 + kin has mask mask_a(half*8 + kin); chunk 4nb + c3 (c3 < 4) is stored at
+// 4nb + (c3 ^ mask): one base per row half plus compile-time offsets.
+struct VAddr {
+    const uint8_t MLA_LDS *vb[2];
+    __device__ __forceinline__ explicit VAddr(const uint8_t MLA_LDS *t) {
+        const int l = threadIdx.x & 63;
+        const int G = l >> 4, lam = l & 15;
+        const int kin = (G >> 1) * 4 + (lam >> 2);     // key within an 8-key group
+        const int colb = (G & 1) * 16 + 4 * (lam & 3);  // column within a 32-column block
+        const int c3 = colb >> 3, cb = (colb & 7) * 2;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+            vb[half] = t + (half * 8 + kin) * fl::PA + ((c3 ^ mask_a(half * 8 + kin)) * 16) + cb;
+    }
+    __device__ __forceinline__ bf16x8 load(int i) const {  // step i = (ks, nb) = (i/16, i%16)
+        const int off = (i >> 4) * 16 * fl::PA + (i & 15) * 64;
+        return tr_pair(vb[0] + off, vb[1] + off);
+    }
+};
+
+constexpr int PV_AHEAD = 4;
+
+// Weight of key slot e (e < 16) of this lane: exp2(s*sc - m); masked keys give 0.
+__device__ __forceinline__ void soft_piece(const f32x16 &s, int e, float sc, float nmu,
+                                           float &psum, bf16x8 (&p)[2]) {
+    const float pe = __builtin_amdgcn_exp2f(fmaf(s[e], sc, nmu));
+    psum += pe;
+    p[e >> 3][e & 7] = f2bf(pe);
+}
+
+// O^T += V^T P^T over the 32 keys of a tile: 32 steps (ks, nb) with a read-ahead ring
+// whose first PV_AHEAD entries the caller loaded; fill(i) is placed after MFMA i.
+template <typename Fill>
+__device__ __forceinline__ void pv_tile(WaveState &st, const VAddr &va_addr,
+                                        bf16x8 (&va)[PV_AHEAD], const bf16x8 (&p)[2], Fill fill) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
         const int ks = i >> 4, nb = i & 15;
         st.o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % PV_AHEAD], p[ks], st.o[nb], 0, 0,
                                                            0);
         const int ni = i + PV_AHEAD;
-        if (ni < 32) va[i % PV_AHEAD] = tr_pair(vaddr(ni, 0), vaddr(ni, 1));
-        if (i < 8) {
-            const float pe = __builtin_amdgcn_exp2f(fmaf(s[8 + i], sc, nmu));
-            psum += pe;
-            p[1][i] = f2bf(pe);
-        }
+        if (ni < 32) va[i % PV_AHEAD] = va_addr.load(ni);
+        fill(i);
         __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+// Softmax of one tile's raw scores s while the O update of the previous tile runs: step 0
+// masks and sets the reference, steps 1..16 compute one weight each, step 17 tests for
+// overflow.  The weights land in p, their sum in psum.
+struct SoftFill {
+    WaveState &st;
+    f32x16 &s;
+    bf16x8 (&p)[2];
+    float &psum;
+    float &nmu;
+    int key0, lim, wave_lim_min;
+    float sc;
+    __device__ __forceinline__ void operator()(int i) const {
+        if (i == 0) nmu = softmax_prep(st, s, key0, lim, wave_lim_min, sc);
+        if (i >= 1 && i <= 16) soft_piece(s, i - 1, sc, nmu, psum, p);
+        if (i == 17) softmax_check(st, s, psum, sc);
+    }
+};
+
+// Whole-tile step without the cross-tile pipeline (Q8_0 stream): scores, softmax, O.
+__device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t MLA_LDS *t, int key0,
+                                            int lim, int wave_lim_min, float sc) {
+    const VAddr va_addr(t);
+    bf16x8 va[PV_AHEAD];
+    f32x16 s = score_tile(st, t, [&](int kk) {
+        if (kk >= 36 - PV_AHEAD) va[kk - (36 - PV_AHEAD)] = va_addr.load(kk - (36 - PV_AHEAD));
+    });
+    float nmu = 0.0f, psum = 0.0f;
+    bf16x8 p[2];
+    const SoftFill soft{st, s, p, psum, nmu, key0, lim, wave_lim_min, sc};
+#pragma unroll
+    for (int i = 0; i < 18; ++i) soft(i);
     st.lsum += psum;
+    pv_tile(st, va_addr, va, p, [](int) {});
 }
 
 // Rows that are not valid load a valid row's query instead (their keys are all masked,
@@ -364,28 +433,53 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
         constexpr int PER = 9;  // copy instructions per wave per tile (issue_chunk_bf16)
         const int last = n_rows - 1;
 #pragma unroll
-        for (int s = 0; s < NS - 1; ++s)
+        for (int s = 0; s < 2; ++s)
             if (s < ntiles) issue_tile_bf16<NW>(rows, kbeg + s * fl::NK, last, lds + s * fl::TILE_BYTES);
+        // Iteration t: wait for tile t, scores of tile t (with the copy of tile t+2 into
+        // the stage tile t-2 used, free since the barrier), then the O update of tile t-1
+        // carrying the softmax of tile t.  Tile t-1 stays resident for its V reads.
+        static_assert(NS == 4, "tiles t-1 .. t+2 resident or in flight");
+        bf16x8 pprev[2];
         for (int ti = 0; ti < ntiles; ++ti) {
-            // wait until this wave's copies for tile ti landed
-            const int after = min(NS - 2, ntiles - 1 - ti);  // tiles issued after ti
-            if (after >= 2) {
-                MLA_WAIT_VMCNT(2 * PER);
-            } else if (after == 1) {
+            if (ti + 1 < ntiles) {
                 MLA_WAIT_VMCNT(PER);
             } else {
                 MLA_WAIT_VMCNT(0);
             }
             __syncthreads();
-            const int nx = ti + NS - 1;
+            const int nx = ti + 2;
             uint8_t MLA_LDS *ndst = lds + (nx % NS) * fl::TILE_BYTES;
             const int nkey0 = kbeg + nx * fl::NK;
             const bool more = nx < ntiles;
-            auto pf = [&](int i) {
-                if (more) issue_chunk_bf16<NW>(rows, nkey0, last, ndst, i);
-            };
-            attend_tile(st, lds + (ti % NS) * fl::TILE_BYTES, kbeg + ti * fl::NK, lim, wlim, sc,
-                        pf);
+            // The whole copy is issued before the score loop starts its LDS read ring: the
+            // compiler follows an LDS-direct copy with a wait for every outstanding LDS
+            // read, which inside the ring would stall the next MFMA.
+            if (more) issue_tile_bf16<NW>(rows, nkey0, last, ndst);
+            const VAddr vprev(lds + ((ti + NS - 1) % NS) * fl::TILE_BYTES);
+            bf16x8 va[PV_AHEAD];
+            f32x16 s = score_tile(st, lds + (ti % NS) * fl::TILE_BYTES, [&](int kk) {
+                if (ti > 0 && kk >= 36 - PV_AHEAD)
+                    va[kk - (36 - PV_AHEAD)] = vprev.load(kk - (36 - PV_AHEAD));
+            });
+            float nmu = 0.0f, psum = 0.0f;
+            bf16x8 pcur[2];
+            const SoftFill soft{st, s, pcur, psum, nmu, kbeg + ti * fl::NK, lim, wlim, sc};
+            if (ti > 0) {
+                pv_tile(st, vprev, va, pprev, soft);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 18; ++i) soft(i);
+            }
+            st.lsum += psum;
+            pprev[0] = pcur[0];
+            pprev[1] = pcur[1];
+        }
+        {
+            const VAddr vlast(lds + ((ntiles - 1) % NS) * fl::TILE_BYTES);
+            bf16x8 va[PV_AHEAD];
+#pragma unroll
+            for (int i = 0; i < PV_AHEAD; ++i) va[i] = vlast.load(i);
+            pv_tile(st, vlast, va, pprev, [](int) {});
         }
         __syncthreads();
     } else {
@@ -407,8 +501,7 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             if (ti + 2 < ntiles)
                 issue_tile_q8<NW>(rows, kbeg + (ti + 2) * fl::NK, n_rows,
                                   raw + (ti % 2) * Q8_RAW_STAGE);
-            attend_tile(st, lds + (ti % 2) * fl::TILE_BYTES, kbeg + ti * fl::NK, lim, wlim, sc,
-                        NoPrefetch{});
+            attend_tile(st, lds + (ti % 2) * fl::TILE_BYTES, kbeg + ti * fl::NK, lim, wlim, sc);
             if (ti + 1 < ntiles) {
                 if (ti + 2 < ntiles) {
                     MLA_WAIT_VMCNT(PER);
