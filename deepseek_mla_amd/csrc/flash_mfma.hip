@@ -226,11 +226,19 @@ __device__ __forceinline__ void dequant_tile_q8(const uint8_t MLA_LDS *raw, int 
 }
 
 // Per-wave attention state and the tile computation.
+//
+// Waves 2p and 2p+1 of a workgroup form a pair over 64 rows.  Each wave computes the
+// scores and the softmax of its own 32 rows; the pair swaps the bf16 weights P through
+// LDS, and each wave accumulates O for all 64 rows over its half of the latent columns.
+// Every V^T fragment read from LDS then feeds two MFMAs (one per row block), halving
+// the V reads, while the score MFMAs are not duplicated.
 struct WaveState {
-    bf16x8 q[36];     // Q^T fragments: lane l holds row l%32, dims kk*16 + (l/32)*8 .. +7
-    f32x16 o[16];     // O^T accumulators: block nb covers latent columns nb*32 .. nb*32+31
-    float m;          // frozen reference max of the row (scaled, log2 domain)
-    float lsum;       // this lane's share of the softmax denominator
+    bf16x8 q[36];     // Q^T fragments of the own rows: lane l holds row l%32,
+                      // dims kk*16 + (l/32)*8 .. +7
+    f32x16 o[8][2];   // O^T: column block nb of this wave's half (columns
+                      // half*256 + nb*32 ..), row block rb (0: own rows, 1: partner's)
+    float m;          // frozen reference max of the own row (scaled, log2 domain)
+    float lsum;       // this lane's share of the own row's softmax denominator
     bool bad;         // a score exceeded m + FREEZE_LIMIT: this pass is discarded
 };
 
@@ -319,29 +327,30 @@ __device__ __forceinline__ void softmax_check(WaveState &st, const f32x16 &s, fl
 }
 static_assert(fl::FREEZE_LIMIT == 64.0f, "softmax_check compares against 2^64");
 
-// V^T fragment addressing of the tile in stage t for O^T += V^T P^T.  Lane: key
-// kin + 8*half (+16 ks) and 4 columns at colb of each 32-column block.  Row
-// ks*16 + half*8 + kin has mask mask_a(half*8 + kin); chunk 4nb + c3 (c3 < 4) is stored at
-// 4nb + (c3 ^ mask): one base per row half plus compile-time offsets.
+// V^T fragment addressing of the tile in stage t for O^T += V^T P^T, over the column
+// half `ch` (uniform).  Lane: key kin + 8*h (+16 ks) and 4 columns at colb of each
+// 32-column block.  Row ks*16 + h*8 + kin has mask mask_a(h*8 + kin); chunk 4nb + c3
+// (c3 < 4) is stored at 4nb + (c3 ^ mask): one base per row half plus compile-time
+// offsets.
 struct VAddr {
     const uint8_t MLA_LDS *vb[2];
-    __device__ __forceinline__ explicit VAddr(const uint8_t MLA_LDS *t) {
+    __device__ __forceinline__ VAddr(const uint8_t MLA_LDS *t, int ch) {
         const int l = threadIdx.x & 63;
         const int G = l >> 4, lam = l & 15;
         const int kin = (G >> 1) * 4 + (lam >> 2);     // key within an 8-key group
         const int colb = (G & 1) * 16 + 4 * (lam & 3);  // column within a 32-column block
         const int c3 = colb >> 3, cb = (colb & 7) * 2;
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
-            vb[half] = t + (half * 8 + kin) * fl::PA + ((c3 ^ mask_a(half * 8 + kin)) * 16) + cb;
+        for (int h = 0; h < 2; ++h)
+            vb[h] = t + ch * 512 + (h * 8 + kin) * fl::PA + ((c3 ^ mask_a(h * 8 + kin)) * 16) + cb;
     }
-    __device__ __forceinline__ bf16x8 load(int i) const {  // step i = (ks, nb) = (i/16, i%16)
-        const int off = (i >> 4) * 16 * fl::PA + (i & 15) * 64;
+    __device__ __forceinline__ bf16x8 load(int i) const {  // step i = (ks, nb) = (i/8, i%8)
+        const int off = (i >> 3) * 16 * fl::PA + (i & 7) * 64;
         return tr_pair(vb[0] + off, vb[1] + off);
     }
 };
 
-constexpr int PV_AHEAD = 4;
+constexpr int PV_AHEAD = 2;  // V^T read-ahead in PV steps (two MFMAs each)
 
 // Weight of key slot e (e < 16) of this lane: exp2(s*sc - m); masked keys give 0.
 __device__ __forceinline__ void soft_piece(const f32x16 &s, int e, float sc, float nmu,
@@ -351,19 +360,25 @@ __device__ __forceinline__ void soft_piece(const f32x16 &s, int e, float sc, flo
     p[e >> 3][e & 7] = f2bf(pe);
 }
 
-// O^T += V^T P^T over the 32 keys of a tile: 32 steps (ks, nb) with a read-ahead ring
-// whose first PV_AHEAD entries the caller loaded; fill(i) is placed after MFMA i.
+// O^T += V^T P^T over the 32 keys of a tile for both row blocks: 16 steps (ks, nb), each
+// one V^T fragment and two MFMAs (own weights pown, partner's weights poth), with a
+// read-ahead ring whose first PV_AHEAD entries the caller loaded; fill(j) follows MFMA j.
 template <typename Fill>
 __device__ __forceinline__ void pv_tile(WaveState &st, const VAddr &va_addr,
-                                        bf16x8 (&va)[PV_AHEAD], const bf16x8 (&p)[2], Fill fill) {
+                                        bf16x8 (&va)[PV_AHEAD], const bf16x8 (&pown)[2],
+                                        const bf16x8 (&poth)[2], Fill fill) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const int ks = i >> 4, nb = i & 15;
-        st.o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % PV_AHEAD], p[ks], st.o[nb], 0, 0,
-                                                           0);
+    for (int i = 0; i < 16; ++i) {
+        const int ks = i >> 3, nb = i & 7;
+        st.o[nb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % PV_AHEAD], pown[ks],
+                                                              st.o[nb][0], 0, 0, 0);
+        fill(2 * i);
+        __builtin_amdgcn_sched_barrier(0);
+        st.o[nb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % PV_AHEAD], poth[ks],
+                                                              st.o[nb][1], 0, 0, 0);
         const int ni = i + PV_AHEAD;
-        if (ni < 32) va[i % PV_AHEAD] = va_addr.load(ni);
-        fill(i);
+        if (ni < 16) va[i % PV_AHEAD] = va_addr.load(ni);
+        fill(2 * i + 1);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -386,21 +401,41 @@ struct SoftFill {
     }
 };
 
-// Whole-tile step without the cross-tile pipeline (Q8_0 stream): scores, softmax, O.
-__device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t MLA_LDS *t, int key0,
-                                            int lim, int wave_lim_min, float sc) {
-    const VAddr va_addr(t);
+// Weight exchange buffer: 2 KB per wave (p[0] at lane*16, p[1] at 1024 + lane*16).
+constexpr int PBUF_BYTES = 4 * 2048;
+__device__ __forceinline__ void put_p(uint8_t MLA_LDS *pbuf, const bf16x8 (&p)[2]) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    bf16x8 MLA_LDS *slot = (bf16x8 MLA_LDS *)(pbuf + w * 2048);
+    slot[l] = p[0];
+    slot[64 + l] = p[1];
+}
+__device__ __forceinline__ void get_partner_p(const uint8_t MLA_LDS *pbuf, bf16x8 (&p)[2]) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const bf16x8 MLA_LDS *slot = (const bf16x8 MLA_LDS *)(pbuf + (w ^ 1) * 2048);
+    p[0] = slot[l];
+    p[1] = slot[64 + l];
+}
+
+// Whole-tile step without the cross-tile pipeline (Q8_0 stream): scores, softmax, weight
+// exchange, O.  The caller separates consecutive calls by a workgroup barrier.
+__device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t MLA_LDS *t,
+                                            uint8_t MLA_LDS *pbuf, int key0, int lim,
+                                            int wave_lim_min, float sc) {
+    const VAddr va_addr(t, (threadIdx.x >> 6) & 1);
     bf16x8 va[PV_AHEAD];
     f32x16 s = score_tile(st, t, [&](int kk) {
         if (kk >= 36 - PV_AHEAD) va[kk - (36 - PV_AHEAD)] = va_addr.load(kk - (36 - PV_AHEAD));
     });
     float nmu = 0.0f, psum = 0.0f;
-    bf16x8 p[2];
+    bf16x8 p[2], po[2];
     const SoftFill soft{st, s, p, psum, nmu, key0, lim, wave_lim_min, sc};
 #pragma unroll
     for (int i = 0; i < 18; ++i) soft(i);
     st.lsum += psum;
-    pv_tile(st, va_addr, va, p, [](int) {});
+    put_p(pbuf, p);
+    __syncthreads();
+    get_partner_p(pbuf, po);
+    pv_tile(st, va_addr, va, p, po, [](int) {});
 }
 
 // Rows that are not valid load a valid row's query instead (their keys are all masked,
@@ -414,21 +449,27 @@ __device__ __forceinline__ void load_q(WaveState &st, const bf16 *__restrict__ q
 
 __device__ __forceinline__ void init_acc(WaveState &st, float m0) {
 #pragma unroll
-    for (int nb = 0; nb < 16; ++nb)
+    for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) st.o[nb][e] = 0.0f;
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) st.o[nb][rb][e] = 0.0f;
     st.m = m0;
     st.lsum = 0.0f;
     st.bad = false;
 }
 
 // Stream keys [kbeg, kend) of `rows` (bf16 or Q8_0) through LDS and attend every tile.
+// pbuf: the weight exchange buffer (PBUF_BYTES of LDS).
 template <int NW, int NS, bool Q8>
 __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
+                                            uint8_t MLA_LDS *pbuf,
                                             const uint8_t *__restrict__ rows, int n_rows,
                                             int kbeg, int kend, int lim, int wlim, float sc) {
+    static_assert(NW == 4, "two wave pairs per workgroup");
     if (kend <= kbeg) return;
     const int ntiles = (kend - kbeg + fl::NK - 1) / fl::NK;
+    const int ch = (threadIdx.x >> 6) & 1;  // column half of this wave
     if constexpr (!Q8) {
         constexpr int PER = 9;  // copy instructions per wave per tile (issue_chunk_bf16)
         const int last = n_rows - 1;
@@ -437,7 +478,10 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             if (s < ntiles) issue_tile_bf16<NW>(rows, kbeg + s * fl::NK, last, lds + s * fl::TILE_BYTES);
         // Iteration t: wait for tile t, scores of tile t (with the copy of tile t+2 into
         // the stage tile t-2 used, free since the barrier), then the O update of tile t-1
-        // carrying the softmax of tile t.  Tile t-1 stays resident for its V reads.
+        // carrying the softmax of tile t.  Tile t-1 stays resident for its V reads.  The
+        // weights of tile t go to the exchange buffer at the end of iteration t; the
+        // partner reads them in iteration t+1 before the middle barrier, which orders
+        // those reads before the buffer is overwritten.
         static_assert(NS == 4, "tiles t-1 .. t+2 resident or in flight");
         bf16x8 pprev[2];
         for (int ti = 0; ti < ntiles; ++ti) {
@@ -451,13 +495,13 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             uint8_t MLA_LDS *ndst = lds + (nx % NS) * fl::TILE_BYTES;
             const int nkey0 = kbeg + nx * fl::NK;
             const bool more = nx < ntiles;
-            // The whole copy is issued before the score loop starts its LDS read ring: the
-            // compiler follows an LDS-direct copy with a wait for every outstanding LDS
-            // read, which inside the ring would stall the next MFMA.
-            if (more) issue_tile_bf16<NW>(rows, nkey0, last, ndst);
-            const VAddr vprev(lds + ((ti + NS - 1) % NS) * fl::TILE_BYTES);
+            // The copy's 9 instructions are spread over the score MFMAs: issued together,
+            // the four waves' 36 instructions queue behind each other in the CU's memory
+            // address unit.
+            const VAddr vprev(lds + ((ti + NS - 1) % NS) * fl::TILE_BYTES, ch);
             bf16x8 va[PV_AHEAD];
             f32x16 s = score_tile(st, lds + (ti % NS) * fl::TILE_BYTES, [&](int kk) {
+                if ((kk & 3) == 1 && more) issue_chunk_bf16<NW>(rows, nkey0, last, ndst, kk >> 2);
                 if (ti > 0 && kk >= 36 - PV_AHEAD)
                     va[kk - (36 - PV_AHEAD)] = vprev.load(kk - (36 - PV_AHEAD));
             });
@@ -465,21 +509,27 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             bf16x8 pcur[2];
             const SoftFill soft{st, s, pcur, psum, nmu, kbeg + ti * fl::NK, lim, wlim, sc};
             if (ti > 0) {
-                pv_tile(st, vprev, va, pprev, soft);
+                bf16x8 poth[2];
+                get_partner_p(pbuf, poth);
+                __syncthreads();
+                pv_tile(st, vprev, va, pprev, poth, soft);
             } else {
 #pragma unroll
                 for (int i = 0; i < 18; ++i) soft(i);
             }
             st.lsum += psum;
+            put_p(pbuf, pcur);
             pprev[0] = pcur[0];
             pprev[1] = pcur[1];
         }
+        __syncthreads();
         {
-            const VAddr vlast(lds + ((ntiles - 1) % NS) * fl::TILE_BYTES);
-            bf16x8 va[PV_AHEAD];
+            const VAddr vlast(lds + ((ntiles - 1) % NS) * fl::TILE_BYTES, ch);
+            bf16x8 va[PV_AHEAD], poth[2];
 #pragma unroll
             for (int i = 0; i < PV_AHEAD; ++i) va[i] = vlast.load(i);
-            pv_tile(st, vlast, va, pprev, [](int) {});
+            get_partner_p(pbuf, poth);
+            pv_tile(st, vlast, va, pprev, poth, [](int) {});
         }
         __syncthreads();
     } else {
@@ -501,7 +551,8 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             if (ti + 2 < ntiles)
                 issue_tile_q8<NW>(rows, kbeg + (ti + 2) * fl::NK, n_rows,
                                   raw + (ti % 2) * Q8_RAW_STAGE);
-            attend_tile(st, lds + (ti % 2) * fl::TILE_BYTES, kbeg + ti * fl::NK, lim, wlim, sc);
+            attend_tile(st, lds + (ti % 2) * fl::TILE_BYTES, pbuf, kbeg + ti * fl::NK, lim, wlim,
+                        sc);
             if (ti + 1 < ntiles) {
                 if (ti + 2 < ntiles) {
                     MLA_WAIT_VMCNT(PER);
@@ -514,18 +565,31 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
                 __syncthreads();
             }
         }
+        __syncthreads();
     }
+}
+
+// Small shared integers live in the unused pad of latent row 0 of stage 0 (bytes
+// 1024 .. 1087, never written by tile copies nor read by the tile loop), so that the
+// stages and the weight exchange buffer can take all of LDS.
+struct Misc {
+    int kmax, flag, wmin[4];
+};
+static_assert(sizeof(Misc) <= fl::PA - 1024, "misc fits the pad");
+__device__ __forceinline__ Misc *misc_of(uint8_t *lds_generic) {
+    return (Misc *)(lds_generic + 1024);
 }
 
 // Runs the key stream for the workgroup, repeating it once if any row was marked.
 template <int NW, int NS, bool Q8>
-__device__ __forceinline__ void attend_range(WaveState &st, uint8_t MLA_LDS *lds, int *flag,
+__device__ __forceinline__ void attend_range(WaveState &st, uint8_t MLA_LDS *lds,
+                                             uint8_t MLA_LDS *pbuf, int *flag,
                                              const uint8_t *__restrict__ rows, int n_rows,
                                              int kbeg, int kend, int lim, int wlim, float sc) {
     float m0 = -INFINITY;
     for (int pass = 0; pass < 2; ++pass) {
         init_acc(st, m0);
-        stream_keys<NW, NS, Q8>(st, lds, rows, n_rows, kbeg, kend, lim, wlim, sc);
+        stream_keys<NW, NS, Q8>(st, lds, pbuf, rows, n_rows, kbeg, kend, lim, wlim, sc);
         if (threadIdx.x == 0) *flag = 0;
         __syncthreads();
         if (__builtin_amdgcn_ballot_w64(st.bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1);
@@ -537,75 +601,97 @@ __device__ __forceinline__ void attend_range(WaveState &st, uint8_t MLA_LDS *lds
     }
 }
 
-// Final normalisation.  Returns lse (natural log) for this lane's row; writes o / l into
-// the caller's store functor per 4 consecutive columns.
+// Final normalisation.  Each wave holds O for its own rows (rb 0) and its partner's
+// (rb 1) over its column half; the pair swaps the row denominators through LDS.  Calls
+// store(rb, col, 4 values) per 4 consecutive columns and returns lse (natural log) of
+// this lane's own row.
 template <typename Store>
-__device__ __forceinline__ float finish(WaveState &st, Store store) {
-    const int l = threadIdx.x & 63, hi = l >> 5;
+__device__ __forceinline__ float finish(WaveState &st, uint8_t MLA_LDS *pbuf, Store store) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, hi = l >> 5;
     const float lt = pair_sum(st.lsum);
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    float MLA_LDS *den = (float MLA_LDS *)pbuf;  // buffer free: the key stream ended on a barrier
+    if (l < 32) den[w * 32 + l] = lt;
+    __syncthreads();
+    const float lo = den[(w ^ 1) * 32 + (l & 31)];
+    __syncthreads();
+    const float inv[2] = {lt > 0.0f ? 1.0f / lt : 0.0f, lo > 0.0f ? 1.0f / lo : 0.0f};
+    const int ch = w & 1;
 #pragma unroll
-    for (int nb = 0; nb < 16; ++nb)
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int col = nb * 32 + g * 8 + hi * 4;
-            store(col, st.o[nb][g * 4 + 0] * inv, st.o[nb][g * 4 + 1] * inv,
-                  st.o[nb][g * 4 + 2] * inv, st.o[nb][g * 4 + 3] * inv);
-        }
+        for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = ch * 256 + nb * 32 + g * 8 + hi * 4;
+                const f32x16 &o = st.o[nb][rb];
+                store(rb, col, o[g * 4 + 0] * inv[rb], o[g * 4 + 1] * inv[rb],
+                      o[g * 4 + 2] * inv[rb], o[g * 4 + 3] * inv[rb]);
+            }
     return lt > 0.0f ? (st.m + __log2f(lt)) * fl::LN2 : -INFINITY;
 }
 
 constexpr int PF_NW = 4, PF_NS = 4;
 
 // Prefill.  Rows are the flattened (token, head-in-chunk) pairs of all head chunks:
-// block -> (chunk, group of 128 rows), heavy (late) groups first, consecutive groups
-// on the same XCD so that co-running workgroups stream the same cache rows.
+// block -> (chunk, group of 128 rows), heavy (late) groups first.
 __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
     const bf16 *__restrict__ q_cat, const int32_t *__restrict__ pos, int T, int H,
     const uint8_t *__restrict__ cache, int n_kv, int hc, int n_groups, int n_chunks, float sc,
     bf16 *__restrict__ o_lat, float *__restrict__ lse) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     uint8_t MLA_LDS *lds = (uint8_t MLA_LDS *)lds_raw;
-    __shared__ int kmax_sh, flag_sh, wmin_sh[PF_NW];
-    const int total = n_groups * n_chunks;
-    // XCD-aware bijection: blocks bid, bid+8, ... run on one XCD; give each XCD a
-    // contiguous range of logical indices.
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7, kx = bid >> 3;
-    const int q = total >> 3, rem = total & 7;
-    const int logical = xcd * q + min(xcd, rem) + kx;
-    const int g2 = total - 1 - logical;  // heavy first
-    const int chunk = g2 / n_groups, grp = g2 % n_groups;
+    uint8_t MLA_LDS *pbuf = lds + PF_NS * fl::TILE_BYTES;
+    Misc *misc = misc_of(lds_raw);
+    // Blocks are dispatched in index order, round-robin over the 8 XCDs.  Order: the
+    // heaviest row group (latest tokens) first, all head chunks of a group together, so
+    // every XCD receives an even share of heavy and light groups (a contiguous range per
+    // XCD would give one XCD all the heavy groups), and co-running workgroups stream the
+    // same cache rows from key 0 upwards.
+    const int chunk = blockIdx.x % n_chunks;
+    const int grp = n_groups - 1 - blockIdx.x / n_chunks;
 
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
     const int rows_total = T * hc;
-    const int r = grp * (32 * PF_NW) + w * 32 + (l & 31);
-    const bool valid = r < rows_total;
-    const int t = valid ? r / hc : 0;
-    const int h = chunk * hc + (valid ? r % hc : 0);
+    // row (token t, head h) of lane l's row in wave `wave`; false past the last row
+    auto row_of = [&](int l, int wave, int &t, int &h) {
+        const int r = grp * (32 * PF_NW) + wave * 32 + (l & 31);
+        const bool v = r < rows_total;
+        t = v ? r / hc : 0;
+        h = chunk * hc + (v ? r % hc : 0);
+        return v;
+    };
+    int t, h;
+    const bool valid = row_of(threadIdx.x & 63, w, t, h);
     int lim = -1;
     if (valid) lim = min(pos[t], n_kv - 1);
 
     // key range of the group (max) and of each wave (min of the rows' last visible key)
-    if (threadIdx.x < PF_NW) wmin_sh[threadIdx.x] = INT32_MAX;
-    if (threadIdx.x == 0) kmax_sh = -1;
+    if (threadIdx.x < PF_NW) misc->wmin[threadIdx.x] = INT32_MAX;
+    if (threadIdx.x == 0) misc->kmax = -1;
     __syncthreads();
-    atomicMax(&kmax_sh, lim);
-    atomicMin(&wmin_sh[w], lim);
+    atomicMax(&misc->kmax, lim);
+    atomicMin(&misc->wmin[w], lim);
     WaveState st;
     load_q(st, q_cat + ((int64_t)t * H + h) * fl::W);
     __syncthreads();
-    const int kend = kmax_sh + 1;
-    attend_range<PF_NW, PF_NS, false>(st, lds, &flag_sh, cache, n_kv, 0, kend, lim, wmin_sh[w],
-                                      sc);
-    bf16 *dst = o_lat + ((int64_t)t * H + h) * fl::R;
-    const float ls = finish(st, [&](int col, float a, float b, float c, float d) {
-        if (valid) {
+    const int kend = misc->kmax + 1;
+    const int wlim = misc->wmin[w];
+    attend_range<PF_NW, PF_NS, false>(st, lds, pbuf, &misc->flag, cache, n_kv, 0, kend, lim,
+                                      wlim, sc);
+    // The rows are recomputed from an opaque lane index: values kept from before the key
+    // stream would stay live across it and crowd out the tile loop's registers.
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));
+    int ta, ha, tb, hb;
+    const bool ok[2] = {row_of(l, w, ta, ha), row_of(l, w ^ 1, tb, hb)};
+    bf16 *dst[2] = {o_lat + ((int64_t)ta * H + ha) * fl::R, o_lat + ((int64_t)tb * H + hb) * fl::R};
+    const float ls = finish(st, pbuf, [&](int rb, int col, float a, float b, float c, float d) {
+        if (ok[rb]) {
             bf16x4 v = {f2bf(a), f2bf(b), f2bf(c), f2bf(d)};
-            *(bf16x4 *)(dst + col) = v;
+            *(bf16x4 *)(dst[rb] + col) = v;
         }
     });
-    if (lse && valid && l < 32) lse[(int64_t)t * H + h] = ls;
+    if (lse && ok[0] && l < 32) lse[(int64_t)ta * H + ha] = ls;
 }
 
 hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int T, int H,
@@ -615,7 +701,7 @@ hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int 
     const int rows = T * hc;
     const int n_groups = (rows + 32 * PF_NW - 1) / (32 * PF_NW);
     const int n_chunks = H / hc;
-    const size_t shm = (size_t)PF_NS * fl::TILE_BYTES;
+    const size_t shm = (size_t)PF_NS * fl::TILE_BYTES + PBUF_BYTES;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)flash_prefill_bf16_kernel,
@@ -640,27 +726,33 @@ __global__ __launch_bounds__(64 * DC_NW, 1) void flash_decode_kernel(
     int split_len, float sc, bf16 *__restrict__ part_o, float *__restrict__ part_lse) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     uint8_t MLA_LDS *lds = (uint8_t MLA_LDS *)lds_raw;
+    constexpr size_t STAGES_BYTES =
+        Q8 ? 2 * (size_t)fl::TILE_BYTES + 2 * (size_t)Q8_RAW_STAGE : DC_NS * (size_t)fl::TILE_BYTES;
+    uint8_t MLA_LDS *pbuf = lds + STAGES_BYTES;
+    Misc *misc = misc_of(lds_raw);
     const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int h = hg * (32 * DC_NW) + w * 32 + (l & 31);
-    const bool valid = h < H;
+    const int h2 = hg * (32 * DC_NW) + (w ^ 1) * 32 + (l & 31);
+    const bool valid = h < H, valid2 = h2 < H;
     const int nk = min(n_kv[b], n_kv_max);  // rows past n_kv_max are never read
     const int k0 = s * split_len;
     const int k1 = min(k0 + split_len, nk);
     WaveState st;
     load_q(st, q_cat + ((int64_t)b * H + (valid ? h : 0)) * fl::W);
     const uint8_t *rows = cache + b * seq_stride;
-    __shared__ int flag_sh;
-    attend_range<DC_NW, DC_NS, Q8>(st, lds, &flag_sh, rows, nk, k0, k1, k1 - 1, k1 - 1, sc);
-    const int64_t pi = ((int64_t)b * n_splits + s) * H + h;
-    bf16 *dst = part_o + pi * fl::R;
-    const float ls = finish(st, [&](int col, float a, float b_, float c, float d) {
-        if (valid) {
+    attend_range<DC_NW, DC_NS, Q8>(st, lds, pbuf, &misc->flag, rows, nk, k0, k1, k1 - 1, k1 - 1,
+                                   sc);
+    const int64_t pi = ((int64_t)b * n_splits + s) * H;
+    bf16 *dst[2] = {part_o + (pi + h) * fl::R, part_o + (pi + h2) * fl::R};
+    const bool ok[2] = {valid, valid2};
+    const float ls = finish(st, pbuf, [&](int rb, int col, float a, float b_, float c, float d) {
+        if (ok[rb]) {
             bf16x4 v = {f2bf(a), f2bf(b_), f2bf(c), f2bf(d)};
-            *(bf16x4 *)(dst + col) = v;
+            *(bf16x4 *)(dst[rb] + col) = v;
         }
     });
-    if (valid && l < 32) part_lse[pi] = ls;
+    if (valid && l < 32) part_lse[pi + h] = ls;
 }
 
 hipError_t launch_flash_decode_bf16(const bf16 *q_cat, const void *cache, int cache_q8,
@@ -671,7 +763,7 @@ hipError_t launch_flash_decode_bf16(const bf16 *q_cat, const void *cache, int ca
     const int hgroups = (H + 32 * DC_NW - 1) / (32 * DC_NW);
     dim3 grid(n_splits, B, hgroups);
     if (cache_q8) {
-        const size_t shm = 2 * (size_t)fl::TILE_BYTES + 2 * (size_t)Q8_RAW_STAGE;
+        const size_t shm = 2 * (size_t)fl::TILE_BYTES + 2 * (size_t)Q8_RAW_STAGE + PBUF_BYTES;
         static bool attr_set = false;
         if (!attr_set) {
             hipError_t e = hipFuncSetAttribute((const void *)flash_decode_kernel<true>,
@@ -683,7 +775,7 @@ hipError_t launch_flash_decode_bf16(const bf16 *q_cat, const void *cache, int ca
                            (const uint8_t *)cache, seq_stride_bytes, n_kv, n_kv_max, n_splits, split_len,
                            scale * fl::LOG2E, part_o, part_lse);
     } else {
-        const size_t shm = (size_t)DC_NS * fl::TILE_BYTES;
+        const size_t shm = (size_t)DC_NS * fl::TILE_BYTES + PBUF_BYTES;
         static bool attr_set = false;
         if (!attr_set) {
             hipError_t e = hipFuncSetAttribute((const void *)flash_decode_kernel<false>,
