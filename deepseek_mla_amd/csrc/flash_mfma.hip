@@ -32,7 +32,21 @@
 // bank conflicts (see mask_a and mask_b).
 #include "common.h"
 
+#include <type_traits>
+#include <utility>
+
 namespace mla {
+
+// Calls f(std::integral_constant<int, K>) for K = 0 .. N-1 (fully unrolled, K usable in
+// constant expressions).
+template <typename F, int... K>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, K...>) {
+    (f(std::integral_constant<int, K>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 namespace fl {
 constexpr int R = 512, DR = 64, W = 576;
@@ -135,6 +149,39 @@ __device__ __forceinline__ void issue_chunk_bf16(const uint8_t *__restrict__ row
         lds_copy16(rows + (int64_t)key0 * fl::RB,
                    (uint32_t)(kr * fl::RB + fl::R * 2 + (((l & 7) ^ mask_b(k)) * 16)),
                    lds_u32(dst + fl::A_BYTES + w * 1024));
+    }
+}
+
+// Copy plan of a full tile (all 32 keys inside the cache) for wave w: one uniform source
+// address per tile (key0 + 8w) plus a compile-time row step per instruction, and lane
+// offsets fixed for the whole stream.  Latent row 8w + i uses mask_a(8w + i) =
+// (2w + i/4) & 3, so rows i < 4 and i >= 4 take two lane offsets.  The rope instruction
+// covers rows 8w .. 8w+7.  (The instruction's immediate offset is left at 0: it would
+// move the LDS destination as well.)
+struct CopyPlan {
+    uint32_t va0, va1, vb;
+};
+__device__ __forceinline__ CopyPlan make_copy_plan() {
+    const int w = threadIdx.x >> 6;
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));  // recomputed where used, not kept live across the loop
+    CopyPlan c;
+    c.va0 = (uint32_t)((l ^ mask_a(8 * w)) * 16);
+    c.va1 = (uint32_t)((l ^ mask_a(8 * w + 4)) * 16);
+    c.vb = (uint32_t)((l >> 3) * fl::RB + fl::R * 2 + (((l & 7) ^ mask_b(8 * w + (l >> 3))) * 16));
+    return c;
+}
+
+// Part I (0 .. 8) of a full tile's copy for this wave: sbase = rows + (key0 + 8w) * 1152
+// (uniform), dst = the LDS stage.
+template <int I>
+__device__ __forceinline__ void issue_part_full(const uint8_t *sbase, const CopyPlan &c,
+                                                uint32_t dst, int w) {
+    if constexpr (I < 8) {
+        lds_copy16(sbase + I * fl::RB, I < 4 ? c.va0 : c.va1,
+                   dst + (uint32_t)((8 * w + I) * fl::PA));
+    } else {
+        lds_copy16(sbase, c.vb, dst + (uint32_t)(fl::A_BYTES + w * 1024));
     }
 }
 
@@ -269,14 +316,14 @@ __device__ __forceinline__ f32x16 score_tile(const WaveState &st, const uint8_t 
     bf16x8 a[QK_AHEAD];
 #pragma unroll
     for (int kk = 0; kk < QK_AHEAD; ++kk) a[kk] = *(const bf16x8 MLA_LDS *)kaddr(kk);
-#pragma unroll
-    for (int kk = 0; kk < 36; ++kk) {
+    static_for<36>([&](auto kc) {
+        constexpr int kk = decltype(kc)::value;
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk % QK_AHEAD], st.q[kk], s, 0, 0, 0);
-        const int nk = kk + QK_AHEAD;
-        if (nk < 36) a[kk % QK_AHEAD] = *(const bf16x8 MLA_LDS *)kaddr(nk);
-        fill(kk);
+        constexpr int nk = kk + QK_AHEAD;
+        if constexpr (nk < 36) a[kk % QK_AHEAD] = *(const bf16x8 MLA_LDS *)kaddr(nk);
+        fill(kc);
         __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     return s;
 }
 
@@ -286,13 +333,16 @@ __device__ __forceinline__ f32x16 score_tile(const WaveState &st, const uint8_t 
 // no reference yet or is marked (wave-uniform branch).  Returns the exponent offset -m.
 __device__ __forceinline__ float softmax_prep(WaveState &st, f32x16 &s, int key0, int lim,
                                               int wave_lim_min, float sc) {
-    const int hi = (threadIdx.x & 63) >> 5;
-    if (key0 + fl::NK - 1 > wave_lim_min) {  // masking only where some row ends in the tile
+    {
+        // Slot e holds key key0 + hi*4 + (e/4)*8 + e%4: its constant part is compared with
+        // one per-lane bound, raised past the tile where no row of the wave ends in it.
+        // (Unconditional: with a branch here the compiler keeps two copies of the scores
+        // live and runs out of registers.)
+        const int rel = (key0 + fl::NK - 1 > wave_lim_min)
+                            ? lim - key0 - (((threadIdx.x & 63) >> 5) << 2)
+                            : fl::NK;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int key = key0 + (e >> 2) * 8 + hi * 4 + (e & 3);
-            s[e] = (key <= lim) ? s[e] : -INFINITY;
-        }
+        for (int e = 0; e < 16; ++e) s[e] = ((e >> 2) * 8 + (e & 3) <= rel) ? s[e] : -INFINITY;
     }
     if (__builtin_amdgcn_ballot_w64((st.m == -INFINITY && key0 <= lim) || st.bad)) {
         float tmax = -INFINITY;
@@ -367,25 +417,26 @@ template <typename Fill>
 __device__ __forceinline__ void pv_tile(WaveState &st, const VAddr &va_addr,
                                         bf16x8 (&va)[PV_AHEAD], const bf16x8 (&pown)[2],
                                         const bf16x8 (&poth)[2], Fill fill) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int ks = i >> 3, nb = i & 7;
+    static_for<16>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int ks = i >> 3, nb = i & 7;
         st.o[nb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % PV_AHEAD], pown[ks],
                                                               st.o[nb][0], 0, 0, 0);
-        fill(2 * i);
+        fill(std::integral_constant<int, 2 * i>{});
         __builtin_amdgcn_sched_barrier(0);
         st.o[nb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % PV_AHEAD], poth[ks],
                                                               st.o[nb][1], 0, 0, 0);
-        const int ni = i + PV_AHEAD;
-        if (ni < 16) va[i % PV_AHEAD] = va_addr.load(ni);
-        fill(2 * i + 1);
+        constexpr int ni = i + PV_AHEAD;
+        if constexpr (ni < 16) va[i % PV_AHEAD] = va_addr.load(ni);
+        fill(std::integral_constant<int, 2 * i + 1>{});
         __builtin_amdgcn_sched_barrier(0);
-    }
+    });
 }
 
-// Softmax of one tile's raw scores s while the O update of the previous tile runs: step 0
-// masks and sets the reference, steps 1..16 compute one weight each, step 17 tests for
-// overflow.  The weights land in p, their sum in psum.
+// Softmax of one tile's raw scores s while the O update of the previous tile runs (one
+// step per MFMA, 32 steps): step 0 masks and sets the reference, odd step 2e+1 computes
+// weight e (about two VALU operations per MFMA, which issue in the MFMA's shadow), step
+// 31 also tests for overflow.  The weights land in p, their sum in psum.
 struct SoftFill {
     WaveState &st;
     f32x16 &s;
@@ -396,8 +447,8 @@ struct SoftFill {
     float sc;
     __device__ __forceinline__ void operator()(int i) const {
         if (i == 0) nmu = softmax_prep(st, s, key0, lim, wave_lim_min, sc);
-        if (i >= 1 && i <= 16) soft_piece(s, i - 1, sc, nmu, psum, p);
-        if (i == 17) softmax_check(st, s, psum, sc);
+        if (i & 1) soft_piece(s, i >> 1, sc, nmu, psum, p);
+        if (i == 31) softmax_check(st, s, psum, sc);
     }
 };
 
@@ -409,11 +460,16 @@ __device__ __forceinline__ void put_p(uint8_t MLA_LDS *pbuf, const bf16x8 (&p)[2
     slot[l] = p[0];
     slot[64 + l] = p[1];
 }
-__device__ __forceinline__ void get_partner_p(const uint8_t MLA_LDS *pbuf, bf16x8 (&p)[2]) {
+// Weights of wave (w ^ flip) from the exchange buffer: flip 1 reads the partner's, flip 0
+// reads back this wave's own (so they need not stay in registers across the score MFMAs).
+__device__ __forceinline__ void get_p(const uint8_t MLA_LDS *pbuf, int flip, bf16x8 (&p)[2]) {
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const bf16x8 MLA_LDS *slot = (const bf16x8 MLA_LDS *)(pbuf + (w ^ 1) * 2048);
+    const bf16x8 MLA_LDS *slot = (const bf16x8 MLA_LDS *)(pbuf + (w ^ flip) * 2048);
     p[0] = slot[l];
     p[1] = slot[64 + l];
+}
+__device__ __forceinline__ void get_partner_p(const uint8_t MLA_LDS *pbuf, bf16x8 (&p)[2]) {
+    get_p(pbuf, 1, p);
 }
 
 // Whole-tile step without the cross-tile pipeline (Q8_0 stream): scores, softmax, weight
@@ -430,7 +486,7 @@ __device__ __forceinline__ void attend_tile(WaveState &st, const uint8_t MLA_LDS
     bf16x8 p[2], po[2];
     const SoftFill soft{st, s, p, psum, nmu, key0, lim, wave_lim_min, sc};
 #pragma unroll
-    for (int i = 0; i < 18; ++i) soft(i);
+    for (int i = 0; i < 32; ++i) soft(i);
     st.lsum += psum;
     put_p(pbuf, p);
     __syncthreads();
@@ -483,7 +539,6 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
         // partner reads them in iteration t+1 before the middle barrier, which orders
         // those reads before the buffer is overwritten.
         static_assert(NS == 4, "tiles t-1 .. t+2 resident or in flight");
-        bf16x8 pprev[2];
         for (int ti = 0; ti < ntiles; ++ti) {
             if (ti + 1 < ntiles) {
                 MLA_WAIT_VMCNT(PER);
@@ -495,41 +550,58 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             uint8_t MLA_LDS *ndst = lds + (nx % NS) * fl::TILE_BYTES;
             const int nkey0 = kbeg + nx * fl::NK;
             const bool more = nx < ntiles;
+            // Full tiles take the fast copy path spread over the score MFMAs; the one tile
+            // reaching past the cache's last row clamps per row and is issued at once.
+            const bool full = nkey0 + fl::NK - 1 <= last;
+            const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+            const uint8_t *sbase = rows + (int64_t)(nkey0 + 8 * wu) * fl::RB;
+            const uint32_t dsts = lds_u32(ndst);
+            const CopyPlan plan = make_copy_plan();
+            if (more && !full) issue_tile_bf16<NW>(rows, nkey0, last, ndst);  // once per stream
             // The copy's 9 instructions are spread over the score MFMAs: issued together,
             // the four waves' 36 instructions queue behind each other in the CU's memory
             // address unit.
             const VAddr vprev(lds + ((ti + NS - 1) % NS) * fl::TILE_BYTES, ch);
             bf16x8 va[PV_AHEAD];
-            f32x16 s = score_tile(st, lds + (ti % NS) * fl::TILE_BYTES, [&](int kk) {
-                if ((kk & 3) == 1 && more) issue_chunk_bf16<NW>(rows, nkey0, last, ndst, kk >> 2);
+            f32x16 s = score_tile(st, lds + (ti % NS) * fl::TILE_BYTES, [&](auto kc) {
+                constexpr int kk = decltype(kc)::value;
                 if (ti > 0 && kk >= 36 - PV_AHEAD)
                     va[kk - (36 - PV_AHEAD)] = vprev.load(kk - (36 - PV_AHEAD));
             });
             float nmu = 0.0f, psum = 0.0f;
             bf16x8 pcur[2];
             const SoftFill soft{st, s, pcur, psum, nmu, kbeg + ti * fl::NK, lim, wlim, sc};
+            // Copy parts go between the O-update MFMAs (even steps; the softmax takes the
+            // odd ones): that phase leaves LDS bandwidth for the copies' writes, while the
+            // score MFMAs already keep LDS busy with K-fragment reads.
+            auto fill = [&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                soft(j);
+                if constexpr ((j & 3) == 2 || j == 0) {
+                    if (more && full) issue_part_full<(j == 0 ? 8 : j >> 2)>(sbase, plan, dsts, wu);
+                }
+            };
             if (ti > 0) {
-                bf16x8 poth[2];
+                bf16x8 pown[2], poth[2];
+                get_p(pbuf, 0, pown);
                 get_partner_p(pbuf, poth);
                 __syncthreads();
-                pv_tile(st, vprev, va, pprev, poth, soft);
+                pv_tile(st, vprev, va, pown, poth, fill);
             } else {
-#pragma unroll
-                for (int i = 0; i < 18; ++i) soft(i);
+                static_for<32>(fill);
             }
             st.lsum += psum;
             put_p(pbuf, pcur);
-            pprev[0] = pcur[0];
-            pprev[1] = pcur[1];
         }
         __syncthreads();
         {
             const VAddr vlast(lds + ((ntiles - 1) % NS) * fl::TILE_BYTES, ch);
-            bf16x8 va[PV_AHEAD], poth[2];
+            bf16x8 va[PV_AHEAD], pown[2], poth[2];
 #pragma unroll
             for (int i = 0; i < PV_AHEAD; ++i) va[i] = vlast.load(i);
+            get_p(pbuf, 0, pown);
             get_partner_p(pbuf, poth);
-            pv_tile(st, vlast, va, pprev, poth, [](int) {});
+            pv_tile(st, vlast, va, pown, poth, [](int) {});
         }
         __syncthreads();
     } else {
