@@ -1,0 +1,110 @@
+"""Checks on the gfx950 assembly of the flash kernels (CPU only: hipcc cross-compiles).
+
+The bf16 tile copies are written as inline asm (LDS-direct loads through M0) that the
+compiler's wait tracking does not see; their correctness rests on properties of the
+generated code that these tests pin:
+
+* M0 is written only by those copy sequences (the asm clobbers M0, which the compiler
+  does not preserve across it);
+* no LDS-direct load carries a nonzero immediate offset (the offset would move the LDS
+  destination as well as the source);
+* no scratch (spill) access sits inside a tile loop that issues copies: the loop's hand
+  placed vmcnt waits count only copies, and a spill reload there would also stall on
+  every copy in flight.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from deepseek_mla_amd import build as B
+
+SRC = os.path.join(B.CSRC, "flash_mfma.hip")
+BF16_KERNELS = ("flash_prefill_bf16_kernel", "flash_decode_kernelILb0E")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None,
+                                reason="hipcc not available")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("asm") / "flash.s"
+    cmd = [B.HIPCC, *[f for f in B.FLAGS if f != "-fPIC"], "--cuda-device-only", "-S", SRC,
+           "-o", str(out)]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    assert r.returncode == 0, r.stdout.decode(errors="replace")[-4000:]
+    return out.read_text()
+
+
+def kernel_bodies(text):
+    """name -> list of instruction lines (label and comment lines kept for loop parsing)."""
+    bodies, cur, name = {}, None, None
+    for line in text.splitlines():
+        m = re.match(r"^(_Z\w+):", line)
+        if m:
+            name, cur = m.group(1), []
+            bodies[name] = cur
+            continue
+        if cur is not None:
+            if line.strip().startswith(".Lfunc_end"):
+                cur = None
+                continue
+            cur.append(line)
+    return bodies
+
+
+def bf16_bodies(text):
+    b = {n: body for n, body in kernel_bodies(text).items() if any(k in n for k in BF16_KERNELS)}
+    assert len(b) == 2, sorted(kernel_bodies(text))
+    return b
+
+
+def test_m0_written_only_by_copy_asm(asm):
+    for name, body in bf16_bodies(asm).items():
+        in_asm = False
+        for line in body:
+            s = line.strip()
+            if s.startswith(";;#ASMSTART"):
+                in_asm = True
+            elif s.startswith(";;#ASMEND"):
+                in_asm = False
+            elif not s.startswith(";") and re.search(r"\bm0\b", s):
+                assert in_asm, f"{name}: compiler-generated M0 use: {s}"
+
+
+def test_lds_loads_have_no_immediate_offset(asm):
+    for line in asm.splitlines():
+        s = line.strip()
+        if s.startswith("global_load_lds") or s.startswith("buffer_load") and " lds" in s:
+            m = re.search(r"offset:(0x[0-9a-fA-F]+|\d+)", s)
+            assert m is None or int(m.group(1), 0) == 0, s
+
+
+def test_no_spill_access_in_copy_loops(asm):
+    for name, body in bf16_bodies(asm).items():
+        labels = {}
+        for i, line in enumerate(body):
+            m = re.match(r"^(\.LBB\w+):", line)
+            if m:
+                labels[m.group(1)] = i
+        edges = []  # (header line, back-edge line) of every loop
+        for i, line in enumerate(body):
+            m = re.match(r"^\s*s_c?branch\w*\s+(\.LBB\w+)\s*$", line)
+            if m and m.group(1) in labels and labels[m.group(1)] < i:
+                edges.append((labels[m.group(1)], i))
+        loops = 0
+        for h, e in edges:
+            if any(h < h2 <= e and (h2, e2) != (h, e) for h2, e2 in edges):
+                continue  # not innermost (the outer pass loop may spill around the tile loop)
+            seg = body[h:e + 1]
+            instrs = [l.strip() for l in seg if l.strip() and not l.strip().startswith((";", "."))]
+            if not any(x.startswith("global_load_lds") for x in instrs):
+                continue
+            if sum(x.startswith("v_mfma") for x in instrs) < 60:
+                continue  # only the tile loops
+            loops += 1
+            spills = [x for x in instrs if x.startswith("scratch_")]
+            assert not spills, f"{name}: spill access in the tile loop: {spills[:3]}"
+        assert loops >= 1, f"{name}: tile loop not found"
