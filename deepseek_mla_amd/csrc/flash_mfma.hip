@@ -526,6 +526,11 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
     if (kend <= kbeg) return;
     const int ntiles = (kend - kbeg + fl::NK - 1) / fl::NK;
     const int ch = (threadIdx.x >> 6) & 1;  // column half of this wave
+    // Finish every earlier vector-memory load (queries, row bounds) before the first tile
+    // copy.  The compiler cannot see the copies; a load it still counted as pending would
+    // get a wait for all outstanding vector-memory operations inside the tile loop, which
+    // would also drain the tile copies in flight on every tile.
+    MLA_WAIT_VMCNT(0);
     if constexpr (!Q8) {
         constexpr int PER = 9;  // copy instructions per wave per tile (issue_chunk_bf16)
         const int last = n_rows - 1;
@@ -570,7 +575,12 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             });
             float nmu = 0.0f, psum = 0.0f;
             bf16x8 pcur[2];
-            const SoftFill soft{st, s, pcur, psum, nmu, kbeg + ti * fl::NK, lim, wlim, sc};
+            // The row bound is made opaque per tile: values the compiler would derive from
+            // it once and keep across the loop end up spilled, and a spill reload pending at
+            // the loop would bring a wait for all vector-memory operations into it.
+            int lim_t = lim;
+            asm volatile("" : "+v"(lim_t));
+            const SoftFill soft{st, s, pcur, psum, nmu, kbeg + ti * fl::NK, lim_t, wlim, sc};
             // Copy parts go between the O-update MFMAs (even steps; the softmax takes the
             // odd ones): that phase leaves LDS bandwidth for the copies' writes, while the
             // score MFMAs already keep LDS busy with K-fragment reads.
@@ -673,34 +683,55 @@ __device__ __forceinline__ void attend_range(WaveState &st, uint8_t MLA_LDS *lds
     }
 }
 
-// Final normalisation.  Each wave holds O for its own rows (rb 0) and its partner's
-// (rb 1) over its column half; the pair swaps the row denominators through LDS.  Calls
-// store(rb, col, 4 values) per 4 consecutive columns and returns lse (natural log) of
-// this lane's own row.
-template <typename Store>
-__device__ __forceinline__ float finish(WaveState &st, uint8_t MLA_LDS *pbuf, Store store) {
+// Final normalisation and output.  Each wave holds O for its own rows (rb 0) and its
+// partner's (rb 1) over its column half; the pair swaps the row denominators through
+// LDS.  The normalised bf16 rows are staged in LDS (the tile stages are free once the key
+// stream ended) and written out one 1 KB row per instruction: stores straight from the
+// MFMA layout would scatter 8 bytes per lane over 32 rows.  row_dst(r) gives the output
+// row of workgroup row r (0 .. 127; own rows of wave w are 32w .. 32w+31), or nullptr
+// for rows past the end.  Returns lse (natural log) of this lane's own row.
+constexpr int OPITCH = 1032;  // staged row pitch: rows 2 banks apart, 8-byte writes conflict-free
+constexpr int OSTAGE_BYTES = 128 * OPITCH;
+template <typename RowDst>
+__device__ __forceinline__ float finish(WaveState &st, uint8_t MLA_LDS *stage,
+                                        uint8_t MLA_LDS *pbuf, RowDst row_dst) {
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, hi = l >> 5;
     const float lt = pair_sum(st.lsum);
     float MLA_LDS *den = (float MLA_LDS *)pbuf;  // buffer free: the key stream ended on a barrier
     if (l < 32) den[w * 32 + l] = lt;
     __syncthreads();
     const float lo = den[(w ^ 1) * 32 + (l & 31)];
-    __syncthreads();
     const float inv[2] = {lt > 0.0f ? 1.0f / lt : 0.0f, lo > 0.0f ? 1.0f / lo : 0.0f};
     const int ch = w & 1;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb) {
+        const int r = (w ^ rb) * 32 + (l & 31);
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int col = ch * 256 + nb * 32 + g * 8 + hi * 4;
                 const f32x16 &o = st.o[nb][rb];
-                store(rb, col, o[g * 4 + 0] * inv[rb], o[g * 4 + 1] * inv[rb],
-                      o[g * 4 + 2] * inv[rb], o[g * 4 + 3] * inv[rb]);
+                const bf16x4 v = {f2bf(o[g * 4 + 0] * inv[rb]), f2bf(o[g * 4 + 1] * inv[rb]),
+                                  f2bf(o[g * 4 + 2] * inv[rb]), f2bf(o[g * 4 + 3] * inv[rb])};
+                *(bf16x4 MLA_LDS *)(stage + r * OPITCH + col * 2) = v;
             }
+    }
+    __syncthreads();
+    for (int j = 0; j < 32; ++j) {
+        const int r = w * 32 + j;
+        bf16 *dst = row_dst(r);
+        if (dst) {
+            const uint8_t MLA_LDS *src = stage + r * OPITCH + l * 16;
+            const u32x2 a = *(const u32x2 MLA_LDS *)src;
+            const u32x2 b = *(const u32x2 MLA_LDS *)(src + 8);
+            const u32x4 v = {a[0], a[1], b[0], b[1]};
+            *(u32x4 *)(dst + l * 8) = v;
+        }
+    }
     return lt > 0.0f ? (st.m + __log2f(lt)) * fl::LN2 : -INFINITY;
 }
+static_assert(OSTAGE_BYTES <= 4 * fl::TILE_BYTES, "output staging fits the tile stages");
 
 constexpr int PF_NW = 4, PF_NS = 4;
 
@@ -750,20 +781,17 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
     const int wlim = misc->wmin[w];
     attend_range<PF_NW, PF_NS, false>(st, lds, pbuf, &misc->flag, cache, n_kv, 0, kend, lim,
                                       wlim, sc);
-    // The rows are recomputed from an opaque lane index: values kept from before the key
-    // stream would stay live across it and crowd out the tile loop's registers.
+    // Output rows are recomputed here: values kept from before the key stream would stay
+    // live across it and crowd out the tile loop's registers.
     int l = threadIdx.x & 63;
     asm volatile("" : "+v"(l));
-    int ta, ha, tb, hb;
-    const bool ok[2] = {row_of(l, w, ta, ha), row_of(l, w ^ 1, tb, hb)};
-    bf16 *dst[2] = {o_lat + ((int64_t)ta * H + ha) * fl::R, o_lat + ((int64_t)tb * H + hb) * fl::R};
-    const float ls = finish(st, pbuf, [&](int rb, int col, float a, float b, float c, float d) {
-        if (ok[rb]) {
-            bf16x4 v = {f2bf(a), f2bf(b), f2bf(c), f2bf(d)};
-            *(bf16x4 *)(dst[rb] + col) = v;
-        }
+    const float ls = finish(st, lds, pbuf, [&](int r) -> bf16 * {
+        const int rr = grp * (32 * PF_NW) + r;
+        if (rr >= rows_total) return nullptr;
+        return o_lat + ((int64_t)(rr / hc) * H + chunk * hc + rr % hc) * fl::R;
     });
-    if (lse && ok[0] && l < 32) lse[(int64_t)ta * H + ha] = ls;
+    int ta, ha;
+    if (lse && row_of(l, w, ta, ha) && l < 32) lse[(int64_t)ta * H + ha] = ls;
 }
 
 hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int T, int H,
@@ -789,6 +817,14 @@ hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int 
 
 constexpr int DC_NW = 4, DC_NS = 4;
 
+// LDS ahead of the weight exchange buffer: tile stages (bf16: 4 stages; Q8_0: 2 bf16
+// stages and 2 raw stages), at least the output staging area.
+__host__ __device__ constexpr size_t dc_stage_bytes(bool q8) {
+    const size_t st = q8 ? 2 * (size_t)fl::TILE_BYTES + 2 * (size_t)Q8_RAW_STAGE
+                         : DC_NS * (size_t)fl::TILE_BYTES;
+    return st > (size_t)OSTAGE_BYTES ? st : (size_t)OSTAGE_BYTES;
+}
+
 // Decode partials.  Block (split s, sequence b, head group hg); rows = heads
 // hg*128 .. +127 of sequence b; keys [s*split_len, min((s+1)*split_len, n_kv[b])).
 template <bool Q8>
@@ -798,15 +834,12 @@ __global__ __launch_bounds__(64 * DC_NW, 1) void flash_decode_kernel(
     int split_len, float sc, bf16 *__restrict__ part_o, float *__restrict__ part_lse) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     uint8_t MLA_LDS *lds = (uint8_t MLA_LDS *)lds_raw;
-    constexpr size_t STAGES_BYTES =
-        Q8 ? 2 * (size_t)fl::TILE_BYTES + 2 * (size_t)Q8_RAW_STAGE : DC_NS * (size_t)fl::TILE_BYTES;
-    uint8_t MLA_LDS *pbuf = lds + STAGES_BYTES;
+    uint8_t MLA_LDS *pbuf = lds + dc_stage_bytes(Q8);
     Misc *misc = misc_of(lds_raw);
     const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int h = hg * (32 * DC_NW) + w * 32 + (l & 31);
-    const int h2 = hg * (32 * DC_NW) + (w ^ 1) * 32 + (l & 31);
-    const bool valid = h < H, valid2 = h2 < H;
+    const bool valid = h < H;
     const int nk = min(n_kv[b], n_kv_max);  // rows past n_kv_max are never read
     const int k0 = s * split_len;
     const int k1 = min(k0 + split_len, nk);
@@ -816,13 +849,9 @@ __global__ __launch_bounds__(64 * DC_NW, 1) void flash_decode_kernel(
     attend_range<DC_NW, DC_NS, Q8>(st, lds, pbuf, &misc->flag, rows, nk, k0, k1, k1 - 1, k1 - 1,
                                    sc);
     const int64_t pi = ((int64_t)b * n_splits + s) * H;
-    bf16 *dst[2] = {part_o + (pi + h) * fl::R, part_o + (pi + h2) * fl::R};
-    const bool ok[2] = {valid, valid2};
-    const float ls = finish(st, pbuf, [&](int rb, int col, float a, float b_, float c, float d) {
-        if (ok[rb]) {
-            bf16x4 v = {f2bf(a), f2bf(b_), f2bf(c), f2bf(d)};
-            *(bf16x4 *)(dst[rb] + col) = v;
-        }
+    const int hbase = hg * (32 * DC_NW);
+    const float ls = finish(st, lds, pbuf, [&](int r) -> bf16 * {
+        return hbase + r < H ? part_o + (pi + hbase + r) * fl::R : nullptr;
     });
     if (valid && l < 32) part_lse[pi + h] = ls;
 }
@@ -835,7 +864,7 @@ hipError_t launch_flash_decode_bf16(const bf16 *q_cat, const void *cache, int ca
     const int hgroups = (H + 32 * DC_NW - 1) / (32 * DC_NW);
     dim3 grid(n_splits, B, hgroups);
     if (cache_q8) {
-        const size_t shm = 2 * (size_t)fl::TILE_BYTES + 2 * (size_t)Q8_RAW_STAGE + PBUF_BYTES;
+        const size_t shm = dc_stage_bytes(true) + PBUF_BYTES;
         static bool attr_set = false;
         if (!attr_set) {
             hipError_t e = hipFuncSetAttribute((const void *)flash_decode_kernel<true>,
@@ -847,7 +876,7 @@ hipError_t launch_flash_decode_bf16(const bf16 *q_cat, const void *cache, int ca
                            (const uint8_t *)cache, seq_stride_bytes, n_kv, n_kv_max, n_splits, split_len,
                            scale * fl::LOG2E, part_o, part_lse);
     } else {
-        const size_t shm = (size_t)DC_NS * fl::TILE_BYTES + PBUF_BYTES;
+        const size_t shm = dc_stage_bytes(false) + PBUF_BYTES;
         static bool attr_set = false;
         if (!attr_set) {
             hipError_t e = hipFuncSetAttribute((const void *)flash_decode_kernel<false>,
