@@ -840,11 +840,12 @@ __global__ __launch_bounds__(64 * DC_NW, 1) void flash_decode_kernel(
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int h = hg * (32 * DC_NW) + w * 32 + (l & 31);
     const bool valid = h < H;
+    WaveState st;
+    // the query loads go out before the sequence length is read: the two latencies overlap
+    load_q(st, q_cat + ((int64_t)b * H + (valid ? h : 0)) * fl::W);
     const int nk = min(n_kv[b], n_kv_max);  // rows past n_kv_max are never read
     const int k0 = s * split_len;
     const int k1 = min(k0 + split_len, nk);
-    WaveState st;
-    load_q(st, q_cat + ((int64_t)b * H + (valid ? h : 0)) * fl::W);
     const uint8_t *rows = cache + b * seq_stride;
     attend_range<DC_NW, DC_NS, Q8>(st, lds, pbuf, &misc->flag, rows, nk, k0, k1, k1 - 1, k1 - 1,
                                    sc);
