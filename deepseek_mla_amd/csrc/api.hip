@@ -240,11 +240,22 @@ int mla_out_proj(const mla_dims *d, mla_dtype act, const void *o_lat, const void
                                    HDv, HDv, HDv, D, 1, 0, 0, 0, st);
     } else {
         if (R % 8 || Dv % 8) return MLA_ERR_UNSUPPORTED;
-        e = launch_gemm_nt_bf16((const bf16 *)o_lat, (const bf16 *)wv_b, (bf16 *)v_scratch, T, Dv,
-                                R, (int64_t)H * R, R, HDv, H, R, (int64_t)Dv * R, Dv, st);
-        if (e == hipSuccess)
-            e = launch_gemm_nt_bf16((const bf16 *)v_scratch, (const bf16 *)wo, (bf16 *)out, T, D,
-                                    HDv, HDv, HDv, D, 1, 0, 0, 0, st);
+        const bf16 *ol = (const bf16 *)o_lat, *wv = (const bf16 *)wv_b, *w_o = (const bf16 *)wo;
+        bf16 *v = (bf16 *)v_scratch;
+        // few tokens (decode): both products are streams over the weights
+        const bool few = gemv_nt_bf16_ok(ol, wv, T, R, (int64_t)H * R, R, R, (int64_t)Dv * R) &&
+                         gemv_nt_bf16_ok(v, w_o, T, HDv, HDv, HDv, 0, 0);
+        if (few) {
+            e = launch_gemv_nt_bf16(ol, wv, v, T, Dv, R, (int64_t)H * R, R, HDv, H, R,
+                                    (int64_t)Dv * R, Dv, st);
+            if (e == hipSuccess)
+                e = launch_gemv_nt_bf16(v, w_o, (bf16 *)out, T, D, HDv, HDv, HDv, D, 1, 0, 0, 0, st);
+        } else {
+            e = launch_gemm_nt_bf16(ol, wv, v, T, Dv, R, (int64_t)H * R, R, HDv, H, R,
+                                    (int64_t)Dv * R, Dv, st);
+            if (e == hipSuccess)
+                e = launch_gemm_nt_bf16(v, w_o, (bf16 *)out, T, D, HDv, HDv, HDv, D, 1, 0, 0, 0, st);
+        }
     }
     return hip_status(e);
 }

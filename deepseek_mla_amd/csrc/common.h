@@ -64,6 +64,13 @@ hipError_t launch_dequant_q8_0(const uint8_t *rows, float *out, int64_t n_rows, 
 hipError_t launch_gemm_nt_bf16(const bf16 *A, const bf16 *B, bf16 *C, int M, int N, int K,
                                int64_t lda, int64_t ldb, int64_t ldc, int batch, int64_t sA,
                                int64_t sB, int64_t sC, hipStream_t st);
+// few-row NT product (M <= GEMV_MAX_M rows of A), a stream over B; see gemv.hip
+constexpr int GEMV_MAX_M = 8;
+bool gemv_nt_bf16_ok(const bf16 *A, const bf16 *B, int M, int K, int64_t lda, int64_t ldb,
+                     int64_t sA, int64_t sB);
+hipError_t launch_gemv_nt_bf16(const bf16 *A, const bf16 *B, bf16 *C, int M, int N, int K,
+                               int64_t lda, int64_t ldb, int64_t ldc, int batch, int64_t sA,
+                               int64_t sB, int64_t sC, hipStream_t st);
 hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int T, int H,
                                      const bf16 *cache, int n_kv, int hc, float scale,
                                      bf16 *o_lat, float *lse, hipStream_t st);

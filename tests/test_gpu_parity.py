@@ -338,3 +338,22 @@ def test_v3_decode_q8_sampled_heads(dev):
         ro, rl = oracle.attention(d, qc[b:b + 1][:, heads], x["pos"][b:b + 1], rows)
         report(f"o_lat seq {b}", rel_err_stored(got["o_lat"][b][heads], ro[0], "q8_0"), 2e-2)
         report(f"lse seq {b} (abs)", float(np.abs(got["lse"][b][heads] - rl[0]).max()), 2e-2)
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 9])
+def test_out_proj_few_and_many_tokens(dev, T):
+    """Late projections at V3 dims across the few-token stream (T <= 8) and the matrix-core
+    tile path (T = 9), against the oracle on the same bf16 inputs."""
+    from deepseek_mla_amd import mla
+    d = synth.deepseek_dims(128, 7168)
+    x = synth.generate(d, 1, 8, seed=71, mode="bf16")
+    rng = np.random.default_rng(72)
+    o_lat = synth.round_bf16(rng.standard_normal((T, 128, 512)) * 0.2)
+    rv, ro = oracle.out_proj(d, o_lat, x["wv_b"], x["wo"])
+    tb = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(torch.bfloat16)
+    v = torch.empty((T, 128 * 128), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, 7168), dtype=torch.bfloat16, device=dev)
+    mla.mla_out_proj(mla.make_dims(d), mla.BF16, tb(o_lat), tb(x["wv_b"]), tb(x["wo"]), v, out, T)
+    torch.cuda.synchronize()
+    report("v", rel_err_stored(v.float().cpu().numpy(), rv, "bf16"), 2e-2)
+    report("out", rel_err_stored(out.float().cpu().numpy(), ro, "bf16"), 2e-2)
