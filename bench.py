@@ -38,11 +38,11 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 # passes scaled by a 512 MiB copy (fetch x2.0, write x1.0); the summaries and commands are
 # in profiles/.  Valid only for the kernel source they were taken on (sha256 prefix).
 TRAFFIC = {
-    "src": ("deepseek_mla_amd/csrc/flash_mfma.hip", "ccf41e0558d589da"),
-    "lite_prefill": 61.55e6 + 47.32e6,
-    "v3_long_prefill": 10187.41e6 + 1514.14e6,
-    "v3_decode": (51.78e6 + 81.73e6) + (68.20e6 + 0.14e6),       # partial kernel + combine
-    "v3_decode_q8": (279.56e6 + 100.53e6) + (68.20e6 + 0.54e6),  # partial kernel + combine
+    "src": ("deepseek_mla_amd/csrc/flash_mfma.hip", "af02fb833509d34d"),
+    "lite_prefill": 60.75e6 + 37.36e6,
+    "v3_long_prefill": 18548.08e6 + 1195.38e6,
+    "v3_decode": (41.74e6 + 36.31e6) + (34.69e6 + 0.14e6),       # partial kernel + combine
+    "v3_decode_q8": (246.21e6 + 34.21e6) + (34.70e6 + 0.54e6),  # partial kernel + combine
 }
 
 
