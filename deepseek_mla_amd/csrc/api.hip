@@ -34,7 +34,7 @@ int auto_splits(const mla_dims *d, int kv, int B, int n_kv_max) {
         int s = (n_kv_max + 255) / 256;
         return s < 1 ? 1 : (s > 64 ? 64 : s);
     }
-    const int hgroups = (d->n_head + 127) / 128;
+    const int hgroups = (d->n_head + decode_heads_per_block() - 1) / decode_heads_per_block();
     const int per_seq = (B * hgroups);
     int s = (NUM_CUS + per_seq - 1) / per_seq;
     // at least 4 tiles of 32 keys per split

@@ -74,6 +74,8 @@ hipError_t launch_gemv_nt_bf16(const bf16 *A, const bf16 *B, bf16 *C, int M, int
 hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int T, int H,
                                      const bf16 *cache, int n_kv, int hc, float scale,
                                      bf16 *o_lat, float *lse, hipStream_t st);
+// heads per workgroup of the decode kernel (the split planner fills the CUs with it)
+int decode_heads_per_block();
 hipError_t launch_flash_decode_bf16(const bf16 *q_cat, const void *cache, int cache_q8,
                                     int64_t seq_stride_bytes, const int32_t *n_kv, int n_kv_max,
                                     int B, int H,

@@ -1,0 +1,273 @@
+// Latent-cache tile layout in LDS and the copies that fill it (gfx950), shared by the
+// prefill and decode attention kernels.
+//
+// A cache row is [c_kv (512 bf16) | k_rope (64 bf16)] (1152 B), or its Q8_0 form of 18
+// blocks {binary16 scale, int8 q[32]} (612 B).  A tile holds 32 consecutive rows.
+//
+// LDS tile layout (32 keys, 38912 B).  The latent part (512 bf16 = 64 chunks of 16 B per
+// key) sits in rows of pitch 1088 B, logical chunk c at chunk c ^ mask_a(k); the rope part
+// (64 bf16 = 8 chunks) follows in rows of 128 B, chunk c at c ^ mask_b(k).  One copy
+// instruction then moves one whole latent row (uniform global address, lane-contiguous
+// LDS), and both the 16-byte K-fragment reads of 16 consecutive rows and the transposing
+// V reads of 4 consecutive rows are free of bank conflicts (see mask_a and mask_b).
+#pragma once
+
+#include "common.h"
+
+#include <type_traits>
+#include <utility>
+
+namespace mla {
+// Calls f(std::integral_constant<int, K>) for K = 0 .. N-1 (fully unrolled, K usable in
+// constant expressions).
+template <typename F, int... K>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, K...>) {
+    (f(std::integral_constant<int, K>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+namespace fl {
+constexpr int R = 512, DR = 64, W = 576;
+constexpr int RB = W * 2;         // 1152 bytes per bf16 row
+constexpr int WCH = W / 8;        // 72 chunks of 16 B per row
+constexpr int NK = 32;            // keys per tile
+constexpr int PA = 1088;                    // latent row pitch: 1024 B + 64 B pad
+constexpr int A_BYTES = NK * PA;            // 34816 B
+constexpr int PB = 128;                     // rope row pitch
+constexpr int TILE_BYTES = A_BYTES + NK * PB;  // 38912 B
+constexpr int Q8_RB = W / 32 * 34;          // 612 B per Q8_0 row
+constexpr int Q8_TILE_BYTES = NK * Q8_RB;   // 19584 B, 16-B aligned for aligned tiles
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float FREEZE_LIMIT = 64.0f;  // log2 units a score may exceed the frozen max by
+}  // namespace fl
+
+// LDS has 64 banks of 4 B, i.e. 16 groups of 16 B.
+// Latent rows: the pitch of 1088 B moves row k by 4k groups and the mask XORs the low
+// two chunk bits with (k >> 2) & 3, so
+//  - 16 consecutive rows read at one logical chunk (K fragments, 16 lanes per cycle)
+//    land in 16 distinct groups: 4 * (k & 3) picks the high part, the mask the low part;
+//  - a ds_read_b64_tr_b16 half-wave reads 4 consecutive rows (one mask value) x 4
+//    chunks: the rows pick distinct high parts, the chunks distinct low parts.
+__device__ __forceinline__ int mask_a(int k) { return (k >> 2) & 3; }
+// Rope rows (128 B = half a bank row): even and odd rows take the two halves, and bits
+// (k1, k2, k3) of the row index as bits (2, 1, 0) of the mask spread 8 even (odd) rows
+// over the 8 groups of their half.
+__device__ __forceinline__ int mask_b(int k) {
+    return (((k >> 1) & 1) << 2) | (((k >> 2) & 1) << 1) | ((k >> 3) & 1);
+}
+// Byte offset of logical chunk c (0 .. 71) of key k in a tile.
+__device__ __forceinline__ int tile_off(int k, int c) {
+    return c < 64 ? k * fl::PA + ((c ^ mask_a(k)) * 16)
+                  : fl::A_BYTES + k * fl::PB + (((c - 64) ^ mask_b(k)) * 16);
+}
+
+// Lanes l and l^32 hold the same query row; these combine the pair (ds_bpermute).
+// Both halves compute (x[l % 32] op x[32 + l % 32]), so the results are bit-identical.
+__device__ __forceinline__ float pair_max(float x) {
+    const float y = __shfl_xor(x, 32);
+    return (threadIdx.x & 32) ? fmaxf(y, x) : fmaxf(x, y);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const float y = __shfl_xor(x, 32);
+    return (threadIdx.x & 32) ? y + x : x + y;
+}
+
+__device__ __forceinline__ bf16x8 tr_pair(const uint8_t MLA_LDS *p0, const uint8_t MLA_LDS *p1) {
+    s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS *)p0);
+    s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 MLA_LDS *)p1);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// One LDS-direct copy instruction: lane l moves 16 bytes from sbase + voff (sbase uniform)
+// to LDS address lds_addr + 16*l (lds_addr uniform, through M0).  Written as inline asm so
+// that the compiler's LDS wait tracking does not see it: the compiler follows the builtin
+// form with a wait for every outstanding LDS read, which would drain the read rings of the
+// tile loop.  Completion is tracked by hand: a vmcnt wait and a barrier precede every read
+// of a copied tile, and no other vector-memory instruction is issued in the tile loop.
+__device__ __forceinline__ void lds_copy16(const uint8_t *sbase, uint32_t voff,
+                                           uint32_t lds_addr) {
+    const uint64_t a = (uint64_t)sbase;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint64_t su = ((uint64_t)hi << 32) | lo;
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(su), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+        : "memory", "m0");
+}
+
+// Dword form of lds_copy16: lane l moves 4 bytes from sbase + voff to lds_addr + 4*l.
+__device__ __forceinline__ void lds_copy4(const uint8_t *sbase, uint32_t voff, uint32_t lds_addr) {
+    const uint64_t a = (uint64_t)sbase;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint64_t su = ((uint64_t)hi << 32) | lo;
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %0, %1"
+        :
+        : "v"(voff), "s"(su), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+        : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const uint8_t MLA_LDS *p) {
+    return (uint32_t)(uintptr_t)p;
+}
+
+// Async copy of one bf16 tile (32 keys from key0; keys past `last` re-read key `last`,
+// they are masked out of the softmax) into LDS stage `dst`.  Part i (0 .. 8) of wave w:
+// parts 0..7 copy the latent row 8w + i (one instruction, uniform source row), part 8
+// copies the rope rows 8w .. 8w+7 (one instruction).
+template <int NW>
+__device__ __forceinline__ void issue_chunk_bf16(const uint8_t *__restrict__ rows, int key0,
+                                                 int last, uint8_t MLA_LDS *dst, int i) {
+    static_assert(NW == 4, "one latent row per instruction: 8 rows and one rope part per wave");
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l = threadIdx.x & 63;
+    if (i < 8) {
+        const int k = w * 8 + i;
+        const uint8_t *src = rows + (int64_t)min(key0 + k, last) * fl::RB;
+        lds_copy16(src, (uint32_t)((l ^ mask_a(k)) * 16), lds_u32(dst + k * fl::PA));
+    } else {
+        // rows past `last` are clamped per lane; offsets stay below 32 rows
+        const int k = w * 8 + (l >> 3);
+        const int kr = min(k, last - key0);
+        lds_copy16(rows + (int64_t)key0 * fl::RB,
+                   (uint32_t)(kr * fl::RB + fl::R * 2 + (((l & 7) ^ mask_b(k)) * 16)),
+                   lds_u32(dst + fl::A_BYTES + w * 1024));
+    }
+}
+
+// Copy plan of a full tile (all 32 keys inside the cache) for wave w: one uniform source
+// address per tile (key0 + 8w) plus a compile-time row step per instruction, and lane
+// offsets fixed for the whole stream.  Latent row 8w + i uses mask_a(8w + i) =
+// (2w + i/4) & 3, so rows i < 4 and i >= 4 take two lane offsets.  The rope instruction
+// covers rows 8w .. 8w+7.  (The instruction's immediate offset is left at 0: it would
+// move the LDS destination as well.)
+struct CopyPlan {
+    uint32_t va0, va1, vb;
+};
+__device__ __forceinline__ CopyPlan make_copy_plan() {
+    const int w = threadIdx.x >> 6;
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));  // recomputed where used, not kept live across the loop
+    CopyPlan c;
+    c.va0 = (uint32_t)((l ^ mask_a(8 * w)) * 16);
+    c.va1 = (uint32_t)((l ^ mask_a(8 * w + 4)) * 16);
+    c.vb = (uint32_t)((l >> 3) * fl::RB + fl::R * 2 + (((l & 7) ^ mask_b(8 * w + (l >> 3))) * 16));
+    return c;
+}
+
+// Part I (0 .. 8) of a full tile's copy for this wave: sbase = rows + (key0 + 8w) * 1152
+// (uniform), dst = the LDS stage.
+template <int I>
+__device__ __forceinline__ void issue_part_full(const uint8_t *sbase, const CopyPlan &c,
+                                                uint32_t dst, int w) {
+    if constexpr (I < 8) {
+        lds_copy16(sbase + I * fl::RB, I < 4 ? c.va0 : c.va1,
+                   dst + (uint32_t)((8 * w + I) * fl::PA));
+    } else {
+        lds_copy16(sbase, c.vb, dst + (uint32_t)(fl::A_BYTES + w * 1024));
+    }
+}
+
+template <int NW>
+__device__ __forceinline__ void issue_tile_bf16(const uint8_t *__restrict__ rows, int key0,
+                                                int last, uint8_t MLA_LDS *dst) {
+#pragma unroll
+    for (int i = 0; i < 9; ++i) issue_chunk_bf16<NW>(rows, key0, last, dst, i);
+}
+
+// Issue the async copy of the raw Q8_0 bytes of a 32-row tile into LDS, one dword per
+// lane (612-byte rows are dword aligned, not 16-byte aligned).  Dwords past the
+// sequence's last row re-read its final dword; the dequant pass zeroes those rows.
+// 80 instructions of 64 dwords cover the 4896-dword tile; the stage holds 20480 B.
+constexpr int Q8_RAW_DW = fl::Q8_TILE_BYTES / 4;      // 4896
+constexpr int Q8_RAW_INST = (Q8_RAW_DW + 63) / 64 + 3; // 80 (rounded up to a multiple of 4)
+constexpr int Q8_RAW_STAGE = Q8_RAW_INST * 256;        // 20480 B
+static_assert(Q8_RAW_INST * 64 >= Q8_RAW_DW, "raw tile coverage");
+
+template <int NW>
+__device__ __forceinline__ void issue_tile_q8(const uint8_t *__restrict__ rows, int key0,
+                                              int n_rows, uint8_t MLA_LDS *dst) {
+    static_assert(Q8_RAW_INST % NW == 0, "raw copies must split evenly over waves");
+    constexpr int NI = Q8_RAW_INST / NW;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w >= NW) return;  // only waves 0 .. NW-1 copy
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));  // recompute offsets per call (see issue_tile_bf16)
+    // tile-relative dword index of the sequence's last dword (uniform, 32-bit)
+    const int64_t rem = (int64_t)(n_rows - key0) * (fl::Q8_RB / 4) - 1;
+    const int last_rel = (int)(rem < Q8_RAW_INST * 64 ? rem : Q8_RAW_INST * 64);
+    const uint8_t *gbase = rows + (int64_t)key0 * fl::Q8_RB;
+    // inline-asm copies (lds_copy4): the compiler's wait tracking does not see them, so
+    // it inserts no waits for them; every read of a copied tile follows a vmcnt wait and
+    // a workgroup barrier placed by hand
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int inst = w * NI + i;
+        const uint32_t off = (uint32_t)min(inst * 64 + l, last_rel) * 4u;
+        lds_copy4(gbase, off, lds_u32(dst + inst * 256));
+    }
+}
+
+// Number of async-copy instructions a wave issues per Q8_0 tile (for vmcnt waits).
+template <int NW> __host__ __device__ constexpr int q8_inst_per_wave() {
+    return Q8_RAW_INST / NW;
+}
+
+// Dequantise the raw Q8_0 tile (LDS) into the bf16 tile layout (LDS).  Task = (row,
+// block of 32 values); rows with key0 + k >= n_rows are written as zeros.
+template <int NW>
+__device__ __forceinline__ void dequant_tile_q8(const uint8_t MLA_LDS *raw, int key0, int n_rows,
+                                                uint8_t MLA_LDS *dst) {
+    constexpr int NB = fl::W / 32;  // 18 blocks per row
+    for (int task = threadIdx.x; task < fl::NK * NB; task += 64 * NW) {
+        const int k = task / NB, b = task % NB;
+        const int off = k * fl::Q8_RB + b * 34;       // block start, 2-byte aligned
+        const int a0 = off & ~3, sh = (off & 2) * 8;  // dword-aligned window
+        uint32_t wv[10];
+#pragma unroll
+        for (int i = 0; i < 10; ++i) {
+            const int o = a0 + 4 * i;
+            wv[i] = (o < fl::Q8_TILE_BYTES) ? *(const uint32_t MLA_LDS *)(raw + o) : 0u;
+        }
+        // bytes starting at `off`: shift the window right by sh bits
+        uint32_t bb[9];
+#pragma unroll
+        for (int i = 0; i < 9; ++i)
+            bb[i] = sh ? ((wv[i] >> 16) | (wv[i + 1] << 16)) : wv[i];
+        const bool valid = (key0 + k) < n_rows;
+        const float d = valid ? (float)__builtin_bit_cast(_Float16, (uint16_t)(bb[0] & 0xFFFF)) : 0.0f;
+        // codes: bytes 2..33 of the block = bb[0]>>16 .. bb[8]&0xFFFF
+        bf16 v[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int byte = 2 + i;
+            const uint32_t word = bb[byte >> 2];
+            const int8_t q = (int8_t)((word >> ((byte & 3) * 8)) & 0xFF);
+            v[i] = f2bf(d * (float)q);
+        }
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int c = b * 4 + qq;
+            uint8_t MLA_LDS *p = dst + tile_off(k, c);
+            bf16x8 t;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t[e] = v[qq * 8 + e];
+            *(bf16x8 MLA_LDS *)p = t;
+        }
+    }
+}
+
+}  // namespace mla

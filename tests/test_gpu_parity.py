@@ -270,6 +270,89 @@ def test_decode_splits(dev, mode):
             report("lse (abs)", float(np.abs(lse[b].cpu().numpy() - ref[b][1][0]).max()), TOL[mode])
 
 
+def _decode_run(d, q, rows_list, lens, mode, ns):
+    """mla_attn_decode on B sequences (bf16 queries q [B,H,576]); rows_list holds the float
+    rows (bf16-rounded) of each sequence.  Returns o_lat, lse as numpy."""
+    from deepseek_mla_amd import mla
+    B, H = q.shape[0], q.shape[1]
+    Nmax = max(r.shape[0] for r in rows_list)
+    pad = [np.concatenate([r, np.zeros((Nmax - r.shape[0], 576), np.float32)]) for r in rows_list]
+    if mode == "q8_0":
+        cache = torch.from_numpy(np.stack([oracle.q8_0_quantize(r) for r in pad])).to(dev_name())
+        stride, kv = 612 * Nmax, mla.Q8_0
+    else:
+        cache = torch.from_numpy(np.stack(pad)).to(dev_name()).to(torch.bfloat16)
+        stride, kv = 1152 * Nmax, mla.BF16
+    qd = torch.from_numpy(q).to(dev_name()).to(torch.bfloat16)
+    nkv = torch.tensor(lens, dtype=torch.int32, device=dev_name())
+    cd = mla.make_dims(d)
+    wsb = mla.mla_decode_workspace_bytes(cd, B, Nmax, ns)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev_name())
+    o = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev_name())
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev_name())
+    mla.mla_attn_decode(cd, mla.BF16, kv, qd, cache, stride, nkv, B, Nmax, ns, o, lse, ws, wsb)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def dev_name():
+    return "cuda"
+
+
+@pytest.mark.parametrize("mode", ["bf16", "q8_0"])
+def test_decode_score_jump_repass(dev, mode):
+    """Decode: a key whose score exceeds its split's first-tile max by far more than 2^64
+    (base 2) triggers the repeated pass; split counts 1 and 3 put the key in a later tile
+    of its split.  The result still matches the oracle.
+
+    The jump row is made of half-integers with a maximum of 63.5 in every 32-value block,
+    so its Q8_0 codes (scale 0.5) and their bf16 conversion are exact: a row some 400 times
+    the size of the others would otherwise magnify the bf16 rounding of dequantised values
+    (a documented step of the Q8_0 path) past the tolerance, and the test is about the
+    repeated pass."""
+    d = synth.deepseek_dims(128, 7168)
+    N = 300
+    rng = np.random.default_rng(45)
+    q = synth.round_bf16(rng.standard_normal((1, 128, 576)).astype(np.float32) * 0.1)
+    rows = synth.round_bf16(rng.standard_normal((N, 576)).astype(np.float32) * 0.1)
+    jump = np.clip(np.round(q[0, 5].astype(np.float64) * 800.0), -127, 127).reshape(18, 32)
+    for blk in jump:  # one code of +-127 per block: amax 63.5, scale exactly 0.5
+        i = int(np.argmax(np.abs(blk)))
+        blk[i] = 127.0 if blk[i] >= 0 else -127.0
+    rows[250] = (jump.reshape(576) * 0.5).astype(np.float32)  # ~150 nats for head 5
+    if mode == "q8_0":
+        rows = oracle.q8_0_dequantize(oracle.q8_0_quantize(rows), 576)
+    s_max = d.scale * rows[250].astype(np.float64) @ q[0, 5].astype(np.float64)
+    assert s_max > 60.0
+    ro, rl = oracle.attention(d, q, np.array([N - 1], np.int32), rows)
+    for ns in (1, 3):
+        o, lse = _decode_run(d, q, [rows], [N], mode, ns)
+        print(f" splits={ns}")
+        report("o_lat", rel_err_stored(o[0], ro[0], mode), TOL[mode])
+        report("lse (abs)", float(np.abs(lse[0] - rl[0]).max()), TOL[mode])
+
+
+@pytest.mark.parametrize("H", [16, 96])
+def test_decode_partial_head_groups(dev, H):
+    """Decode with head counts that leave a 64-head workgroup partly empty (16: one group;
+    96: a full and a half group), 3 sequences of ragged length, bf16 and Q8_0 caches."""
+    d = synth.deepseek_dims(H, 2048)
+    lens = [33, 130, 77]
+    rng = np.random.default_rng(46 + H)
+    q = synth.round_bf16(rng.standard_normal((3, H, 576)).astype(np.float32) * 0.3)
+    rows = [synth.round_bf16(rng.standard_normal((n, 576)).astype(np.float32)) for n in lens]
+    for mode in ("bf16", "q8_0"):
+        rr = rows if mode == "bf16" else [oracle.q8_0_dequantize(oracle.q8_0_quantize(r), 576)
+                                          for r in rows]
+        for ns in (1, 2, 0):
+            o, lse = _decode_run(d, q, rr, lens, mode, ns)
+            for b in range(3):
+                ro, rl = oracle.attention(d, q[b:b + 1], np.array([lens[b] - 1], np.int32), rr[b])
+                print(f" {mode} splits={ns} seq={b}")
+                report("o_lat", rel_err_stored(o[b], ro[0], mode), TOL[mode])
+                report("lse (abs)", float(np.abs(lse[b] - rl[0]).max()), TOL[mode])
+
+
 # ------------------------------------------------------- full-size configs ---
 
 def _sample(T, k, seed):
