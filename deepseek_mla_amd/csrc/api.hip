@@ -188,8 +188,7 @@ int mla_attn_decode(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *
         row_bytes = (int64_t)W * (kv == MLA_F32 ? 4 : 2);
     }
     if (B > 1 && kv_seq_stride_bytes < row_bytes * n_kv_max) return MLA_ERR_INVALID_ARG;
-    if (kv_seq_stride_bytes < 0 || (kv != MLA_Q8_0 && kv_seq_stride_bytes % 16) ||
-        (kv == MLA_Q8_0 && kv_seq_stride_bytes % 4))
+    if (kv_seq_stride_bytes < 0 || kv_seq_stride_bytes % 16)
         return MLA_ERR_INVALID_ARG;
     if (kv != MLA_F32 && !bf16_attn_dims(d)) return MLA_ERR_UNSUPPORTED;
     if (kv == MLA_F32 && d->kv_lora_rank > 1024) return MLA_ERR_UNSUPPORTED;

@@ -341,6 +341,22 @@ __device__ __forceinline__ void wait_groups(int n) {
     }
 }
 
+// Waits until at most n of this wave's copy instructions are outstanding, n a sum of up
+// to three Q8_0 tile counts (5 each, the last possibly 20): 0, 5, 10, 15, 20, 25 or 30.
+__device__ __forceinline__ void wait_vm_q8(int n) {
+    switch (n) {
+    case 0: MLA_WAIT_VMCNT(0); break;
+    case 5: MLA_WAIT_VMCNT(5); break;
+    case 10: MLA_WAIT_VMCNT(10); break;
+    case 15: MLA_WAIT_VMCNT(15); break;
+    case 20: MLA_WAIT_VMCNT(20); break;
+    case 25: MLA_WAIT_VMCNT(25); break;
+    default: MLA_WAIT_VMCNT(30); break;
+    }
+}
+static_assert(Q8_X4_INST / dq::NW == 5 && q8_inst_per_wave<dq::NW>() == 20,
+              "wait_vm_q8 enumerates sums of 5 and 20");
+
 // One pass over keys [k0, k1) of `rows` (nk rows in the sequence); Q8: rows are Q8_0.
 // bf16: the O update of tile t-1 (with the softmax of tile t between its MFMAs) follows
 // the scores of tile t; one barrier per tile; two tiles in flight.  Q8_0: each tile's
@@ -433,19 +449,30 @@ __device__ __forceinline__ void dq_stream(DqState &st, uint8_t MLA_LDS *lds,
         }
         __syncthreads();
     } else {
-        constexpr int PER = q8_inst_per_wave<dq::NW>();
+        // Raw tiles: 16-byte copies (5 per wave) for tiles inside the sequence, dword
+        // copies clamped to the sequence's last byte (20 per wave) for the one tile that
+        // reaches past it, which can only be the split's last tile.
+        constexpr int PX = Q8_X4_INST / dq::NW, PD = q8_inst_per_wave<dq::NW>();
+        const bool tail = k0 + ntiles * fl::NK > nk;
+        auto cnt = [&](int j) { return (tail && j == ntiles - 1) ? PD : PX; };
         uint8_t MLA_LDS *raw = lds + 2 * fl::TILE_BYTES;
-        for (int i = 0; i < dq::NRAW; ++i)
-            if (i < ntiles) issue_tile_q8<dq::NW>(rows, k0 + i * fl::NK, nk, raw + i * Q8_RAW_STAGE);
-        // raw tile 0 (and the query copies issued before it) landed
-        {
-            const int n = min(3, ntiles - 1);
-            if (n >= 3) {
-                MLA_WAIT_VMCNT(3 * PER);
+        auto issue_raw = [&](int j) {
+            uint8_t MLA_LDS *dst = raw + (j % dq::NRAW) * Q8_RAW_STAGE;
+            if (tail && j == ntiles - 1) {
+                issue_tile_q8<dq::NW>(rows, k0 + j * fl::NK, nk, dst);
             } else {
-                wait_groups<PER>(n);
+                issue_tile_q8_full<dq::NW>(rows, k0 + j * fl::NK, dst);
             }
-        }
+        };
+        // waits until raw tile j has landed, given that tiles up to `issued` were issued
+        auto wait_raw = [&](int j, int issued) {
+            int n = 0;
+            for (int i = j + 1; i <= issued; ++i) n += cnt(i);
+            wait_vm_q8(n);
+        };
+        for (int i = 0; i < dq::NRAW; ++i)
+            if (i < ntiles) issue_raw(i);
+        wait_raw(0, min(dq::NRAW, ntiles) - 1);  // raw tile 0 and the query copies before it
         __syncthreads();
         if (first) {
             read_query(st, qs);
@@ -454,11 +481,9 @@ __device__ __forceinline__ void dq_stream(DqState &st, uint8_t MLA_LDS *lds,
         dequant_tile_q8<dq::NW>(raw, k0, nk, lds);
         for (int t = 0; t < ntiles; ++t) {
             // raw tile t+1 landed (raw tiles up to t+3 issued)
-            if (t + 1 < ntiles) wait_groups<PER>(min(2, ntiles - 2 - t));
+            if (t + 1 < ntiles) wait_raw(t + 1, min(t + 3, ntiles - 1));
             __syncthreads();  // bf16 tile t complete; tile t-1's O update done everywhere
-            if (t + 4 < ntiles)
-                issue_tile_q8<dq::NW>(rows, k0 + (t + 4) * fl::NK, nk,
-                                      raw + ((t + 4) % dq::NRAW) * Q8_RAW_STAGE);
+            if (t + 4 < ntiles) issue_raw(t + 4);
             const uint8_t MLA_LDS *tile = lds + (t & 1) * fl::TILE_BYTES;
             f32x4 s[2];
             score_tile_q(st, tile, ka, s, [](auto) {});

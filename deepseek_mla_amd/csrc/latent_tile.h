@@ -221,6 +221,32 @@ __device__ __forceinline__ void issue_tile_q8(const uint8_t *__restrict__ rows, 
     }
 }
 
+// Copy of a raw Q8_0 tile whose 32 rows all lie inside the sequence, in 16-byte pieces
+// (the tile's 19584 bytes are 1224 pieces, 16-byte aligned when the sequence base is):
+// 20 instructions, Q8_X4_INST / NW per wave; instruction i, lane l moves piece
+// min(64 i + l, 1223) to the same offset of the stage (lanes past the tile repeat the
+// last piece into the stage's spare bytes).
+constexpr int Q8_X4_INST = 20;
+static_assert(Q8_X4_INST * 1024 >= fl::Q8_TILE_BYTES && Q8_X4_INST * 1024 <= Q8_RAW_STAGE,
+              "16-byte raw copies cover the tile and stay inside the stage");
+template <int NW>
+__device__ __forceinline__ void issue_tile_q8_full(const uint8_t *__restrict__ rows, int key0,
+                                                   uint8_t MLA_LDS *dst) {
+    static_assert(Q8_X4_INST % NW == 0, "raw copies must split evenly over waves");
+    constexpr int NI = Q8_X4_INST / NW;
+    constexpr int LAST = fl::Q8_TILE_BYTES / 16 - 1;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));
+    const uint8_t *gbase = rows + (int64_t)key0 * fl::Q8_RB;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int inst = w * NI + i;
+        lds_copy16(gbase, (uint32_t)min(inst * 64 + l, LAST) * 16u, lds_u32(dst + inst * 1024));
+    }
+}
+static_assert(fl::Q8_TILE_BYTES % 16 == 0, "a tile is a whole number of 16-byte pieces");
+
 // Number of async-copy instructions a wave issues per Q8_0 tile (for vmcnt waits).
 template <int NW> __host__ __device__ constexpr int q8_inst_per_wave() {
     return Q8_RAW_INST / NW;

@@ -51,17 +51,21 @@ class LayerStep:
         self.n_seq = S
         if mode == "q8_0":
             rb = mla.mla_q8_0_row_bytes(W)
-            self.cache = torch.empty((S, n_kv, rb), dtype=torch.uint8, device=device)
+            # sequences start 16-byte aligned: the stride is n_kv rows rounded up to 16 B
+            self.cache = torch.empty((S, (n_kv * rb + 15) // 16 * 16), dtype=torch.uint8,
+                                     device=device)
             for s in range(S):  # quantise one sequence at a time (bounded float32 staging)
                 rows = _dev(synth.cache_rows(inputs["c_kv"][s], inputs["k_rope"][s]),
                             torch.float32, device)
                 mla.mla_quantize_q8_0(rows, self.cache[s], n_kv, W)
                 del rows
             self.row_bytes = rb
+            self.seq_stride = int(self.cache.shape[1])
         else:
             rows = np.concatenate([inputs["c_kv"], inputs["k_rope"]], axis=-1)
             self.cache = _dev(rows, tdt, device)
             self.row_bytes = W * (4 if mode == "f32" else 2)
+            self.seq_stride = n_kv * self.row_bytes
         # identical copies of the cache, used in rotation (keeps timing honest when the
         # cache would otherwise stay resident in the last-level cache between steps)
         self.caches = [self.cache] + [self.cache.clone() for _ in range(cache_copies - 1)]
@@ -90,7 +94,7 @@ class LayerStep:
                                  self.scratch_cap_mib, stream)
         else:
             mla.mla_attn_decode(self.cdims, self.act, self.kv, self.q_cat, self.cache,
-                                self.n_kv * self.row_bytes, self.n_kv_dev, self.n_seq, self.n_kv,
+                                self.seq_stride, self.n_kv_dev, self.n_seq, self.n_kv,
                                 self.n_splits, self.o_lat, self.lse, self.workspace,
                                 self.ws_bytes, stream)
 

@@ -123,7 +123,9 @@ int32_t mla_decode_auto_splits(const mla_dims *dims, mla_dtype kv, int32_t B, in
  * Splits with no row contribute nothing (lse_s = -inf).
  * q_cat [B][H][W] (act); kv_cache: sequence b's rows start at byte offset
  * b * kv_seq_stride_bytes (rows of W values for F32/BF16, of W/32*34 bytes for
- * Q8_0); n_kv [B] int32 on the device, each in [1, n_kv_max]; o_lat [B][H][R] (act);
+ * Q8_0), the stride a multiple of 16 bytes (a Q8_0 sequence of N rows therefore takes
+ * N*W/32*34 bytes rounded up to 16); n_kv [B] int32 on the device, each in
+ * [1, n_kv_max]; o_lat [B][H][R] (act);
  * lse [B][H] float32 or NULL; workspace of at least
  * mla_decode_workspace_bytes(dims, B, n_kv_max, n_splits) bytes (device, 16-byte
  * aligned), contents need not be initialised.

@@ -248,9 +248,9 @@ def test_decode_splits(dev, mode):
     ref = [oracle.attention(d, qc[b:b + 1], x["pos"][b:b + 1], rows_f[b][:lens[b]]) for b in range(2)]
     qd = torch.from_numpy(qc).to(dev).to(torch.bfloat16)
     if mode == "q8_0":
-        cache = torch.from_numpy(np.stack([oracle.q8_0_quantize(synth.cache_rows(
-            x["c_kv"][b], x["k_rope"][b])) for b in range(2)])).to(dev)
-        stride, kv = 612 * Nmax, mla.Q8_0
+        qb, stride = q8_cache([synth.cache_rows(x["c_kv"][b], x["k_rope"][b]) for b in range(2)],
+                              Nmax)
+        cache, kv = torch.from_numpy(qb).to(dev), mla.Q8_0
     else:
         cache = torch.from_numpy(np.stack(rows_f)).to(dev).to(torch.bfloat16)
         stride, kv = 1152 * Nmax, mla.BF16
@@ -270,6 +270,17 @@ def test_decode_splits(dev, mode):
             report("lse (abs)", float(np.abs(lse[b].cpu().numpy() - ref[b][1][0]).max()), TOL[mode])
 
 
+def q8_cache(float_rows, Nmax):
+    """Q8_0 bytes of each sequence (float rows [n, 576], n <= Nmax) in a [B][stride] uint8
+    buffer, stride = 612*Nmax rounded up to 16 bytes (the decode ABI's alignment)."""
+    stride = (612 * Nmax + 15) // 16 * 16
+    buf = np.zeros((len(float_rows), stride), np.uint8)
+    for b, r in enumerate(float_rows):
+        q = oracle.q8_0_quantize(r).reshape(-1)
+        buf[b, :q.size] = q
+    return buf, stride
+
+
 def _decode_run(d, q, rows_list, lens, mode, ns):
     """mla_attn_decode on B sequences (bf16 queries q [B,H,576]); rows_list holds the float
     rows (bf16-rounded) of each sequence.  Returns o_lat, lse as numpy."""
@@ -278,8 +289,8 @@ def _decode_run(d, q, rows_list, lens, mode, ns):
     Nmax = max(r.shape[0] for r in rows_list)
     pad = [np.concatenate([r, np.zeros((Nmax - r.shape[0], 576), np.float32)]) for r in rows_list]
     if mode == "q8_0":
-        cache = torch.from_numpy(np.stack([oracle.q8_0_quantize(r) for r in pad])).to(dev_name())
-        stride, kv = 612 * Nmax, mla.Q8_0
+        qb, stride = q8_cache(pad, Nmax)
+        cache, kv = torch.from_numpy(qb).to(dev_name()), mla.Q8_0
     else:
         cache = torch.from_numpy(np.stack(pad)).to(dev_name()).to(torch.bfloat16)
         stride, kv = 1152 * Nmax, mla.BF16
