@@ -117,9 +117,20 @@ int mla_absorb_q(const mla_dims *d, mla_dtype act, const void *q_nope, const voi
     return hip_status(e);
 }
 
+size_t mla_prefill_workspace_bytes(const mla_dims *d, mla_dtype kv, int32_t T, int32_t n_kv,
+                                   uint32_t scratch_cap_mib) {
+    if (!dims_ok(d) || T < 1 || n_kv < 1) return 0;
+    if (kv != MLA_BF16 || !bf16_attn_dims(d)) return 0;
+    const int H = d->n_head;
+    const double size_mib = (double)T * (double)n_kv * (double)H * 4.0 / (1024.0 * 1024.0);
+    const int hc = mla_heads_per_chunk(H, size_mib, scratch_cap_mib);
+    return prefill_workspace_bytes(T, H, n_kv, hc);
+}
+
 int mla_attn_prefill(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *q_cat,
                      const int32_t *pos, int32_t T, const void *kv_cache, int32_t n_kv,
-                     void *o_lat, float *lse, uint32_t scratch_cap_mib, void *stream) {
+                     void *o_lat, float *lse, uint32_t scratch_cap_mib, void *workspace,
+                     size_t workspace_bytes, void *stream) {
     if (!dims_ok(d) || !act_ok(act) || T < 0 || n_kv < 1) return MLA_ERR_INVALID_ARG;
     if (kv != MLA_F32 && kv != MLA_BF16 && kv != MLA_Q8_0) return MLA_ERR_INVALID_ARG;
     if (kv == MLA_Q8_0) return MLA_ERR_UNSUPPORTED;
@@ -142,9 +153,11 @@ int mla_attn_prefill(const mla_dims *d, mla_dtype act, mla_dtype kv, const void 
     }
     if (!bf16_attn_dims(d)) return MLA_ERR_UNSUPPORTED;
     if ((int64_t)T * hc > INT32_MAX / 2) return MLA_ERR_UNSUPPORTED;
+    const size_t need = prefill_workspace_bytes(T, H, n_kv, hc);
+    if (need && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
     return hip_status(launch_flash_prefill_bf16((const bf16 *)q_cat, pos, T, H,
                                                 (const bf16 *)kv_cache, n_kv, hc, d->scale,
-                                                (bf16 *)o_lat, lse, st));
+                                                (bf16 *)o_lat, lse, workspace, st));
 }
 
 int32_t mla_decode_auto_splits(const mla_dims *d, mla_dtype kv, int32_t B, int32_t n_kv_max) {

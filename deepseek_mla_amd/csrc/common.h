@@ -71,9 +71,13 @@ bool gemv_nt_bf16_ok(const bf16 *A, const bf16 *B, int M, int K, int64_t lda, in
 hipError_t launch_gemv_nt_bf16(const bf16 *A, const bf16 *B, bf16 *C, int M, int N, int K,
                                int64_t lda, int64_t ldb, int64_t ldc, int batch, int64_t sA,
                                int64_t sB, int64_t sC, hipStream_t st);
+// prefill key parts: parts per row group (keys per part in *ks), and the workspace the
+// merge of parts needs (0 when every group is one part)
+int prefill_parts(int T, int H, int n_kv, int *ks);
+size_t prefill_workspace_bytes(int T, int H, int n_kv, int hc);
 hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int T, int H,
                                      const bf16 *cache, int n_kv, int hc, float scale,
-                                     bf16 *o_lat, float *lse, hipStream_t st);
+                                     bf16 *o_lat, float *lse, void *ws, hipStream_t st);
 // heads per workgroup of the decode kernel (the split planner fills the CUs with it)
 int decode_heads_per_block();
 hipError_t launch_flash_decode_bf16(const bf16 *q_cat, const void *cache, int cache_q8,

@@ -32,6 +32,8 @@
 // bank conflicts (see mask_a and mask_b).
 #include "latent_tile.h"
 
+#include <algorithm>
+
 namespace mla {
 
 // Per-wave attention state and the tile computation.
@@ -439,31 +441,86 @@ __device__ __forceinline__ float finish(WaveState &st, uint8_t MLA_LDS *stage,
 }
 static_assert(OSTAGE_BYTES <= 4 * fl::TILE_BYTES, "output staging fits the tile stages");
 
-constexpr int PF_NW = 4, PF_NS = 4;
+// Normalised rows in float32 (partial results that are merged later keep full precision:
+// a merged row can be much smaller than its parts).  Row r goes to dst + r*R floats,
+// written straight from the accumulators (16 bytes per lane: 32-byte runs per row).
+// Returns lse (natural log) of this lane's own row.
+__device__ __forceinline__ float finish_f32(WaveState &st, uint8_t MLA_LDS *pbuf,
+                                            float *__restrict__ dst) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, hi = l >> 5;
+    const float lt = pair_sum(st.lsum);
+    float MLA_LDS *den = (float MLA_LDS *)pbuf;  // buffer free: the key stream ended on a barrier
+    if (l < 32) den[w * 32 + l] = lt;
+    __syncthreads();
+    const float lo = den[(w ^ 1) * 32 + (l & 31)];
+    const float inv[2] = {lt > 0.0f ? 1.0f / lt : 0.0f, lo > 0.0f ? 1.0f / lo : 0.0f};
+    const int ch = w & 1;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        float *row = dst + (int64_t)((w ^ rb) * 32 + (l & 31)) * fl::R + ch * 256 + hi * 4;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x16 &o = st.o[nb][rb];
+                const f32x4 v = {o[g * 4 + 0] * inv[rb], o[g * 4 + 1] * inv[rb],
+                                 o[g * 4 + 2] * inv[rb], o[g * 4 + 3] * inv[rb]};
+                *(f32x4 *)(row + nb * 32 + g * 8) = v;
+            }
+    }
+    return lt > 0.0f ? (st.m + __log2f(lt)) * fl::LN2 : -INFINITY;
+}
 
-// Prefill.  Rows are the flattened (token, head-in-chunk) pairs of all head chunks:
-// block -> (chunk, group of 128 rows), heavy (late) groups first.
+constexpr int PF_NW = 4, PF_NS = 4;
+constexpr int PF_ROWS = 32 * PF_NW;  // rows per workgroup
+constexpr int PF_MAX_PARTS = 4;      // key parts per row group (the merge keeps 8 weights)
+constexpr int PF_MAX_ITEMS = 1024;   // (row group, part) items when groups are cut
+// Block order of a cut prefill (a kernel argument: 2 KB, within the argument limit).
+struct PrefillOrder {
+    uint16_t item[PF_MAX_ITEMS];  // unit * nparts + part, by decreasing estimated work
+};
+static_assert(PF_MAX_PARTS <= 8, "the merge holds one log-sum-exp per part in lp[8]");
+
+// Prefill.  Rows are the flattened (token, head-in-chunk) pairs of all head chunks; a
+// group of 128 rows attends to its keys in parts of ks keys (part p: keys [p*ks,
+// (p+1)*ks)), one workgroup per (group, part).  A group whose keys fit one part writes
+// its rows directly.  Otherwise every part writes its normalised rows (float32) and their
+// log-sum-exp to the workspace slot (group, part), part 0 records the group's part count,
+// and prefill_merge_kernel merges the slots after this kernel.  The part boundaries
+// depend only on ks, so a row's result does not depend on how rows are grouped (head
+// chunks): a row whose keys all lie in one part merges that part with weight exactly 1.
 __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
     const bf16 *__restrict__ q_cat, const int32_t *__restrict__ pos, int T, int H,
     const uint8_t *__restrict__ cache, int n_kv, int hc, int n_groups, int n_chunks, float sc,
-    bf16 *__restrict__ o_lat, float *__restrict__ lse) {
+    bf16 *__restrict__ o_lat, float *__restrict__ lse, int ks, int nparts,
+    float *__restrict__ ws_o, float *__restrict__ ws_lse, int *__restrict__ ws_np,
+    const PrefillOrder order) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     uint8_t MLA_LDS *lds = (uint8_t MLA_LDS *)lds_raw;
     uint8_t MLA_LDS *pbuf = lds + PF_NS * fl::TILE_BYTES;
     Misc *misc = misc_of(lds_raw);
-    // Blocks are dispatched in index order, round-robin over the 8 XCDs.  Order: the
-    // heaviest row group (latest tokens) first, all head chunks of a group together, so
-    // every XCD receives an even share of heavy and light groups (a contiguous range per
-    // XCD would give one XCD all the heavy groups), and co-running workgroups stream the
-    // same cache rows from key 0 upwards.
-    const int chunk = blockIdx.x % n_chunks;
-    const int grp = n_groups - 1 - blockIdx.x / n_chunks;
-
+    // Blocks are dispatched in index order, round-robin over the 8 XCDs and over the
+    // shader engines inside each, and a block waits for a free CU on its engine even when
+    // other engines have one: neighbouring blocks must carry similar work.  With one part
+    // per group, units (row group, head chunk) go heaviest group (latest tokens) first,
+    // the chunks of a group together.  With several parts, order.item lists the (unit,
+    // part) items sorted by estimated work.
+    int unit, part;
+    if (nparts == 1) {
+        unit = blockIdx.x;
+        part = 0;
+    } else {
+        const int it = order.item[blockIdx.x];
+        unit = it / nparts;
+        part = it % nparts;
+    }
+    const int chunk = unit % n_chunks;
+    const int grp = n_groups - 1 - unit / n_chunks;
     const int w = threadIdx.x >> 6;
     const int rows_total = T * hc;
     // row (token t, head h) of lane l's row in wave `wave`; false past the last row
     auto row_of = [&](int l, int wave, int &t, int &h) {
-        const int r = grp * (32 * PF_NW) + wave * 32 + (l & 31);
+        const int r = grp * PF_ROWS + wave * 32 + (l & 31);
         const bool v = r < rows_total;
         t = v ? r / hc : 0;
         h = chunk * hc + (v ? r % hc : 0);
@@ -480,37 +537,126 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
     __syncthreads();
     atomicMax(&misc->kmax, lim);
     atomicMin(&misc->wmin[w], lim);
-    WaveState st;
-    load_q(st, q_cat + ((int64_t)t * H + h) * fl::W);
     __syncthreads();
     const int kend = misc->kmax + 1;
+    const int np = (kend + ks - 1) / ks;  // parts holding keys of this group
+    if (part >= np) return;               // uniform: nothing to attend to
+    WaveState st;
+    load_q(st, q_cat + ((int64_t)t * H + h) * fl::W);
     const int wlim = misc->wmin[w];
-    // The stream starts at key 0.  Kept opaque: folded into the loop, the constant leads
-    // the compiler to keep more values live across the tile loop, which then spills.
-    int kbeg = 0;
+    // Kept opaque: folded into the loop, a constant start leads the compiler to keep more
+    // values live across the tile loop, which then spills.
+    int kbeg = part * ks;
     asm volatile("" : "+s"(kbeg));
-    attend_range<PF_NW, PF_NS>(st, lds, pbuf, &misc->flag, cache, n_kv, kbeg, kend, lim,
-                               wlim, sc);
+    attend_range<PF_NW, PF_NS>(st, lds, pbuf, &misc->flag, cache, n_kv, kbeg,
+                               min(kbeg + ks, kend), lim, wlim, sc);
     // Output rows are recomputed here: values kept from before the key stream would stay
     // live across it and crowd out the tile loop's registers.
     int l = threadIdx.x & 63;
     asm volatile("" : "+v"(l));
-    const float ls = finish(st, lds, pbuf, [&](int r) -> bf16 * {
-        const int rr = grp * (32 * PF_NW) + r;
-        if (rr >= rows_total) return nullptr;
-        return o_lat + ((int64_t)(rr / hc) * H + chunk * hc + rr % hc) * fl::R;
-    });
-    int ta, ha;
-    if (lse && row_of(l, w, ta, ha) && l < 32) lse[(int64_t)ta * H + ha] = ls;
+    if (np == 1) {
+        const float ls = finish(st, lds, pbuf, [&](int r) -> bf16 * {
+            const int rr = grp * PF_ROWS + r;
+            if (rr >= rows_total) return nullptr;
+            return o_lat + ((int64_t)(rr / hc) * H + chunk * hc + rr % hc) * fl::R;
+        });
+        int ta, ha;
+        if (lse && row_of(l, w, ta, ha) && l < 32) lse[(int64_t)ta * H + ha] = ls;
+        return;
+    }
+    const int gid = chunk * n_groups + grp;
+    const int64_t slot = (int64_t)gid * nparts + part;
+    if (part == 0 && threadIdx.x == 0) ws_np[gid] = np;
+    const float ls = finish_f32(st, pbuf, ws_o + slot * PF_ROWS * fl::R);
+    if (l < 32) ws_lse[slot * PF_ROWS + w * 32 + l] = ls;
+}
+
+// Merge of the key parts of the row groups that were cut (flash_prefill_bf16_kernel):
+// lse = log sum_p exp(lse_p), o = sum_p exp(lse_p - lse) o_p, the split-KV combine.
+// Block (group, slab of 4 rows); wave w takes one row, lane l columns 8l .. 8l+7.
+constexpr int MG_ROWS = 4;
+__global__ __launch_bounds__(64 * MG_ROWS) void prefill_merge_kernel(
+    int T, int H, int hc, int n_groups, int nparts, const int *__restrict__ ws_np,
+    const float *__restrict__ ws_o, const float *__restrict__ ws_lse, bf16 *__restrict__ o_lat,
+    float *__restrict__ lse) {
+    const int gid = blockIdx.x / (PF_ROWS / MG_ROWS);
+    const int np = ws_np[gid];
+    if (np <= 1) return;  // written directly by its only part
+    const int chunk = gid / n_groups, grp = gid % n_groups;
+    const int r = (blockIdx.x % (PF_ROWS / MG_ROWS)) * MG_ROWS + (threadIdx.x >> 6);
+    const int rr = grp * PF_ROWS + r;
+    if (rr >= T * hc) return;
+    const int l = threadIdx.x & 63;
+    const int64_t slot0 = (int64_t)gid * nparts;
+    float lp[PF_MAX_PARTS];
+    float m = -INFINITY;
+    for (int p = 0; p < np; ++p) {
+        lp[p] = ws_lse[(slot0 + p) * PF_ROWS + r];
+        m = fmaxf(m, lp[p]);
+    }
+    float ssum = 0.0f;
+    for (int p = 0; p < np; ++p) ssum += expf(lp[p] - m);  // m finite: part 0 holds key 0
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < np; ++p) {
+        const float wt = expf(lp[p] - m) / ssum;
+        const float *src = ws_o + ((slot0 + p) * PF_ROWS + r) * fl::R + l * 8;
+        const f32x4 a = *(const f32x4 *)src, b = *(const f32x4 *)(src + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[e] += wt * a[e];
+            acc[4 + e] += wt * b[e];
+        }
+    }
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = f2bf(acc[e]);
+    const int64_t orow = (int64_t)(rr / hc) * H + chunk * hc + rr % hc;
+    *(bf16x8 *)(o_lat + orow * fl::R + l * 8) = o;
+    if (lse && l == 0) lse[orow] = m + logf(ssum);
+}
+
+// Parts per row group and keys per part.  Few row groups (fewer than two per CU) leave
+// the longest groups setting the time; their keys are then cut into up to 4 parts of a
+// fixed size (a multiple of the 32-key tile), chosen from T*H and n_kv only.
+int prefill_parts(int T, int H, int n_kv, int *ks) {
+    constexpr int NUM_CUS = 256;
+    const int64_t groups = ((int64_t)T * H + PF_ROWS - 1) / PF_ROWS;
+    int P = 1;
+    if (groups < 2 * NUM_CUS) {
+        P = (int)((2 * NUM_CUS + groups - 1) / groups);
+        if (P > PF_MAX_PARTS) P = PF_MAX_PARTS;
+        while (P > 1 && groups * P > PF_MAX_ITEMS) --P;
+    }
+    int K = (n_kv + P - 1) / P;
+    K = (K + fl::NK - 1) / fl::NK * fl::NK;
+    *ks = K;
+    return (n_kv + K - 1) / K;
+}
+
+size_t prefill_workspace_bytes(int T, int H, int n_kv, int hc) {
+    int ks;
+    const int P = prefill_parts(T, H, n_kv, &ks);
+    if (P == 1) return 0;
+    const int64_t G = (int64_t)(H / hc) * (((int64_t)T * hc + PF_ROWS - 1) / PF_ROWS);
+    const size_t cnt = ((size_t)G * 4 + 255) & ~(size_t)255;  // part count per group
+    const size_t ls = ((size_t)G * P * PF_ROWS * 4 + 255) & ~(size_t)255;
+    return cnt + ls + (size_t)G * P * PF_ROWS * fl::R * 4;
 }
 
 hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int T, int H,
                                      const bf16 *cache, int n_kv, int hc, float scale,
-                                     bf16 *o_lat, float *lse, hipStream_t st) {
+                                     bf16 *o_lat, float *lse, void *ws, hipStream_t st) {
     if (T <= 0) return hipSuccess;
     const int rows = T * hc;
-    const int n_groups = (rows + 32 * PF_NW - 1) / (32 * PF_NW);
+    const int n_groups = (rows + PF_ROWS - 1) / PF_ROWS;
     const int n_chunks = H / hc;
+    int ks;
+    const int P = prefill_parts(T, H, n_kv, &ks);
+    const int64_t G = (int64_t)n_chunks * n_groups;
+    int *ws_np = (int *)ws;
+    float *ws_lse = (float *)((char *)ws + (((size_t)G * 4 + 255) & ~(size_t)255));
+    float *ws_o = (float *)((char *)ws_lse + (((size_t)G * P * PF_ROWS * 4 + 255) & ~(size_t)255));
+    if (P == 1) ws_np = nullptr, ws_lse = nullptr, ws_o = nullptr;
     const size_t shm = (size_t)PF_NS * fl::TILE_BYTES + PBUF_BYTES;
     static bool attr_set = false;
     if (!attr_set) {
@@ -519,9 +665,43 @@ hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int 
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(flash_prefill_bf16_kernel, dim3(n_groups * n_chunks), dim3(64 * PF_NW), shm,
+    // Block order of a cut prefill: items by decreasing estimated tile count, estimated
+    // with the usual prefill positions (the T tokens are the last T of the n_kv cached
+    // rows).  Only the schedule depends on this estimate, never the results.
+    // The order depends only on (T, H, n_kv, hc); it is kept for the next call.
+    static PrefillOrder order;
+    static int64_t order_key[4] = {-1, -1, -1, -1};
+    const int64_t key[4] = {T, H, n_kv, hc};
+    if (P > 1 && !std::equal(key, key + 4, order_key)) {
+        const int n_items = (int)G * P;
+        auto tiles_of = [&](int it) {
+            const int u = it / P, p = it % P;
+            const int g = n_groups - 1 - u / n_chunks;
+            const int64_t last_row = std::min<int64_t>((int64_t)(g + 1) * PF_ROWS, (int64_t)T * hc) - 1;
+            const int64_t kend = std::min<int64_t>(n_kv, (int64_t)n_kv - T + last_row / hc + 1);
+            const int64_t k = std::max<int64_t>(0, std::min<int64_t>(ks, kend - (int64_t)p * ks));
+            return (k + fl::NK - 1) / fl::NK;
+        };
+        int64_t work[PF_MAX_ITEMS];
+        for (int it = 0; it < n_items; ++it) {
+            order.item[it] = (uint16_t)it;
+            work[it] = tiles_of(it);
+        }
+        std::stable_sort(order.item, order.item + n_items,
+                         [&](uint16_t a, uint16_t b) { return work[a] > work[b]; });
+        std::copy(key, key + 4, order_key);
+    }
+    const unsigned nblocks = (unsigned)(G * P);
+    hipLaunchKernelGGL(flash_prefill_bf16_kernel, dim3(nblocks), dim3(64 * PF_NW), shm,
                        st, q_cat, pos, T, H, (const uint8_t *)cache, n_kv, hc, n_groups, n_chunks,
-                       scale * fl::LOG2E, o_lat, lse);
+                       scale * fl::LOG2E, o_lat, lse, ks, P, ws_o, ws_lse, ws_np, order);
+    if (P > 1) {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(prefill_merge_kernel, dim3((unsigned)(G * (PF_ROWS / MG_ROWS))),
+                           dim3(64 * MG_ROWS), 0, st, T, H, hc, n_groups, P, ws_np, ws_o, ws_lse,
+                           o_lat, lse);
+    }
     return hipGetLastError();
 }
 

@@ -75,6 +75,9 @@ class LayerStep:
         self.lse = torch.empty((self.T, H), dtype=torch.float32, device=device)
         self.v = torch.empty((self.T, H * Dv), dtype=tdt, device=device)
         self.out = torch.empty((self.T, D), dtype=tdt, device=device)
+        self.prefill_ws = (mla.prefill_workspace(self.cdims, self.kv, self.T, n_kv,
+                                                 scratch_cap_mib, device)
+                           if kind == "prefill" else None)
         if kind == "decode":
             self.n_kv_dev = torch.full((S,), n_kv, dtype=torch.int32, device=device)
             wsb = mla.mla_decode_workspace_bytes(self.cdims, S, n_kv, n_splits)
@@ -91,7 +94,7 @@ class LayerStep:
         if self.kind == "prefill":
             mla.mla_attn_prefill(self.cdims, self.act, self.kv, self.q_cat, self.pos, self.T,
                                  self.cache, self.n_kv, self.o_lat, self.lse,
-                                 self.scratch_cap_mib, stream)
+                                 self.scratch_cap_mib, self.prefill_ws, stream)
         else:
             mla.mla_attn_decode(self.cdims, self.act, self.kv, self.q_cat, self.cache,
                                 self.seq_stride, self.n_kv_dev, self.n_seq, self.n_kv,

@@ -17,7 +17,8 @@ F32, BF16, Q8_0 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 # Every symbol include/mla.h declares.
-EXPORTS = ("mla_absorb_q", "mla_attn_prefill", "mla_heads_per_chunk", "mla_decode_workspace_bytes",
+EXPORTS = ("mla_absorb_q", "mla_attn_prefill", "mla_prefill_workspace_bytes",
+           "mla_heads_per_chunk", "mla_decode_workspace_bytes",
            "mla_decode_auto_splits", "mla_attn_decode", "mla_out_proj", "mla_quantize_q8_0",
            "mla_dequant_q8_0", "mla_q8_0_row_bytes", "mla_status_str")
 
@@ -56,7 +57,8 @@ def lib() -> ctypes.CDLL:
         sig = {
             "mla_absorb_q": ([D, ctypes.c_int, vp, vp, vp, vp, vp, i32, vp], ctypes.c_int),
             "mla_attn_prefill": ([D, ctypes.c_int, ctypes.c_int, vp, vp, i32, vp, i32, vp, vp,
-                                  ctypes.c_uint32, vp], ctypes.c_int),
+                                  ctypes.c_uint32, vp, sz, vp], ctypes.c_int),
+            "mla_prefill_workspace_bytes": ([D, ctypes.c_int, i32, i32, ctypes.c_uint32], sz),
             "mla_heads_per_chunk": ([i32, ctypes.c_double, ctypes.c_uint32], i32),
             "mla_decode_workspace_bytes": ([D, i32, i32, i32], sz),
             "mla_decode_auto_splits": ([D, ctypes.c_int, i32, i32], i32),
@@ -114,10 +116,26 @@ def mla_absorb_q(dims, act, q_nope, q_rope, pos, wk_b, q_cat, T, stream=None):
                               T, _s(stream)), "mla_absorb_q")
 
 
+def mla_prefill_workspace_bytes(dims, kv, T, n_kv, scratch_cap_mib=0):
+    return lib().mla_prefill_workspace_bytes(_d(dims), kv, T, n_kv, scratch_cap_mib)
+
+
+def prefill_workspace(dims, kv, T, n_kv, scratch_cap_mib=0, device="cuda"):
+    """A workspace of the size mla_attn_prefill needs (None if it needs none)."""
+    import torch
+    n = mla_prefill_workspace_bytes(dims, kv, T, n_kv, scratch_cap_mib)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def mla_attn_prefill(dims, act, kv, q_cat, pos, T, kv_cache, n_kv, o_lat, lse=None,
-                     scratch_cap_mib=0, stream=None):
+                     scratch_cap_mib=0, workspace=None, stream=None):
+    """workspace: a tensor from prefill_workspace() (allocated here when None)."""
+    if workspace is None:
+        workspace = prefill_workspace(dims, kv, T, n_kv, scratch_cap_mib, q_cat.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mla_attn_prefill(_d(dims), act, kv, _p(q_cat), _p(pos), T, _p(kv_cache), n_kv,
-                                  _p(o_lat), _p(lse), scratch_cap_mib, _s(stream)),
+                                  _p(o_lat), _p(lse), scratch_cap_mib, _p(workspace), nbytes,
+                                  _s(stream)),
            "mla_attn_prefill")
 
 

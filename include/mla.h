@@ -48,7 +48,7 @@ typedef enum mla_status {
     MLA_OK = 0,
     MLA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, odd Dr, bad dtype combination */
     MLA_ERR_UNSUPPORTED = -2, /* valid request that no kernel implements (see each call) */
-    MLA_ERR_WORKSPACE = -3,   /* decode workspace smaller than mla_decode_workspace_bytes() */
+    MLA_ERR_WORKSPACE = -3,   /* workspace smaller than the matching *_workspace_bytes() */
     MLA_ERR_HIP = -4          /* the HIP runtime reported an error on launch */
 } mla_status;
 
@@ -92,11 +92,23 @@ int mla_absorb_q(const mla_dims *dims, mla_dtype act, const void *q_nope, const 
  * intermediate, so the cap only changes the work decomposition: results are
  * bitwise identical for every cap.
  * Supported: act == kv == MLA_F32 (any dims), act == kv == MLA_BF16 (R 512, Dr 64).
+ * workspace: device memory of at least mla_prefill_workspace_bytes(dims, kv, T, n_kv,
+ * scratch_cap_mib) bytes (may be NULL when that is 0).  When few row groups would leave
+ * the longest ones setting the time, the bf16 kernel cuts every row's keys into parts
+ * at fixed boundaries and merges the parts' partial results with the split-KV combine
+ * (the same log-sum-exp merge as decode); the workspace holds those partials.  Its
+ * contents need not be initialised.  Calls sharing a workspace must not overlap.
  * Errors: INVALID_ARG (nulls, T < 0, n_kv < 1, dtype mix), UNSUPPORTED (Q8_0 cache,
- * bf16 with other R/Dr). */
+ * bf16 with other R/Dr), WORKSPACE (workspace missing or too small). */
 int mla_attn_prefill(const mla_dims *dims, mla_dtype act, mla_dtype kv, const void *q_cat,
                      const int32_t *pos, int32_t T, const void *kv_cache, int32_t n_kv,
-                     void *o_lat, float *lse, uint32_t scratch_cap_mib, void *stream);
+                     void *o_lat, float *lse, uint32_t scratch_cap_mib, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/* Workspace bytes mla_attn_prefill needs for these arguments (0: none).  Host-only;
+ * returns 0 for invalid arguments. */
+size_t mla_prefill_workspace_bytes(const mla_dims *dims, mla_dtype kv, int32_t T, int32_t n_kv,
+                                   uint32_t scratch_cap_mib);
 
 /* Heads per chunk for the -amb rule (absorption page, section 8.3): if
  * size_mib > cap, the smallest niter >= 2 with n_head % niter == 0 and

@@ -51,13 +51,13 @@ def test_invalid_arguments_rejected_without_gpu():
     assert L.mla_absorb_q(ctypes.byref(d), 0, p, p, p, p, p, -1, None) == mla.ERR_INVALID_ARG
     assert L.mla_absorb_q(ctypes.byref(d), 0, None, None, None, None, None, 0, None) == mla.OK
     # prefill: Q8_0 cache unsupported, bf16 needs the 512/64 latent row, dtype mix invalid
-    assert L.mla_attn_prefill(ctypes.byref(d), 1, 2, p, p, 4, p, 8, p, None, 0, None) == \
+    assert L.mla_attn_prefill(ctypes.byref(d), 1, 2, p, p, 4, p, 8, p, None, 0, None, 0, None) == \
         mla.ERR_UNSUPPORTED
-    assert L.mla_attn_prefill(ctypes.byref(d), 1, 1, p, p, 4, p, 8, p, None, 0, None) == \
+    assert L.mla_attn_prefill(ctypes.byref(d), 1, 1, p, p, 4, p, 8, p, None, 0, None, 0, None) == \
         mla.ERR_UNSUPPORTED
-    assert L.mla_attn_prefill(ctypes.byref(d), 0, 1, p, p, 4, p, 8, p, None, 0, None) == \
+    assert L.mla_attn_prefill(ctypes.byref(d), 0, 1, p, p, 4, p, 8, p, None, 0, None, 0, None) == \
         mla.ERR_INVALID_ARG
-    assert L.mla_attn_prefill(ctypes.byref(d), 0, 0, p, p, 4, p, 0, p, None, 0, None) == \
+    assert L.mla_attn_prefill(ctypes.byref(d), 0, 0, p, p, 4, p, 0, p, None, 0, None, 0, None) == \
         mla.ERR_INVALID_ARG
     # decode: workspace too small; Q8_0 needs a width multiple of 32 (tiny rows are 80 wide)
     ws = mla.mla_decode_workspace_bytes(d, 2, 100, 3)
