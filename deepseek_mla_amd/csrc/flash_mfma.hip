@@ -359,16 +359,19 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
     }
 }
 
-// Small shared integers live in the unused pad of latent row 0 of stage 0 (bytes
-// 1024 .. 1087, never written by tile copies nor read by the tile loop), so that the
-// stages and the weight exchange buffer can take all of LDS.
+// Small shared integers live in the last bytes of the weight exchange buffer, which the
+// key stream alone writes: the group's key range is read before the stream starts, the
+// pass flag is written and read after it ends (the stream starts and ends on a barrier),
+// and the denominators of finish take only the buffer's first 512 bytes.  The tile stages
+// hold the query staging before the stream, so no pad there is free.
 struct Misc {
     int kmax, flag, wmin[4];
 };
-static_assert(sizeof(Misc) <= fl::PA - 1024, "misc fits the pad");
-__device__ __forceinline__ Misc *misc_of(uint8_t *lds_generic) {
-    return (Misc *)(lds_generic + 1024);
+static_assert(sizeof(Misc) <= PBUF_BYTES - 512, "misc clear of the denominators");
+__device__ __forceinline__ Misc *misc_of(uint8_t *pbuf_generic) {
+    return (Misc *)(pbuf_generic + PBUF_BYTES - 64);
 }
+static_assert(sizeof(Misc) <= 64, "misc fits the last 64 bytes");
 
 // Runs the key stream for the workgroup, repeating it once if any row was marked.
 template <int NW, int NS>
@@ -403,7 +406,9 @@ constexpr int OSTAGE_BYTES = 128 * OPITCH;
 template <typename RowDst>
 __device__ __forceinline__ float finish(WaveState &st, uint8_t MLA_LDS *stage,
                                         uint8_t MLA_LDS *pbuf, RowDst row_dst) {
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, hi = l >> 5;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));  // recomputed, not kept from before the key stream
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, hi = l >> 5;
     const float lt = pair_sum(st.lsum);
     float MLA_LDS *den = (float MLA_LDS *)pbuf;  // buffer free: the key stream ended on a barrier
     if (l < 32) den[w * 32 + l] = lt;
@@ -447,7 +452,9 @@ static_assert(OSTAGE_BYTES <= 4 * fl::TILE_BYTES, "output staging fits the tile 
 // Returns lse (natural log) of this lane's own row.
 __device__ __forceinline__ float finish_f32(WaveState &st, uint8_t MLA_LDS *pbuf,
                                             float *__restrict__ dst) {
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, hi = l >> 5;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));  // recomputed, not kept from before the key stream
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, hi = l >> 5;
     const float lt = pair_sum(st.lsum);
     float MLA_LDS *den = (float MLA_LDS *)pbuf;  // buffer free: the key stream ended on a barrier
     if (l < 32) den[w * 32 + l] = lt;
@@ -498,7 +505,7 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     uint8_t MLA_LDS *lds = (uint8_t MLA_LDS *)lds_raw;
     uint8_t MLA_LDS *pbuf = lds + PF_NS * fl::TILE_BYTES;
-    Misc *misc = misc_of(lds_raw);
+    Misc *misc = misc_of(lds_raw + PF_NS * fl::TILE_BYTES);
     // Blocks are dispatched in index order, round-robin over the 8 XCDs and over the
     // shader engines inside each, and a block waits for a free CU on its engine even when
     // other engines have one: neighbouring blocks must carry similar work.  With one part
@@ -516,7 +523,7 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
     }
     const int chunk = unit % n_chunks;
     const int grp = n_groups - 1 - unit / n_chunks;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar
     const int rows_total = T * hc;
     // row (token t, head h) of lane l's row in wave `wave`; false past the last row
     auto row_of = [&](int l, int wave, int &t, int &h) {
@@ -550,10 +557,13 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
     asm volatile("" : "+s"(kbeg));
     attend_range<PF_NW, PF_NS>(st, lds, pbuf, &misc->flag, cache, n_kv, kbeg,
                                min(kbeg + ks, kend), lim, wlim, sc);
-    // Output rows are recomputed here: values kept from before the key stream would stay
-    // live across it and crowd out the tile loop's registers.
-    int l = threadIdx.x & 63;
-    asm volatile("" : "+v"(l));
+    // Output rows are recomputed here from the thread index: values kept from before the
+    // key stream would stay live across it, crowd out the tile loop's registers and come
+    // back as spill reloads among the output stores (each reload waits for every store
+    // issued before it).
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int l = tid & 63;
     if (np == 1) {
         const float ls = finish(st, lds, pbuf, [&](int r) -> bf16 * {
             const int rr = grp * PF_ROWS + r;
