@@ -478,19 +478,32 @@ __device__ __forceinline__ void dq_stream(DqState &st, uint8_t MLA_LDS *lds,
             read_query(st, qs);
             __syncthreads();  // the query staging (bf16 stages) is free
         }
-        dequant_tile_q8<dq::NW>(raw, k0, nk, lds);
+        DequantQ8{raw, lds, k0, nk}.all();
         for (int t = 0; t < ntiles; ++t) {
             // raw tile t+1 landed (raw tiles up to t+3 issued)
             if (t + 1 < ntiles) wait_raw(t + 1, min(t + 3, ntiles - 1));
             __syncthreads();  // bf16 tile t complete; tile t-1's O update done everywhere
             if (t + 4 < ntiles) issue_raw(t + 4);
             const uint8_t MLA_LDS *tile = lds + (t & 1) * fl::TILE_BYTES;
+            // the dequantisation of raw tile t+1 runs between the score MFMAs of tile t:
+            // task m is fetched after score step 2m and converted after step 2m+2
+            const bool next = t + 1 < ntiles;
+            const DequantQ8 dqz{raw + ((t + 1) % dq::NRAW) * Q8_RAW_STAGE,
+                                lds + ((t + 1) & 1) * fl::TILE_BYTES, k0 + (t + 1) * fl::NK, nk};
+            DequantQ8::Words dw[2];
             f32x4 s[2];
-            score_tile_q(st, tile, ka, s, [](auto) {});
-            if (t + 1 < ntiles)
-                dequant_tile_q8<dq::NW>(raw + ((t + 1) % dq::NRAW) * Q8_RAW_STAGE,
-                                        k0 + (t + 1) * fl::NK, nk,
-                                        lds + ((t + 1) & 1) * fl::TILE_BYTES);
+            score_tile_q(st, tile, ka, s, [&](auto kc) {
+                constexpr int kk = decltype(kc)::value;
+                if constexpr ((kk & 1) == 0) {
+                    constexpr int m = kk >> 1;
+                    if (next) {
+                        if constexpr (m >= 1) dqz.convert(m - 1, dw[(m - 1) & 1]);
+                        if constexpr (m < DequantQ8::TASKS) dw[m & 1] = dqz.load(m);
+                    }
+                }
+            });
+            static_assert(2 * (DequantQ8::TASKS - 1) < dq::KSTEPS, "all fetches inside the score steps");
+            if (next) dqz.convert(DequantQ8::TASKS - 1, dw[(DequantQ8::TASKS - 1) & 1]);
             softmax_tile(st, s, k0 + t * fl::NK, k1, sc, t == 0 && !have_m, lds, pbuf);
             __syncthreads();  // weights visible
             bf16x8 pt[2][2];

@@ -252,48 +252,72 @@ template <int NW> __host__ __device__ constexpr int q8_inst_per_wave() {
     return Q8_RAW_INST / NW;
 }
 
-// Dequantise the raw Q8_0 tile (LDS) into the bf16 tile layout (LDS).  Task = (row,
-// block of 32 values); rows with key0 + k >= n_rows are written as zeros.
-template <int NW>
-__device__ __forceinline__ void dequant_tile_q8(const uint8_t MLA_LDS *raw, int key0, int n_rows,
-                                                uint8_t MLA_LDS *dst) {
-    constexpr int NB = fl::W / 32;  // 18 blocks per row
-    for (int task = threadIdx.x; task < fl::NK * NB; task += 64 * NW) {
-        const int k = task / NB, b = task % NB;
-        const int off = k * fl::Q8_RB + b * 34;       // block start, 2-byte aligned
-        const int a0 = off & ~3, sh = (off & 2) * 8;  // dword-aligned window
-        uint32_t wv[10];
-#pragma unroll
-        for (int i = 0; i < 10; ++i) {
-            const int o = a0 + 4 * i;
-            wv[i] = (o < fl::Q8_TILE_BYTES) ? *(const uint32_t MLA_LDS *)(raw + o) : 0u;
-        }
-        // bytes starting at `off`: shift the window right by sh bits
-        uint32_t bb[9];
-#pragma unroll
-        for (int i = 0; i < 9; ++i)
-            bb[i] = sh ? ((wv[i] >> 16) | (wv[i + 1] << 16)) : wv[i];
-        const bool valid = (key0 + k) < n_rows;
-        const float d = valid ? (float)__builtin_bit_cast(_Float16, (uint16_t)(bb[0] & 0xFFFF)) : 0.0f;
-        // codes: bytes 2..33 of the block = bb[0]>>16 .. bb[8]&0xFFFF
-        bf16 v[32];
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const int byte = 2 + i;
-            const uint32_t word = bb[byte >> 2];
-            const int8_t q = (int8_t)((word >> ((byte & 3) * 8)) & 0xFF);
-            v[i] = f2bf(d * (float)q);
-        }
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            const int c = b * 4 + qq;
-            uint8_t MLA_LDS *p = dst + tile_off(k, c);
-            bf16x8 t;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) t[e] = v[qq * 8 + e];
-            *(bf16x8 MLA_LDS *)p = t;
-        }
+// Dequantisation of a raw Q8_0 tile (LDS, the global byte image) into the bf16 tile
+// layout (LDS), in tasks of one 16-byte output chunk: 8 values of one 32-value block.
+// Thread x of the 256-thread workgroup takes row k = x / 8 and chunks c = x % 8 + 8 i,
+// i = 0 .. 8 (32 rows x 72 chunks = 2304 tasks, 9 per thread), so that every offset is a
+// per-thread base plus a constant: the block of chunk c starts 68 i bytes after that of
+// chunk x % 8 (two 34-byte blocks per 8 chunks), and latent chunks land 128 i bytes apart
+// (the row mask only permutes the low two chunk bits).  load(i) fetches the task's scale
+// and the 2-3 dwords holding its 8 codes; convert(i) forms the values and writes the
+// chunk, so that the two can sit between other work.  Value = float(d) * q, exact in
+// float32 (an 11-bit by 8-bit product), computed as fma(q + 128, d, -128 d) on the code
+// with its sign bit flipped (an unsigned byte); rows with key0 + k >= n_rows are written
+// as zeros.
+struct DequantQ8 {
+    const uint8_t MLA_LDS *raw;
+    uint8_t MLA_LDS *dst;
+    int key0, n_rows;
+    static constexpr int TASKS = 9;
+    static_assert(fl::NK * (fl::W / 8) == TASKS * 256, "9 chunk tasks per thread");
+
+    struct Words {
+        uint32_t w0, w1, w2;
+        uint16_t d;
+    };
+    // per-thread bases: raw offset of the scale of chunk x % 8's block, byte offset of the
+    // codes inside their first dword (0 or 2), LDS offset of the first latent chunk
+    __device__ __forceinline__ static int row() { return (int)(threadIdx.x >> 3); }
+    __device__ __forceinline__ static int blk0() {
+        const int x = (int)threadIdx.x;
+        return (x >> 3) * fl::Q8_RB + ((x >> 2) & 1) * 34;
     }
-}
+    __device__ __forceinline__ Words load(int i) const {
+        const int x = (int)threadIdx.x;
+        const int blk = blk0() + 68 * i;
+        const int o = blk + 2 + (x & 3) * 8;
+        const int a0 = o & ~3;
+        Words r;
+        r.w0 = *(const uint32_t MLA_LDS *)(raw + a0);
+        r.w1 = *(const uint32_t MLA_LDS *)(raw + a0 + 4);
+        r.w2 = *(const uint32_t MLA_LDS *)(raw + a0 + 8);  // inside the stage's spare bytes at the end
+        r.d = *(const uint16_t MLA_LDS *)(raw + blk);
+        return r;
+    }
+    __device__ __forceinline__ void convert(int i, const Words &r) const {
+        const int x = (int)threadIdx.x, k = row();
+        const uint32_t sh = (uint32_t)((blk0() + 2 + (x & 3) * 8) & 3);  // same for every i
+        const uint32_t lo = __builtin_amdgcn_alignbyte(r.w1, r.w0, sh) ^ 0x80808080u;
+        const uint32_t hi = __builtin_amdgcn_alignbyte(r.w2, r.w1, sh) ^ 0x80808080u;
+        const bool valid = key0 + k < n_rows;
+        const float d = valid ? (float)__builtin_bit_cast(_Float16, r.d) : 0.0f;
+        const float nd = -128.0f * d;  // exact: a power-of-two multiple
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[e] = f2bf(fmaf((float)((lo >> (8 * e)) & 0xFF), d, nd));
+            v[4 + e] = f2bf(fmaf((float)((hi >> (8 * e)) & 0xFF), d, nd));
+        }
+        const int c0 = x & 7;
+        const int off = i < 8 ? k * fl::PA + ((c0 ^ mask_a(k)) << 4) + 128 * i
+                              : fl::A_BYTES + k * fl::PB + ((c0 ^ mask_b(k)) << 4);
+        *(bf16x8 MLA_LDS *)(dst + off) = v;
+    }
+    __device__ __forceinline__ void all() const {
+#pragma unroll
+        for (int i = 0; i < TASKS; ++i) convert(i, load(i));
+    }
+};
+static_assert(fl::Q8_TILE_BYTES + 8 <= Q8_RAW_STAGE, "the last task's third word stays in the stage");
 
 }  // namespace mla
