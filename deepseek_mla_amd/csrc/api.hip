@@ -26,7 +26,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 hipStream_t as_stream(void *s) { return (hipStream_t)s; }
 
 constexpr int SIMT_SPLIT_GRAIN = 64;
-constexpr int MAX_SPLITS = 4096;  // the combine step keeps one weight per split in LDS
+constexpr int MAX_SPLITS = 4096;  // largest split count accepted
 constexpr int MFMA_SPLIT_GRAIN = 32;
 
 int auto_splits(const mla_dims *d, int kv, int B, int n_kv_max) {

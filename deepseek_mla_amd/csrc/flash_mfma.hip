@@ -59,9 +59,14 @@ struct WaveState {
 // copy issue) between the MFMAs.  Latent chunk 2kk + hi (kk < 32) is stored at
 // 4*(kk/2) + ((2*(kk%2) + hi) ^ mask_a(k)): two lane-dependent bases plus compile-time
 // offsets; the four rope chunks (kk = 32 .. 35) take one address each.
+//
+// Causal masking rides on the chain's starting value: in a tile where some row of the
+// wave ends (edge, wave-uniform) a slot past the row's bound starts at -inf, which every
+// finite product leaves at -inf, so its weight comes out 0; other tiles start at 0.
+// Slot e of a lane holds key key0 + hi*4 + (e/4)*8 + e%4.
 template <typename Fill>
 __device__ __forceinline__ f32x16 score_tile(const WaveState &st, const uint8_t MLA_LDS *t,
-                                             Fill fill) {
+                                             bool edge, int key0, int lim, Fill fill) {
     const int l = threadIdx.x & 63, hi = l >> 5;
     const int k = l & 31;
     const int ma = mask_a(k), mb = mask_b(k);
@@ -74,15 +79,26 @@ __device__ __forceinline__ f32x16 score_tile(const WaveState &st, const uint8_t 
         return kk < 32 ? kb[kk & 1] + (kk >> 1) * 64 : rowb + (((2 * (kk - 32) + hi) ^ mb) * 16);
     };
     f32x16 s;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] = 0.0f;
     constexpr int QK_AHEAD = 4;
     bf16x8 a[QK_AHEAD];
 #pragma unroll
     for (int kk = 0; kk < QK_AHEAD; ++kk) a[kk] = *(const bf16x8 MLA_LDS *)kaddr(kk);
     static_for<36>([&](auto kc) {
         constexpr int kk = decltype(kc)::value;
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk % QK_AHEAD], st.q[kk], s, 0, 0, 0);
+        if constexpr (kk == 0) {
+            if (edge) {
+                const int rel = lim - key0 - (hi << 2);
+                f32x16 b;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) b[e] = ((e >> 2) * 8 + (e & 3) <= rel) ? 0.0f : -INFINITY;
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], st.q[0], b, 0, 0, 0);
+            } else {
+                const f32x16 z = {};
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], st.q[0], z, 0, 0, 0);
+            }
+        } else {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk % QK_AHEAD], st.q[kk], s, 0, 0, 0);
+        }
         constexpr int nk = kk + QK_AHEAD;
         if constexpr (nk < 36) a[kk % QK_AHEAD] = *(const bf16x8 MLA_LDS *)kaddr(nk);
         fill(kc);
@@ -91,23 +107,12 @@ __device__ __forceinline__ f32x16 score_tile(const WaveState &st, const uint8_t 
     return s;
 }
 
-// Softmax set-up for the raw scores s of keys key0 .. key0+31 (lane: row l%32, keys
-// (e/4)*8 + hi*4 + e%4); keys past lim are masked.  The row's reference max is frozen at
-// its first visible tile, so the tile max is only needed while some row of the wave has
-// no reference yet or is marked (wave-uniform branch).  Returns the exponent offset -m.
-__device__ __forceinline__ float softmax_prep(WaveState &st, f32x16 &s, int key0, int lim,
-                                              int wave_lim_min, float sc) {
-    {
-        // Slot e holds key key0 + hi*4 + (e/4)*8 + e%4: its constant part is compared with
-        // one per-lane bound, raised past the tile where no row of the wave ends in it.
-        // (Unconditional: with a branch here the compiler keeps two copies of the scores
-        // live and runs out of registers.)
-        const int rel = (key0 + fl::NK - 1 > wave_lim_min)
-                            ? lim - key0 - (((threadIdx.x & 63) >> 5) << 2)
-                            : fl::NK;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = ((e >> 2) * 8 + (e & 3) <= rel) ? s[e] : -INFINITY;
-    }
+// Softmax set-up for the raw scores s of keys key0 .. key0+31 (masked keys already hold
+// -inf, see score_tile).  The row's reference max is frozen at its first visible tile, so
+// the tile max is only needed while some row of the wave has no reference yet or is
+// marked (wave-uniform branch).  Returns the exponent offset -m.
+__device__ __forceinline__ float softmax_prep(WaveState &st, const f32x16 &s, int key0, int lim,
+                                              float sc) {
     if (__builtin_amdgcn_ballot_w64((st.m == -INFINITY && key0 <= lim) || st.bad)) {
         float tmax = -INFINITY;
 #pragma unroll
@@ -207,10 +212,10 @@ struct SoftFill {
     bf16x8 (&p)[2];
     float &psum;
     float &nmu;
-    int key0, lim, wave_lim_min;
+    int key0, lim;
     float sc;
     __device__ __forceinline__ void operator()(int i) const {
-        if (i == 0) nmu = softmax_prep(st, s, key0, lim, wave_lim_min, sc);
+        if (i == 0) nmu = softmax_prep(st, s, key0, lim, sc);
         if (i & 1) soft_piece(s, i >> 1, sc, nmu, psum, p);
         if (i == 31) softmax_check(st, s, psum, sc);
     }
@@ -310,27 +315,29 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             // address unit.
             const VAddr vprev(lds + ((ti + NS - 1) % NS) * fl::TILE_BYTES, ch);
             bf16x8 va[PV_AHEAD];
-            f32x16 s = score_tile(st, lds + (ti % NS) * fl::TILE_BYTES, [&](auto kc) {
+            const int key0 = kbeg + ti * fl::NK;
+            // The row bound is made opaque per tile: values the compiler would derive from
+            // it once and keep across the loop end up spilled, and a spill reload pending at
+            // the loop would bring a wait for all vector-memory operations into it.
+            int lim_t = lim;
+            asm volatile("" : "+v"(lim_t));
+            f32x16 s = score_tile(st, lds + (ti % NS) * fl::TILE_BYTES, key0 + fl::NK - 1 > wlim, key0,
+                                  lim_t, [&](auto kc) {
                 constexpr int kk = decltype(kc)::value;
                 if (ti > 0 && kk >= 36 - PV_AHEAD)
                     va[kk - (36 - PV_AHEAD)] = vprev.load(kk - (36 - PV_AHEAD));
             });
             float nmu = 0.0f, psum = 0.0f;
             bf16x8 pcur[2];
-            // The row bound is made opaque per tile: values the compiler would derive from
-            // it once and keep across the loop end up spilled, and a spill reload pending at
-            // the loop would bring a wait for all vector-memory operations into it.
-            int lim_t = lim;
-            asm volatile("" : "+v"(lim_t));
-            const SoftFill soft{st, s, pcur, psum, nmu, kbeg + ti * fl::NK, lim_t, wlim, sc};
+            const SoftFill soft{st, s, pcur, psum, nmu, key0, lim_t, sc};
             // Copy parts go between the O-update MFMAs (even steps; the softmax takes the
             // odd ones): that phase leaves LDS bandwidth for the copies' writes, while the
             // score MFMAs already keep LDS busy with K-fragment reads.
             auto fill = [&](auto jc) {
                 constexpr int j = decltype(jc)::value;
                 soft(j);
-                if constexpr ((j & 3) == 2 || j == 0) {
-                    if (more && full) issue_part_full<(j == 0 ? 8 : j >> 2)>(sbase, plan, dsts, wu);
+                if constexpr ((j & 3) == 2 || j == 16) {
+                    if (more && full) issue_part_full<(j == 16 ? 8 : j >> 2)>(sbase, plan, dsts, wu);
                 }
             };
             if (ti > 0) {

@@ -258,10 +258,12 @@ hipError_t launch_flash_simt_decode(const mla_dims &d, const float *q_cat, const
 // lse = log sum_s exp(lse_s); o = sum_s exp(lse_s - lse) o_s (partials o_s float32 on the
 // float32 path, bfloat16 on the bf16 / Q8_0 path).  Splits with lse_s = -inf contribute
 // nothing.  Block (b*H + h, slice of CB_COLS columns) of CB_T threads: thread
-// (phase, group) accumulates 8 adjacent columns over splits phase, phase + CB_PH, ...
-// (one 16- or 32-byte load per split, several in flight), the phases are then summed
-// through LDS in a fixed order.
+// (phase, group) takes 8 adjacent columns of splits phase + CB_PH * i.  It loads CB_U of
+// its splits at once (lse and partial rows, all in flight together) and folds them into
+// a running (max, sum, 8 weighted columns) with one rescale per batch; the CB_PH phases
+// are then merged through LDS in a fixed order.
 constexpr int CB_T = 256, CB_COLS = 128, CB_GROUPS = CB_COLS / 8, CB_PH = CB_T / CB_GROUPS;
+constexpr int CB_U = 8;
 
 template <typename PT> struct Vec8;
 template <> struct Vec8<float> {
@@ -282,65 +284,76 @@ __global__ __launch_bounds__(CB_T) void combine_kernel(const PT *__restrict__ pa
                                                        const float *__restrict__ part_lse, int H,
                                                        int R, int S, OT *__restrict__ o_lat,
                                                        float *__restrict__ lse) {
-    extern __shared__ float wsh[];  // [S] weights | [CB_T] reduction | [CB_PH][CB_COLS] sums
-    float *red = wsh + S;
-    float *acc_sh = red + CB_T;
+    __shared__ float m_sh[CB_PH], l_sh[CB_PH];
+    __shared__ float acc_sh[CB_PH][CB_COLS];
     const int bh = blockIdx.x;
     const int b = bh / H, h = bh % H;
     const int tid = threadIdx.x;
-    const float *pl = part_lse + (int64_t)b * S * H + h;
-    float mx = -INFINITY;
-    for (int s = tid; s < S; s += CB_T) mx = fmaxf(mx, pl[(int64_t)s * H]);
-    red[tid] = mx;
-    __syncthreads();
-    for (int o = CB_T / 2; o > 0; o >>= 1) {
-        if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-        __syncthreads();
-    }
-    mx = red[0];
-    __syncthreads();
-    float sum = 0.0f;
-    for (int s = tid; s < S; s += CB_T) {
-        const float wgt = (mx == -INFINITY) ? 0.0f : expf(pl[(int64_t)s * H] - mx);
-        wsh[s] = wgt;
-        sum += wgt;
-    }
-    red[tid] = sum;
-    __syncthreads();
-    for (int o = CB_T / 2; o > 0; o >>= 1) {
-        if (tid < o) red[tid] += red[tid + o];
-        __syncthreads();
-    }
-    sum = red[0];
-    const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
     const int grp = tid % CB_GROUPS, ph = tid / CB_GROUPS;
     const int c0 = blockIdx.y * CB_COLS + grp * 8;
+    const float *pl = part_lse + (int64_t)b * S * H + h;
+    const PT *po = part_o + ((int64_t)b * S * H + h) * R + c0;
+    const int64_t stride = (int64_t)H * R;
+    float m = -INFINITY, lsum = 0.0f;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (c0 < R) {
-        const PT *po = part_o + ((int64_t)b * S * H + h) * R + c0;
-        const int64_t stride = (int64_t)H * R;
-#pragma unroll 4
-        for (int s = ph; s < S; s += CB_PH) {
-            float v[8];
-            if (R % 8 == 0) {  // rows of 8-column groups: aligned vector loads, no overrun
-                Vec8<PT>::load(po + (int64_t)s * stride, v);
-            } else {
-                for (int i = 0; i < 8; ++i)
-                    v[i] = (c0 + i < R) ? ld_f(po + (int64_t)s * stride + i) : 0.0f;
-            }
-            const float wgt = wsh[s];
+    for (int s0 = ph; s0 < S; s0 += CB_PH * CB_U) {
+        float x[CB_U], v[CB_U][8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt, v[i], acc[i]);
+        for (int i = 0; i < CB_U; ++i) {
+            const int s = s0 + i * CB_PH;
+            x[i] = s < S ? pl[(int64_t)s * H] : -INFINITY;
+            if (s < S && c0 < R) {
+                if (R % 8 == 0) {  // rows of 8-column groups: aligned vector loads, no overrun
+                    Vec8<PT>::load(po + (int64_t)s * stride, v[i]);
+                } else {
+                    for (int e = 0; e < 8; ++e)
+                        v[i][e] = (c0 + e < R) ? ld_f(po + (int64_t)s * stride + e) : 0.0f;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
+            }
         }
+        float mc = m;
+#pragma unroll
+        for (int i = 0; i < CB_U; ++i) mc = fmaxf(mc, x[i]);
+        if (mc == -INFINITY) continue;  // no visible split yet
+        const float r = __expf(m - mc);  // 0 while m = -inf (nothing accumulated)
+        lsum *= r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= r;
+#pragma unroll
+        for (int i = 0; i < CB_U; ++i) {
+            if (x[i] == -INFINITY) continue;  // an empty split's row is never weighted
+            const float wgt = __expf(x[i] - mc);
+            lsum += wgt;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(wgt, v[i][e], acc[e]);
+        }
+        m = mc;
+    }
+    if (grp == 0) {  // every group of a phase holds the same max and sum
+        m_sh[ph] = m;
+        l_sh[ph] = lsum;
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc_sh[ph * CB_COLS + grp * 8 + i] = acc[i];
+    for (int e = 0; e < 8; ++e) acc_sh[ph][grp * 8 + e] = acc[e];
     __syncthreads();
+    float mx = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < CB_PH; ++p) mx = fmaxf(mx, m_sh[p]);
+    float f[CB_PH], sum = 0.0f;
+#pragma unroll
+    for (int p = 0; p < CB_PH; ++p) {
+        f[p] = (mx == -INFINITY || m_sh[p] == -INFINITY) ? 0.0f : __expf(m_sh[p] - mx);
+        sum += f[p] * l_sh[p];
+    }
     if (tid < CB_COLS) {
         const int c = blockIdx.y * CB_COLS + tid;
         float tot = 0.0f;
-        for (int p = 0; p < CB_PH; ++p) tot += acc_sh[p * CB_COLS + tid];
-        if (c < R) st_f(o_lat + ((int64_t)b * H + h) * R + c, tot * inv);
+#pragma unroll
+        for (int p = 0; p < CB_PH; ++p) tot = fmaf(f[p], acc_sh[p][tid], tot);
+        if (c < R) st_f(o_lat + ((int64_t)b * H + h) * R + c, sum > 0.0f ? tot / sum : 0.0f);
     }
     if (lse && blockIdx.y == 0 && tid == 0)
         lse[(int64_t)b * H + h] = sum > 0.0f ? mx + logf(sum) : -INFINITY;
@@ -350,8 +363,7 @@ template <typename PT, typename OT>
 hipError_t launch_combine(const PT *part_o, const float *part_lse, int B, int H, int R,
                           int n_splits, OT *o_lat, float *lse, hipStream_t st) {
     dim3 grid(B * H, (R + CB_COLS - 1) / CB_COLS);
-    const size_t shm = sizeof(float) * (n_splits + CB_T + CB_PH * CB_COLS);
-    hipLaunchKernelGGL((combine_kernel<PT, OT>), grid, dim3(CB_T), shm, st, part_o, part_lse, H,
+    hipLaunchKernelGGL((combine_kernel<PT, OT>), grid, dim3(CB_T), 0, st, part_o, part_lse, H,
                        R, n_splits, o_lat, lse);
     return hipGetLastError();
 }
