@@ -36,22 +36,28 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 # HBM bytes per launch of the dominant kernel(s), from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # passes scaled by a 512 MiB copy (fetch x2.0, write x1.0); the summaries and commands are
-# in profiles/.  Valid only for the kernel source they were taken on (sha256 prefix).
+# in profiles/.  Valid only for the kernel sources they were taken on (sha256 prefix over
+# the files listed, in order).
 TRAFFIC = {
-    "src": ("deepseek_mla_amd/csrc/flash_mfma.hip", "af02fb833509d34d"),
-    "lite_prefill": 60.75e6 + 37.36e6,
-    "v3_long_prefill": 18548.08e6 + 1195.38e6,
-    "v3_decode": (41.74e6 + 36.31e6) + (34.69e6 + 0.14e6),       # partial kernel + combine
-    "v3_decode_q8": (246.21e6 + 34.21e6) + (34.70e6 + 0.54e6),  # partial kernel + combine
+    "src": (("deepseek_mla_amd/csrc/flash_mfma.hip", "deepseek_mla_amd/csrc/decode_mfma.hip",
+             "deepseek_mla_amd/csrc/latent_tile.h", "deepseek_mla_amd/csrc/simt.hip",
+             "deepseek_mla_amd/csrc/common.h"), "0fcc65c51e767430"),
+    "lite_prefill": (77.40e6 + 87.97e6) + (68.21e6 + 16.91e6),      # prefill kernel + merge
+    "v3_long_prefill": 9770.82e6 + 1161.82e6,
+    "v3_decode": (39.24e6 + 16.84e6) + (17.42e6 + 0.14e6),          # partial kernel + combine
+    "v3_decode_q8": (245.72e6 + 16.84e6) + (17.42e6 + 0.54e6),      # partial kernel + combine
 }
 
 
 def measured_traffic(name):
     import hashlib
-    path, sha = TRAFFIC["src"]
-    with open(os.path.join(ROOT, path), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest()[:16] != sha:
-            return None  # kernel changed since the counters were taken
+    paths, sha = TRAFFIC["src"]
+    h = hashlib.sha256()
+    for path in paths:
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest()[:16] != sha:
+        return None  # kernels changed since the counters were taken
     return TRAFFIC.get(name)
 
 
@@ -175,7 +181,7 @@ def run_one(name, steps, warmup, with_cpu, n_splits=0):
         entry["value"] = entry["step_tflops"]
         entry["unit"] = "TFLOP/s"
         entry["attention_tflops"] = ach
-        entry["roofline"] = {"kernel": "flash_prefill_bf16_kernel", "bound": "mfma",
+        entry["roofline"] = {"kernel": "flash_prefill_bf16_kernel (+ prefill_merge_kernel for cut row groups)", "bound": "mfma",
                              "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": ach / BF16_PEAK_TFLOPS, "traffic": measured_traffic(name),
                              "per_launch": f"{fl['attention']} FLOP = visible pairs x "
