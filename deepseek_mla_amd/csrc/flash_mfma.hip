@@ -372,7 +372,7 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
 // and the denominators of finish take only the buffer's first 512 bytes.  The tile stages
 // hold the query staging before the stream, so no pad there is free.
 struct Misc {
-    int kmax, flag, wmin[4];
+    int flag, wmax[4], wmin[4];
 };
 static_assert(sizeof(Misc) <= PBUF_BYTES - 512, "misc clear of the denominators");
 __device__ __forceinline__ Misc *misc_of(uint8_t *pbuf_generic) {
@@ -546,13 +546,20 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
     if (valid) lim = min(pos[t], n_kv - 1);
 
     // key range of the group (max) and of each wave (min of the rows' last visible key)
-    if (threadIdx.x < PF_NW) misc->wmin[threadIdx.x] = INT32_MAX;
-    if (threadIdx.x == 0) misc->kmax = -1;
+    // Butterfly reductions within the wave, one barrier for the group (atomics on one LDS
+    // word would be serialised lane by lane).
+    int wmx = lim, wmn = lim;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        wmx = max(wmx, __shfl_xor(wmx, o));
+        wmn = min(wmn, __shfl_xor(wmn, o));
+    }
+    if ((threadIdx.x & 63) == 0) {
+        misc->wmax[w] = wmx;
+        misc->wmin[w] = wmn;
+    }
     __syncthreads();
-    atomicMax(&misc->kmax, lim);
-    atomicMin(&misc->wmin[w], lim);
-    __syncthreads();
-    const int kend = misc->kmax + 1;
+    const int kend = max(max(misc->wmax[0], misc->wmax[1]), max(misc->wmax[2], misc->wmax[3])) + 1;
     const int np = (kend + ks - 1) / ks;  // parts holding keys of this group
     if (part >= np) return;               // uniform: nothing to attend to
     WaveState st;
