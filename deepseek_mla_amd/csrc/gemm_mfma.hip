@@ -7,6 +7,7 @@
 // v_mfma_f32_32x32x16_bf16.  Operand tiles are staged through LDS (double buffered)
 // with a 16-byte-chunk XOR swizzle so that fragment reads are bank-conflict free.
 #include "common.h"
+#include "lds_dma.h"
 
 namespace mla {
 
@@ -108,10 +109,211 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(const bf16 *__restric
         }
 }
 
+// ---------------------------------------------------------------------------------
+// Larger-tile form for K a multiple of 64: workgroup tile BM x 128 (BM = 256 or 128) x 64,
+// 4 waves as 2 x 2, each wave (BM/2) x 64.  Operand tiles go straight from global memory
+// to LDS (global_load_lds_dwordx4, one instruction per 8 rows of 128 B), NS stages deep
+// (NS - 1 k-tiles in flight while one is consumed; 2 stages when K is only two k-tiles,
+// so that two workgroups fit a CU).  In LDS, logical
+// 16-byte chunk c of tile row r sits at chunk c ^ ((r >> 1) & 7) (the copies take their
+// source chunk accordingly): the fragment reads of 8 consecutive rows then hit 8
+// distinct bank groups.  The product is computed transposed, D^T[n][m] = B_tile A_tile^T,
+// so that a lane ends up with 4 consecutive columns of one output row; the tile is staged
+// in LDS as bf16 rows and written with 16-byte stores.
+constexpr int GL_BN = 128, GL_BK = 64;
+constexpr int GL_ROWB = GL_BK * 2;  // 128 B per tile row
+constexpr int GL_OPITCH = GL_BN * 2 + 16;  // staged output row pitch: rows 4 banks apart
+__host__ __device__ constexpr int gl_stage_bytes(int bm) { return (bm + GL_BN) * GL_ROWB; }
+__device__ __forceinline__ int gl_swz(int r) { return (r >> 1) & 7; }
+
+// Source offsets of this lane's copies, fixed for the whole K loop: wave w copies A rows
+// [w*BM/4, (w+1)*BM/4) and B rows [32w, 32w + 32), 8 rows per instruction; rows past the
+// matrix end re-read its last row (those results are not stored).
+template <int BM>
+struct GlPlan {
+    uint32_t a[BM / 32], b[4];
+    __device__ __forceinline__ GlPlan(int M, int N, int64_t lda, int64_t ldb, int m0, int n0) {
+        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+#pragma unroll
+        for (int j = 0; j < BM / 32; ++j) {
+            const int r = w * (BM / 4) + 8 * j + (l >> 3);
+            const int rr = min(m0 + r, M - 1) - m0;
+            a[j] = (uint32_t)((int64_t)rr * lda * 2 + (((l & 7) ^ gl_swz(r)) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = w * 32 + 8 * j + (l >> 3);
+            const int rr = min(n0 + r, N - 1) - n0;
+            b[j] = (uint32_t)((int64_t)rr * ldb * 2 + (((l & 7) ^ gl_swz(r)) << 4));
+        }
+    }
+    // copies of k-tile [k0, k0 + 64) into the stage at LDS address dst
+    __device__ __forceinline__ void issue(const uint8_t *abase, const uint8_t *bbase, int k0,
+                                          uint32_t dst) const {
+        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+        for (int j = 0; j < BM / 32; ++j)
+            lds_copy16(abase + 2 * k0, a[j], dst + (w * (BM / 4) + 8 * j) * GL_ROWB);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            lds_copy16(bbase + 2 * k0, b[j], dst + BM * GL_ROWB + (w * 32 + 8 * j) * GL_ROWB);
+    }
+};
+
+template <int BM, int NS>
+__global__ __launch_bounds__(256) void gemm_nt_bf16_lds_kernel(
+    const bf16 *__restrict__ A, const bf16 *__restrict__ B, bf16 *__restrict__ C, int M, int N,
+    int K, int64_t lda, int64_t ldb, int64_t ldc, int64_t sA, int64_t sB, int64_t sC) {
+    constexpr int MB = BM / 64;            // 32-row m blocks per wave
+    constexpr int CP = BM / 32 + 4;        // copy instructions per wave per k-tile
+    constexpr int SB = gl_stage_bytes(BM);
+    static_assert(NS * SB <= 163840 && BM * GL_OPITCH <= NS * SB, "LDS budget");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+    uint8_t MLA_LDS *lds = (uint8_t MLA_LDS *)lds_raw;
+    const int bz = blockIdx.z;
+    A += bz * sA;
+    B += bz * sB;
+    C += bz * sC;
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * GL_BN;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+    const int wm = (w >> 1) * (BM / 2), wn = (w & 1) * 64;
+    const uint32_t lbase = lds_u32(lds);
+    const GlPlan<BM> plan(M, N, lda, ldb, m0, n0);
+    const uint8_t *abase = (const uint8_t *)(A + (int64_t)m0 * lda);
+    const uint8_t *bbase = (const uint8_t *)(B + (int64_t)n0 * ldb);
+
+    f32x16 acc[2][MB];  // [n block][m block], D^T layout
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
+
+    // fragment rows of this lane: B-tile rows (n) as the MFMA A operand, A-tile rows (m)
+    // as the MFMA B operand; logical chunk 2*ks + (l >> 5) for k step ks
+    int boff[2], aoff[MB];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = wn + 32 * j + (l & 31);
+        boff[j] = BM * GL_ROWB + r * GL_ROWB;
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        const int r = wm + 32 * i + (l & 31);
+        aoff[i] = r * GL_ROWB;
+    }
+    const int hi = l >> 5;
+    auto chunk = [&](int rowoff, int ks) {  // byte offset of the lane's chunk in a row
+        const int r = rowoff / GL_ROWB;
+        return rowoff + ((((ks << 1) + hi) ^ gl_swz(r)) << 4);
+    };
+
+    const int nk = K / GL_BK;
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < nk) plan.issue(abase, bbase, s * GL_BK, lbase + s * SB);
+    for (int kt = 0; kt < nk; ++kt) {
+        // k-tile kt landed (later ones may still be in flight: at most NS - 2 of them)
+        const int ahead = min(nk - 1 - kt, NS - 2);
+        if (ahead >= 2) {
+            MLA_WAIT_VMCNT(2 * CP);
+        } else if (ahead == 1) {
+            MLA_WAIT_VMCNT(CP);
+        } else {
+            MLA_WAIT_VMCNT(0);
+        }
+        __syncthreads();  // k-tile kt landed everywhere; k-tile kt-1 no longer read
+        if (kt + NS - 1 < nk)
+            plan.issue(abase, bbase, (kt + NS - 1) * GL_BK, lbase + ((kt + NS - 1) % NS) * SB);
+        const uint8_t MLA_LDS *st = lds + (kt % NS) * SB;
+        // fragments of k step ks+1 are read while the MFMAs of step ks run
+        bf16x8 bf[2][2], af[2][MB];
+        auto fetch = [&](int ks, int b) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bf[b][j] = *(const bf16x8 MLA_LDS *)(st + chunk(boff[j], ks));
+#pragma unroll
+            for (int i = 0; i < MB; ++i) af[b][i] = *(const bf16x8 MLA_LDS *)(st + chunk(aoff[i], ks));
+        };
+        fetch(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < GL_BK / 16; ++ks) {
+            if (ks + 1 < GL_BK / 16) fetch(ks + 1, (ks + 1) & 1);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[ks & 1][j], af[ks & 1][i],
+                                                                        acc[j][i], 0, 0, 0);
+        }
+    }
+    __syncthreads();  // stages free: staging of the output tile
+    // lane: output row m = wm + 32i + (l & 31); columns n = wn + 32j + 8g + 4*hi + 0..3
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            const int m = wm + 32 * i + (l & 31);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = wn + 32 * j + 8 * g + 4 * hi;
+                const bf16x4 v = {f2bf(acc[j][i][4 * g]), f2bf(acc[j][i][4 * g + 1]),
+                                  f2bf(acc[j][i][4 * g + 2]), f2bf(acc[j][i][4 * g + 3])};
+                *(bf16x4 MLA_LDS *)(lds + m * GL_OPITCH + n * 2) = v;
+            }
+        }
+    __syncthreads();
+    // 16 chunks of 16 B per row; thread t takes chunks t, t + 256, ...
+#pragma unroll
+    for (int it = 0; it < BM / 16; ++it) {
+        const int q = threadIdx.x + 256 * it;
+        const int r = q >> 4, c = q & 15;
+        if (m0 + r < M && n0 + 8 * c < N) {
+            const uint8_t MLA_LDS *src = lds + r * GL_OPITCH + c * 16;
+            const u32x2 a = *(const u32x2 MLA_LDS *)src;
+            const u32x2 b = *(const u32x2 MLA_LDS *)(src + 8);
+            const u32x4 v = {a[0], a[1], b[0], b[1]};
+            *(u32x4 *)(C + (int64_t)(m0 + r) * ldc + n0 + 8 * c) = v;
+        }
+    }
+}
+
+template <int BM, int NS>
+static hipError_t launch_lds_gemm(const bf16 *A, const bf16 *B, bf16 *C, int M, int N, int K,
+                                  int64_t lda, int64_t ldb, int64_t ldc, int batch, int64_t sA,
+                                  int64_t sB, int64_t sC, hipStream_t st) {
+    static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
+    const int shm = NS * gl_stage_bytes(BM);
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)gemm_nt_bf16_lds_kernel<BM, NS>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, shm);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    dim3 grid((N + GL_BN - 1) / GL_BN, (M + BM - 1) / BM, batch);
+    hipLaunchKernelGGL((gemm_nt_bf16_lds_kernel<BM, NS>), grid, dim3(256), shm, st, A, B, C, M, N, K,
+                       lda, ldb, ldc, sA, sB, sC);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_nt_bf16(const bf16 *A, const bf16 *B, bf16 *C, int M, int N, int K,
                                int64_t lda, int64_t ldb, int64_t ldc, int batch, int64_t sA,
                                int64_t sB, int64_t sC, hipStream_t st) {
     if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
+    auto al16 = [](const void *p) { return ((uintptr_t)p & 15) == 0; };
+    if (K % GL_BK == 0 && N % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0 && ldc % 8 == 0 &&
+        sA % 8 == 0 && sB % 8 == 0 && sC % 8 == 0 && al16(A) && al16(B) && al16(C)) {
+        // K of two k-tiles: 128-row tiles, 2 stages (64 KB: two workgroups per CU).  Longer
+        // K: 256-row tiles, 3 stages, when they still give two workgroups per CU, else
+        // 128-row tiles, 4 stages.
+        if (K <= 2 * GL_BK)
+            return launch_lds_gemm<128, 2>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, st);
+        const int64_t t256 = (int64_t)((N + GL_BN - 1) / GL_BN) * ((M + 255) / 256) * batch;
+        if (t256 >= 512)
+            return launch_lds_gemm<256, 3>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, st);
+        return launch_lds_gemm<128, 4>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, st);
+    }
     dim3 grid((N + GB_N - 1) / GB_N, (M + GB_M - 1) / GB_M, batch);
     hipLaunchKernelGGL(gemm_nt_bf16_kernel, grid, dim3(256), 0, st, A, B, C, M, N, K, lda, ldb,
                        ldc, sA, sB, sC);

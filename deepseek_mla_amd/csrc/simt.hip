@@ -72,32 +72,111 @@ hipError_t launch_gemm_nt_f32(const float *A, const float *B, float *C, int M, i
 
 // ------------------------------------------------------------------ query RoPE
 // q_cat[t][h][R + 2i .. R + 2i+1] = rotation of (q_rope[t][h][2i], q_rope[t][h][2i+1]) by
-// pos[t] * base^(-2i/Dr).  Angles, sines and cosines in double; one block per token.
+// the angle pos[t] * base^(-2i/Dr).  The angle is formed and reduced to [-pi, pi] in
+// double (at pos ~ 1e5 a float angle would be off by ~1e-2 rad); its sine and cosine are
+// then taken in float (|error| ~1e-7) and the rotation is done in float.  A block takes
+// RQ_TOK tokens: its threads first tabulate (cos, sin) per (token, pair) in LDS, then
+// rotate 4 pairs (8 values) per step, all heads.  The first RQ_PRE groups of each thread
+// are loaded before the angles are formed, so that their latency overlaps that work.
+constexpr int RQ_TOK = 8, RQ_T = 256, RQ_PRE = 4;
+
+template <typename T> struct Vec8;
+template <> struct Vec8<float> {
+    static __device__ __forceinline__ void load(const float *p, float *v) {
+        const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
+        for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+    }
+    static __device__ __forceinline__ void store(float *p, const float *v) {
+        const f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+        *(f32x4 *)p = a;
+        *(f32x4 *)(p + 4) = b;
+    }
+};
+template <> struct Vec8<bf16> {
+    static __device__ __forceinline__ void load(const bf16 *p, float *v) {
+        const bf16x8 a = *(const bf16x8 *)p;
+        for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
+    }
+    static __device__ __forceinline__ void store(bf16 *p, const float *v) {
+        bf16x8 a;
+        for (int i = 0; i < 8; ++i) a[i] = (bf16)v[i];
+        *(bf16x8 *)p = a;
+    }
+};
+
 template <typename T>
-__global__ __launch_bounds__(256) void rope_q_kernel(const T *__restrict__ q_rope,
-                                                     const int32_t *__restrict__ pos,
-                                                     T *__restrict__ q_cat, int H, int R, int Dr,
-                                                     float base) {
-    extern __shared__ double cs[];  // [Dr/2][2]
-    const int t = blockIdx.x;
+__global__ __launch_bounds__(RQ_T) void rope_q_kernel(const T *__restrict__ q_rope,
+                                                      const int32_t *__restrict__ pos,
+                                                      T *__restrict__ q_cat, int T_, int H, int R,
+                                                      int Dr, float base, bool vec) {
+    extern __shared__ float cs[];  // [RQ_TOK][Dr/2][2]
+    const int t0 = blockIdx.x * RQ_TOK;
     const int half = Dr / 2;
-    const double p = (double)pos[t];
-    for (int i = threadIdx.x; i < half; i += blockDim.x) {
-        double theta = pow((double)base, -2.0 * (double)i / (double)Dr);
-        double ang = p * theta;
-        cs[2 * i] = cos(ang);
-        cs[2 * i + 1] = sin(ang);
+    const int ntok = min(RQ_TOK, T_ - t0);
+    const int quads = half / 4;  // groups of 4 pairs
+    const int nvec = vec ? ntok * H * quads : 0;
+    auto vrow = [&](int e, int &tt, int &g) {  // row (t, h) of group e; tt, g: token, group
+        tt = e / (H * quads);
+        const int rem = e % (H * quads);
+        g = rem % quads;
+        return (int64_t)(t0 + tt) * H + rem / quads;
+    };
+    float pre[RQ_PRE][8];
+#pragma unroll
+    for (int k = 0; k < RQ_PRE; ++k) {
+        const int e = threadIdx.x + RQ_T * k;
+        if (e < nvec) {
+            int tt, g;
+            const int64_t row = vrow(e, tt, g);
+            Vec8<T>::load(q_rope + row * Dr + 8 * g, pre[k]);
+        }
+    }
+    const double lb = log2((double)base);
+    constexpr double TWO_PI = 6.283185307179586;
+    for (int j = threadIdx.x; j < ntok * half; j += blockDim.x) {
+        const int tt = j / half, i = j % half;
+        const double ang = (double)pos[t0 + tt] * exp2(-2.0 * (double)i / (double)Dr * lb);
+        const double r = fma(-rint(ang / TWO_PI), TWO_PI, ang);
+        float sn, cn;
+        sincosf((float)r, &sn, &cn);
+        cs[2 * j] = cn;
+        cs[2 * j + 1] = sn;
     }
     __syncthreads();
     const int W = R + Dr;
-    for (int e = threadIdx.x; e < H * half; e += blockDim.x) {
-        int h = e / half, i = e % half;
-        const T *src = q_rope + ((int64_t)t * H + h) * Dr + 2 * i;
-        double a = (double)ld_f(src), b = (double)ld_f(src + 1);
-        double c = cs[2 * i], s = cs[2 * i + 1];
-        T *dst = q_cat + ((int64_t)t * H + h) * W + R + 2 * i;
-        st_f(dst, (float)(a * c - b * s));
-        st_f(dst + 1, (float)(a * s + b * c));
+    auto rotate = [&](int e, const float *v) {
+        int tt, g;
+        const int64_t row = vrow(e, tt, g);
+        float o[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float c = cs[2 * (tt * half + 4 * g + k)], sn = cs[2 * (tt * half + 4 * g + k) + 1];
+            o[2 * k] = fmaf(v[2 * k], c, -v[2 * k + 1] * sn);
+            o[2 * k + 1] = fmaf(v[2 * k], sn, v[2 * k + 1] * c);
+        }
+        Vec8<T>::store(q_cat + row * W + R + 8 * g, o);
+    };
+    if (vec) {  // Dr and R multiples of 8, 16-byte aligned bases: aligned 8-value accesses
+#pragma unroll
+        for (int k = 0; k < RQ_PRE; ++k)
+            if (threadIdx.x + RQ_T * k < nvec) rotate(threadIdx.x + RQ_T * k, pre[k]);
+        for (int e = threadIdx.x + RQ_T * RQ_PRE; e < nvec; e += RQ_T) {
+            int tt, g;
+            const int64_t row = vrow(e, tt, g);
+            float v[8];
+            Vec8<T>::load(q_rope + row * Dr + 8 * g, v);
+            rotate(e, v);
+        }
+    } else {
+        for (int e = threadIdx.x; e < ntok * H * half; e += blockDim.x) {
+            const int tt = e / (H * half), rem = e % (H * half);
+            const int h = rem / half, i = rem % half;
+            const int64_t row = (int64_t)(t0 + tt) * H + h;
+            const float a = ld_f(q_rope + row * Dr + 2 * i), b = ld_f(q_rope + row * Dr + 2 * i + 1);
+            const float c = cs[2 * (tt * half + i)], sn = cs[2 * (tt * half + i) + 1];
+            st_f(q_cat + row * W + R + 2 * i, fmaf(a, c, -b * sn));
+            st_f(q_cat + row * W + R + 2 * i + 1, fmaf(a, sn, b * c));
+        }
     }
 }
 
@@ -105,9 +184,11 @@ template <typename T>
 hipError_t launch_rope_q(const T *q_rope, const int32_t *pos, T *q_cat, int T_, int H, int R,
                          int Dr, float base, hipStream_t st) {
     if (T_ <= 0) return hipSuccess;
-    size_t shm = sizeof(double) * (size_t)Dr;
-    hipLaunchKernelGGL(rope_q_kernel<T>, dim3(T_), dim3(256), shm, st, q_rope, pos, q_cat, H, R,
-                       Dr, base);
+    const size_t shm = sizeof(float) * (size_t)RQ_TOK * Dr;
+    auto al16 = [](const void *p) { return ((uintptr_t)p & 15) == 0; };
+    const bool vec = Dr % 8 == 0 && R % 8 == 0 && al16(q_rope) && al16(q_cat);
+    hipLaunchKernelGGL(rope_q_kernel<T>, dim3((T_ + RQ_TOK - 1) / RQ_TOK), dim3(RQ_T), shm, st,
+                       q_rope, pos, q_cat, T_, H, R, Dr, base, vec);
     return hipGetLastError();
 }
 template hipError_t launch_rope_q<float>(const float *, const int32_t *, float *, int, int, int,
@@ -264,20 +345,6 @@ hipError_t launch_flash_simt_decode(const mla_dims &d, const float *q_cat, const
 // are then merged through LDS in a fixed order.
 constexpr int CB_T = 256, CB_COLS = 128, CB_GROUPS = CB_COLS / 8, CB_PH = CB_T / CB_GROUPS;
 constexpr int CB_U = 8;
-
-template <typename PT> struct Vec8;
-template <> struct Vec8<float> {
-    static __device__ __forceinline__ void load(const float *p, float *v) {
-        const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
-        for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
-    }
-};
-template <> struct Vec8<bf16> {
-    static __device__ __forceinline__ void load(const bf16 *p, float *v) {
-        const bf16x8 a = *(const bf16x8 *)p;
-        for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
-    }
-};
 
 template <typename PT, typename OT>
 __global__ __launch_bounds__(CB_T) void combine_kernel(const PT *__restrict__ part_o,
