@@ -239,12 +239,14 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_lds_kernel(
 #pragma unroll
         for (int ks = 0; ks < GL_BK / 16; ++ks) {
             if (ks + 1 < GL_BK / 16) fetch(ks + 1, (ks + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);  // reads of step ks+1 go out before step ks's MFMAs
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
                     acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[ks & 1][j], af[ks & 1][i],
                                                                         acc[j][i], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     __syncthreads();  // stages free: staging of the output tile
