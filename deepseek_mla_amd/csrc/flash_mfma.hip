@@ -33,6 +33,8 @@
 #include "latent_tile.h"
 
 #include <algorithm>
+#include <utility>
+#include <vector>
 
 namespace mla {
 
@@ -490,8 +492,10 @@ constexpr int PF_ROWS = 32 * PF_NW;  // rows per workgroup
 constexpr int PF_MAX_PARTS = 4;      // key parts per row group (the merge keeps 8 weights)
 constexpr int PF_MAX_ITEMS = 1024;   // (row group, part) items when groups are cut
 // Block order of a cut prefill (a kernel argument: 2 KB, within the argument limit).
+constexpr int PF_LISTS = 256;       // workgroups of a cut prefill: one per CU, each with a list
 struct PrefillOrder {
-    uint16_t item[PF_MAX_ITEMS];  // unit * nparts + part, by decreasing estimated work
+    uint16_t item[PF_MAX_ITEMS];  // unit * nparts + part, grouped by workgroup
+    uint16_t start[PF_LISTS + 1];  // workgroup b takes item[start[b] .. start[b + 1])
 };
 static_assert(PF_MAX_PARTS <= 8, "the merge holds one log-sum-exp per part in lp[8]");
 
@@ -503,31 +507,17 @@ static_assert(PF_MAX_PARTS <= 8, "the merge holds one log-sum-exp per part in lp
 // and prefill_merge_kernel merges the slots after this kernel.  The part boundaries
 // depend only on ks, so a row's result does not depend on how rows are grouped (head
 // chunks): a row whose keys all lie in one part merges that part with weight exactly 1.
-__global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
-    const bf16 *__restrict__ q_cat, const int32_t *__restrict__ pos, int T, int H,
-    const uint8_t *__restrict__ cache, int n_kv, int hc, int n_groups, int n_chunks, float sc,
-    bf16 *__restrict__ o_lat, float *__restrict__ lse, int ks, int nparts,
-    float *__restrict__ ws_o, float *__restrict__ ws_lse, int *__restrict__ ws_np,
-    const PrefillOrder order) {
+// One (row group, head chunk, key part) item of the prefill; returns with the LDS free
+// for the next item except for a final barrier (the caller's).
+__device__ __forceinline__ void prefill_item(
+    int unit, int part, const bf16 *__restrict__ q_cat, const int32_t *__restrict__ pos, int T,
+    int H, const uint8_t *__restrict__ cache, int n_kv, int hc, int n_groups, int n_chunks,
+    float sc, bf16 *__restrict__ o_lat, float *__restrict__ lse, int ks, int nparts,
+    float *__restrict__ ws_o, float *__restrict__ ws_lse, int *__restrict__ ws_np) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     uint8_t MLA_LDS *lds = (uint8_t MLA_LDS *)lds_raw;
     uint8_t MLA_LDS *pbuf = lds + PF_NS * fl::TILE_BYTES;
     Misc *misc = misc_of(lds_raw + PF_NS * fl::TILE_BYTES);
-    // Blocks are dispatched in index order, round-robin over the 8 XCDs and over the
-    // shader engines inside each, and a block waits for a free CU on its engine even when
-    // other engines have one: neighbouring blocks must carry similar work.  With one part
-    // per group, units (row group, head chunk) go heaviest group (latest tokens) first,
-    // the chunks of a group together.  With several parts, order.item lists the (unit,
-    // part) items sorted by estimated work.
-    int unit, part;
-    if (nparts == 1) {
-        unit = blockIdx.x;
-        part = 0;
-    } else {
-        const int it = order.item[blockIdx.x];
-        unit = it / nparts;
-        part = it % nparts;
-    }
     const int chunk = unit % n_chunks;
     const int grp = n_groups - 1 - unit / n_chunks;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar
@@ -595,6 +585,34 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
     if (l < 32) ws_lse[slot * PF_ROWS + w * 32 + l] = ls;
 }
 
+// Blocks are dispatched in index order, round-robin over the 8 XCDs and over the shader
+// engines inside each, and a block waits for a free CU on its engine even when other
+// engines have one: neighbouring blocks must carry similar work.  With one part per
+// group (large prefills), block b takes unit b; units (row group, head chunk) go
+// heaviest group (latest tokens) first, the chunks of a group together.  With several
+// parts (small prefills), one workgroup per CU works through its own list of (unit,
+// part) items, balanced on the host by estimated work (order.start / order.item), so
+// that neither the dispatch order nor per-workgroup start-up costs decide the balance.
+__global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
+    const bf16 *__restrict__ q_cat, const int32_t *__restrict__ pos, int T, int H,
+    const uint8_t *__restrict__ cache, int n_kv, int hc, int n_groups, int n_chunks, float sc,
+    bf16 *__restrict__ o_lat, float *__restrict__ lse, int ks, int nparts,
+    float *__restrict__ ws_o, float *__restrict__ ws_lse, int *__restrict__ ws_np,
+    const PrefillOrder order) {
+    if (nparts == 1) {
+        prefill_item(blockIdx.x, 0, q_cat, pos, T, H, cache, n_kv, hc, n_groups, n_chunks, sc,
+                     o_lat, lse, ks, nparts, ws_o, ws_lse, ws_np);
+        return;
+    }
+    const int k1 = order.start[blockIdx.x + 1];
+    for (int k = order.start[blockIdx.x]; k < k1; ++k) {
+        const int it = order.item[k];
+        prefill_item(it / nparts, it % nparts, q_cat, pos, T, H, cache, n_kv, hc, n_groups,
+                     n_chunks, sc, o_lat, lse, ks, nparts, ws_o, ws_lse, ws_np);
+        __syncthreads();  // the item's output staging and exchange areas are free again
+    }
+}
+
 // Merge of the key parts of the row groups that were cut (flash_prefill_bf16_kernel):
 // lse = log sum_p exp(lse_p), o = sum_p exp(lse_p - lse) o_p, the split-KV combine.
 // Block (group, slab of 4 rows); wave w takes one row, lane l columns 8l .. 8l+7.
@@ -639,22 +657,99 @@ __global__ __launch_bounds__(64 * MG_ROWS) void prefill_merge_kernel(
     if (lse && l == 0) lse[orow] = m + logf(ssum);
 }
 
+// Host estimate of an item's time on MI355X (microseconds, fitted to measured item
+// durations of the persistent cut prefill): a fixed cost (queries, key bounds, output
+// rows), a cost per 32-key tile, an extra for writing a part instead of the final rows,
+// and the cost of an item whose part holds no keys.  Only schedules depend on it.
+constexpr double PF_COST_FIXED = 13.8, PF_COST_TILE = 2.07, PF_COST_CUT = 1.4, PF_COST_EMPTY = 2.24;
+
+// Estimated tiles of part p of row group g (counted from the first tokens) and whether
+// the group is cut, for the usual prefill positions (the T tokens are the last T of the
+// n_kv cached rows).
+static int est_tiles(int g, int p, int ks, int T, int hc, int n_kv, bool *cut) {
+    const int64_t last_row = std::min<int64_t>((int64_t)(g + 1) * PF_ROWS, (int64_t)T * hc) - 1;
+    const int64_t kend = std::min<int64_t>(n_kv, (int64_t)n_kv - T + last_row / hc + 1);
+    *cut = kend > ks;
+    const int64_t k = std::max<int64_t>(0, std::min<int64_t>(ks, kend - (int64_t)p * ks));
+    return (int)((k + fl::NK - 1) / fl::NK);
+}
+static double est_cost(int tiles, bool cut) {
+    return tiles > 0 ? PF_COST_FIXED + PF_COST_TILE * tiles + (cut ? PF_COST_CUT : 0.0)
+                     : PF_COST_EMPTY;
+}
+
+// Longest-processing-time-first assignment of n items (costs c) to nb workgroups;
+// owner[k] is the workgroup of the k-th item in `sorted` (items by decreasing cost).
+// Returns the largest workgroup load.
+static double lpt_assign(const double *c, int n, int nb, uint16_t *sorted, uint16_t *owner) {
+    for (int i = 0; i < n; ++i) sorted[i] = (uint16_t)i;
+    std::stable_sort(sorted, sorted + n, [&](uint16_t a, uint16_t b) { return c[a] > c[b]; });
+    std::vector<std::pair<double, int>> heap;
+    for (int b = 0; b < nb; ++b) heap.push_back({0.0, b});
+    auto gt = [](const std::pair<double, int> &x, const std::pair<double, int> &y) { return x > y; };
+    std::make_heap(heap.begin(), heap.end(), gt);
+    double worst = 0.0;
+    for (int k = 0; k < n; ++k) {
+        std::pop_heap(heap.begin(), heap.end(), gt);
+        auto &top = heap.back();
+        top.first += c[sorted[k]];
+        if (owner) owner[k] = (uint16_t)top.second;
+        worst = std::max(worst, top.first);
+        std::push_heap(heap.begin(), heap.end(), gt);
+    }
+    return worst;
+}
+
 // Parts per row group and keys per part.  Few row groups (fewer than two per CU) leave
 // the longest groups setting the time; their keys are then cut into up to 4 parts of a
-// fixed size (a multiple of the 32-key tile), chosen from T*H and n_kv only.
+// fixed size ks (a multiple of the 32-key tile).  ks is chosen to minimise the estimated
+// time of the persistent schedule, computed for the unchunked grouping, so that it
+// depends on (T, H, n_kv) only: the part boundaries, hence the results, do not depend on
+// the head-chunk cap.  Part counts leave room for the extra groups of a chunked grouping
+// within the work-list capacity.
 int prefill_parts(int T, int H, int n_kv, int *ks) {
     constexpr int NUM_CUS = 256;
+    *ks = n_kv;
     const int64_t groups = ((int64_t)T * H + PF_ROWS - 1) / PF_ROWS;
-    int P = 1;
-    if (groups < 2 * NUM_CUS) {
-        P = (int)((2 * NUM_CUS + groups - 1) / groups);
-        if (P > PF_MAX_PARTS) P = PF_MAX_PARTS;
-        while (P > 1 && groups * P > PF_MAX_ITEMS) --P;
+    if (groups >= 2 * NUM_CUS || n_kv <= fl::NK) return 1;
+    static int64_t cache_key[3] = {-1, -1, -1};
+    static int cache_ks = 0;
+    const int64_t key[3] = {T, H, n_kv};
+    if (std::equal(key, key + 3, cache_key)) {
+        *ks = cache_ks;
+        return (n_kv + cache_ks - 1) / cache_ks;
     }
-    int K = (n_kv + P - 1) / P;
-    K = (K + fl::NK - 1) / fl::NK * fl::NK;
-    *ks = K;
-    return (n_kv + K - 1) / K;
+    const int pmax = (int)std::min<int64_t>(PF_MAX_PARTS, PF_MAX_ITEMS / (groups + H));
+    double best = 1e30;
+    int best_ks = n_kv;
+    std::vector<double> c;
+    std::vector<uint16_t> sorted;
+    for (int P = 1; P <= std::max(1, pmax); ++P) {
+        const int lo = P == 1 ? n_kv : (n_kv + P - 1) / P;
+        const int hi = P == 1 ? n_kv : (n_kv + P - 2) / (P - 1) - 1;
+        for (int k = (lo + fl::NK - 1) / fl::NK * fl::NK; k <= std::max(lo, hi); k += fl::NK) {
+            if (P > 1 && (n_kv + k - 1) / k != P) continue;
+            const int kk = P == 1 ? n_kv : k;
+            c.assign((size_t)groups * P, 0.0);
+            sorted.resize(c.size());
+            for (int g = 0; g < (int)groups; ++g)
+                for (int p = 0; p < P; ++p) {
+                    bool cut;
+                    const int t = est_tiles(g, p, kk, T, H, n_kv, &cut);
+                    c[(size_t)g * P + p] = est_cost(t, P > 1 && cut);
+                }
+            const double m = lpt_assign(c.data(), (int)c.size(), NUM_CUS, sorted.data(), nullptr);
+            if (m < best - 1e-9) {
+                best = m;
+                best_ks = kk;
+            }
+            if (P == 1) break;
+        }
+    }
+    std::copy(key, key + 3, cache_key);
+    cache_ks = best_ks;
+    *ks = best_ks;
+    return (n_kv + best_ks - 1) / best_ks;
 }
 
 size_t prefill_workspace_bytes(int T, int H, int n_kv, int hc) {
@@ -689,33 +784,40 @@ hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int 
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    // Block order of a cut prefill: items by decreasing estimated tile count, estimated
-    // with the usual prefill positions (the T tokens are the last T of the n_kv cached
-    // rows).  Only the schedule depends on this estimate, never the results.
-    // The order depends only on (T, H, n_kv, hc); it is kept for the next call.
+    // Work lists of a cut prefill: items by decreasing estimated cost (tiles plus a fixed
+    // per-item cost), each assigned to the least loaded of the PF_LISTS workgroups (longest
+    // processing time first).  Estimated with the usual prefill positions (the T tokens
+    // are the last T of the n_kv cached rows): only the schedule depends on this estimate,
+    // never the results (every item is listed; one without keys returns at once).  The
+    // lists depend only on (T, H, n_kv, hc); they are kept for the next call.
     static PrefillOrder order;
     static int64_t order_key[4] = {-1, -1, -1, -1};
+    static int n_lists = 0;
     const int64_t key[4] = {T, H, n_kv, hc};
+    if (P > 1 && G * P > PF_MAX_ITEMS) return hipErrorInvalidValue;  // prefill_parts leaves room
     if (P > 1 && !std::equal(key, key + 4, order_key)) {
         const int n_items = (int)G * P;
-        auto tiles_of = [&](int it) {
-            const int u = it / P, p = it % P;
-            const int g = n_groups - 1 - u / n_chunks;
-            const int64_t last_row = std::min<int64_t>((int64_t)(g + 1) * PF_ROWS, (int64_t)T * hc) - 1;
-            const int64_t kend = std::min<int64_t>(n_kv, (int64_t)n_kv - T + last_row / hc + 1);
-            const int64_t k = std::max<int64_t>(0, std::min<int64_t>(ks, kend - (int64_t)p * ks));
-            return (k + fl::NK - 1) / fl::NK;
-        };
-        int64_t work[PF_MAX_ITEMS];
+        double cost[PF_MAX_ITEMS];
         for (int it = 0; it < n_items; ++it) {
-            order.item[it] = (uint16_t)it;
-            work[it] = tiles_of(it);
+            const int u = it / P, p = it % P;
+            bool cut;
+            const int t = est_tiles(n_groups - 1 - u / n_chunks, p, ks, T, hc, n_kv, &cut);
+            cost[it] = est_cost(t, cut);
         }
-        std::stable_sort(order.item, order.item + n_items,
-                         [&](uint16_t a, uint16_t b) { return work[a] > work[b]; });
+        uint16_t sorted[PF_MAX_ITEMS], owner[PF_MAX_ITEMS];
+        n_lists = std::min(PF_LISTS, n_items);
+        lpt_assign(cost, n_items, n_lists, sorted, owner);
+        int count[PF_LISTS];
+        std::fill(count, count + n_lists, 0);
+        for (int k = 0; k < n_items; ++k) ++count[owner[k]];
+        order.start[0] = 0;
+        for (int b = 0; b < n_lists; ++b) order.start[b + 1] = (uint16_t)(order.start[b] + count[b]);
+        int fillp[PF_LISTS];
+        for (int b = 0; b < n_lists; ++b) fillp[b] = order.start[b];
+        for (int k = 0; k < n_items; ++k) order.item[fillp[owner[k]]++] = sorted[k];
         std::copy(key, key + 4, order_key);
     }
-    const unsigned nblocks = (unsigned)(G * P);
+    const unsigned nblocks = P > 1 ? (unsigned)n_lists : (unsigned)G;
     hipLaunchKernelGGL(flash_prefill_bf16_kernel, dim3(nblocks), dim3(64 * PF_NW), shm,
                        st, q_cat, pos, T, H, (const uint8_t *)cache, n_kv, hc, n_groups, n_chunks,
                        scale * fl::LOG2E, o_lat, lse, ks, P, ws_o, ws_lse, ws_np, order);
