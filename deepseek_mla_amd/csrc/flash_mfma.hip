@@ -630,23 +630,36 @@ __global__ __launch_bounds__(64 * MG_ROWS) void prefill_merge_kernel(
     if (rr >= T * hc) return;
     const int l = threadIdx.x & 63;
     const int64_t slot0 = (int64_t)gid * nparts;
+    // the lse and the rows of every part are requested together (one memory latency)
     float lp[PF_MAX_PARTS];
-    float m = -INFINITY;
-    for (int p = 0; p < np; ++p) {
-        lp[p] = ws_lse[(slot0 + p) * PF_ROWS + r];
-        m = fmaxf(m, lp[p]);
-    }
-    float ssum = 0.0f;
-    for (int p = 0; p < np; ++p) ssum += expf(lp[p] - m);  // m finite: part 0 holds key 0
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < np; ++p) {
-        const float wt = expf(lp[p] - m) / ssum;
-        const float *src = ws_o + ((slot0 + p) * PF_ROWS + r) * fl::R + l * 8;
-        const f32x4 a = *(const f32x4 *)src, b = *(const f32x4 *)(src + 4);
+    f32x4 va[PF_MAX_PARTS], vb[PF_MAX_PARTS];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc[e] += wt * a[e];
-            acc[4 + e] += wt * b[e];
+    for (int p = 0; p < PF_MAX_PARTS; ++p) {
+        if (p < np) {
+            lp[p] = ws_lse[(slot0 + p) * PF_ROWS + r];
+            const float *src = ws_o + ((slot0 + p) * PF_ROWS + r) * fl::R + l * 8;
+            va[p] = *(const f32x4 *)src;
+            vb[p] = *(const f32x4 *)(src + 4);
+        }
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < PF_MAX_PARTS; ++p)
+        if (p < np) m = fmaxf(m, lp[p]);
+    float ssum = 0.0f;
+#pragma unroll
+    for (int p = 0; p < PF_MAX_PARTS; ++p)
+        if (p < np) ssum += expf(lp[p] - m);  // m finite: part 0 holds key 0
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < PF_MAX_PARTS; ++p) {
+        if (p < np) {
+            const float wt = expf(lp[p] - m) / ssum;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[e] += wt * va[p][e];
+                acc[4 + e] += wt * vb[p][e];
+            }
         }
     }
     bf16x8 o;
