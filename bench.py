@@ -40,12 +40,12 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 # the files listed, in order).
 TRAFFIC = {
     "src": (("deepseek_mla_amd/csrc/flash_mfma.hip", "deepseek_mla_amd/csrc/decode_mfma.hip",
-             "deepseek_mla_amd/csrc/latent_tile.h", "deepseek_mla_amd/csrc/simt.hip",
-             "deepseek_mla_amd/csrc/common.h"), "0fcc65c51e767430"),
-    "lite_prefill": (77.40e6 + 87.97e6) + (68.21e6 + 16.91e6),      # prefill kernel + merge
-    "v3_long_prefill": 9770.82e6 + 1161.82e6,
-    "v3_decode": (39.24e6 + 16.84e6) + (17.42e6 + 0.14e6),          # partial kernel + combine
-    "v3_decode_q8": (245.72e6 + 16.84e6) + (17.42e6 + 0.54e6),      # partial kernel + combine
+             "deepseek_mla_amd/csrc/latent_tile.h", "deepseek_mla_amd/csrc/lds_dma.h",
+             "deepseek_mla_amd/csrc/simt.hip", "deepseek_mla_amd/csrc/common.h"), "0b61018a92ec56da"),
+    "lite_prefill": (71.40e6 + 82.25e6) + (61.83e6 + 15.32e6),      # prefill kernel + merge
+    "v3_long_prefill": 9804.56e6 + 1195.38e6,
+    "v3_decode": (39.24e6 + 16.84e6) + (17.43e6 + 0.14e6),          # partial kernel + combine
+    "v3_decode_q8": (245.73e6 + 16.84e6) + (17.43e6 + 0.54e6),      # partial kernel + combine
 }
 
 
