@@ -451,3 +451,51 @@ def test_out_proj_few_and_many_tokens(dev, T):
     torch.cuda.synchronize()
     report("v", rel_err_stored(v.float().cpu().numpy(), rv, "bf16"), 2e-2)
     report("out", rel_err_stored(out.float().cpu().numpy(), ro, "bf16"), 2e-2)
+
+
+# ------------------------------------------------- projections, other shapes ---
+
+@pytest.mark.parametrize("T", [37, 300])
+def test_projections_ragged_dims(dev, T):
+    """Absorption and late projections in bf16 at dims off the DeepSeek grid: Dn = 72 (a K
+    that is not a whole number of 64-deep k-tiles: the 32-deep GEMM), Dv = 40 and
+    d_model = 200 (partial 128-column output tiles of the LDS-staged GEMM), T ragged."""
+    import dataclasses
+    from deepseek_mla_amd import mla
+    d = dataclasses.replace(synth.LITE, qk_nope=72, v_head=40, d_model=200,
+                            scale=1.0 / math.sqrt(72 + 64))
+    x = synth.generate(d, T, 8, seed=91, mode="bf16", pos=np.arange(T, dtype=np.int32) * 7)
+    ref_q = oracle.absorb_q(d, x["q_nope"], x["q_rope"], x["pos"], x["wk_b"])
+    rng = np.random.default_rng(92)
+    o_lat = synth.round_bf16(rng.standard_normal((T, d.n_head, 512)) * 0.2)
+    rv, ro = oracle.out_proj(d, o_lat, x["wv_b"], x["wo"])
+    tb = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(torch.bfloat16)
+    q_cat = torch.empty((T, d.n_head, d.row), dtype=torch.bfloat16, device=dev)
+    pos = torch.from_numpy(x["pos"]).to(dev)
+    md = mla.make_dims(d)
+    mla.mla_absorb_q(md, mla.BF16, tb(x["q_nope"]), tb(x["q_rope"]), pos, tb(x["wk_b"]), q_cat, T)
+    v = torch.empty((T, d.n_head * d.v_head), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, d.d_model), dtype=torch.bfloat16, device=dev)
+    mla.mla_out_proj(md, mla.BF16, tb(o_lat), tb(x["wv_b"]), tb(x["wo"]), v, out, T)
+    torch.cuda.synchronize()
+    report("q_cat", rel_err_stored(q_cat.float().cpu().numpy(), ref_q, "bf16"), 2e-2)
+    report("v", rel_err_stored(v.float().cpu().numpy(), rv, "bf16"), 2e-2)
+    report("out", rel_err_stored(out.float().cpu().numpy(), ro, "bf16"), 2e-2)
+
+
+def test_rope_odd_width_f32(dev):
+    """Query RoPE with a rope width that is not a multiple of 8 (the one-pair path) and
+    positions up to 1e5, float32 mode."""
+    import dataclasses
+    from deepseek_mla_amd import mla
+    d = dataclasses.replace(synth.TINY, qk_rope=6, scale=1.0 / math.sqrt(32 + 6))
+    T = 19
+    pos = (np.arange(T, dtype=np.int64) * 5261 % 100003).astype(np.int32)
+    x = synth.generate(d, T, 8, seed=93, mode="f32", pos=pos)
+    ref_q = oracle.absorb_q(d, x["q_nope"], x["q_rope"], x["pos"], x["wk_b"])
+    tf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    q_cat = torch.empty((T, d.n_head, d.row), dtype=torch.float32, device=dev)
+    mla.mla_absorb_q(mla.make_dims(d), mla.F32, tf(x["q_nope"]), tf(x["q_rope"]),
+                     torch.from_numpy(x["pos"]).to(dev), tf(x["wk_b"]), q_cat, T)
+    torch.cuda.synchronize()
+    report("q_cat", rel_err_stored(q_cat.cpu().numpy(), ref_q, "f32"), 1e-4)
