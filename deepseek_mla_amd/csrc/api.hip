@@ -107,12 +107,8 @@ int mla_absorb_q(const mla_dims *d, mla_dtype act, const void *q_nope, const voi
                                      d->rope_base, st);
     } else {
         if (Dn % 8) return MLA_ERR_UNSUPPORTED;
-        e = launch_gemm_nt_bf16((const bf16 *)q_nope, (const bf16 *)wk_b, (bf16 *)q_cat, T, R, Dn,
-                                (int64_t)H * Dn, Dn, (int64_t)H * W, H, Dn, (int64_t)R * Dn, W,
-                                st);
-        if (e == hipSuccess)
-            e = launch_rope_q<bf16>((const bf16 *)q_rope, pos, (bf16 *)q_cat, T, H, R, Dr,
-                                    d->rope_base, st);
+        e = launch_absorb_bf16((const bf16 *)q_nope, (const bf16 *)q_rope, pos, (const bf16 *)wk_b,
+                               (bf16 *)q_cat, T, H, R, Dn, Dr, d->rope_base, st);
     }
     return hip_status(e);
 }

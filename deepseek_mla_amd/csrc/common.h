@@ -61,6 +61,9 @@ hipError_t launch_dequant_q8_0(const uint8_t *rows, float *out, int64_t n_rows, 
                                hipStream_t st);
 
 // bf16 MFMA path
+hipError_t launch_absorb_bf16(const bf16 *q_nope, const bf16 *q_rope, const int32_t *pos,
+                              const bf16 *wk_b, bf16 *q_cat, int T, int H, int R, int Dn, int Dr,
+                              float base, hipStream_t st);
 hipError_t launch_gemm_nt_bf16(const bf16 *A, const bf16 *B, bf16 *C, int M, int N, int K,
                                int64_t lda, int64_t ldb, int64_t ldc, int batch, int64_t sA,
                                int64_t sB, int64_t sC, hipStream_t st);

@@ -160,10 +160,43 @@ struct GlPlan {
     }
 };
 
+// Query RoPE carried by the absorption GEMM (batch index = head h, C = q_cat of head h,
+// row stride ldc): after its output tile, workgroup (x, y, h) rotates the rope part of rows
+// [m0 + x*rpb, m0 + (x+1)*rpb) (rpb = BM / gridDim.x, rounded up), writing
+// q_cat[t][h][R + 2i ..] from q_rope[t][h][2i ..] by the angle pos[t] * base^(-2i/Dr).  The
+// angle is formed and reduced to [-pi, pi] in double (at pos ~ 1e5 a float angle would be
+// off by ~1e-2 rad), its sine and cosine are taken in float.  q_rope == nullptr: none.
+struct RopeTail {
+    const bf16 *q_rope;
+    const int32_t *pos;
+    float base;
+    int H, Dr, R;
+};
+
+__device__ __forceinline__ void rope_rows(const RopeTail &rp, bf16 *__restrict__ C, int64_t ldc,
+                                          int h, int t0, int t1) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const int half = rp.Dr / 2;
+    const double lb = log2((double)rp.base);
+    constexpr double TWO_PI = 6.283185307179586;
+    for (int j = threadIdx.x; j < (t1 - t0) * half; j += blockDim.x) {
+        const int t = t0 + j / half, i = j % half;
+        const double ang = (double)rp.pos[t] * exp2(-2.0 * (double)i / (double)rp.Dr * lb);
+        const double r = fma(-rint(ang / TWO_PI), TWO_PI, ang);
+        float sn, cn;
+        sincosf((float)r, &sn, &cn);
+        const bf16x2 x = *(const bf16x2 *)(rp.q_rope + ((int64_t)t * rp.H + h) * rp.Dr + 2 * i);
+        const float a = (float)x[0], b = (float)x[1];
+        const bf16x2 v = {(bf16)fmaf(a, cn, -b * sn), (bf16)fmaf(a, sn, b * cn)};
+        *(bf16x2 *)(C + (int64_t)t * ldc + rp.R + 2 * i) = v;
+    }
+}
+
 template <int BM, int NS>
 __global__ __launch_bounds__(256) void gemm_nt_bf16_lds_kernel(
     const bf16 *__restrict__ A, const bf16 *__restrict__ B, bf16 *__restrict__ C, int M, int N,
-    int K, int64_t lda, int64_t ldb, int64_t ldc, int64_t sA, int64_t sB, int64_t sC) {
+    int K, int64_t lda, int64_t ldb, int64_t ldc, int64_t sA, int64_t sB, int64_t sC,
+    const RopeTail rope) {
     constexpr int MB = BM / 64;            // 32-row m blocks per wave
     constexpr int CP = BM / 32 + 4;        // copy instructions per wave per k-tile
     constexpr int SB = gl_stage_bytes(BM);
@@ -278,12 +311,17 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_lds_kernel(
             *(u32x4 *)(C + (int64_t)(m0 + r) * ldc + n0 + 8 * c) = v;
         }
     }
+    if (rope.q_rope) {  // uniform
+        const int rpb = (BM + (int)gridDim.x - 1) / (int)gridDim.x;
+        const int t0 = m0 + (int)blockIdx.x * rpb;
+        rope_rows(rope, C, ldc, bz, min(t0, M), min(t0 + rpb, min(m0 + BM, M)));
+    }
 }
 
 template <int BM, int NS>
 static hipError_t launch_lds_gemm(const bf16 *A, const bf16 *B, bf16 *C, int M, int N, int K,
                                   int64_t lda, int64_t ldb, int64_t ldc, int batch, int64_t sA,
-                                  int64_t sB, int64_t sC, hipStream_t st) {
+                                  int64_t sB, int64_t sC, const RopeTail &rope, hipStream_t st) {
     static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
     const int shm = NS * gl_stage_bytes(BM);
     static bool attr_set = false;
@@ -295,31 +333,67 @@ static hipError_t launch_lds_gemm(const bf16 *A, const bf16 *B, bf16 *C, int M, 
     }
     dim3 grid((N + GL_BN - 1) / GL_BN, (M + BM - 1) / BM, batch);
     hipLaunchKernelGGL((gemm_nt_bf16_lds_kernel<BM, NS>), grid, dim3(256), shm, st, A, B, C, M, N, K,
-                       lda, ldb, ldc, sA, sB, sC);
+                       lda, ldb, ldc, sA, sB, sC, rope);
     return hipGetLastError();
+}
+
+// The LDS-staged kernel when the shape allows it (returns false otherwise, nothing launched).
+static bool try_lds_gemm(const bf16 *A, const bf16 *B, bf16 *C, int M, int N, int K, int64_t lda,
+                         int64_t ldb, int64_t ldc, int batch, int64_t sA, int64_t sB, int64_t sC,
+                         const RopeTail &rope, hipStream_t st, hipError_t *e) {
+    auto al16 = [](const void *p) { return ((uintptr_t)p & 15) == 0; };
+    if (!(K % GL_BK == 0 && N % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0 && ldc % 8 == 0 &&
+          sA % 8 == 0 && sB % 8 == 0 && sC % 8 == 0 && al16(A) && al16(B) && al16(C)))
+        return false;
+    // K of two k-tiles: 128-row tiles, 2 stages (64 KB: two workgroups per CU).  Longer K:
+    // 256-row tiles, 3 stages, when they still give two workgroups per CU, else 128-row
+    // tiles, 4 stages.
+    if (K <= 2 * GL_BK) {
+        *e = launch_lds_gemm<128, 2>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, rope, st);
+        return true;
+    }
+    const int64_t t256 = (int64_t)((N + GL_BN - 1) / GL_BN) * ((M + 255) / 256) * batch;
+    if (t256 >= 512)
+        *e = launch_lds_gemm<256, 3>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, rope, st);
+    else
+        *e = launch_lds_gemm<128, 4>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, rope, st);
+    return true;
 }
 
 hipError_t launch_gemm_nt_bf16(const bf16 *A, const bf16 *B, bf16 *C, int M, int N, int K,
                                int64_t lda, int64_t ldb, int64_t ldc, int batch, int64_t sA,
                                int64_t sB, int64_t sC, hipStream_t st) {
     if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
-    auto al16 = [](const void *p) { return ((uintptr_t)p & 15) == 0; };
-    if (K % GL_BK == 0 && N % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0 && ldc % 8 == 0 &&
-        sA % 8 == 0 && sB % 8 == 0 && sC % 8 == 0 && al16(A) && al16(B) && al16(C)) {
-        // K of two k-tiles: 128-row tiles, 2 stages (64 KB: two workgroups per CU).  Longer
-        // K: 256-row tiles, 3 stages, when they still give two workgroups per CU, else
-        // 128-row tiles, 4 stages.
-        if (K <= 2 * GL_BK)
-            return launch_lds_gemm<128, 2>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, st);
-        const int64_t t256 = (int64_t)((N + GL_BN - 1) / GL_BN) * ((M + 255) / 256) * batch;
-        if (t256 >= 512)
-            return launch_lds_gemm<256, 3>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, st);
-        return launch_lds_gemm<128, 4>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, st);
-    }
+    hipError_t e = hipSuccess;
+    const RopeTail none{nullptr, nullptr, 0.0f, 0, 0, 0};
+    if (try_lds_gemm(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, none, st, &e)) return e;
     dim3 grid((N + GB_N - 1) / GB_N, (M + GB_M - 1) / GB_M, batch);
     hipLaunchKernelGGL(gemm_nt_bf16_kernel, grid, dim3(256), 0, st, A, B, C, M, N, K, lda, ldb,
                        ldc, sA, sB, sC);
     return hipGetLastError();
+}
+
+// Absorption: q_cat[t][h][:R] = wk_b[h] . q_nope[t][h] and the query RoPE into
+// q_cat[t][h][R:].  For few tokens (decode) in one launch when the LDS-staged GEMM takes
+// the shape (the rope rows ride on its workgroups: a second launch would cost more than
+// the work); otherwise the GEMM and the RoPE kernel one after the other (riding on the
+// GEMM, every head's workgroups would recompute the same angles).
+hipError_t launch_absorb_bf16(const bf16 *q_nope, const bf16 *q_rope, const int32_t *pos,
+                              const bf16 *wk_b, bf16 *q_cat, int T, int H, int R, int Dn, int Dr,
+                              float base, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    const int W = R + Dr;
+    const RopeTail rope{q_rope, pos, base, H, Dr, R};
+    hipError_t e = hipSuccess;
+    constexpr int FUSE_MAX_T = 64;
+    if (T <= FUSE_MAX_T && Dr % 2 == 0 && R % 2 == 0 && ((uintptr_t)q_rope & 3) == 0 &&
+        try_lds_gemm(q_nope, wk_b, q_cat, T, R, Dn, (int64_t)H * Dn, Dn, (int64_t)H * W, H, Dn,
+                     (int64_t)R * Dn, W, rope, st, &e))
+        return e;
+    e = launch_gemm_nt_bf16(q_nope, wk_b, q_cat, T, R, Dn, (int64_t)H * Dn, Dn, (int64_t)H * W, H,
+                            Dn, (int64_t)R * Dn, W, st);
+    if (e != hipSuccess) return e;
+    return launch_rope_q<bf16>(q_rope, pos, q_cat, T, H, R, Dr, base, st);
 }
 
 }  // namespace mla
