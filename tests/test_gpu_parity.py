@@ -156,6 +156,25 @@ def test_bf16_prefill_small(dev, T, N, pos0):
     check_stages(L.outputs(), ref, "bf16")
 
 
+@pytest.mark.parametrize("T,N", [(200, 333), (700, 1500)])
+def test_bf16_prefill_unordered_positions(dev, T, N):
+    """Query positions in no order and with repeats (not the last T rows of the cache): the
+    cut prefill's work lists and key-part sizes are estimated from the usual layout, so this
+    checks that only the schedule, never the result, depends on that estimate."""
+    from deepseek_mla_amd import layer
+    d = synth.deepseek_dims(16, 2048)
+    rng = np.random.default_rng(37 + T)
+    pos = rng.integers(0, N, size=T).astype(np.int32)
+    pos[: T // 4] = N - 1  # several full rows
+    rng.shuffle(pos)
+    x, rows = small_prefill(d, "bf16", T, N, seed=41 + T, pos=pos)
+    ref = oracle_chain(d, x, rows)
+    L = layer.LayerStep(d, "bf16", "prefill", x, N)
+    L.step()
+    torch.cuda.synchronize()
+    check_stages(L.outputs(), ref, "bf16")
+
+
 def test_bf16_prefill_chunked_vs_unchunked_bitwise(dev):
     """Force real chunking with a T*N*H*4 intermediate above 128 MiB (16 heads)."""
     from deepseek_mla_amd import layer, mla
