@@ -117,10 +117,57 @@ def time_workload(w, steps, warmup, copies=1, n_splits=0):
     res = {"ms_per_step": wall * 1e3, "absorb_ms": float(parts[:, 0].mean()),
            "attention_ms": float(parts[:, 1].mean()), "out_proj_ms": float(parts[:, 2].mean()),
            "attention_ms_min": float(parts[:, 1].min())}
+    res["cache_append"] = time_append(w, L, steps)
     pos = L.pos.cpu().numpy()
     del L
     torch.cuda.empty_cache()
     return res, pos
+
+
+def time_append(w, L, reps):
+    """mla_cache_append of the workload's new tokens (prefill: the T query tokens at their
+    positions; decode: one token per sequence at its last row), timed on its own after
+    the step (it is the call that precedes a step, not part of it)."""
+    import torch
+    from deepseek_mla_amd import mla
+    d = w.dims
+    R, Dr = d.kv_lora_rank, d.qk_rope
+    W = R + Dr
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 1000)
+    n_new = w.T if w.kind == "prefill" else w.n_seq
+    c_kv = torch.randn((n_new, R), generator=g, device="cuda").to(L.tdt)
+    k_rope = torch.randn((n_new, Dr), generator=g, device="cuda").to(L.tdt)
+    if w.kind == "prefill":
+        pos, dst, n_rows = L.pos, None, w.n_kv
+    else:
+        assert L.seq_stride == w.n_kv * L.row_bytes
+        pos = torch.full((n_new,), w.n_kv - 1, dtype=torch.int32, device="cuda")
+        dst = torch.arange(n_new, dtype=torch.int64, device="cuda") * w.n_kv + (w.n_kv - 1)
+        n_rows = w.n_kv * w.n_seq
+    cache = L.caches[0]
+    stream = torch.cuda.current_stream()
+
+    def run():
+        mla.mla_cache_append(L.cdims, L.act, L.kv, c_kv, k_rope, pos, n_new, cache, n_rows,
+                             dst_row=dst, stream=stream)
+
+    for _ in range(3):
+        run()
+    reps = max(reps, 20)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    in_b = 4 if w.mode == "f32" else 2
+    nbytes = n_new * (W * in_b + 4 + (8 if dst is not None else 0) + L.row_bytes)
+    return {"kernel": "cache_append_kernel", "tokens": n_new, "us_per_launch": us,
+            "bytes_per_launch": nbytes, "GB/s": nbytes / (us * 1e-6) / 1e9,
+            "frac_hbm": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "bytes": "per token: c_kv + k_rope inputs, pos (+ dst_row), one cache row"}
 
 
 def cpu_baseline(w, max_queries):
@@ -175,7 +222,8 @@ def run_one(name, steps, warmup, with_cpu, n_splits=0):
     total = sum(fl.values())
     entry = {"workload": name, "ms_per_step": res["ms_per_step"],
              "kernel_ms": {k: res[k] for k in ("absorb_ms", "attention_ms", "out_proj_ms")},
-             "step_tflops": total / (res["ms_per_step"] * 1e-3) / 1e12}
+             "step_tflops": total / (res["ms_per_step"] * 1e-3) / 1e12,
+             "cache_append": res["cache_append"]}
     if w.kind == "prefill":
         ach = fl["attention"] / (res["attention_ms"] * 1e-3) / 1e12
         entry["value"] = entry["step_tflops"]
@@ -263,6 +311,7 @@ def main():
         "roofline": main_entry["roofline"],
         "kernel_ms": main_entry["kernel_ms"],
         "attention_tflops": main_entry.get("attention_tflops"),
+        "cache_append": main_entry["cache_append"],
         "workloads": extras,
     }
     if "cpu_baseline" in main_entry:

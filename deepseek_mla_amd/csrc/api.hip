@@ -283,4 +283,26 @@ int mla_dequant_q8_0(const void *rows, float *out, int64_t n_rows, int32_t width
                                           as_stream(stream)));
 }
 
+int mla_cache_append(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *c_kv,
+                     const void *k_rope, const int32_t *pos, const int64_t *dst_row, int32_t T,
+                     void *cache, int64_t n_rows, void *stream) {
+    if (!dims_ok(d) || !act_ok(act) || T < 0 || n_rows < 0) return MLA_ERR_INVALID_ARG;
+    if (kv != MLA_F32 && kv != MLA_BF16 && kv != MLA_Q8_0) return MLA_ERR_INVALID_ARG;
+    if (kv != MLA_Q8_0 && kv != act) return MLA_ERR_INVALID_ARG;
+    const int R = d->kv_lora_rank, Dr = d->qk_rope;
+    if (kv == MLA_Q8_0 && (R + Dr) % 32) return MLA_ERR_INVALID_ARG;
+    if ((int64_t)(R + Dr) * 4 > 65536) return MLA_ERR_UNSUPPORTED;
+    if (T == 0) return MLA_OK;
+    if (!c_kv || !k_rope || !pos || !cache) return MLA_ERR_INVALID_ARG;
+    hipStream_t st = as_stream(stream);
+    hipError_t e;
+    if (act == MLA_F32)
+        e = launch_cache_append<float>((const float *)c_kv, (const float *)k_rope, pos, dst_row, T,
+                                       R, Dr, d->rope_base, kv, cache, n_rows, st);
+    else
+        e = launch_cache_append<bf16>((const bf16 *)c_kv, (const bf16 *)k_rope, pos, dst_row, T, R,
+                                      Dr, d->rope_base, kv, cache, n_rows, st);
+    return hip_status(e);
+}
+
 }  // extern "C"

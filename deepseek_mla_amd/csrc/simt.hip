@@ -80,6 +80,16 @@ hipError_t launch_gemm_nt_f32(const float *A, const float *B, float *C, int M, i
 // are loaded before the angles are formed, so that their latency overlaps that work.
 constexpr int RQ_TOK = 8, RQ_T = 256, RQ_PRE = 4;
 
+// cos and sin of the RoPE angle pos * base^(-2i/Dr): the angle formed and reduced to
+// [-pi, pi] in double, the sine and cosine taken in float.
+__device__ __forceinline__ void rope_cs(int32_t pos, int i, int Dr, double log2_base, float *c,
+                                        float *s) {
+    constexpr double TWO_PI = 6.283185307179586;
+    const double ang = (double)pos * exp2(-2.0 * (double)i / (double)Dr * log2_base);
+    const double r = fma(-rint(ang / TWO_PI), TWO_PI, ang);
+    sincosf((float)r, s, c);
+}
+
 template <typename T> struct Vec8;
 template <> struct Vec8<float> {
     static __device__ __forceinline__ void load(const float *p, float *v) {
@@ -132,13 +142,10 @@ __global__ __launch_bounds__(RQ_T) void rope_q_kernel(const T *__restrict__ q_ro
         }
     }
     const double lb = log2((double)base);
-    constexpr double TWO_PI = 6.283185307179586;
     for (int j = threadIdx.x; j < ntok * half; j += blockDim.x) {
-        const int tt = j / half, i = j % half;
-        const double ang = (double)pos[t0 + tt] * exp2(-2.0 * (double)i / (double)Dr * lb);
-        const double r = fma(-rint(ang / TWO_PI), TWO_PI, ang);
+        const int tt = j / half;
         float sn, cn;
-        sincosf((float)r, &sn, &cn);
+        rope_cs(pos[t0 + tt], j % half, Dr, lb, &cn, &sn);
         cs[2 * j] = cn;
         cs[2 * j + 1] = sn;
     }
@@ -442,20 +449,12 @@ template hipError_t launch_combine<bf16, bf16>(const bf16 *, const float *, int,
 // ------------------------------------------------------------------------ Q8_0
 // One thread per 32-value block.  Block layout: binary16 scale (little endian) then
 // 32 int8 codes; blocks are 34 bytes, so scales sit at 2-byte alignment.
-__global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float *__restrict__ x,
-                                                            uint8_t *__restrict__ rows,
-                                                            int64_t n_blocks, int nb_row,
-                                                            int width) {
-    const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (blk >= n_blocks) return;
-    const int64_t r = blk / nb_row;
-    const int b = (int)(blk % nb_row);
-    const float *v = x + r * width + (int64_t)b * 32;
+// One 32-value block v -> 34 bytes at out (2-byte aligned).
+__device__ __forceinline__ void q8_0_block(const float *v, uint8_t *out) {
     float amax = 0.0f;
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
     const float d = amax / 127.0f;
     const _Float16 hd = (_Float16)d;
-    uint8_t *out = rows + r * (int64_t)nb_row * 34 + (int64_t)b * 34;
     *(uint16_t *)out = __builtin_bit_cast(uint16_t, hd);
     for (int i = 0; i < 32; i += 2) {
         int q0 = 0, q1 = 0;
@@ -465,6 +464,17 @@ __global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float *__restr
         }
         *(uint16_t *)(out + 2 + i) = (uint16_t)((q0 & 0xFF) | ((q1 & 0xFF) << 8));
     }
+}
+
+__global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float *__restrict__ x,
+                                                            uint8_t *__restrict__ rows,
+                                                            int64_t n_blocks, int nb_row,
+                                                            int width) {
+    const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (blk >= n_blocks) return;
+    const int64_t r = blk / nb_row;
+    const int b = (int)(blk % nb_row);
+    q8_0_block(x + r * width + (int64_t)b * 32, rows + r * (int64_t)nb_row * 34 + (int64_t)b * 34);
 }
 
 __global__ __launch_bounds__(256) void dequant_q8_0_kernel(const uint8_t *__restrict__ rows,
@@ -504,5 +514,70 @@ hipError_t launch_dequant_q8_0(const uint8_t *rows, float *out, int64_t n_rows, 
                        rows, out, n, nb, width);
     return hipGetLastError();
 }
+
+// ------------------------------------------------------------ latent cache append
+// Row pos[t] of the cache <- [c_kv[t] (R) | RoPE(k_rope[t], pos[t]) (Dr)], stored as
+// float32, bfloat16 (rounded to nearest even) or Q8_0 (the block quantiser above).  The
+// rotation is the query's (rope_cs, adjacent pairs).  The destination row is row[t], or
+// pos[t] when row is null; tokens whose destination lies outside [0, n_rows) are skipped.
+// One wave per token; the row is assembled in LDS as float32, then stored.
+template <typename TI, int KV>
+__global__ __launch_bounds__(64) void cache_append_kernel(const TI *__restrict__ c_kv,
+                                                          const TI *__restrict__ k_rope,
+                                                          const int32_t *__restrict__ pos,
+                                                          const int64_t *__restrict__ dst_row,
+                                                          int R, int Dr, float base, void *cache,
+                                                          int64_t n_rows) {
+    extern __shared__ float row[];  // [R + Dr]
+    const int t = blockIdx.x, l = threadIdx.x;
+    const int32_t p = pos[t];
+    const int64_t r = dst_row ? dst_row[t] : (int64_t)p;
+    if (r < 0 || r >= n_rows) return;  // uniform
+    const int W = R + Dr;
+    for (int j = l; j < R; j += 64) row[j] = ld_f(c_kv + (int64_t)t * R + j);
+    const double lb = log2((double)base);
+    for (int i = l; i < Dr / 2; i += 64) {
+        float c, s;
+        rope_cs(p, i, Dr, lb, &c, &s);
+        const float a = ld_f(k_rope + (int64_t)t * Dr + 2 * i), b = ld_f(k_rope + (int64_t)t * Dr + 2 * i + 1);
+        row[R + 2 * i] = fmaf(a, c, -b * s);
+        row[R + 2 * i + 1] = fmaf(a, s, b * c);
+    }
+    __syncthreads();
+    if constexpr (KV == MLA_F32) {
+        float *dst = (float *)cache + r * W;
+        for (int j = l; j < W; j += 64) dst[j] = row[j];
+    } else if constexpr (KV == MLA_BF16) {
+        bf16 *dst = (bf16 *)cache + r * W;
+        for (int j = l; j < W; j += 64) dst[j] = (bf16)row[j];
+    } else {
+        uint8_t *dst = (uint8_t *)cache + r * (W / 32 * 34);
+        for (int b = l; b < W / 32; b += 64) q8_0_block(row + 32 * b, dst + 34 * b);
+    }
+}
+
+template <typename TI>
+hipError_t launch_cache_append(const TI *c_kv, const TI *k_rope, const int32_t *pos,
+                               const int64_t *dst_row, int T, int R, int Dr, float base, int kv,
+                               void *cache, int64_t n_rows, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    const size_t shm = sizeof(float) * (size_t)(R + Dr);
+    if (kv == MLA_F32)
+        hipLaunchKernelGGL((cache_append_kernel<TI, MLA_F32>), dim3(T), dim3(64), shm, st, c_kv,
+                           k_rope, pos, dst_row, R, Dr, base, cache, n_rows);
+    else if (kv == MLA_BF16)
+        hipLaunchKernelGGL((cache_append_kernel<TI, MLA_BF16>), dim3(T), dim3(64), shm, st, c_kv,
+                           k_rope, pos, dst_row, R, Dr, base, cache, n_rows);
+    else
+        hipLaunchKernelGGL((cache_append_kernel<TI, MLA_Q8_0>), dim3(T), dim3(64), shm, st, c_kv,
+                           k_rope, pos, dst_row, R, Dr, base, cache, n_rows);
+    return hipGetLastError();
+}
+template hipError_t launch_cache_append<float>(const float *, const float *, const int32_t *,
+                                               const int64_t *, int, int, int, float, int, void *,
+                                               int64_t, hipStream_t);
+template hipError_t launch_cache_append<bf16>(const bf16 *, const bf16 *, const int32_t *,
+                                              const int64_t *, int, int, int, float, int, void *,
+                                              int64_t, hipStream_t);
 
 }  // namespace mla

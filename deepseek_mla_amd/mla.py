@@ -19,8 +19,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 # Every symbol include/mla.h declares.
 EXPORTS = ("mla_absorb_q", "mla_attn_prefill", "mla_prefill_workspace_bytes",
            "mla_heads_per_chunk", "mla_decode_workspace_bytes",
-           "mla_decode_auto_splits", "mla_attn_decode", "mla_out_proj", "mla_quantize_q8_0",
-           "mla_dequant_q8_0", "mla_q8_0_row_bytes", "mla_status_str")
+           "mla_decode_auto_splits", "mla_attn_decode", "mla_out_proj", "mla_cache_append",
+           "mla_quantize_q8_0", "mla_dequant_q8_0", "mla_q8_0_row_bytes", "mla_status_str")
 
 
 class MLAError(RuntimeError):
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
             "mla_attn_decode": ([D, ctypes.c_int, ctypes.c_int, vp, vp, i64, vp, i32, i32, i32,
                                  vp, vp, vp, sz, vp], ctypes.c_int),
             "mla_out_proj": ([D, ctypes.c_int, vp, vp, vp, vp, vp, i32, vp], ctypes.c_int),
+            "mla_cache_append": ([D, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i32, vp, i64,
+                                  vp], ctypes.c_int),
             "mla_quantize_q8_0": ([vp, vp, i64, i32, vp], ctypes.c_int),
             "mla_dequant_q8_0": ([vp, vp, i64, i32, vp], ctypes.c_int),
             "mla_q8_0_row_bytes": ([i32], i32),
@@ -161,6 +163,12 @@ def mla_attn_decode(dims, act, kv, q_cat, kv_cache, kv_seq_stride_bytes, n_kv, B
 def mla_out_proj(dims, act, o_lat, wv_b, wo, v_scratch, out, T, stream=None):
     _check(lib().mla_out_proj(_d(dims), act, _p(o_lat), _p(wv_b), _p(wo), _p(v_scratch), _p(out),
                               T, _s(stream)), "mla_out_proj")
+
+
+def mla_cache_append(dims, act, kv, c_kv, k_rope, pos, T, cache, n_rows, dst_row=None,
+                     stream=None):
+    _check(lib().mla_cache_append(_d(dims), act, kv, _p(c_kv), _p(k_rope), _p(pos), _p(dst_row), T,
+                                  _p(cache), n_rows, _s(stream)), "mla_cache_append")
 
 
 def mla_quantize_q8_0(x, rows, n_rows, width, stream=None):

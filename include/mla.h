@@ -168,6 +168,29 @@ int mla_out_proj(const mla_dims *dims, mla_dtype act, const void *o_lat, const v
 int mla_quantize_q8_0(const float *x, void *rows, int64_t n_rows, int32_t width, void *stream);
 int mla_dequant_q8_0(const void *rows, float *out, int64_t n_rows, int32_t width, void *stream);
 
+/* Append new tokens to the latent cache (absorption page, section 4: the cache keeps
+ * one row per token holding the compressed c_kv and the rotated shared key; section
+ * 8.1: an 8-bit Q8_0 cache).  For token t:
+ *   row = [ c_kv[t][0:R] | RoPE(k_rope[t], pos[t]) ]          (W = R + Dr values)
+ * with the rotation of mla_absorb_q (adjacent pairs, angle pos * rope_base^(-2i/Dr)); the
+ * key is rotated once, on entry (the "llama.cpp KV cache" page, section 2.3, re-rotates
+ * cached keys on a shift, so the cache holds rotated keys),
+ * written at cache row dst_row[t] (int64, device), or at row pos[t] when dst_row is
+ * NULL, converted to the kv type: float32; bfloat16 rounded to nearest even; Q8_0 by
+ * the rule of mla_quantize_q8_0 (bitwise the same bytes as quantizing the float32 row).
+ * c_kv [T][R] and k_rope [T][Dr] (pre-RoPE) of dtype act, pos [T] int32 (device),
+ * cache [n_rows][W] rows of kv dtype (Q8_0: W/32*34 bytes per row).  Tokens whose
+ * destination row lies outside [0, n_rows) are skipped.  Two tokens with the same
+ * destination race (either may win).  c_kv is taken as given: any normalisation
+ * belongs to the projection that produced it.
+ * Supported: act MLA_F32 or MLA_BF16 with kv == act, or kv MLA_Q8_0 (W % 32 == 0);
+ * W <= 16384.  T == 0 is a no-op.
+ * Errors: INVALID_ARG (nulls, T < 0, n_rows < 0, dtype mix, Q8_0 with W % 32 != 0),
+ * UNSUPPORTED (W > 16384). */
+int mla_cache_append(const mla_dims *dims, mla_dtype act, mla_dtype kv, const void *c_kv,
+                     const void *k_rope, const int32_t *pos, const int64_t *dst_row, int32_t T,
+                     void *cache, int64_t n_rows, void *stream);
+
 /* Bytes of one Q8_0 row of `width` values (width/32*34), or -1 if width is not a
  * positive multiple of 32.  Host-only. */
 int32_t mla_q8_0_row_bytes(int32_t width);

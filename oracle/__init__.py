@@ -157,6 +157,49 @@ def q8_0_dequantize(b, width):
     return out
 
 
+def bf16_round(x):
+    """float32 -> nearest bfloat16 (ties to even), returned as float32 (NaN kept NaN)."""
+    x = _c(x)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    out = (r & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+    return np.where(np.isnan(x), x, out).astype(np.float32)
+
+
+def cache_rows_new(dims, c_kv, k_rope, pos):
+    """The rows new tokens add to the latent cache: [c_kv[t] | RoPE(k_rope[t], pos[t])].
+
+    Section 4 of the absorption page keeps, per token, the compressed latent and the
+    rotated shared key side by side; the key is rotated at its own position once, when
+    it enters the cache (the rule of the KV-cache page, section 2.3).  float32 [T, W]."""
+    c_kv, k_rope, pos = _c(c_kv), _c(k_rope), _c(pos, np.int32)
+    T = c_kv.shape[0]
+    rows = np.empty((T, dims.kv_lora_rank + dims.qk_rope), dtype=np.float32)
+    for t in range(T):
+        rows[t, :dims.kv_lora_rank] = c_kv[t]
+        rows[t, dims.kv_lora_rank:] = rope(k_rope[t], int(pos[t]), dims.rope_base)
+    return rows
+
+
+def cache_append(dims, kv, cache, c_kv, k_rope, pos, dst_row=None):
+    """Returns a copy of cache with the new rows stored at dst_row[t] (pos[t] if None).
+
+    kv is "f32", "bf16" (cache float32 [N, W] holding bfloat16 values) or "q8_0" (cache
+    uint8 [N, W/32*34]).  Destinations outside [0, N) are skipped."""
+    rows = cache_rows_new(dims, c_kv, k_rope, pos)
+    dst = np.asarray(pos if dst_row is None else dst_row, dtype=np.int64)
+    out = np.array(cache, copy=True)
+    if kv == "bf16":
+        rows = bf16_round(rows)
+    elif kv == "q8_0":
+        rows = q8_0_quantize(rows)
+    for t, r in enumerate(dst):
+        if 0 <= r < out.shape[0]:
+            out[r] = rows[t]
+    return out
+
+
 def heads_per_chunk(n_head: int, size_mib: float, cap_mib: int) -> int:
     return int(lib().orc_heads_per_chunk(int(n_head), float(size_mib), int(cap_mib)))
 

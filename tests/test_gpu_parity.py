@@ -518,3 +518,168 @@ def test_rope_odd_width_f32(dev):
                      torch.from_numpy(x["pos"]).to(dev), tf(x["wk_b"]), q_cat, T)
     torch.cuda.synchronize()
     report("q_cat", rel_err_stored(q_cat.cpu().numpy(), ref_q, "f32"), 1e-4)
+
+
+# --------------------------------------------------------- cache append ---
+
+def _append_check(got, ref, d, mode, rows):
+    """Appended rows: c_kv columns bit for bit.  The RoPE columns differ by the float32
+    sine/cosine of the kernel against the oracle's double (a few 1e-7 absolute): float32
+    within 1e-5 of the row's rms; bf16 within one bf16 ulp plus 1e-5; Q8_0 RoPE blocks
+    one code apart with scales one binary16 ulp apart, c_kv blocks byte for byte."""
+    R, W = d.kv_lora_rank, d.kv_lora_rank + d.qk_rope
+    if mode == "q8_0":
+        nb = W // 32
+        g = got[rows].reshape(len(rows), nb, 34)
+        r = ref[rows].reshape(len(rows), nb, 34)
+        nc = R // 32
+        assert np.array_equal(g[:, :nc], r[:, :nc])
+        gs = g[:, nc:, :2].copy().view(np.uint16).astype(np.int32)
+        rs = r[:, nc:, :2].copy().view(np.uint16).astype(np.int32)
+        assert np.abs(gs - rs).max() <= 1
+        gq = g[:, nc:, 2:].view(np.int8).astype(np.int32)
+        rq = r[:, nc:, 2:].view(np.int8).astype(np.int32)
+        assert np.abs(gq - rq).max() <= 1
+        return
+    g, r = got[rows].astype(np.float64), ref[rows].astype(np.float64)
+    assert np.array_equal(g[:, :R], r[:, :R])
+    if mode == "bf16":
+        assert (np.abs(g[:, R:] - r[:, R:]) <= 2.0 ** -7 * np.abs(r[:, R:]) + 1e-5).all()
+    else:
+        report("rope", rel_err(g[:, R:], r[:, R:]), 1e-5)
+
+
+def _append_run(d, mode, c_kv, k_rope, pos, n_rows, fill, dst_row=None):
+    """mla_cache_append into a cache filled with `fill`; returns the cache as numpy
+    (float32 values for f32 / bf16, bytes for Q8_0)."""
+    from deepseek_mla_amd import mla
+    W = d.kv_lora_rank + d.qk_rope
+    T = c_kv.shape[0]
+    act = mla.F32 if mode == "f32" else mla.BF16
+    tdt = torch.float32 if mode == "f32" else torch.bfloat16
+    if mode == "q8_0":
+        cache = torch.full((n_rows, W // 32 * 34), fill, dtype=torch.uint8, device="cuda")
+        kv = mla.Q8_0
+    else:
+        cache = torch.full((n_rows, W), fill, dtype=tdt, device="cuda")
+        kv = act
+    ct = torch.from_numpy(np.ascontiguousarray(c_kv)).to("cuda").to(tdt)
+    kt = torch.from_numpy(np.ascontiguousarray(k_rope)).to("cuda").to(tdt)
+    pt = torch.from_numpy(np.ascontiguousarray(pos, np.int32)).to("cuda")
+    dt = None if dst_row is None else torch.from_numpy(np.asarray(dst_row, np.int64)).to("cuda")
+    mla.mla_cache_append(mla.make_dims(d), act, kv, ct, kt, pt, T, cache, n_rows, dst_row=dt)
+    torch.cuda.synchronize()
+    return cache.cpu().numpy() if mode == "q8_0" else cache.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("mode", ["f32", "bf16", "q8_0"])
+def test_cache_append_small(dev, mode):
+    """77 tokens (a ragged count) at scattered positions up to 1e5 through dst_row, plus
+    position-indexed rows, a token aimed below 0 and one past the end; every other row
+    keeps its fill."""
+    d = synth.TINY if mode == "f32" else synth.deepseek_dims(16, 2048)
+    T, N = 77, 300
+    rng = np.random.default_rng(61)
+    c = rng.standard_normal((T, d.kv_lora_rank)).astype(np.float32)
+    k = (rng.standard_normal((T, d.qk_rope)) * 3).astype(np.float32)
+    if mode != "f32":
+        c, k = synth.round_bf16(c), synth.round_bf16(k)
+    # position-indexed: a permutation of distinct rows, one -1 and one N
+    pos = rng.permutation(N)[:T].astype(np.int32)
+    pos[5], pos[40] = -1, N
+    fill = 0xAB if mode == "q8_0" else 7.0
+    got = _append_run(d, mode, c, k, pos, N, fill)
+    base = np.full_like(got, fill)
+    ref = oracle.cache_append(d, mode, base, c, k, pos)
+    hit = sorted(int(p) for p in pos if 0 <= p < N)
+    assert len(hit) == T - 2
+    _append_check(got, ref, d, mode, hit)
+    miss = [r for r in range(N) if r not in set(hit)]
+    assert np.array_equal(got[miss], base[miss])
+    # explicit destinations with large rotation positions
+    pos2 = (np.arange(T, dtype=np.int64) * 7919 % 100003).astype(np.int32)
+    dst = rng.permutation(N)[:T].astype(np.int64)
+    got2 = _append_run(d, mode, c, k, pos2, N, fill, dst_row=dst)
+    ref2 = oracle.cache_append(d, mode, base, c, k, pos2, dst_row=dst)
+    _append_check(got2, ref2, d, mode, sorted(int(r) for r in dst))
+    print(f"  {mode}: {T} tokens, rows checked", flush=True)
+
+
+@pytest.mark.parametrize("mode", ["bf16", "q8_0"])
+def test_cache_append_then_decode(dev, mode):
+    """Two V3 sequences (Nmax 300 rows each) filled entirely by mla_cache_append through
+    dst_row = b*Nmax + pos, then attended by mla_attn_decode: the result matches the
+    oracle's attention over the oracle's appended rows."""
+    from deepseek_mla_amd import mla
+    d = synth.deepseek_dims(128, 7168)
+    W, Nmax, lens = 576, 300, [300, 123]
+    rng = np.random.default_rng(62)
+    c = synth.round_bf16(rng.standard_normal((2 * Nmax, 512)).astype(np.float32))
+    k = synth.round_bf16(rng.standard_normal((2 * Nmax, 64)).astype(np.float32))
+    pos = np.tile(np.arange(Nmax, dtype=np.int32), 2)
+    dst = np.arange(2 * Nmax, dtype=np.int64)
+    fill = 0 if mode == "q8_0" else 0.0
+    got = _append_run(d, mode, c, k, pos, 2 * Nmax, fill, dst_row=dst)
+    base = np.zeros_like(got)
+    ref = oracle.cache_append(d, mode, base, c, k, pos, dst_row=dst)
+    _append_check(got, ref, d, mode, list(range(2 * Nmax)))
+    rows_ref = oracle.q8_0_dequantize(ref, W) if mode == "q8_0" else ref
+    x = synth.generate(d, 1, 8, seed=63, n_seq=2, mode="bf16")
+    qpos = np.array([l - 1 for l in lens], np.int32)
+    qc = synth.round_bf16(oracle.absorb_q(d, x["q_nope"], x["q_rope"], qpos, x["wk_b"]))
+    if mode == "q8_0":
+        cache, stride, kv = torch.from_numpy(got).to(dev), 612 * Nmax, mla.Q8_0
+    else:
+        cache = torch.from_numpy(got).to(dev).to(torch.bfloat16)
+        stride, kv = 1152 * Nmax, mla.BF16
+    nkv = torch.tensor(lens, dtype=torch.int32, device=dev)
+    cd = mla.make_dims(d)
+    wsb = mla.mla_decode_workspace_bytes(cd, 2, Nmax, 0)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    o = torch.empty((2, 128, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((2, 128), dtype=torch.float32, device=dev)
+    mla.mla_attn_decode(cd, mla.BF16, kv, torch.from_numpy(qc).to(dev).to(torch.bfloat16), cache,
+                        stride, nkv, 2, Nmax, 0, o, lse, ws, wsb)
+    torch.cuda.synchronize()
+    for b in range(2):
+        r = rows_ref[b * Nmax: b * Nmax + lens[b]]
+        ro, rl = oracle.attention(d, qc[b:b + 1], qpos[b:b + 1], r)
+        report("o_lat", rel_err_stored(o[b].float().cpu().numpy(), ro[0], mode), TOL[mode])
+        report("lse (abs)", float(np.abs(lse[b].cpu().numpy() - rl[0]).max()), TOL[mode])
+
+
+def test_cache_append_v3_long_prefill_rows(dev):
+    """The long-context prefill's own append: 8192 new V3 tokens at positions
+    24576..32767 into a 32768-row bf16 cache; every new row checked, every old row kept."""
+    d = synth.deepseek_dims(128, 7168)
+    T, N, p0 = 8192, 32768, 24576
+    rng = np.random.default_rng(64)
+    c = synth.round_bf16(rng.standard_normal((T, 512)).astype(np.float32))
+    k = synth.round_bf16(rng.standard_normal((T, 64)).astype(np.float32))
+    pos = np.arange(p0, p0 + T, dtype=np.int32)
+    got = _append_run(d, "bf16", c, k, pos, N, 0.5)
+    assert (got[:p0] == 0.5).all()
+    new = oracle.bf16_round(oracle.cache_rows_new(d, c, k, pos))
+    ref = np.full_like(got, 0.5)
+    ref[p0:] = new
+    _append_check(got, ref, d, "bf16", list(range(p0, N)))
+
+
+def test_cache_append_v3_decode_q8_rows(dev):
+    """The Q8_0 decode workload's append: one token per sequence for 4 sequences of
+    98304 rows, each at its last row (position 98303), through dst_row."""
+    d = synth.deepseek_dims(128, 7168)
+    B, N = 4, 98304
+    rng = np.random.default_rng(65)
+    c = synth.round_bf16(rng.standard_normal((B, 512)).astype(np.float32))
+    k = synth.round_bf16(rng.standard_normal((B, 64)).astype(np.float32))
+    pos = np.full(B, N - 1, np.int32)
+    dst = np.arange(B, dtype=np.int64) * N + (N - 1)
+    got = _append_run(d, "q8_0", c, k, pos, B * N, 0x5A, dst_row=dst)
+    rows = [int(r) for r in dst]
+    ref = np.full_like(got, 0x5A)
+    ref[rows] = oracle.q8_0_quantize(oracle.cache_rows_new(d, c, k, pos))
+    _append_check(got, ref, d, "q8_0", rows)
+    untouched = np.ones(B * N, bool)
+    untouched[rows] = False
+    assert (got[untouched] == 0x5A).all()

@@ -388,3 +388,98 @@ def test_accounting_reproduces_page_table():
     assert round(100 * (1 - accounting.latent_cache_bytes_per_token(d) /
                         accounting.decompressed_cache_bytes_per_token(d)), 1) == \
         g["compression_rate_percent"]
+
+
+# ---------------------------------------------------------- cache append ---
+
+def _append_inputs(d, T, seed):
+    rng = np.random.default_rng(seed)
+    c_kv = rng.standard_normal((T, d.kv_lora_rank)).astype(np.float32)
+    k_rope = rng.standard_normal((T, d.qk_rope)).astype(np.float32)
+    return c_kv, k_rope
+
+
+def test_cache_append_position_zero_is_concatenation():
+    """At position 0 every rotation angle is 0: the new row is exactly [c_kv | k_rope]."""
+    d = small_dims()
+    c, k = _append_inputs(d, 5, 1)
+    rows = oracle.cache_rows_new(d, c, k, np.zeros(5, np.int32))
+    assert np.array_equal(rows, np.concatenate([c, k], axis=1))
+
+
+def test_cache_append_rope_relative_position():
+    """The score between a query rotated by mla_absorb_q's rule at position m and a key
+    rotated on entry at position n depends on m - n only.  Closed form per pair i
+    (complex view q = a + ib, k = c + id): Re(q conj(k) e^{i (m-n) theta_i}),
+    theta_i = base^(-2i/Dr), evaluated in float64 here."""
+    d = small_dims(H=1, Dr=16)
+    rng = np.random.default_rng(5)
+    q_rope = rng.standard_normal((3, 1, d.qk_rope)).astype(np.float32)
+    kr = rng.standard_normal((3, d.qk_rope)).astype(np.float32)
+    zero_nope = np.zeros((3, 1, d.qk_nope), np.float32)
+    wk_b = np.zeros((1, d.kv_lora_rank, d.qk_nope), np.float32)
+    m = np.array([7, 1000, 40000], np.int32)
+    n = np.array([3, 999, 12345], np.int32)
+    qc = oracle.absorb_q(d, zero_nope, q_rope, m, wk_b)[:, 0, d.kv_lora_rank:]
+    kc = oracle.cache_rows_new(d, np.zeros((3, d.kv_lora_rank), np.float32), kr, n)
+    kc = kc[:, d.kv_lora_rank:]
+    for t in range(3):
+        got = float(np.dot(qc[t].astype(np.float64), kc[t].astype(np.float64)))
+        a, b = q_rope[t, 0, 0::2].astype(np.float64), q_rope[t, 0, 1::2].astype(np.float64)
+        c, e = kr[t, 0::2].astype(np.float64), kr[t, 1::2].astype(np.float64)
+        th = 10000.0 ** (-2.0 * np.arange(d.qk_rope // 2) / d.qk_rope)
+        phi = (float(m[t]) - float(n[t])) * th
+        want = float(((a * c + b * e) * np.cos(phi) - (b * c - a * e) * np.sin(phi)).sum())
+        assert abs(got - want) <= 1e-5 * (1 + abs(want)), (t, got, want)
+        # each rotated pair keeps its length
+        pn = np.hypot(kc[t, 0::2].astype(np.float64), kc[t, 1::2].astype(np.float64))
+        assert np.allclose(pn, np.hypot(c, e), rtol=1e-6)
+
+
+def test_cache_append_destinations():
+    """New rows land at pos[t] (or dst_row[t]); other rows, and tokens aimed outside
+    [0, N), leave the cache unchanged."""
+    d = small_dims()
+    W = d.kv_lora_rank + d.qk_rope
+    c, k = _append_inputs(d, 4, 2)
+    pos = np.array([2, 9, -1, 5], np.int32)
+    base = np.full((8, W), 7.0, np.float32)
+    out = oracle.cache_append(d, "f32", base, c, k, pos)
+    rows = oracle.cache_rows_new(d, c, k, pos)
+    for r in range(8):
+        want = {2: rows[0], 5: rows[3]}.get(r, base[r])
+        assert np.array_equal(out[r], want)
+    out2 = oracle.cache_append(d, "f32", base, c, k, pos, dst_row=np.array([0, 1, 7, 8]))
+    assert np.array_equal(out2[[0, 1, 7]], rows[[0, 1, 2]])
+    assert np.array_equal(out2[2:7], base[2:7])
+
+
+def test_cache_append_q8_0_within_half_step():
+    """A Q8_0 appended row dequantises to within half a quantisation step (d/2, plus the
+    binary16 rounding of d times 127) of the float row, block by block."""
+    d = small_dims(Dr=32)
+    W = d.kv_lora_rank + d.qk_rope
+    c, k = _append_inputs(d, 6, 3)
+    pos = np.array([0, 1, 2, 3, 4, 5], np.int32)
+    q = oracle.cache_append(d, "q8_0", np.zeros((6, W // 32 * 34), np.uint8), c, k, pos)
+    rows = oracle.cache_rows_new(d, c, k, pos)
+    deq = oracle.q8_0_dequantize(q, W)
+    blk = rows.reshape(6, -1, 32)
+    dstep = np.abs(blk).max(axis=2, keepdims=True) / 127.0
+    bound = dstep / 2 + 127 * dstep * 2.0 ** -11 + 1e-12
+    assert (np.abs(deq.reshape(blk.shape) - blk) <= bound).all()
+
+
+def test_bf16_round_ties_and_library():
+    """Round to nearest even at the halfway points, and agreement with torch's float32 ->
+    bfloat16 conversion on random values."""
+    torch = pytest.importorskip("torch")
+    x = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, -(1 + 2 ** -8),
+                  np.inf, -0.0], np.float32)
+    want = np.array([1.0, 1 + 2 ** -6, 1 + 2 ** -7, -1.0, np.inf, -0.0], np.float32)
+    got = oracle.bf16_round(x)
+    assert np.array_equal(got, want)
+    assert np.signbit(got[5])
+    r = np.random.default_rng(9).standard_normal(10000).astype(np.float32) * 100
+    t = torch.from_numpy(r).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(oracle.bf16_round(r), t)
