@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla.so")
-SOURCES = ["api.hip", "simt.hip", "gemm_mfma.hip", "gemv.hip", "flash_mfma.hip", "decode_mfma.hip"]
+SOURCES = ["api.hip", "simt.hip", "gemm_mfma.hip", "gemv.hip", "flash_mfma.hip", "decode_mfma.hip",
+           "flash_mha.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

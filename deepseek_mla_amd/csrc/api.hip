@@ -283,6 +283,53 @@ int mla_dequant_q8_0(const void *rows, float *out, int64_t n_rows, int32_t width
                                           as_stream(stream)));
 }
 
+// The materialised path's kernels are written for the DeepSeek head shape.
+static bool materialized_dims(const mla_dims *d) {
+    return d->qk_nope == 128 && d->qk_rope == 64 && d->v_head == 128 && d->kv_lora_rank % 8 == 0 &&
+           d->scale > 0.0f;
+}
+
+static int materialized_hc(const mla_dims *d, int32_t T, int32_t n_kv, uint32_t cap) {
+    const double size_mib = (double)T * (double)n_kv * (double)d->n_head * 4.0 / (1024.0 * 1024.0);
+    return mla_heads_per_chunk(d->n_head, size_mib, cap);
+}
+
+size_t mla_materialized_workspace_bytes(const mla_dims *d, int32_t T, int32_t n_kv,
+                                        uint32_t scratch_cap_mib) {
+    if (!dims_ok(d) || T < 1 || n_kv < 1 || !materialized_dims(d)) return 0;
+    return materialized_workspace_bytes(T, d->n_head, d->kv_lora_rank, n_kv,
+                                        materialized_hc(d, T, n_kv, scratch_cap_mib));
+}
+
+int mla_prefill_materialized(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *q_nope,
+                             const void *q_rope, const int32_t *pos, int32_t T,
+                             const void *kv_cache, int32_t n_kv, const void *wk_b,
+                             const void *wv_b, const void *wo, void *v_out, void *out, float *lse,
+                             uint32_t scratch_cap_mib, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    if (!dims_ok(d) || !act_ok(act) || T < 0 || n_kv < 1) return MLA_ERR_INVALID_ARG;
+    if (kv != MLA_F32 && kv != MLA_BF16 && kv != MLA_Q8_0) return MLA_ERR_INVALID_ARG;
+    if (act != MLA_BF16 || kv != MLA_BF16 || !materialized_dims(d)) return MLA_ERR_UNSUPPORTED;
+    if (T == 0) return MLA_OK;
+    if (!q_nope || !q_rope || !pos || !kv_cache || !wk_b || !wv_b || !v_out) return MLA_ERR_INVALID_ARG;
+    if ((wo == nullptr) != (out == nullptr)) return MLA_ERR_INVALID_ARG;
+    const int H = d->n_head, R = d->kv_lora_rank;
+    const int hc = materialized_hc(d, T, n_kv, scratch_cap_mib);
+    const size_t need = materialized_workspace_bytes(T, H, R, n_kv, hc);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)) return MLA_ERR_WORKSPACE;
+    hipStream_t st = as_stream(stream);
+    hipError_t e = launch_prefill_materialized(
+        (const bf16 *)q_nope, (const bf16 *)q_rope, pos, T, H, R, (const bf16 *)kv_cache, n_kv,
+        (const bf16 *)wk_b, (const bf16 *)wv_b, hc, d->scale, d->rope_base, (bf16 *)v_out, lse,
+        workspace, st);
+    if (e == hipSuccess && wo) {
+        const int HDv = H * d->v_head;
+        e = launch_gemm_nt_bf16((const bf16 *)v_out, (const bf16 *)wo, (bf16 *)out, T, d->d_model,
+                                HDv, HDv, HDv, d->d_model, 1, 0, 0, 0, st);
+    }
+    return hip_status(e);
+}
+
 int mla_cache_append(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *c_kv,
                      const void *k_rope, const int32_t *pos, const int64_t *dst_row, int32_t T,
                      void *cache, int64_t n_rows, void *stream) {

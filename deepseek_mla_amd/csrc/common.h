@@ -12,6 +12,9 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -71,6 +74,10 @@ hipError_t launch_absorb_bf16(const bf16 *q_nope, const bf16 *q_rope, const int3
 hipError_t launch_gemm_nt_bf16(const bf16 *A, const bf16 *B, bf16 *C, int M, int N, int K,
                                int64_t lda, int64_t ldb, int64_t ldc, int batch, int64_t sA,
                                int64_t sB, int64_t sC, hipStream_t st);
+// the same product with a binary16 result (rounded to nearest even)
+hipError_t launch_gemm_nt_bf16_f16out(const bf16 *A, const bf16 *B, f16 *C, int M, int N, int K,
+                                      int64_t lda, int64_t ldb, int64_t ldc, int batch,
+                                      int64_t sA, int64_t sB, int64_t sC, hipStream_t st);
 // few-row NT product (M <= GEMV_MAX_M rows of A), a stream over B; see gemv.hip
 constexpr int GEMV_MAX_M = 8;
 bool gemv_nt_bf16_ok(const bf16 *A, const bf16 *B, int M, int K, int64_t lda, int64_t ldb,
@@ -85,6 +92,13 @@ size_t prefill_workspace_bytes(int T, int H, int n_kv, int hc);
 hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int T, int H,
                                      const bf16 *cache, int n_kv, int hc, float scale,
                                      bf16 *o_lat, float *lse, void *ws, hipStream_t st);
+// materialised (pp_opt) prefill: Dn 128, Dr 64, Dv 128; workspace bytes and the launch
+size_t materialized_workspace_bytes(int T, int H, int R, int n_kv, int hc);
+hipError_t launch_prefill_materialized(const bf16 *q_nope, const bf16 *q_rope, const int32_t *pos,
+                                       int T, int H, int R, const bf16 *cache, int n_kv,
+                                       const bf16 *wk_b, const bf16 *wv_b, int hc, float scale,
+                                       float rope_base, bf16 *v_out, float *lse, void *ws,
+                                       hipStream_t st);
 // heads per workgroup of the decode kernel (the split planner fills the CUs with it)
 int decode_heads_per_block();
 hipError_t launch_flash_decode_bf16(const bf16 *q_cat, const void *cache, int cache_q8,

@@ -1,0 +1,390 @@
+// Materialised prefill (the pp_opt path of the page "ik_llama.cpp MLA matrix absorption",
+// section 8.4): for long prompts over a long cache, each head's keys and values are
+// decompressed from the latent cache once,
+//   k_nope[h][j] = c_kv[j] . wk_b[h]      (Dn = 128 per key)
+//   v[h][j]      = wv_b[h] . c_kv[j]      (Dv = 128 per key, stored transposed)
+// and attention runs as ordinary causal multi-head attention with a 192-wide query
+// [q_nope | RoPE(q_rope)] against [k_nope | k_rope] (k_rope read from the cache rows,
+// shared by all heads) and a 128-wide value.  Per visible (query, key, head) that is
+// 2 * (192 + 128) = 640 FLOP instead of the absorbed path's 2 * (576 + 512) = 2176.
+// Heads run in chunks chosen by the -amb rule (section 8.3), which bounds the
+// decompressed keys and values held at once.
+//
+// flash_mha_kernel: a workgroup owns 32*NW query tokens of one head; wave w owns 32 of
+// them.  Keys stream through LDS in tiles of 64 (LDS-direct copies, three stages):
+//   S^T[key][row] = K_tile (64 x 192) x Q^T          24 MFMA 32x32x16 per wave
+//   O^T[dv][row] += V^T_tile (128 x 64) x P^T        16 MFMA 32x32x16 per wave
+// The transposed products put one query row in each lane (lanes l and l^32 share it), so
+// the softmax statistics are lane-local plus one exchange.  Inside each 16-key group of
+// a tile, LDS row m holds key m with bits 2 and 3 swapped: the score slots a lane then
+// holds are exactly the 8 consecutive keys the P^T operand of the value product needs,
+// so the weights go from the score registers into the value MFMA without an exchange.
+// Softmax: FlashAttention-2 recurrence in base 2 (running max, rescale of the 128-wide
+// accumulator when the max grows).
+//
+// Precision: the decompressed keys and values, the weights P and the query's nope part
+// are held in binary16 (11 significant bits; the cache, the rope parts and all inputs
+// stay bfloat16): with bfloat16 for these three intermediate roundings the result moves
+// about 4x further from the exact one than with none at all, with binary16 it stays at
+// the rounding of the stored output.  Values beyond binary16's range (|x| > 65504) in
+// q_nope or in a decompressed key or value are outside this path's domain.
+#include "lds_dma.h"
+
+#include <algorithm>
+
+namespace mla {
+
+namespace mh {
+constexpr int DN = 128, DR = 64, DQK = 192, DV = 128;
+constexpr int NK = 64;                         // keys per tile
+constexpr int KN_BYTES = NK * DN * 2;          // 16384: k_nope rows, 256 B each
+constexpr int KR_BYTES = NK * DR * 2;          // 8192: k_rope rows, 128 B each
+constexpr int VT_BYTES = DV * NK * 2;          // 16384: V^T rows (one per dv), 128 B each
+constexpr int STAGE = KN_BYTES + KR_BYTES + VT_BYTES;  // 40960
+constexpr int NS = 3;                          // stages
+constexpr int NW = 8;                          // waves per workgroup
+constexpr int ROWS = 32 * NW;                  // query tokens per workgroup
+constexpr int PER_WAVE = 5;                    // copy instructions per wave per tile
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+}  // namespace mh
+
+// LDS row of key k within a tile (bits 2 and 3 swapped; an involution).
+__device__ __forceinline__ int mh_perm(int k) {
+    return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+// Bank swizzles (LDS: 16 groups of 16 bytes).  k_nope rows are 256 B (16 groups): chunk c of
+// row m sits at c ^ (m & 15), so 16 consecutive rows read at one chunk hit 16 groups.
+// k_rope and V^T rows are 128 B (8 groups): odd rows take the upper half, and chunk c of
+// row m sits at c ^ ((m >> 1) & 7).
+__device__ __forceinline__ int kn_off(int m, int c) { return m * 256 + ((c ^ (m & 15)) << 4); }
+__device__ __forceinline__ int h8_off(int m, int c) { return m * 128 + ((c ^ ((m >> 1) & 7)) << 4); }
+
+// Issue the 5 copy instructions of wave w for the tile of keys key0 .. key0+63 into stage
+// dst.  Keys past `last` re-read row `last` (k_nope, k_rope); V^T rows are padded with
+// zeros up to a multiple of 64 keys, so whole tiles are always in bounds.
+__device__ __forceinline__ void mh_issue_tile(const uint8_t *kn, const uint8_t *cache,
+                                              int64_t row_bytes, int rope_off, const uint8_t *vt,
+                                              int64_t vt_pitch, int key0, int last,
+                                              uint32_t dst, int w) {
+    const int l = threadIdx.x & 63;
+    // k_nope: instructions 2w, 2w+1 cover LDS rows 4i .. 4i+3
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int i = 2 * w + j;
+        const int m = 4 * i + (l >> 4), s = l & 15;
+        const int c = s ^ (m & 15);
+        const int key = min(key0 + mh_perm(m), last);
+        lds_copy16(kn + (int64_t)key0 * 256, (uint32_t)((key - key0) * 256 + c * 16),
+                   dst + i * 1024);
+    }
+    // k_rope: instruction w covers LDS rows 8w .. 8w+7 (from the cache rows)
+    {
+        const int m = 8 * w + (l >> 3), s = l & 7;
+        const int c = s ^ ((m >> 1) & 7);
+        const int key = min(key0 + mh_perm(m), last);
+        lds_copy16(cache + (int64_t)key0 * row_bytes,
+                   (uint32_t)((int64_t)(key - key0) * row_bytes + rope_off + c * 16),
+                   dst + mh::KN_BYTES + w * 1024);
+    }
+    // V^T: instructions 2w, 2w+1 cover dv rows 8i .. 8i+7 (keys key0 .. key0+63)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int i = 2 * w + j;
+        const int dv = 8 * i + (l >> 3), s = l & 7;
+        const int c = s ^ ((dv >> 1) & 7);
+        lds_copy16(vt + (int64_t)key0 * 2, (uint32_t)(dv * vt_pitch + c * 16),
+                   dst + mh::KN_BYTES + mh::KR_BYTES + i * 1024);
+    }
+}
+
+// One (head, token block) per workgroup.  kn: [hc][n_kv][128], vt: [hc][128][vt_len] (binary16)
+// (vt_len a multiple of 64, zero past n_kv), q_nope [T][H][128], q_rope_rot [T][H][64]
+// (already rotated), cache rows of row_bytes with k_rope at rope_off.  Writes
+// v_out[t][h*128 ..] (bf16, normalised) and lse[t][h] (natural log) for h = h0 + chunk head.
+__global__ __launch_bounds__(512) void flash_mha_kernel(
+    const bf16 *__restrict__ q_nope, const bf16 *__restrict__ q_rope_rot,
+    const int32_t *__restrict__ pos, int T, int H, int h0, int hc,
+    const uint8_t *__restrict__ kn_all, const uint8_t *__restrict__ cache, int64_t row_bytes,
+    int rope_off, const uint8_t *__restrict__ vt_all, int vt_len, int n_kv, float sc,
+    bf16 *__restrict__ v_out, float *__restrict__ lse) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
+    uint8_t MLA_LDS *lds = (uint8_t MLA_LDS *)smem_raw;
+    int *red = (int *)(smem_raw + mh::NS * mh::STAGE);  // [NW] wave key bounds
+
+    // block -> (head, token block): the blocks of one head share an XCD (block ids go
+    // round-robin over the 8 XCDs) when hc is a multiple of 8; heaviest blocks first.
+    const int nqb = (T + mh::ROWS - 1) / mh::ROWS;
+    const int L = blockIdx.x;
+    int hh, qr;
+    if (hc % 8 == 0) {
+        hh = (L & 7) + 8 * (L / (8 * nqb));
+        qr = (L >> 3) % nqb;
+    } else {
+        hh = L / nqb;
+        qr = L % nqb;
+    }
+    const int qb = nqb - 1 - qr;
+    const int h = h0 + hh;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l = threadIdx.x & 63, hi = l >> 5, r = l & 31;
+    const int t = qb * mh::ROWS + 32 * w + r;
+    const bool valid = t < T;
+    const int tq = valid ? t : T - 1;
+    int lim = valid ? min(pos[tq], n_kv - 1) : -1;
+
+    // queries: fragment kk holds dims kk*16 + hi*8 .. +7 of the row (nope part in binary16)
+    f16x8 qn16[8];
+    bf16x8 qr16[4];
+    {
+        const bf16 *qn = q_nope + ((int64_t)tq * H + h) * mh::DN + hi * 8;
+        const bf16 *qp = q_rope_rot + ((int64_t)tq * H + h) * mh::DR + hi * 8;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const bf16x8 x = *(const bf16x8 *)(qn + kk * 16);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qn16[kk][e] = (f16)(float)x[e];
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qr16[kk] = *(const bf16x8 *)(qp + kk * 16);
+    }
+    // key bounds: wave max / min of the row limits, then the workgroup max
+    int wmax = lim, wmin = valid ? lim : INT32_MAX;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+        wmax = max(wmax, __shfl_xor(wmax, o));
+        wmin = min(wmin, __shfl_xor(wmin, o));
+    }
+    wmax = __builtin_amdgcn_readfirstlane(wmax);
+    wmin = __builtin_amdgcn_readfirstlane(wmin);
+    if (l == 0) red[w] = wmax;
+    __syncthreads();
+    int kend = -1;
+#pragma unroll
+    for (int i = 0; i < mh::NW; ++i) kend = max(kend, red[i]);
+    kend += 1;  // keys [0, kend) are visible to some row of the workgroup
+    const int ntiles = (kend + mh::NK - 1) / mh::NK;
+
+    const uint8_t *kn = kn_all + (int64_t)hh * n_kv * mh::DN * 2;
+    const uint8_t *vt = vt_all + (int64_t)hh * mh::DV * vt_len * 2;
+    const int64_t vt_pitch = (int64_t)vt_len * 2;
+    const int last = n_kv - 1;
+    const uint32_t lbase = lds_u32(lds);
+
+    f32x16 o[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[nb][e] = 0.0f;
+    float m = -INFINITY, lsum = 0.0f;
+
+    // the query and bound loads must be complete before the copies (their completion is
+    // tracked by counting outstanding vector-memory operations)
+    MLA_WAIT_VMCNT(0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+        if (s < ntiles)
+            mh_issue_tile(kn, cache, row_bytes, rope_off, vt, vt_pitch, s * mh::NK, last,
+                          lbase + s * mh::STAGE, w);
+
+    for (int ti = 0; ti < ntiles; ++ti) {
+        if (ti + 1 < ntiles) {
+            MLA_WAIT_VMCNT(mh::PER_WAVE);
+        } else {
+            MLA_WAIT_VMCNT(0);
+        }
+        __syncthreads();
+        if (ti + 2 < ntiles)
+            mh_issue_tile(kn, cache, row_bytes, rope_off, vt, vt_pitch, (ti + 2) * mh::NK, last,
+                          lbase + ((ti + 2) % mh::NS) * mh::STAGE, w);
+        const int key0 = ti * mh::NK;
+        if (key0 > wmax) continue;  // no row of this wave sees these keys
+        const uint8_t MLA_LDS *st = lds + (ti % mh::NS) * mh::STAGE;
+        const uint8_t MLA_LDS *skn = st;
+        const uint8_t MLA_LDS *skr = st + mh::KN_BYTES;
+        const uint8_t MLA_LDS *svt = st + mh::KN_BYTES + mh::KR_BYTES;
+
+        // scores: two 32-key blocks, slot e of block j is key
+        // key0 + 32j + 16(e>>3) + 8hi + (e&7)
+        f32x16 s[2];
+        const bool edge = key0 + mh::NK - 1 > wmin;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (edge) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    s[j][e] = (key0 + 32 * j + 16 * (e >> 3) + 8 * hi + (e & 7) <= lim) ? 0.0f
+                                                                                         : -INFINITY;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) s[j][e] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < 12; ++kk) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int mrow = 32 * j + r;
+                if (kk < 8) {
+                    const f16x8 a = *(const f16x8 MLA_LDS *)(skn + kn_off(mrow, 2 * kk + hi));
+                    s[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qn16[kk], s[j], 0, 0, 0);
+                } else {
+                    const bf16x8 a = *(const bf16x8 MLA_LDS *)(skr + h8_off(mrow, 2 * (kk - 8) + hi));
+                    s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr16[kk - 8], s[j], 0, 0, 0);
+                }
+            }
+        }
+        // online softmax (base 2): running max over the row (this lane's 32 slots and the
+        // partner lane's), rescale when it grows
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[j][e]);
+        {
+            const float y = __shfl_xor(tmax, 32);
+            tmax = hi ? fmaxf(y, tmax) : fmaxf(tmax, y);
+        }
+        const float mnew = fmaxf(m, tmax * sc);
+        const float nmu = (mnew == -INFINITY) ? 0.0f : -mnew;
+        if (__builtin_amdgcn_ballot_w64(mnew > m)) {
+            const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);
+            lsum *= alpha;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[nb][e] *= alpha;
+        }
+        m = mnew;
+        f16x8 p[4];  // p[ks]: keys key0 + 16ks + 8hi .. +7
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(fmaf(s[j][e], sc, nmu));
+                lsum += pe;
+                p[2 * j + (e >> 3)][e & 7] = (f16)pe;
+            }
+        // O^T += V^T P^T: A = V^T rows dv = 32nb + r, keys 16ks + 8hi .. +7 (chunk 2ks+hi)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                const f16x8 a = *(const f16x8 MLA_LDS *)(svt + h8_off(32 * nb + r, 2 * ks + hi));
+                o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, p[ks], o[nb], 0, 0, 0);
+            }
+    }
+
+    if (!valid) return;
+    float ltot;
+    {
+        const float y = __shfl_xor(lsum, 32);
+        ltot = hi ? y + lsum : lsum + y;
+    }
+    const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+    bf16 *orow = v_out + ((int64_t)t * H + h) * mh::DV;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            bf16x4 v4;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) v4[b] = f2bf(o[nb][4 * a + b] * inv);
+            *(bf16x4 *)(orow + 32 * nb + 8 * a + 4 * hi) = v4;
+        }
+    if (lse && hi == 0)
+        lse[(int64_t)t * H + h] = ltot > 0.0f ? (m + __log2f(ltot)) * mh::LN2 : -INFINITY;
+}
+
+// wk_b [H][R][Dn] -> wk_bT [H][Dn][R] (32 x 32 tiles through LDS).
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16 *__restrict__ src,
+                                                             bf16 *__restrict__ dst, int rows,
+                                                             int cols) {
+    __shared__ bf16 tile[32][33];
+    const int64_t b = blockIdx.z;
+    const bf16 *s = src + b * rows * cols;
+    bf16 *d = dst + b * rows * cols;
+    const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    for (int i = ty; i < 32; i += 8)
+        if (r0 + i < rows && c0 + tx < cols) tile[i][tx] = s[(int64_t)(r0 + i) * cols + c0 + tx];
+    __syncthreads();
+    for (int i = ty; i < 32; i += 8)
+        if (c0 + i < cols && r0 + tx < rows) d[(int64_t)(c0 + i) * rows + r0 + tx] = tile[tx][i];
+}
+
+// Zero columns [from, pitch) of `rows` rows of a binary16 matrix with row pitch `pitch`.
+__global__ __launch_bounds__(256) void zero_cols_kernel(f16 *__restrict__ x, int64_t rows,
+                                                        int pitch, int from) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int w = pitch - from;
+    if (i >= rows * w) return;
+    x[(i / w) * pitch + from + (int)(i % w)] = (f16)0.0f;
+}
+
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int vt_len_of(int n_kv) { return (n_kv + mh::NK - 1) / mh::NK * mh::NK; }
+
+size_t materialized_workspace_bytes(int T, int H, int R, int n_kv, int hc) {
+    return al256((size_t)H * mh::DN * R * 2) + al256((size_t)T * H * mh::DR * 2) +
+           al256((size_t)hc * n_kv * mh::DN * 2) + al256((size_t)hc * mh::DV * vt_len_of(n_kv) * 2);
+}
+
+hipError_t launch_prefill_materialized(const bf16 *q_nope, const bf16 *q_rope, const int32_t *pos,
+                                       int T, int H, int R, const bf16 *cache, int n_kv,
+                                       const bf16 *wk_b, const bf16 *wv_b, int hc, float scale,
+                                       float rope_base, bf16 *v_out, float *lse, void *ws,
+                                       hipStream_t st) {
+    using namespace mh;
+    uint8_t *p = (uint8_t *)ws;
+    bf16 *wk_bT = (bf16 *)p;
+    p += al256((size_t)H * DN * R * 2);
+    bf16 *qr = (bf16 *)p;
+    p += al256((size_t)T * H * DR * 2);
+    f16 *kn = (f16 *)p;
+    p += al256((size_t)hc * n_kv * DN * 2);
+    f16 *vt = (f16 *)p;
+    const int vt_len = vt_len_of(n_kv);
+    const int W = R + DR;
+    hipError_t e;
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((DN + 31) / 32, (R + 31) / 32, H), dim3(256), 0,
+                       st, wk_b, wk_bT, R, DN);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_rope_q<bf16>(q_rope, pos, qr, T, H, 0, DR, rope_base, st)) != hipSuccess)
+        return e;
+    const size_t shm = (size_t)NS * STAGE + 64;
+    static bool attr_set = false;  // per process; every device takes the same value
+    if (!attr_set) {
+        e = hipFuncSetAttribute((const void *)flash_mha_kernel,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int nqb = (T + ROWS - 1) / ROWS;
+    for (int h0 = 0; h0 < H; h0 += hc) {
+        const int nh = std::min(hc, H - h0);
+        // k_nope[i][j][d] = sum_l c_kv[j][l] wk_b[h0+i][l][d]
+        e = launch_gemm_nt_bf16_f16out(cache, wk_bT + (int64_t)h0 * DN * R, kn, n_kv, DN, R, W,
+                                       R, DN, nh, 0, (int64_t)DN * R, (int64_t)n_kv * DN, st);
+        if (e != hipSuccess) return e;
+        // v^T[i][d][j] = sum_l wv_b[h0+i][d][l] c_kv[j][l]
+        e = launch_gemm_nt_bf16_f16out(wv_b + (int64_t)h0 * DV * R, cache, vt, DV, n_kv, R, R, W,
+                                       vt_len, nh, (int64_t)DV * R, 0, (int64_t)DV * vt_len, st);
+        if (e != hipSuccess) return e;
+        if (vt_len > n_kv) {
+            const int64_t n = (int64_t)nh * DV * (vt_len - n_kv);
+            hipLaunchKernelGGL(zero_cols_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                               st, vt, (int64_t)nh * DV, vt_len, n_kv);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(flash_mha_kernel, dim3(nqb * nh), dim3(64 * NW), shm, st, q_nope, qr,
+                           pos, T, H, h0, nh, (const uint8_t *)kn, (const uint8_t *)cache,
+                           (int64_t)W * 2, R * 2, (const uint8_t *)vt, vt_len, n_kv,
+                           scale * LOG2E, v_out, lse);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace mla

@@ -1,5 +1,6 @@
 // bf16 "NT" GEMM on gfx950 matrix cores:
-//   C[b][m][n] = sum_k A[b][m][k] * B[b][n][k]       (bf16 in, fp32 accumulate, bf16 out)
+//   C[b][m][n] = sum_k A[b][m][k] * B[b][n][k]       (bf16 in, fp32 accumulate, bf16 out;
+//                                                     binary16 out on request)
 // Both operands are K-contiguous, which is the layout of all three projections of the
 // absorbed path: q_lat = q_nope . wk_b[h]^T, v = o_lat . wv_b[h]^T, out = v . wo^T.
 //
@@ -9,6 +10,8 @@
 #include "common.h"
 #include "lds_dma.h"
 
+#include <type_traits>
+
 namespace mla {
 
 constexpr int GB_M = 128, GB_N = 128, GB_K = 32;
@@ -17,9 +20,13 @@ constexpr int GB_TILE_BYTES = GB_M * GB_ROWB;     // 8 KiB per operand tile
 
 __device__ __forceinline__ int gswz(int row, int c) { return c ^ ((row >> 2) & 3); }
 
+// fp32 -> output element (both conversions round to nearest even)
+template <typename TO> __device__ __forceinline__ TO cvt_out(float x) { return (TO)x; }
+
+template <typename TO>
 __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(const bf16 *__restrict__ A,
                                                            const bf16 *__restrict__ B,
-                                                           bf16 *__restrict__ C, int M, int N,
+                                                           TO *__restrict__ C, int M, int N,
                                                            int K, int64_t lda, int64_t ldb,
                                                            int64_t ldc, int64_t sA, int64_t sB,
                                                            int64_t sC) {
@@ -104,7 +111,7 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(const bf16 *__restric
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int gm = m0 + wm + i * 32 + (e >> 2) * 8 + (l >> 5) * 4 + (e & 3);
-                if (gm < M && gn < N) C[gm * ldc + gn] = f2bf(acc[i][j][e]);
+                if (gm < M && gn < N) C[gm * ldc + gn] = cvt_out<TO>(acc[i][j][e]);
             }
         }
 }
@@ -192,9 +199,9 @@ __device__ __forceinline__ void rope_rows(const RopeTail &rp, bf16 *__restrict__
     }
 }
 
-template <int BM, int NS>
+template <int BM, int NS, typename TO>
 __global__ __launch_bounds__(256) void gemm_nt_bf16_lds_kernel(
-    const bf16 *__restrict__ A, const bf16 *__restrict__ B, bf16 *__restrict__ C, int M, int N,
+    const bf16 *__restrict__ A, const bf16 *__restrict__ B, TO *__restrict__ C, int M, int N,
     int K, int64_t lda, int64_t ldb, int64_t ldc, int64_t sA, int64_t sB, int64_t sC,
     const RopeTail rope) {
     constexpr int MB = BM / 64;            // 32-row m blocks per wave
@@ -292,9 +299,10 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_lds_kernel(
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = wn + 32 * j + 8 * g + 4 * hi;
-                const bf16x4 v = {f2bf(acc[j][i][4 * g]), f2bf(acc[j][i][4 * g + 1]),
-                                  f2bf(acc[j][i][4 * g + 2]), f2bf(acc[j][i][4 * g + 3])};
-                *(bf16x4 MLA_LDS *)(lds + m * GL_OPITCH + n * 2) = v;
+                typedef TO tox4 __attribute__((ext_vector_type(4)));
+                const tox4 v = {cvt_out<TO>(acc[j][i][4 * g]), cvt_out<TO>(acc[j][i][4 * g + 1]),
+                                cvt_out<TO>(acc[j][i][4 * g + 2]), cvt_out<TO>(acc[j][i][4 * g + 3])};
+                *(tox4 MLA_LDS *)(lds + m * GL_OPITCH + n * 2) = v;
             }
         }
     __syncthreads();
@@ -311,34 +319,37 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_lds_kernel(
             *(u32x4 *)(C + (int64_t)(m0 + r) * ldc + n0 + 8 * c) = v;
         }
     }
-    if (rope.q_rope) {  // uniform
-        const int rpb = (BM + (int)gridDim.x - 1) / (int)gridDim.x;
-        const int t0 = m0 + (int)blockIdx.x * rpb;
-        rope_rows(rope, C, ldc, bz, min(t0, M), min(t0 + rpb, min(m0 + BM, M)));
+    if constexpr (std::is_same<TO, bf16>::value) {
+        if (rope.q_rope) {  // uniform
+            const int rpb = (BM + (int)gridDim.x - 1) / (int)gridDim.x;
+            const int t0 = m0 + (int)blockIdx.x * rpb;
+            rope_rows(rope, C, ldc, bz, min(t0, M), min(t0 + rpb, min(m0 + BM, M)));
+        }
     }
 }
 
-template <int BM, int NS>
-static hipError_t launch_lds_gemm(const bf16 *A, const bf16 *B, bf16 *C, int M, int N, int K,
+template <int BM, int NS, typename TO>
+static hipError_t launch_lds_gemm(const bf16 *A, const bf16 *B, TO *C, int M, int N, int K,
                                   int64_t lda, int64_t ldb, int64_t ldc, int batch, int64_t sA,
                                   int64_t sB, int64_t sC, const RopeTail &rope, hipStream_t st) {
     static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
     const int shm = NS * gl_stage_bytes(BM);
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)gemm_nt_bf16_lds_kernel<BM, NS>,
+        hipError_t e = hipFuncSetAttribute((const void *)gemm_nt_bf16_lds_kernel<BM, NS, TO>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, shm);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     dim3 grid((N + GL_BN - 1) / GL_BN, (M + BM - 1) / BM, batch);
-    hipLaunchKernelGGL((gemm_nt_bf16_lds_kernel<BM, NS>), grid, dim3(256), shm, st, A, B, C, M, N, K,
+    hipLaunchKernelGGL((gemm_nt_bf16_lds_kernel<BM, NS, TO>), grid, dim3(256), shm, st, A, B, C, M, N, K,
                        lda, ldb, ldc, sA, sB, sC, rope);
     return hipGetLastError();
 }
 
 // The LDS-staged kernel when the shape allows it (returns false otherwise, nothing launched).
-static bool try_lds_gemm(const bf16 *A, const bf16 *B, bf16 *C, int M, int N, int K, int64_t lda,
+template <typename TO>
+static bool try_lds_gemm(const bf16 *A, const bf16 *B, TO *C, int M, int N, int K, int64_t lda,
                          int64_t ldb, int64_t ldc, int batch, int64_t sA, int64_t sB, int64_t sC,
                          const RopeTail &rope, hipStream_t st, hipError_t *e) {
     auto al16 = [](const void *p) { return ((uintptr_t)p & 15) == 0; };
@@ -349,28 +360,42 @@ static bool try_lds_gemm(const bf16 *A, const bf16 *B, bf16 *C, int M, int N, in
     // 256-row tiles, 3 stages, when they still give two workgroups per CU, else 128-row
     // tiles, 4 stages.
     if (K <= 2 * GL_BK) {
-        *e = launch_lds_gemm<128, 2>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, rope, st);
+        *e = launch_lds_gemm<128, 2, TO>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, rope, st);
         return true;
     }
     const int64_t t256 = (int64_t)((N + GL_BN - 1) / GL_BN) * ((M + 255) / 256) * batch;
     if (t256 >= 512)
-        *e = launch_lds_gemm<256, 3>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, rope, st);
+        *e = launch_lds_gemm<256, 3, TO>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, rope, st);
     else
-        *e = launch_lds_gemm<128, 4>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, rope, st);
+        *e = launch_lds_gemm<128, 4, TO>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, rope, st);
     return true;
+}
+
+template <typename TO>
+static hipError_t launch_gemm_any(const bf16 *A, const bf16 *B, TO *C, int M, int N, int K,
+                                  int64_t lda, int64_t ldb, int64_t ldc, int batch, int64_t sA,
+                                  int64_t sB, int64_t sC, hipStream_t st) {
+    if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
+    hipError_t e = hipSuccess;
+    const RopeTail none{nullptr, nullptr, 0.0f, 0, 0, 0};
+    if (try_lds_gemm<TO>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, none, st, &e))
+        return e;
+    dim3 grid((N + GB_N - 1) / GB_N, (M + GB_M - 1) / GB_M, batch);
+    hipLaunchKernelGGL(gemm_nt_bf16_kernel<TO>, grid, dim3(256), 0, st, A, B, C, M, N, K, lda,
+                       ldb, ldc, sA, sB, sC);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_nt_bf16(const bf16 *A, const bf16 *B, bf16 *C, int M, int N, int K,
                                int64_t lda, int64_t ldb, int64_t ldc, int batch, int64_t sA,
                                int64_t sB, int64_t sC, hipStream_t st) {
-    if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
-    hipError_t e = hipSuccess;
-    const RopeTail none{nullptr, nullptr, 0.0f, 0, 0, 0};
-    if (try_lds_gemm(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, none, st, &e)) return e;
-    dim3 grid((N + GB_N - 1) / GB_N, (M + GB_M - 1) / GB_M, batch);
-    hipLaunchKernelGGL(gemm_nt_bf16_kernel, grid, dim3(256), 0, st, A, B, C, M, N, K, lda, ldb,
-                       ldc, sA, sB, sC);
-    return hipGetLastError();
+    return launch_gemm_any<bf16>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, st);
+}
+
+hipError_t launch_gemm_nt_bf16_f16out(const bf16 *A, const bf16 *B, f16 *C, int M, int N, int K,
+                                      int64_t lda, int64_t ldb, int64_t ldc, int batch,
+                                      int64_t sA, int64_t sB, int64_t sC, hipStream_t st) {
+    return launch_gemm_any<f16>(A, B, C, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, st);
 }
 
 // Absorption: q_cat[t][h][:R] = wk_b[h] . q_nope[t][h] and the query RoPE into
@@ -387,7 +412,7 @@ hipError_t launch_absorb_bf16(const bf16 *q_nope, const bf16 *q_rope, const int3
     hipError_t e = hipSuccess;
     constexpr int FUSE_MAX_T = 64;
     if (T <= FUSE_MAX_T && Dr % 2 == 0 && R % 2 == 0 && ((uintptr_t)q_rope & 3) == 0 &&
-        try_lds_gemm(q_nope, wk_b, q_cat, T, R, Dn, (int64_t)H * Dn, Dn, (int64_t)H * W, H, Dn,
+        try_lds_gemm<bf16>(q_nope, wk_b, q_cat, T, R, Dn, (int64_t)H * Dn, Dn, (int64_t)H * W, H, Dn,
                      (int64_t)R * Dn, W, rope, st, &e))
         return e;
     e = launch_gemm_nt_bf16(q_nope, wk_b, q_cat, T, R, Dn, (int64_t)H * Dn, Dn, (int64_t)H * W, H,

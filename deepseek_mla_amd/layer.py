@@ -1,7 +1,9 @@
 """One absorbed-MLA layer step on the GPU, driven through the C ABI.
 
 A step is the whole path in the order of the absorption page, section 4:
-mla_absorb_q -> mla_attn_prefill (or mla_attn_decode) -> mla_out_proj.
+mla_absorb_q -> mla_attn_prefill (or mla_attn_decode) -> mla_out_proj.  A prefill step
+on the materialised path (section 8.4) is the single call mla_prefill_materialized
+(decompression, attention and wo).
 Buffers are allocated once with torch (device memory only); every computation runs
 in libmla.so.
 """
@@ -29,7 +31,10 @@ class LayerStep:
 
     def __init__(self, dims: synth.Dims, mode: str, kind: str, inputs: dict, n_kv: int,
                  scratch_cap_mib: int = 0, n_splits: int = 0, cache_copies: int = 1,
-                 device="cuda"):
+                 device="cuda", path: str = "absorbed"):
+        assert path in ("absorbed", "materialized")
+        assert path == "absorbed" or kind == "prefill"
+        self.path = path
         self.dims, self.mode, self.kind = dims, mode, kind
         self.act, self.kv = _MODE[mode]
         self.cdims = mla.make_dims(dims)
@@ -77,7 +82,10 @@ class LayerStep:
         self.out = torch.empty((self.T, D), dtype=tdt, device=device)
         self.prefill_ws = (mla.prefill_workspace(self.cdims, self.kv, self.T, n_kv,
                                                  scratch_cap_mib, device)
-                           if kind == "prefill" else None)
+                           if kind == "prefill" and path == "absorbed" else None)
+        self.mat_ws = (mla.materialized_workspace(self.cdims, self.T, n_kv, scratch_cap_mib,
+                                                  device)
+                       if path == "materialized" else None)
         if kind == "decode":
             self.n_kv_dev = torch.full((S,), n_kv, dtype=torch.int32, device=device)
             wsb = mla.mla_decode_workspace_bytes(self.cdims, S, n_kv, n_splits)
@@ -105,7 +113,19 @@ class LayerStep:
         mla.mla_out_proj(self.cdims, self.act, self.o_lat, self.wv_b, self.wo, self.v, self.out,
                          self.T, stream)
 
+    def materialized(self, stream=None):
+        self.cache = self.caches[self._ci]
+        self._ci = (self._ci + 1) % len(self.caches)
+        mla.mla_prefill_materialized(self.cdims, self.act, self.kv, self.q_nope, self.q_rope,
+                                     self.pos, self.T, self.cache, self.n_kv, self.wk_b,
+                                     self.wv_b, self.v, wo=self.wo, out=self.out, lse=self.lse,
+                                     scratch_cap_mib=self.scratch_cap_mib,
+                                     workspace=self.mat_ws, stream=stream)
+
     def step(self, stream=None):
+        if self.path == "materialized":
+            self.materialized(stream)
+            return
         self.absorb(stream)
         self.attend(stream)
         self.project(stream)
@@ -113,6 +133,8 @@ class LayerStep:
     def outputs(self) -> dict:
         """Host float32 copies of every stage's output."""
         f = lambda t: t.float().cpu().numpy()
+        if self.path == "materialized":
+            return {"lse": f(self.lse), "v": f(self.v), "out": f(self.out)}
         return {"q_cat": f(self.q_cat), "o_lat": f(self.o_lat), "lse": f(self.lse), "v": f(self.v),
                 "out": f(self.out)}
 

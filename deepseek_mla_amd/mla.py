@@ -19,7 +19,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 # Every symbol include/mla.h declares.
 EXPORTS = ("mla_absorb_q", "mla_attn_prefill", "mla_prefill_workspace_bytes",
            "mla_heads_per_chunk", "mla_decode_workspace_bytes",
-           "mla_decode_auto_splits", "mla_attn_decode", "mla_out_proj", "mla_cache_append",
+           "mla_decode_auto_splits", "mla_attn_decode", "mla_out_proj", "mla_prefill_materialized",
+           "mla_materialized_workspace_bytes", "mla_cache_append",
            "mla_quantize_q8_0", "mla_dequant_q8_0", "mla_q8_0_row_bytes", "mla_status_str")
 
 
@@ -65,6 +66,10 @@ def lib() -> ctypes.CDLL:
             "mla_attn_decode": ([D, ctypes.c_int, ctypes.c_int, vp, vp, i64, vp, i32, i32, i32,
                                  vp, vp, vp, sz, vp], ctypes.c_int),
             "mla_out_proj": ([D, ctypes.c_int, vp, vp, vp, vp, vp, i32, vp], ctypes.c_int),
+            "mla_prefill_materialized": ([D, ctypes.c_int, ctypes.c_int, vp, vp, vp, i32, vp, i32,
+                                          vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz, vp],
+                                         ctypes.c_int),
+            "mla_materialized_workspace_bytes": ([D, i32, i32, ctypes.c_uint32], sz),
             "mla_cache_append": ([D, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i32, vp, i64,
                                   vp], ctypes.c_int),
             "mla_quantize_q8_0": ([vp, vp, i64, i32, vp], ctypes.c_int),
@@ -163,6 +168,31 @@ def mla_attn_decode(dims, act, kv, q_cat, kv_cache, kv_seq_stride_bytes, n_kv, B
 def mla_out_proj(dims, act, o_lat, wv_b, wo, v_scratch, out, T, stream=None):
     _check(lib().mla_out_proj(_d(dims), act, _p(o_lat), _p(wv_b), _p(wo), _p(v_scratch), _p(out),
                               T, _s(stream)), "mla_out_proj")
+
+
+def mla_materialized_workspace_bytes(dims, T, n_kv, scratch_cap_mib=0):
+    return lib().mla_materialized_workspace_bytes(_d(dims), T, n_kv, scratch_cap_mib)
+
+
+def materialized_workspace(dims, T, n_kv, scratch_cap_mib=0, device="cuda"):
+    """A workspace of the size mla_prefill_materialized needs (256-byte aligned)."""
+    import torch
+    n = mla_materialized_workspace_bytes(dims, T, n_kv, scratch_cap_mib)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def mla_prefill_materialized(dims, act, kv, q_nope, q_rope, pos, T, kv_cache, n_kv, wk_b, wv_b,
+                             v_out, wo=None, out=None, lse=None, scratch_cap_mib=0,
+                             workspace=None, stream=None):
+    """workspace: a tensor from materialized_workspace() (allocated here when None)."""
+    if workspace is None:
+        workspace = materialized_workspace(dims, T, n_kv, scratch_cap_mib, q_nope.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().mla_prefill_materialized(_d(dims), act, kv, _p(q_nope), _p(q_rope), _p(pos), T,
+                                          _p(kv_cache), n_kv, _p(wk_b), _p(wv_b), _p(wo),
+                                          _p(v_out), _p(out), _p(lse), scratch_cap_mib,
+                                          _p(workspace), nbytes, _s(stream)),
+           "mla_prefill_materialized")
 
 
 def mla_cache_append(dims, act, kv, c_kv, k_rope, pos, T, cache, n_rows, dst_row=None,

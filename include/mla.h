@@ -168,6 +168,39 @@ int mla_out_proj(const mla_dims *dims, mla_dtype act, const void *o_lat, const v
 int mla_quantize_q8_0(const float *x, void *rows, int64_t n_rows, int32_t width, void *stream);
 int mla_dequant_q8_0(const void *rows, float *out, int64_t n_rows, int32_t width, void *stream);
 
+/* Materialised prefill (the pp_opt path, absorption page, section 8.4): the same
+ * attention as mla_absorb_q + mla_attn_prefill + mla_out_proj, computed the unabsorbed
+ * way for long prompts over long caches.  Per chunk of heads (the -amb rule of section
+ * 8.3 with the size of mla_attn_prefill) the keys and values are decompressed from the
+ * cache once:  k_nope[h][j] = wk_b[h]^T c_kv[j] (Dn),  v[h][j] = wv_b[h] c_kv[j] (Dv),
+ * then for every (t, h) and key j <= pos[t], j < n_kv:
+ *   s_j = scale * ([q_nope[t][h] | RoPE(q_rope[t][h], pos[t])] . [k_nope[h][j] | k_rope[j]])
+ *   v_out[t][h] = sum_j softmax(s)_j v[h][j],   lse[t][h] = log sum_j exp(s_j)
+ * and, when wo is given, out[t] = wo . v_out[t] (heads concatenated).  Equal to the
+ * absorbed chain by associativity (section 3); it needs 2(Dn+Dr+Dv) FLOP per visible
+ * (query, key, head) instead of 2(2R+Dr), plus the decompression.
+ * q_nope [T][H][Dn], q_rope [T][H][Dr] (pre-RoPE), pos [T] int32, kv_cache [n_kv][W],
+ * wk_b [H][R][Dn], wv_b [H][Dv][R], wo [D][H*Dv] or NULL, v_out [T][H*Dv], out [T][D] or
+ * NULL (both or neither of wo, out), lse [T][H] float32 or NULL.  Rows with no visible
+ * key get v_out = 0 and lse = -inf.
+ * workspace: at least mla_materialized_workspace_bytes(dims, T, n_kv, scratch_cap_mib)
+ * bytes of device memory, 256-byte aligned, contents need not be initialised; it holds
+ * the transposed wk_b, the rotated query rope and one head chunk's keys and values.
+ * Supported: act == kv == MLA_BF16, Dn 128, Dr 64, Dv 128, R % 8 == 0, scale > 0.
+ * Errors: INVALID_ARG (nulls, T < 0, n_kv < 1), UNSUPPORTED (other dtypes or dims),
+ * WORKSPACE (missing, too small or misaligned). */
+int mla_prefill_materialized(const mla_dims *dims, mla_dtype act, mla_dtype kv,
+                             const void *q_nope, const void *q_rope, const int32_t *pos,
+                             int32_t T, const void *kv_cache, int32_t n_kv, const void *wk_b,
+                             const void *wv_b, const void *wo, void *v_out, void *out, float *lse,
+                             uint32_t scratch_cap_mib, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* Workspace bytes of mla_prefill_materialized (0 for invalid or unsupported arguments).
+ * Host-only. */
+size_t mla_materialized_workspace_bytes(const mla_dims *dims, int32_t T, int32_t n_kv,
+                                        uint32_t scratch_cap_mib);
+
 /* Append new tokens to the latent cache (absorption page, section 4: the cache keeps
  * one row per token holding the compressed c_kv and the rotated shared key; section
  * 8.1: an 8-bit Q8_0 cache).  For token t:
