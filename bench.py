@@ -208,8 +208,54 @@ def cpu_baseline(w, max_queries):
             "sample": sample + "; full step, bytes = latent rows + q_cat + o_lat", "seconds": dt}
 
 
+def run_materialized(name, steps, warmup):
+    """The materialised prefill (one mla_prefill_materialized call per step: rotation of the
+    query rope, per head chunk the k_nope / v decompression and the attention, then wo)."""
+    import torch
+    from deepseek_mla_amd import accounting, layer, synth
+    base = name.split("@")[0]
+    w = synth.WORKLOADS[base]
+    assert w.kind == "prefill"
+    x = synth.generate_workload(w)
+    L = layer.for_workload(w, x, path="materialized")
+    del x
+    log(f"[bench] {name}: {steps} steps after {warmup} warmup")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        L.step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        L.step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    pos = L.pos.cpu().numpy()
+    del L
+    torch.cuda.empty_cache()
+    d = w.dims
+    pairs = accounting.visible_pairs(pos, w.n_kv)
+    attn = pairs * accounting.decompressed_flops_per_pair(d)
+    decomp = 2 * w.n_kv * d.kv_lora_rank * d.n_head * (d.qk_nope + d.v_head)
+    wo = 2 * len(pos) * d.d_model * d.n_head * d.v_head
+    absorbed = sum(step_flops(w, pos).values())
+    return {"workload": name, "path": "materialized (decompress k_nope / v, then 192/128 "
+                                      "causal attention)",
+            "ms_per_step": wall * 1e3, "call_ms": ms,
+            "flops_performed": {"attention": attn, "decompression": decomp, "wo": wo},
+            "performed_tflops": (attn + decomp + wo) / (ms * 1e-3) / 1e12,
+            "absorbed_equivalent_tflops": absorbed / (ms * 1e-3) / 1e12,
+            "note": "absorbed_equivalent_tflops prices the step with the absorbed path's "
+                    "FLOP count (the same result, 3.4x more attention FLOPs per pair)"}
+
+
 def run_one(name, steps, warmup, with_cpu, n_splits=0):
     from deepseek_mla_amd import synth
+    if name.endswith("@materialized"):
+        return run_materialized(name, steps, warmup)
     w = synth.WORKLOADS[name]
     copies = 1
     if w.kind == "decode":
@@ -263,7 +309,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="lite_prefill")
-    ap.add_argument("--extra", default="v3_decode,v3_long_prefill,v3_decode_q8",
+    ap.add_argument("--extra", default="v3_decode,v3_long_prefill,v3_decode_q8,"
+                                       "lite_prefill@materialized,v3_long_prefill@materialized",
                     help="comma-separated extra workloads reported under 'workloads' ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0,

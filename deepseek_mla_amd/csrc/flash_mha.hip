@@ -10,8 +10,8 @@
 // Heads run in chunks chosen by the -amb rule (section 8.3), which bounds the
 // decompressed keys and values held at once.
 //
-// flash_mha_kernel: a workgroup owns 32*NW query tokens of one head; wave w owns 32 of
-// them.  Keys stream through LDS in tiles of 64 (LDS-direct copies, three stages):
+// flash_mha_kernel<NW, NS>: a workgroup owns 32*NW query tokens of one head; wave w owns
+// 32 of them.  Keys stream through LDS in tiles of 64 (LDS-direct copies, NS stages):
 //   S^T[key][row] = K_tile (64 x 192) x Q^T          24 MFMA 32x32x16 per wave
 //   O^T[dv][row] += V^T_tile (128 x 64) x P^T        16 MFMA 32x32x16 per wave
 // The transposed products put one query row in each lane (lanes l and l^32 share it), so
@@ -19,8 +19,10 @@
 // a tile, LDS row m holds key m with bits 2 and 3 swapped: the score slots a lane then
 // holds are exactly the 8 consecutive keys the P^T operand of the value product needs,
 // so the weights go from the score registers into the value MFMA without an exchange.
-// Softmax: FlashAttention-2 recurrence in base 2 (running max, rescale of the 128-wide
-// accumulator when the max grows).
+// Softmax: FlashAttention-2 recurrence in base 2 with a lazy reference: a row's weights
+// are exp2(s - m) against a reference m that is raised (and the 128-wide accumulator and
+// the denominator rescaled) only when a score exceeds it by more than 2^8, so weights
+// stay below 256 (well inside binary16) and most tiles skip the rescale.
 //
 // Precision: the decompressed keys and values, the weights P and the query's nope part
 // are held in binary16 (11 significant bits; the cache, the rope parts and all inputs
@@ -28,9 +30,16 @@
 // about 4x further from the exact one than with none at all, with binary16 it stays at
 // the rounding of the stored output.  Values beyond binary16's range (|x| > 65504) in
 // q_nope or in a decompressed key or value are outside this path's domain.
-#include "lds_dma.h"
+#include "latent_tile.h"  // static_for, lds_copy16
 
 #include <algorithm>
+
+#ifndef MH_NW
+#define MH_NW 8  // waves per workgroup
+#endif
+#ifndef MH_NS
+#define MH_NS 3  // LDS stages
+#endif
 
 namespace mla {
 
@@ -41,12 +50,10 @@ constexpr int KN_BYTES = NK * DN * 2;          // 16384: k_nope rows, 256 B each
 constexpr int KR_BYTES = NK * DR * 2;          // 8192: k_rope rows, 128 B each
 constexpr int VT_BYTES = DV * NK * 2;          // 16384: V^T rows (one per dv), 128 B each
 constexpr int STAGE = KN_BYTES + KR_BYTES + VT_BYTES;  // 40960
-constexpr int NS = 3;                          // stages
-constexpr int NW = 8;                          // waves per workgroup
-constexpr int ROWS = 32 * NW;                  // query tokens per workgroup
-constexpr int PER_WAVE = 5;                    // copy instructions per wave per tile
+constexpr int COPIES = (KN_BYTES + KR_BYTES + VT_BYTES) / 1024;  // 40 copy instructions per tile
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+constexpr float TAU = 8.0f;                    // weights exp2(s - m) stay <= 2^TAU
 }  // namespace mh
 
 // LDS row of key k within a tile (bits 2 and 3 swapped; an involution).
@@ -60,37 +67,41 @@ __device__ __forceinline__ int mh_perm(int k) {
 __device__ __forceinline__ int kn_off(int m, int c) { return m * 256 + ((c ^ (m & 15)) << 4); }
 __device__ __forceinline__ int h8_off(int m, int c) { return m * 128 + ((c ^ ((m >> 1) & 7)) << 4); }
 
-// Issue the 5 copy instructions of wave w for the tile of keys key0 .. key0+63 into stage
-// dst.  Keys past `last` re-read row `last` (k_nope, k_rope); V^T rows are padded with
-// zeros up to a multiple of 64 keys, so whole tiles are always in bounds.
+// Issue the 40/NW copy instructions of wave w for the tile of keys key0 .. key0+63 into
+// stage dst.  Keys past `last` re-read row `last` (k_nope, k_rope); V^T rows are padded
+// with zeros up to a multiple of 64 keys, so whole tiles are always in bounds.
+template <int NW>
 __device__ __forceinline__ void mh_issue_tile(const uint8_t *kn, const uint8_t *cache,
                                               int64_t row_bytes, int rope_off, const uint8_t *vt,
                                               int64_t vt_pitch, int key0, int last,
                                               uint32_t dst, int w) {
+    static_assert(NW == 4 || NW == 8, "copies split evenly over the waves");
     const int l = threadIdx.x & 63;
-    // k_nope: instructions 2w, 2w+1 cover LDS rows 4i .. 4i+3
+    // k_nope: instructions i = (16/NW) w + j cover LDS rows 4i .. 4i+3
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int i = 2 * w + j;
+    for (int j = 0; j < 16 / NW; ++j) {
+        const int i = (16 / NW) * w + j;
         const int m = 4 * i + (l >> 4), s = l & 15;
         const int c = s ^ (m & 15);
         const int key = min(key0 + mh_perm(m), last);
         lds_copy16(kn + (int64_t)key0 * 256, (uint32_t)((key - key0) * 256 + c * 16),
                    dst + i * 1024);
     }
-    // k_rope: instruction w covers LDS rows 8w .. 8w+7 (from the cache rows)
-    {
-        const int m = 8 * w + (l >> 3), s = l & 7;
+    // k_rope: instructions i = (8/NW) w + j cover LDS rows 8i .. 8i+7 (from the cache rows)
+#pragma unroll
+    for (int j = 0; j < 8 / NW; ++j) {
+        const int i = (8 / NW) * w + j;
+        const int m = 8 * i + (l >> 3), s = l & 7;
         const int c = s ^ ((m >> 1) & 7);
         const int key = min(key0 + mh_perm(m), last);
         lds_copy16(cache + (int64_t)key0 * row_bytes,
                    (uint32_t)((int64_t)(key - key0) * row_bytes + rope_off + c * 16),
-                   dst + mh::KN_BYTES + w * 1024);
+                   dst + mh::KN_BYTES + i * 1024);
     }
-    // V^T: instructions 2w, 2w+1 cover dv rows 8i .. 8i+7 (keys key0 .. key0+63)
+    // V^T: instructions i = (16/NW) w + j cover dv rows 8i .. 8i+7 (keys key0 .. key0+63)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int i = 2 * w + j;
+    for (int j = 0; j < 16 / NW; ++j) {
+        const int i = (16 / NW) * w + j;
         const int dv = 8 * i + (l >> 3), s = l & 7;
         const int c = s ^ ((dv >> 1) & 7);
         lds_copy16(vt + (int64_t)key0 * 2, (uint32_t)(dv * vt_pitch + c * 16),
@@ -102,19 +113,21 @@ __device__ __forceinline__ void mh_issue_tile(const uint8_t *kn, const uint8_t *
 // (vt_len a multiple of 64, zero past n_kv), q_nope [T][H][128], q_rope_rot [T][H][64]
 // (already rotated), cache rows of row_bytes with k_rope at rope_off.  Writes
 // v_out[t][h*128 ..] (bf16, normalised) and lse[t][h] (natural log) for h = h0 + chunk head.
-__global__ __launch_bounds__(512) void flash_mha_kernel(
+template <int NW, int NS>
+__global__ __launch_bounds__(64 * NW) void flash_mha_kernel(
     const bf16 *__restrict__ q_nope, const bf16 *__restrict__ q_rope_rot,
     const int32_t *__restrict__ pos, int T, int H, int h0, int hc,
     const uint8_t *__restrict__ kn_all, const uint8_t *__restrict__ cache, int64_t row_bytes,
     int rope_off, const uint8_t *__restrict__ vt_all, int vt_len, int n_kv, float sc,
     bf16 *__restrict__ v_out, float *__restrict__ lse) {
+    constexpr int ROWS = 32 * NW;                 // query tokens per workgroup
+    constexpr int PER_WAVE = mh::COPIES / NW;     // copy instructions per wave per tile
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
     uint8_t MLA_LDS *lds = (uint8_t MLA_LDS *)smem_raw;
-    int *red = (int *)(smem_raw + mh::NS * mh::STAGE);  // [NW] wave key bounds
 
     // block -> (head, token block): the blocks of one head share an XCD (block ids go
     // round-robin over the 8 XCDs) when hc is a multiple of 8; heaviest blocks first.
-    const int nqb = (T + mh::ROWS - 1) / mh::ROWS;
+    const int nqb = (T + ROWS - 1) / ROWS;
     const int L = blockIdx.x;
     int hh, qr;
     if (hc % 8 == 0) {
@@ -128,7 +141,7 @@ __global__ __launch_bounds__(512) void flash_mha_kernel(
     const int h = h0 + hh;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = threadIdx.x & 63, hi = l >> 5, r = l & 31;
-    const int t = qb * mh::ROWS + 32 * w + r;
+    const int t = qb * ROWS + 32 * w + r;
     const bool valid = t < T;
     const int tq = valid ? t : T - 1;
     int lim = valid ? min(pos[tq], n_kv - 1) : -1;
@@ -148,8 +161,16 @@ __global__ __launch_bounds__(512) void flash_mha_kernel(
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) qr16[kk] = *(const bf16x8 *)(qp + kk * 16);
     }
-    // key bounds: wave max / min of the row limits, then the workgroup max
-    int wmax = lim, wmin = valid ? lim : INT32_MAX;
+    // key bounds: wave max / min of the row limits; every wave also reduces the limits of
+    // all the workgroup's rows (lane l reads rows l, l + 64, ...) for the key range
+    int wmax = lim, wmin = valid ? lim : INT32_MAX, gmax = -1;
+#pragma unroll
+    for (int i = 0; i < NW / 2; ++i) {
+        const int tt = qb * ROWS + 64 * i + l;
+        if (tt < T) gmax = max(gmax, min(pos[tt], n_kv - 1));
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) gmax = max(gmax, __shfl_xor(gmax, o));
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) {
         wmax = max(wmax, __shfl_xor(wmax, o));
@@ -157,12 +178,7 @@ __global__ __launch_bounds__(512) void flash_mha_kernel(
     }
     wmax = __builtin_amdgcn_readfirstlane(wmax);
     wmin = __builtin_amdgcn_readfirstlane(wmin);
-    if (l == 0) red[w] = wmax;
-    __syncthreads();
-    int kend = -1;
-#pragma unroll
-    for (int i = 0; i < mh::NW; ++i) kend = max(kend, red[i]);
-    kend += 1;  // keys [0, kend) are visible to some row of the workgroup
+    const int kend = __builtin_amdgcn_readfirstlane(gmax) + 1;  // keys [0, kend) are seen
     const int ntiles = (kend + mh::NK - 1) / mh::NK;
 
     const uint8_t *kn = kn_all + (int64_t)hh * n_kv * mh::DN * 2;
@@ -170,6 +186,21 @@ __global__ __launch_bounds__(512) void flash_mha_kernel(
     const int64_t vt_pitch = (int64_t)vt_len * 2;
     const int last = n_kv - 1;
     const uint32_t lbase = lds_u32(lds);
+
+    // per-lane LDS offsets within a stage: K fragment of step kk (block j adds 8192 for
+    // k_nope, 4096 for k_rope), V^T fragment of key step ks (dv block nb adds 4096)
+    uint32_t koff[12], voff[4];
+#pragma unroll
+    for (int kk = 0; kk < 12; ++kk) {
+        koff[kk] = kk < 8 ? (uint32_t)kn_off(r, 2 * kk + hi)
+                          : (uint32_t)(mh::KN_BYTES + h8_off(r, 2 * (kk - 8) + hi));
+        asm volatile("" : "+v"(koff[kk]));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        voff[ks] = (uint32_t)(mh::KN_BYTES + mh::KR_BYTES + h8_off(r, 2 * ks + hi));
+        asm volatile("" : "+v"(voff[ks]));
+    }
 
     f32x16 o[4];
 #pragma unroll
@@ -180,60 +211,74 @@ __global__ __launch_bounds__(512) void flash_mha_kernel(
 
     // the query and bound loads must be complete before the copies (their completion is
     // tracked by counting outstanding vector-memory operations)
+    // Copies run NS-1 tiles ahead.
+    static_assert(NS == 2 || NS == 3, "one or two tiles in flight");
+    constexpr int DEPTH = NS - 1;
     MLA_WAIT_VMCNT(0);
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < DEPTH; ++s)
         if (s < ntiles)
-            mh_issue_tile(kn, cache, row_bytes, rope_off, vt, vt_pitch, s * mh::NK, last,
-                          lbase + s * mh::STAGE, w);
+            mh_issue_tile<NW>(kn, cache, row_bytes, rope_off, vt, vt_pitch, s * mh::NK, last,
+                              lbase + s * mh::STAGE, w);
 
     for (int ti = 0; ti < ntiles; ++ti) {
-        if (ti + 1 < ntiles) {
-            MLA_WAIT_VMCNT(mh::PER_WAVE);
+        // tile ti landed (with more than one tile in flight, tile ti+1 may not have)
+        if (DEPTH > 1 && ti + 1 < ntiles) {
+            MLA_WAIT_VMCNT(PER_WAVE);
         } else {
             MLA_WAIT_VMCNT(0);
         }
-        __syncthreads();
-        if (ti + 2 < ntiles)
-            mh_issue_tile(kn, cache, row_bytes, rope_off, vt, vt_pitch, (ti + 2) * mh::NK, last,
-                          lbase + ((ti + 2) % mh::NS) * mh::STAGE, w);
+        __syncthreads();  // tile ti landed everywhere; stages of tiles before ti-1 are free
+        if (ti + DEPTH < ntiles)
+            mh_issue_tile<NW>(kn, cache, row_bytes, rope_off, vt, vt_pitch, (ti + DEPTH) * mh::NK,
+                              last, lbase + ((ti + DEPTH) % NS) * mh::STAGE, w);
         const int key0 = ti * mh::NK;
         if (key0 > wmax) continue;  // no row of this wave sees these keys
-        const uint8_t MLA_LDS *st = lds + (ti % mh::NS) * mh::STAGE;
-        const uint8_t MLA_LDS *skn = st;
-        const uint8_t MLA_LDS *skr = st + mh::KN_BYTES;
-        const uint8_t MLA_LDS *svt = st + mh::KN_BYTES + mh::KR_BYTES;
+        const uint8_t MLA_LDS *st = lds + (ti % NS) * mh::STAGE;
 
         // scores: two 32-key blocks, slot e of block j is key
-        // key0 + 32j + 16(e>>3) + 8hi + (e&7)
+        // key0 + 32j + 16(e>>3) + 8hi + (e&7).  Step i = (kk, j) = (i/2, i%2); the K
+        // fragment of step i + SA is read right after the MFMA of step i.
+        // Masked keys ride on the chain's starting value: -inf stays -inf through every
+        // finite product (edge tiles only); other tiles start from the constant 0.
+        constexpr int SA = 6;
+        auto kfrag = [&](int i) -> u32x4 {
+            const int kk = i >> 1, j = i & 1;
+            return *(const u32x4 MLA_LDS *)(st + koff[kk] + (kk < 8 ? 8192 : 4096) * j);
+        };
+        u32x4 ring[SA];
+#pragma unroll
+        for (int i = 0; i < SA; ++i) ring[i] = kfrag(i);
         f32x16 s[2];
         const bool edge = key0 + mh::NK - 1 > wmin;
+        static_for<24>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int kk = i >> 1, j = i & 1;
+            const u32x4 a = ring[i % SA];
+            if constexpr (kk == 0) {
+                if (edge) {
+                    f32x16 b;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            if (edge) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    s[j][e] = (key0 + 32 * j + 16 * (e >> 3) + 8 * hi + (e & 7) <= lim) ? 0.0f
+                    for (int e = 0; e < 16; ++e)
+                        b[e] = (key0 + 32 * j + 16 * (e >> 3) + 8 * hi + (e & 7) <= lim) ? 0.0f
                                                                                          : -INFINITY;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) s[j][e] = 0.0f;
-            }
-        }
-#pragma unroll
-        for (int kk = 0; kk < 12; ++kk) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int mrow = 32 * j + r;
-                if (kk < 8) {
-                    const f16x8 a = *(const f16x8 MLA_LDS *)(skn + kn_off(mrow, 2 * kk + hi));
-                    s[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qn16[kk], s[j], 0, 0, 0);
+                    s[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                                  qn16[0], b, 0, 0, 0);
                 } else {
-                    const bf16x8 a = *(const bf16x8 MLA_LDS *)(skr + h8_off(mrow, 2 * (kk - 8) + hi));
-                    s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr16[kk - 8], s[j], 0, 0, 0);
+                    const f32x16 z = {};
+                    s[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                                  qn16[0], z, 0, 0, 0);
                 }
+            } else if constexpr (kk < 8) {
+                s[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                              qn16[kk], s[j], 0, 0, 0);
+            } else {
+                s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                               qr16[kk - 8], s[j], 0, 0, 0);
             }
-        }
+            if constexpr (i + SA < 24) ring[i % SA] = kfrag(i + SA);
+            __builtin_amdgcn_sched_barrier(0);
+        });
         // online softmax (base 2): running max over the row (this lane's 32 slots and the
         // partner lane's), rescale when it grows
         float tmax = -INFINITY;
@@ -245,17 +290,18 @@ __global__ __launch_bounds__(512) void flash_mha_kernel(
             const float y = __shfl_xor(tmax, 32);
             tmax = hi ? fmaxf(y, tmax) : fmaxf(tmax, y);
         }
-        const float mnew = fmaxf(m, tmax * sc);
-        const float nmu = (mnew == -INFINITY) ? 0.0f : -mnew;
-        if (__builtin_amdgcn_ballot_w64(mnew > m)) {
-            const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);
+        tmax *= sc;
+        if (__builtin_amdgcn_ballot_w64(tmax > m + mh::TAU)) {  // also a row's first keys
+            const float mnew = tmax > m + mh::TAU ? tmax : m;
+            const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // 0 when m = -inf
             lsum *= alpha;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) o[nb][e] *= alpha;
+            m = mnew;
         }
-        m = mnew;
+        const float nmu = (m == -INFINITY) ? 0.0f : -m;
         f16x8 p[4];  // p[ks]: keys key0 + 16ks + 8hi .. +7
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -270,7 +316,7 @@ __global__ __launch_bounds__(512) void flash_mha_kernel(
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
-                const f16x8 a = *(const f16x8 MLA_LDS *)(svt + h8_off(32 * nb + r, 2 * ks + hi));
+                const f16x8 a = *(const f16x8 MLA_LDS *)(st + voff[ks] + 4096 * nb);
                 o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, p[ks], o[nb], 0, 0, 0);
             }
     }
@@ -353,15 +399,16 @@ hipError_t launch_prefill_materialized(const bf16 *q_nope, const bf16 *q_rope, c
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_rope_q<bf16>(q_rope, pos, qr, T, H, 0, DR, rope_base, st)) != hipSuccess)
         return e;
-    const size_t shm = (size_t)NS * STAGE + 64;
+    constexpr int KNW = MH_NW, KNS = MH_NS;
+    const size_t shm = (size_t)KNS * STAGE;
     static bool attr_set = false;  // per process; every device takes the same value
     if (!attr_set) {
-        e = hipFuncSetAttribute((const void *)flash_mha_kernel,
+        e = hipFuncSetAttribute((const void *)flash_mha_kernel<KNW, KNS>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int nqb = (T + ROWS - 1) / ROWS;
+    const int nqb = (T + 32 * KNW - 1) / (32 * KNW);
     for (int h0 = 0; h0 < H; h0 += hc) {
         const int nh = std::min(hc, H - h0);
         // k_nope[i][j][d] = sum_l c_kv[j][l] wk_b[h0+i][l][d]
@@ -378,7 +425,8 @@ hipError_t launch_prefill_materialized(const bf16 *q_nope, const bf16 *q_rope, c
                                st, vt, (int64_t)nh * DV, vt_len, n_kv);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        hipLaunchKernelGGL(flash_mha_kernel, dim3(nqb * nh), dim3(64 * NW), shm, st, q_nope, qr,
+        hipLaunchKernelGGL((flash_mha_kernel<KNW, KNS>), dim3(nqb * nh), dim3(64 * KNW), shm, st,
+                           q_nope, qr,
                            pos, T, H, h0, nh, (const uint8_t *)kn, (const uint8_t *)cache,
                            (int64_t)W * 2, R * 2, (const uint8_t *)vt, vt_len, n_kv,
                            scale * LOG2E, v_out, lse);
