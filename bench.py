@@ -153,21 +153,30 @@ def time_append(w, L, reps):
 
     for _ in range(3):
         run()
+    def run_had():
+        mla.mla_cache_append_hadamard(L.cdims, L.act, L.kv, c_kv, k_rope, pos, n_new, cache,
+                                      n_rows, dst_row=dst, stream=stream)
+
     reps = max(reps, 20)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(reps):
-        run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / reps
     in_b = 4 if w.mode == "f32" else 2
     nbytes = n_new * (W * in_b + 4 + (8 if dst is not None else 0) + L.row_bytes)
-    return {"kernel": "cache_append_kernel", "tokens": n_new, "us_per_launch": us,
-            "bytes_per_launch": nbytes, "GB/s": nbytes / (us * 1e-6) / 1e9,
-            "frac_hbm": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-            "bytes": "per token: c_kv + k_rope inputs, pos (+ dst_row), one cache row"}
+    res = {"kernel": "cache_append_kernel", "tokens": n_new, "bytes_per_launch": nbytes,
+           "bytes": "per token: c_kv + k_rope inputs, pos (+ dst_row), one cache row"}
+    for key, fn in (("", run), ("hadamard_", run_had)):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        res[key + "us_per_launch"] = us
+        res[key + "GB/s"] = nbytes / (us * 1e-6) / 1e9
+    res["frac_hbm"] = res["GB/s"] / HBM_PEAK_GBS
+    return res
 
 
 def cpu_baseline(w, max_queries):

@@ -330,9 +330,11 @@ int mla_prefill_materialized(const mla_dims *d, mla_dtype act, mla_dtype kv, con
     return hip_status(e);
 }
 
-int mla_cache_append(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *c_kv,
-                     const void *k_rope, const int32_t *pos, const int64_t *dst_row, int32_t T,
-                     void *cache, int64_t n_rows, void *stream) {
+static bool pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
+
+static int cache_append_impl(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *c_kv,
+                             const void *k_rope, const int32_t *pos, const int64_t *dst_row,
+                             int32_t T, void *cache, int64_t n_rows, bool hadamard, void *stream) {
     if (!dims_ok(d) || !act_ok(act) || T < 0 || n_rows < 0) return MLA_ERR_INVALID_ARG;
     if (kv != MLA_F32 && kv != MLA_BF16 && kv != MLA_Q8_0) return MLA_ERR_INVALID_ARG;
     if (kv != MLA_Q8_0 && kv != act) return MLA_ERR_INVALID_ARG;
@@ -345,10 +347,43 @@ int mla_cache_append(const mla_dims *d, mla_dtype act, mla_dtype kv, const void 
     hipError_t e;
     if (act == MLA_F32)
         e = launch_cache_append<float>((const float *)c_kv, (const float *)k_rope, pos, dst_row, T,
-                                       R, Dr, d->rope_base, kv, cache, n_rows, st);
+                                       R, Dr, d->rope_base, kv, hadamard, cache, n_rows, st);
     else
         e = launch_cache_append<bf16>((const bf16 *)c_kv, (const bf16 *)k_rope, pos, dst_row, T, R,
-                                      Dr, d->rope_base, kv, cache, n_rows, st);
+                                      Dr, d->rope_base, kv, hadamard, cache, n_rows, st);
+    return hip_status(e);
+}
+
+int mla_cache_append(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *c_kv,
+                     const void *k_rope, const int32_t *pos, const int64_t *dst_row, int32_t T,
+                     void *cache, int64_t n_rows, void *stream) {
+    return cache_append_impl(d, act, kv, c_kv, k_rope, pos, dst_row, T, cache, n_rows, false,
+                             stream);
+}
+
+int mla_cache_append_hadamard(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *c_kv,
+                              const void *k_rope, const int32_t *pos, const int64_t *dst_row,
+                              int32_t T, void *cache, int64_t n_rows, void *stream) {
+    if (!d || !pow2(d->kv_lora_rank)) return MLA_ERR_INVALID_ARG;
+    return cache_append_impl(d, act, kv, c_kv, k_rope, pos, dst_row, T, cache, n_rows, true,
+                             stream);
+}
+
+int mla_hadamard_weights(const mla_dims *d, mla_dtype act, const void *wk_b, const void *wv_b,
+                         void *wk_b_rot, void *wv_b_rot, void *stream) {
+    if (!dims_ok(d) || !act_ok(act) || !pow2(d->kv_lora_rank)) return MLA_ERR_INVALID_ARG;
+    if (!wk_b || !wv_b || !wk_b_rot || !wv_b_rot) return MLA_ERR_INVALID_ARG;
+    if (wk_b == wk_b_rot || wv_b == wv_b_rot) return MLA_ERR_INVALID_ARG;
+    if (d->kv_lora_rank > 16384) return MLA_ERR_UNSUPPORTED;
+    hipStream_t st = as_stream(stream);
+    const int H = d->n_head, R = d->kv_lora_rank, Dn = d->qk_nope, Dv = d->v_head;
+    hipError_t e;
+    if (act == MLA_F32)
+        e = launch_hadamard_weights<float>((const float *)wk_b, (const float *)wv_b,
+                                           (float *)wk_b_rot, (float *)wv_b_rot, H, R, Dn, Dv, st);
+    else
+        e = launch_hadamard_weights<bf16>((const bf16 *)wk_b, (const bf16 *)wv_b, (bf16 *)wk_b_rot,
+                                          (bf16 *)wv_b_rot, H, R, Dn, Dv, st);
     return hip_status(e);
 }
 

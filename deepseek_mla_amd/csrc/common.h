@@ -67,7 +67,10 @@ hipError_t launch_dequant_q8_0(const uint8_t *rows, float *out, int64_t n_rows, 
 template <typename TI>
 hipError_t launch_cache_append(const TI *c_kv, const TI *k_rope, const int32_t *pos,
                                const int64_t *dst_row, int T, int R, int Dr, float base, int kv,
-                               void *cache, int64_t n_rows, hipStream_t st);
+                               bool hadamard, void *cache, int64_t n_rows, hipStream_t st);
+template <typename T>
+hipError_t launch_hadamard_weights(const T *wk_b, const T *wv_b, T *wk_b_rot, T *wv_b_rot, int H,
+                                   int R, int Dn, int Dv, hipStream_t st);
 hipError_t launch_absorb_bf16(const bf16 *q_nope, const bf16 *q_rope, const int32_t *pos,
                               const bf16 *wk_b, bf16 *q_cat, int T, int H, int R, int Dn, int Dr,
                               float base, hipStream_t st);

@@ -515,13 +515,70 @@ hipError_t launch_dequant_q8_0(const uint8_t *rows, float *out, int64_t n_rows, 
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------ Walsh-Hadamard rotation
+// H (n = 2^k) is the normalised Sylvester matrix of the page "llama.cpp KV cache", section
+// 3.1: H[i][j] = (-1)^popcount(i & j) / sqrt(n), symmetric and orthonormal (H H = I).
+// y = H x by the fast transform: k butterfly stages (a, b) -> (a + b, a - b) over
+// element pairs 2^s apart, then the 1/sqrt(n) scale; float32 throughout.  x is in LDS and
+// every thread of the block takes part (the stages are separated by barriers).
+__device__ __forceinline__ void fwht_lds(float *x, int n) {
+    for (int h = 1; h < n; h <<= 1) {
+        __syncthreads();
+        for (int q = threadIdx.x; q < n / 2; q += blockDim.x) {
+            const int i = (q / h) * 2 * h + (q % h);
+            const float a = x[i], b = x[i + h];
+            x[i] = a + b;
+            x[i + h] = a - b;
+        }
+    }
+    __syncthreads();
+    const float sc = rsqrtf((float)n);
+    for (int i = threadIdx.x; i < n; i += blockDim.x) x[i] *= sc;
+    __syncthreads();
+}
+
+// out vector v = H . (in vector v), vector v's element i at
+// (v / inner) * outer + (v % inner) + i * step (the same offsets in `in` and `out`).
+template <typename T>
+__global__ __launch_bounds__(256) void hadamard_vectors_kernel(const T *__restrict__ in,
+                                                               T *__restrict__ out, int n,
+                                                               int64_t inner, int64_t outer,
+                                                               int64_t step) {
+    extern __shared__ float hv[];
+    const int64_t v = blockIdx.x;
+    const int64_t base = (v / inner) * outer + (v % inner);
+    for (int i = threadIdx.x; i < n; i += blockDim.x) hv[i] = ld_f(in + base + i * step);
+    fwht_lds(hv, n);
+    for (int i = threadIdx.x; i < n; i += blockDim.x) st_f(out + base + i * step, hv[i]);
+}
+
+template <typename T>
+hipError_t launch_hadamard_weights(const T *wk_b, const T *wv_b, T *wk_b_rot, T *wv_b_rot, int H,
+                                   int R, int Dn, int Dv, hipStream_t st) {
+    const size_t shm = sizeof(float) * (size_t)R;
+    // wk_b[h] is [R][Dn]: column d of head h (stride Dn) -> H . column
+    hipLaunchKernelGGL(hadamard_vectors_kernel<T>, dim3((unsigned)H * Dn), dim3(256), shm, st, wk_b,
+                       wk_b_rot, R, (int64_t)Dn, (int64_t)R * Dn, (int64_t)Dn);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // wv_b[h] is [Dv][R]: each row (contiguous) -> row . H = (H . row^T)^T (H symmetric)
+    hipLaunchKernelGGL(hadamard_vectors_kernel<T>, dim3((unsigned)H * Dv), dim3(256), shm, st, wv_b,
+                       wv_b_rot, R, (int64_t)1, (int64_t)R, (int64_t)1);
+    return hipGetLastError();
+}
+template hipError_t launch_hadamard_weights<float>(const float *, const float *, float *, float *,
+                                                   int, int, int, int, hipStream_t);
+template hipError_t launch_hadamard_weights<bf16>(const bf16 *, const bf16 *, bf16 *, bf16 *, int,
+                                                  int, int, int, hipStream_t);
+
 // ------------------------------------------------------------ latent cache append
 // Row pos[t] of the cache <- [c_kv[t] (R) | RoPE(k_rope[t], pos[t]) (Dr)], stored as
 // float32, bfloat16 (rounded to nearest even) or Q8_0 (the block quantiser above).  The
 // rotation is the query's (rope_cs, adjacent pairs).  The destination row is row[t], or
 // pos[t] when row is null; tokens whose destination lies outside [0, n_rows) are skipped.
+// HAD: the c_kv part is rotated by H (fwht_lds) before it is stored.
 // One wave per token; the row is assembled in LDS as float32, then stored.
-template <typename TI, int KV>
+template <typename TI, int KV, bool HAD>
 __global__ __launch_bounds__(64) void cache_append_kernel(const TI *__restrict__ c_kv,
                                                           const TI *__restrict__ k_rope,
                                                           const int32_t *__restrict__ pos,
@@ -543,6 +600,7 @@ __global__ __launch_bounds__(64) void cache_append_kernel(const TI *__restrict__
         row[R + 2 * i] = fmaf(a, c, -b * s);
         row[R + 2 * i + 1] = fmaf(a, s, b * c);
     }
+    if constexpr (HAD) fwht_lds(row, R);  // ends on a barrier
     __syncthreads();
     if constexpr (KV == MLA_F32) {
         float *dst = (float *)cache + r * W;
@@ -556,28 +614,39 @@ __global__ __launch_bounds__(64) void cache_append_kernel(const TI *__restrict__
     }
 }
 
+template <typename TI, bool HAD>
+static void launch_append_kv(const TI *c_kv, const TI *k_rope, const int32_t *pos,
+                             const int64_t *dst_row, int T, int R, int Dr, float base, int kv,
+                             void *cache, int64_t n_rows, hipStream_t st) {
+    const size_t shm = sizeof(float) * (size_t)(R + Dr);
+    if (kv == MLA_F32)
+        hipLaunchKernelGGL((cache_append_kernel<TI, MLA_F32, HAD>), dim3(T), dim3(64), shm, st,
+                           c_kv, k_rope, pos, dst_row, R, Dr, base, cache, n_rows);
+    else if (kv == MLA_BF16)
+        hipLaunchKernelGGL((cache_append_kernel<TI, MLA_BF16, HAD>), dim3(T), dim3(64), shm, st,
+                           c_kv, k_rope, pos, dst_row, R, Dr, base, cache, n_rows);
+    else
+        hipLaunchKernelGGL((cache_append_kernel<TI, MLA_Q8_0, HAD>), dim3(T), dim3(64), shm, st,
+                           c_kv, k_rope, pos, dst_row, R, Dr, base, cache, n_rows);
+}
+
 template <typename TI>
 hipError_t launch_cache_append(const TI *c_kv, const TI *k_rope, const int32_t *pos,
                                const int64_t *dst_row, int T, int R, int Dr, float base, int kv,
-                               void *cache, int64_t n_rows, hipStream_t st) {
+                               bool hadamard, void *cache, int64_t n_rows, hipStream_t st) {
     if (T <= 0) return hipSuccess;
-    const size_t shm = sizeof(float) * (size_t)(R + Dr);
-    if (kv == MLA_F32)
-        hipLaunchKernelGGL((cache_append_kernel<TI, MLA_F32>), dim3(T), dim3(64), shm, st, c_kv,
-                           k_rope, pos, dst_row, R, Dr, base, cache, n_rows);
-    else if (kv == MLA_BF16)
-        hipLaunchKernelGGL((cache_append_kernel<TI, MLA_BF16>), dim3(T), dim3(64), shm, st, c_kv,
-                           k_rope, pos, dst_row, R, Dr, base, cache, n_rows);
+    if (hadamard)
+        launch_append_kv<TI, true>(c_kv, k_rope, pos, dst_row, T, R, Dr, base, kv, cache, n_rows, st);
     else
-        hipLaunchKernelGGL((cache_append_kernel<TI, MLA_Q8_0>), dim3(T), dim3(64), shm, st, c_kv,
-                           k_rope, pos, dst_row, R, Dr, base, cache, n_rows);
+        launch_append_kv<TI, false>(c_kv, k_rope, pos, dst_row, T, R, Dr, base, kv, cache, n_rows,
+                                    st);
     return hipGetLastError();
 }
 template hipError_t launch_cache_append<float>(const float *, const float *, const int32_t *,
-                                               const int64_t *, int, int, int, float, int, void *,
-                                               int64_t, hipStream_t);
+                                               const int64_t *, int, int, int, float, int, bool,
+                                               void *, int64_t, hipStream_t);
 template hipError_t launch_cache_append<bf16>(const bf16 *, const bf16 *, const int32_t *,
-                                              const int64_t *, int, int, int, float, int, void *,
-                                              int64_t, hipStream_t);
+                                              const int64_t *, int, int, int, float, int, bool,
+                                              void *, int64_t, hipStream_t);
 
 }  // namespace mla

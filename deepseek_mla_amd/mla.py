@@ -21,6 +21,7 @@ EXPORTS = ("mla_absorb_q", "mla_attn_prefill", "mla_prefill_workspace_bytes",
            "mla_heads_per_chunk", "mla_decode_workspace_bytes",
            "mla_decode_auto_splits", "mla_attn_decode", "mla_out_proj", "mla_prefill_materialized",
            "mla_materialized_workspace_bytes", "mla_cache_append",
+           "mla_cache_append_hadamard", "mla_hadamard_weights",
            "mla_quantize_q8_0", "mla_dequant_q8_0", "mla_q8_0_row_bytes", "mla_status_str")
 
 
@@ -70,6 +71,9 @@ def lib() -> ctypes.CDLL:
                                           vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz, vp],
                                          ctypes.c_int),
             "mla_materialized_workspace_bytes": ([D, i32, i32, ctypes.c_uint32], sz),
+            "mla_cache_append_hadamard": ([D, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i32, vp,
+                                           i64, vp], ctypes.c_int),
+            "mla_hadamard_weights": ([D, ctypes.c_int, vp, vp, vp, vp, vp], ctypes.c_int),
             "mla_cache_append": ([D, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i32, vp, i64,
                                   vp], ctypes.c_int),
             "mla_quantize_q8_0": ([vp, vp, i64, i32, vp], ctypes.c_int),
@@ -199,6 +203,18 @@ def mla_cache_append(dims, act, kv, c_kv, k_rope, pos, T, cache, n_rows, dst_row
                      stream=None):
     _check(lib().mla_cache_append(_d(dims), act, kv, _p(c_kv), _p(k_rope), _p(pos), _p(dst_row), T,
                                   _p(cache), n_rows, _s(stream)), "mla_cache_append")
+
+
+def mla_cache_append_hadamard(dims, act, kv, c_kv, k_rope, pos, T, cache, n_rows, dst_row=None,
+                              stream=None):
+    _check(lib().mla_cache_append_hadamard(_d(dims), act, kv, _p(c_kv), _p(k_rope), _p(pos),
+                                           _p(dst_row), T, _p(cache), n_rows, _s(stream)),
+           "mla_cache_append_hadamard")
+
+
+def mla_hadamard_weights(dims, act, wk_b, wv_b, wk_b_rot, wv_b_rot, stream=None):
+    _check(lib().mla_hadamard_weights(_d(dims), act, _p(wk_b), _p(wv_b), _p(wk_b_rot),
+                                      _p(wv_b_rot), _s(stream)), "mla_hadamard_weights")
 
 
 def mla_quantize_q8_0(x, rows, n_rows, width, stream=None):

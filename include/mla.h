@@ -224,6 +224,30 @@ int mla_cache_append(const mla_dims *dims, mla_dtype act, mla_dtype kv, const vo
                      const void *k_rope, const int32_t *pos, const int64_t *dst_row, int32_t T,
                      void *cache, int64_t n_rows, void *stream);
 
+/* Walsh-Hadamard-rotated latent cache (the "llama.cpp KV cache" page, section 3.1: keys
+ * rotated by an orthonormal Hadamard matrix before quantisation spread the quantisation
+ * noise over all dimensions; the query takes the same rotation, so scores are unchanged).
+ * H is the page's normalised Sylvester matrix of order R (a power of two),
+ * H[i][j] = (-1)^popcount(i & j) / sqrt(R): symmetric, H H = I.
+ *
+ * mla_cache_append_hadamard: mla_cache_append with the c_kv part of each new row replaced
+ *   by H c_kv[t] before it is stored (RoPE part unchanged).  Same arguments, layouts and
+ *   errors; R must be a power of two (else INVALID_ARG).
+ * mla_hadamard_weights: the weights that make a rotated cache give the plain result,
+ *   wk_b_rot[h] = H wk_b[h] ([R][Dn]) and wv_b_rot[h] = wv_b[h] H ([Dv][R]); computed once.
+ *   Since c = H c', the score q_lat . c = (H q_lat) . c' and the output
+ *   wv_b o_lat = (wv_b H) o_lat' (o_lat' attends on the rotated rows): mla_absorb_q with
+ *   wk_b_rot, attention on the rotated cache and mla_out_proj with wv_b_rot compute the
+ *   same layer as the plain chain.  act MLA_F32 or MLA_BF16 (outputs rounded to nearest
+ *   even); outputs must not alias inputs.  Errors: INVALID_ARG (nulls, aliasing, R not a
+ *   power of two), UNSUPPORTED (R > 16384). */
+int mla_cache_append_hadamard(const mla_dims *dims, mla_dtype act, mla_dtype kv,
+                              const void *c_kv, const void *k_rope, const int32_t *pos,
+                              const int64_t *dst_row, int32_t T, void *cache, int64_t n_rows,
+                              void *stream);
+int mla_hadamard_weights(const mla_dims *dims, mla_dtype act, const void *wk_b, const void *wv_b,
+                         void *wk_b_rot, void *wv_b_rot, void *stream);
+
 /* Bytes of one Q8_0 row of `width` values (width/32*34), or -1 if width is not a
  * positive multiple of 32.  Host-only. */
 int32_t mla_q8_0_row_bytes(int32_t width);

@@ -182,12 +182,13 @@ def cache_rows_new(dims, c_kv, k_rope, pos):
     return rows
 
 
-def cache_append(dims, kv, cache, c_kv, k_rope, pos, dst_row=None):
+def cache_append(dims, kv, cache, c_kv, k_rope, pos, dst_row=None, hadamard=False):
     """Returns a copy of cache with the new rows stored at dst_row[t] (pos[t] if None).
 
     kv is "f32", "bf16" (cache float32 [N, W] holding bfloat16 values) or "q8_0" (cache
-    uint8 [N, W/32*34]).  Destinations outside [0, N) are skipped."""
-    rows = cache_rows_new(dims, c_kv, k_rope, pos)
+    uint8 [N, W/32*34]).  Destinations outside [0, N) are skipped.  hadamard: the latent
+    part is rotated first (cache_rows_new_hadamard)."""
+    rows = (cache_rows_new_hadamard if hadamard else cache_rows_new)(dims, c_kv, k_rope, pos)
     dst = np.asarray(pos if dst_row is None else dst_row, dtype=np.int64)
     out = np.array(cache, copy=True)
     if kv == "bf16":
@@ -198,6 +199,40 @@ def cache_append(dims, kv, cache, c_kv, k_rope, pos, dst_row=None):
         if 0 <= r < out.shape[0]:
             out[r] = rows[t]
     return out
+
+
+def hadamard(n: int) -> np.ndarray:
+    """The normalised Walsh-Hadamard matrix of order n (a power of two), built by the
+    doubling of the "llama.cpp KV cache" page, section 3.1: start from 1/sqrt(n) in the
+    corner; each step copies the filled s x s block right and down and its negation to the
+    lower right.  float64."""
+    assert n > 0 and n & (n - 1) == 0
+    h = np.zeros((n, n))
+    h[0, 0] = 1.0 / np.sqrt(n)
+    s = 1
+    while s < n:
+        blk = h[:s, :s].copy()
+        h[s:2 * s, :s] = blk
+        h[:s, s:2 * s] = blk
+        h[s:2 * s, s:2 * s] = -blk
+        s *= 2
+    return h
+
+
+def hadamard_weights(dims, wk_b, wv_b):
+    """(H wk_b[h], wv_b[h] H) per head, float64 products rounded to float32."""
+    h = hadamard(dims.kv_lora_rank)
+    wk = np.einsum("lm,hmd->hld", h, np.asarray(wk_b, np.float64))
+    wv = np.einsum("hdm,ml->hdl", np.asarray(wv_b, np.float64), h)
+    return wk.astype(np.float32), wv.astype(np.float32)
+
+
+def cache_rows_new_hadamard(dims, c_kv, k_rope, pos):
+    """cache_rows_new with the latent part rotated: [H c_kv[t] | RoPE(k_rope[t], pos[t])]."""
+    rows = cache_rows_new(dims, c_kv, k_rope, pos)
+    h = hadamard(dims.kv_lora_rank)
+    rows[:, :dims.kv_lora_rank] = (np.asarray(c_kv, np.float64) @ h.T).astype(np.float32)
+    return rows
 
 
 def heads_per_chunk(n_head: int, size_mib: float, cap_mib: int) -> int:

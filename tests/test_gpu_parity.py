@@ -772,3 +772,153 @@ def test_materialized_v3_long_sampled(dev):
     sel = _sample(w.T, 4, 77)
     ref = oracle_chain(w.dims, x, rows, qsel=sel)
     check_stages(L.outputs(), ref, "bf16", sel=sel, stages=MAT_STAGES)
+
+
+# ------------------------------------------------ Hadamard-rotated cache ---
+
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+def test_hadamard_weights(dev, mode):
+    """GPU rotated weights (fast transform in float32) against the oracle's float64 matrix
+    products: float32 within 1e-5 of each row's rms, bf16 within one bf16 ulp + 1e-6."""
+    from deepseek_mla_amd import mla
+    d = synth.TINY if mode == "f32" else synth.deepseek_dims(16, 2048)
+    x = synth.generate(d, 1, 4, seed=95, mode=mode)
+    wk_r, wv_r = oracle.hadamard_weights(d, x["wk_b"], x["wv_b"])
+    tdt = torch.float32 if mode == "f32" else torch.bfloat16
+    act = mla.F32 if mode == "f32" else mla.BF16
+    wk = torch.from_numpy(x["wk_b"]).to(dev).to(tdt)
+    wv = torch.from_numpy(x["wv_b"]).to(dev).to(tdt)
+    gk, gv = torch.empty_like(wk), torch.empty_like(wv)
+    mla.mla_hadamard_weights(mla.make_dims(d), act, wk, wv, gk, gv)
+    torch.cuda.synchronize()
+    for name, g, r in (("wk_b", gk, wk_r), ("wv_b", gv, wv_r)):
+        g = g.float().cpu().numpy().astype(np.float64)
+        if mode == "f32":
+            report(name, rel_err(g, r), 1e-5)
+        else:
+            assert (np.abs(g - r) <= 2.0 ** -8 * np.abs(r) + 1e-6).all(), name
+
+
+@pytest.mark.parametrize("mode", ["f32", "bf16", "q8_0"])
+def test_cache_append_hadamard(dev, mode):
+    """Rotated append: latent part H c_kv (float32 transform on the GPU, float64 in the
+    oracle), RoPE part as in the plain append."""
+    from deepseek_mla_amd import mla
+    d = synth.TINY if mode == "f32" else synth.deepseek_dims(16, 2048)
+    T, N = 45, 120
+    rng = np.random.default_rng(96)
+    c = rng.standard_normal((T, d.kv_lora_rank)).astype(np.float32)
+    k = rng.standard_normal((T, d.qk_rope)).astype(np.float32)
+    if mode != "f32":
+        c, k = synth.round_bf16(c), synth.round_bf16(k)
+    pos = rng.permutation(N)[:T].astype(np.int32)
+    W = d.kv_lora_rank + d.qk_rope
+    tdt = torch.float32 if mode == "f32" else torch.bfloat16
+    act = mla.F32 if mode == "f32" else mla.BF16
+    if mode == "q8_0":
+        cache = torch.zeros((N, W // 32 * 34), dtype=torch.uint8, device=dev)
+        kv = mla.Q8_0
+    else:
+        cache = torch.zeros((N, W), dtype=tdt, device=dev)
+        kv = act
+    mla.mla_cache_append_hadamard(mla.make_dims(d), act, kv, torch.from_numpy(c).to(dev).to(tdt),
+                                  torch.from_numpy(k).to(dev).to(tdt),
+                                  torch.from_numpy(pos).to(dev), T, cache, N)
+    torch.cuda.synchronize()
+    got = cache.cpu().numpy() if mode == "q8_0" else cache.float().cpu().numpy()
+    ref = oracle.cache_append(d, mode, np.zeros_like(got), c, k, pos, hadamard=True)
+    rows = sorted(int(p) for p in pos)
+    if mode == "q8_0":
+        g = got[rows].reshape(len(rows), -1, 34)
+        r = ref[rows].reshape(len(rows), -1, 34)
+        gs = g[:, :, :2].copy().view(np.uint16).astype(np.int32)
+        rs = r[:, :, :2].copy().view(np.uint16).astype(np.int32)
+        assert np.abs(gs - rs).max() <= 1
+        gq = g[:, :, 2:].view(np.int8).astype(np.int32)
+        rq = r[:, :, 2:].view(np.int8).astype(np.int32)
+        assert np.abs(gq - rq).max() <= 1
+    elif mode == "bf16":
+        g, r = got[rows].astype(np.float64), ref[rows].astype(np.float64)
+        assert (np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 1e-5).all()
+    else:
+        report("rows", rel_err(got[rows], ref[rows]), 1e-5)
+    others = np.setdiff1d(np.arange(N), rows)
+    assert not got[others].any()
+
+
+def _q8_decode_layer(d, c, k, lens, Nmax, x, rotate):
+    """Fill two Q8_0 caches by appends (rotated or not), rotate the weights on the GPU when
+    asked, then absorb -> decode -> out_proj through the C ABI.  Returns out [2, D]."""
+    from deepseek_mla_amd import mla
+    cd = mla.make_dims(d)
+    bt = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(torch.bfloat16)
+    W = d.kv_lora_rank + d.qk_rope
+    cache = torch.zeros((2 * Nmax, W // 32 * 34), dtype=torch.uint8, device="cuda")
+    pos = torch.from_numpy(np.tile(np.arange(Nmax, dtype=np.int32), 2)).to("cuda")
+    append = mla.mla_cache_append_hadamard if rotate else mla.mla_cache_append
+    dst = torch.arange(2 * Nmax, dtype=torch.int64, device="cuda")  # b * Nmax + pos
+    append(cd, mla.BF16, mla.Q8_0, bt(c), bt(k), pos, 2 * Nmax, cache, 2 * Nmax, dst_row=dst)
+    wk, wv = bt(x["wk_b"]), bt(x["wv_b"])
+    if rotate:
+        wk_r, wv_r = torch.empty_like(wk), torch.empty_like(wv)
+        mla.mla_hadamard_weights(cd, mla.BF16, wk, wv, wk_r, wv_r)
+        wk, wv = wk_r, wv_r
+    qpos = torch.tensor([l - 1 for l in lens], dtype=torch.int32, device="cuda")
+    H = d.n_head
+    q_cat = torch.empty((2, H, W), dtype=torch.bfloat16, device="cuda")
+    mla.mla_absorb_q(cd, mla.BF16, bt(x["q_nope"]), bt(x["q_rope"]), qpos, wk, q_cat, 2)
+    nkv = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    wsb = mla.mla_decode_workspace_bytes(cd, 2, Nmax, 0)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    o = torch.empty((2, H, d.kv_lora_rank), dtype=torch.bfloat16, device="cuda")
+    mla.mla_attn_decode(cd, mla.BF16, mla.Q8_0, q_cat, cache, 612 * Nmax, nkv, 2, Nmax, 0, o,
+                        None, ws, wsb)
+    v = torch.empty((2, H * d.v_head), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((2, d.d_model), dtype=torch.bfloat16, device="cuda")
+    mla.mla_out_proj(cd, mla.BF16, o, wv, bt(x["wo"]), v, out, 2)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("outliers", [False, True])
+def test_hadamard_q8_0_decode_layer(dev, outliers):
+    """V3 dims, two sequences (300 and 123 rows) written by appends into Q8_0 caches, plain
+    and Hadamard-rotated (with rotated weights), decoded end to end through the C ABI.
+    Parity: each against the oracle's layer over the oracle's own Q8_0 rows of the same
+    kind (rotated rows with the oracle's rotated weights), within 2e-2.  Accuracy (the
+    page's claim, reported): both against the exact layer over the unquantised rows; with
+    four large latent channels the rotated cache must be the closer one."""
+    d = synth.deepseek_dims(128, 7168)
+    Nmax, lens = 300, [300, 123]
+    W = 576
+    rng = np.random.default_rng(97)
+    c = rng.standard_normal((2 * Nmax, 512)).astype(np.float32)
+    if outliers:
+        c[:, rng.choice(512, size=4, replace=False)] *= 40.0
+    c = synth.round_bf16(c)
+    k = synth.round_bf16(rng.standard_normal((2 * Nmax, 64)).astype(np.float32))
+    x = synth.generate(d, 1, 8, seed=98, n_seq=2, mode="bf16")
+    pos = np.tile(np.arange(Nmax, dtype=np.int32), 2)
+    qpos = [np.array([l - 1], np.int32) for l in lens]
+    # the rotated weights as the layer holds them: bfloat16, rounded to nearest even
+    wk_r, wv_r = (oracle.bf16_round(w) for w in oracle.hadamard_weights(d, x["wk_b"], x["wv_b"]))
+
+    def layer(rows, wk, wv):
+        return np.stack([oracle.mla_absorbed(d, x["q_nope"][b:b + 1], x["q_rope"][b:b + 1],
+                                             qpos[b], rows[b * Nmax: b * Nmax + lens[b]], wk, wv,
+                                             x["wo"])["out"][0] for b in range(2)])
+
+    exact = layer(oracle.cache_rows_new(d, c, k, pos), x["wk_b"], x["wv_b"])
+    acc = {}
+    for rotate in (False, True):
+        got = _q8_decode_layer(d, c, k, lens, Nmax, x, rotate)
+        rows = (oracle.cache_rows_new_hadamard if rotate else oracle.cache_rows_new)(d, c, k, pos)
+        rows = oracle.q8_0_dequantize(oracle.q8_0_quantize(rows), W)
+        ref = layer(rows, wk_r, wv_r) if rotate else layer(rows, x["wk_b"], x["wv_b"])
+        tag = "rotated" if rotate else "plain"
+        report(f"out ({tag} Q8_0 cache, parity)", rel_err_stored(got, ref, "q8_0"), 2e-2)
+        acc[rotate] = rel_err(got, exact)
+        print(f"  out ({tag} Q8_0 cache) vs the exact layer: max|diff|/rms = {acc[rotate]:.3e}",
+              flush=True)
+    if outliers:
+        assert acc[True] < acc[False]

@@ -483,3 +483,82 @@ def test_bf16_round_ties_and_library():
     r = np.random.default_rng(9).standard_normal(10000).astype(np.float32) * 100
     t = torch.from_numpy(r).to(torch.bfloat16).float().numpy()
     assert np.array_equal(oracle.bf16_round(r), t)
+
+
+# ------------------------------------------------------ Hadamard rotation ---
+
+def test_hadamard_matrix():
+    """The page's doubling construction against the closed form
+    H[i][j] = (-1)^popcount(i & j) / sqrt(n), the textbook orders 2 and 4, symmetry and
+    orthonormality."""
+    for n in (1, 2, 4, 8, 64, 512):
+        h = oracle.hadamard(n)
+        i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+        pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i & j)
+        assert np.array_equal(h, (-1.0) ** pc / np.sqrt(n))
+        assert np.array_equal(h, h.T)
+        assert np.abs(h @ h - np.eye(n)).max() <= 1e-12
+    s2 = 1 / np.sqrt(2)
+    assert np.allclose(oracle.hadamard(2), [[s2, s2], [s2, -s2]], atol=0, rtol=0)
+    assert np.array_equal(oracle.hadamard(4) * 2, [[1, 1, 1, 1], [1, -1, 1, -1],
+                                                  [1, 1, -1, -1], [1, -1, -1, 1]])
+
+
+def test_hadamard_rotation_preserves_the_layer():
+    """A cache whose latent rows are rotated, read with the rotated weights, gives the
+    plain layer (H H = I and associativity): absorbed chain on both sides, float32 I/O."""
+    d = small_dims()  # R = 64
+    x = inputs(d, 7, 30, seed=91, pos=np.array([0, 4, 9, 17, 23, 28, 29]))
+    rows_rot = x["rows"].copy()
+    h = oracle.hadamard(d.kv_lora_rank)
+    rows_rot[:, :d.kv_lora_rank] = (x["rows"][:, :d.kv_lora_rank].astype(np.float64) @ h
+                                    ).astype(np.float32)
+    wk_r, wv_r = oracle.hadamard_weights(d, x["wk_b"], x["wv_b"])
+    a = oracle.mla_absorbed(d, x["q_nope"], x["q_rope"], x["pos"], x["rows"], x["wk_b"],
+                            x["wv_b"], x["wo"])
+    b = oracle.mla_absorbed(d, x["q_nope"], x["q_rope"], x["pos"], rows_rot, wk_r, wv_r, x["wo"])
+    assert rel_err(b["out"], a["out"]) <= 1e-5
+    assert np.abs(b["lse"] - a["lse"]).max() <= 1e-5
+
+
+def test_hadamard_append_rows():
+    """cache_append with the rotation stores H c_kv (the closed-form matrix product) and
+    leaves the RoPE part as the plain append does."""
+    d = small_dims(Dr=32)
+    c, k = _append_inputs(d, 5, 92)
+    pos = np.array([3, 0, 7, 1, 2], np.int32)
+    base = np.zeros((8, d.kv_lora_rank + d.qk_rope), np.float32)
+    got = oracle.cache_append(d, "f32", base, c, k, pos, hadamard=True)
+    plain = oracle.cache_append(d, "f32", base, c, k, pos)
+    R = d.kv_lora_rank
+    i, j = np.meshgrid(np.arange(R), np.arange(R), indexing="ij")
+    hm = (-1.0) ** np.vectorize(lambda v: bin(int(v)).count("1"))(i & j) / np.sqrt(R)
+    assert np.abs(got[pos, :R] - (hm @ c.astype(np.float64).T).T).max() <= 1e-6
+    assert np.array_equal(got[:, R:], plain[:, R:])
+
+
+def test_hadamard_q8_0_spreads_outlier_channels():
+    """The page's claim on data it is made for: latents with a few large channels.  The
+    Q8_0 cache of the rotated rows (read with the rotated weights) gives a layer output
+    closer to the exact one than the Q8_0 cache of the plain rows."""
+    d = small_dims(H=4, R=128, Dn=32, Dr=32, Dv=32, D=64)
+    x = inputs(d, 8, 96, seed=93, pos=np.arange(88, 96))
+    rng = np.random.default_rng(94)
+    ch = rng.choice(d.kv_lora_rank, size=4, replace=False)
+    rows = x["rows"].copy()
+    rows[:, ch] *= 40.0
+    exact = oracle.mla_absorbed(d, x["q_nope"], x["q_rope"], x["pos"], rows, x["wk_b"],
+                                x["wv_b"], x["wo"])["out"]
+    W = d.kv_lora_rank + d.qk_rope
+    plain = oracle.q8_0_dequantize(oracle.q8_0_quantize(rows), W)
+    out_plain = oracle.mla_absorbed(d, x["q_nope"], x["q_rope"], x["pos"], plain, x["wk_b"],
+                                    x["wv_b"], x["wo"])["out"]
+    h = oracle.hadamard(d.kv_lora_rank)
+    rot = rows.copy()
+    rot[:, :d.kv_lora_rank] = (rows[:, :d.kv_lora_rank].astype(np.float64) @ h).astype(np.float32)
+    rot = oracle.q8_0_dequantize(oracle.q8_0_quantize(rot), W)
+    wk_r, wv_r = oracle.hadamard_weights(d, x["wk_b"], x["wv_b"])
+    out_rot = oracle.mla_absorbed(d, x["q_nope"], x["q_rope"], x["pos"], rot, wk_r, wv_r,
+                                  x["wo"])["out"]
+    e_plain, e_rot = rel_err(out_plain, exact), rel_err(out_rot, exact)
+    assert e_rot < 0.5 * e_plain, (e_rot, e_plain)
