@@ -387,4 +387,36 @@ int mla_hadamard_weights(const mla_dims *d, mla_dtype act, const void *wk_b, con
     return hip_status(e);
 }
 
+int mla_wkv_b_merge(const mla_dims *d, mla_dtype act, mla_dtype out, const void *wk_b,
+                    const void *wv_b, void *wkv_b, void *stream) {
+    if (!dims_ok(d) || !act_ok(act) || (out != act && out != MLA_Q8_0)) return MLA_ERR_INVALID_ARG;
+    if (!wk_b || !wv_b || !wkv_b) return MLA_ERR_INVALID_ARG;
+    if (out == MLA_Q8_0 && d->kv_lora_rank % 32) return MLA_ERR_INVALID_ARG;
+    const bool q8 = out == MLA_Q8_0;
+    const int H = d->n_head, R = d->kv_lora_rank, Dn = d->qk_nope, Dv = d->v_head;
+    hipStream_t st = as_stream(stream);
+    hipError_t e = act == MLA_F32
+                       ? launch_wkv_merge<float>((const float *)wk_b, (const float *)wv_b, wkv_b,
+                                                 q8, H, R, Dn, Dv, st)
+                       : launch_wkv_merge<bf16>((const bf16 *)wk_b, (const bf16 *)wv_b, wkv_b, q8,
+                                                H, R, Dn, Dv, st);
+    return hip_status(e);
+}
+
+int mla_wkv_b_split(const mla_dims *d, mla_dtype in, mla_dtype act, const void *wkv_b,
+                    void *wk_b, void *wv_b, void *stream) {
+    if (!dims_ok(d) || !act_ok(act) || (in != act && in != MLA_Q8_0)) return MLA_ERR_INVALID_ARG;
+    if (!wk_b || !wv_b || !wkv_b) return MLA_ERR_INVALID_ARG;
+    if (in == MLA_Q8_0 && d->kv_lora_rank % 32) return MLA_ERR_INVALID_ARG;
+    const bool q8 = in == MLA_Q8_0;
+    const int H = d->n_head, R = d->kv_lora_rank, Dn = d->qk_nope, Dv = d->v_head;
+    hipStream_t st = as_stream(stream);
+    hipError_t e = act == MLA_F32
+                       ? launch_wkv_split<float>(wkv_b, q8, (float *)wk_b, (float *)wv_b, H, R, Dn,
+                                                 Dv, st)
+                       : launch_wkv_split<bf16>(wkv_b, q8, (bf16 *)wk_b, (bf16 *)wv_b, H, R, Dn, Dv,
+                                                st);
+    return hip_status(e);
+}
+
 }  // extern "C"

@@ -69,6 +69,12 @@ hipError_t launch_cache_append(const TI *c_kv, const TI *k_rope, const int32_t *
                                const int64_t *dst_row, int T, int R, int Dr, float base, int kv,
                                bool hadamard, void *cache, int64_t n_rows, hipStream_t st);
 template <typename T>
+hipError_t launch_wkv_merge(const T *wk_b, const T *wv_b, void *wkv_b, bool q8, int H, int R,
+                            int Dn, int Dv, hipStream_t st);
+template <typename T>
+hipError_t launch_wkv_split(const void *wkv_b, bool q8, T *wk_b, T *wv_b, int H, int R, int Dn,
+                            int Dv, hipStream_t st);
+template <typename T>
 hipError_t launch_hadamard_weights(const T *wk_b, const T *wv_b, T *wk_b_rot, T *wv_b_rot, int H,
                                    int R, int Dn, int Dv, hipStream_t st);
 hipError_t launch_absorb_bf16(const bf16 *q_nope, const bf16 *q_rope, const int32_t *pos,

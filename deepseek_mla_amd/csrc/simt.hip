@@ -515,6 +515,113 @@ hipError_t launch_dequant_q8_0(const uint8_t *rows, float *out, int64_t n_rows, 
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------ merged wkv_b layout
+// wkv_b[h] ([Dn + Dv][R]) stacks the transposed wk_b[h] ([R][Dn]) over wv_b[h] ([Dv][R]):
+// row i < Dn is k_nope dim i, row Dn + e is v dim e (the merged attn_kv_b tensor of the page
+// "ik_llama.cpp PR #394", section 2.1, reconstructed as in its section 3.3).
+
+// element (h, i, l) of the merged tensor, read from the split pair
+template <typename T>
+__device__ __forceinline__ float wkv_elem(const T *wk_b, const T *wv_b, int h, int i, int l, int R,
+                                          int Dn, int Dv) {
+    return i < Dn ? ld_f(wk_b + ((int64_t)h * R + l) * Dn + i)
+                  : ld_f(wv_b + ((int64_t)h * Dv + (i - Dn)) * R + l);
+}
+
+// merged = act type: one thread per element (writes coalesced along l)
+template <typename T>
+__global__ __launch_bounds__(256) void wkv_merge_kernel(const T *__restrict__ wk_b,
+                                                        const T *__restrict__ wv_b,
+                                                        T *__restrict__ wkv_b, int H, int R, int Dn,
+                                                        int Dv) {
+    const int64_t n = (int64_t)H * (Dn + Dv) * R;
+    const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= n) return;
+    const int l = (int)(x % R);
+    const int64_t hi = x / R;
+    const int i = (int)(hi % (Dn + Dv)), h = (int)(hi / (Dn + Dv));
+    st_f(wkv_b + x, wkv_elem(wk_b, wv_b, h, i, l, R, Dn, Dv));
+}
+
+// merged = Q8_0 rows of R values: one thread per 32-block (the block quantiser above)
+template <typename T>
+__global__ __launch_bounds__(256) void wkv_merge_q8_kernel(const T *__restrict__ wk_b,
+                                                           const T *__restrict__ wv_b,
+                                                           uint8_t *__restrict__ wkv_b, int H, int R,
+                                                           int Dn, int Dv) {
+    const int nb = R / 32;
+    const int64_t n = (int64_t)H * (Dn + Dv) * nb;
+    const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= n) return;
+    const int b = (int)(x % nb);
+    const int64_t hi = x / nb;
+    const int i = (int)(hi % (Dn + Dv)), h = (int)(hi / (Dn + Dv));
+    float v[32];
+    for (int j = 0; j < 32; ++j) v[j] = wkv_elem(wk_b, wv_b, h, i, 32 * b + j, R, Dn, Dv);
+    q8_0_block(v, wkv_b + hi * (int64_t)nb * 34 + (int64_t)b * 34);
+}
+
+// split pair from the merged tensor (act type, or Q8_0 dequantised: d * q, exact in float)
+template <typename T, bool Q8>
+__global__ __launch_bounds__(256) void wkv_split_kernel(const void *__restrict__ wkv_b,
+                                                        T *__restrict__ wk_b, T *__restrict__ wv_b,
+                                                        int H, int R, int Dn, int Dv) {
+    const int64_t n = (int64_t)H * (Dn + Dv) * R;
+    const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= n) return;
+    const int l = (int)(x % R);
+    const int64_t hi = x / R;
+    const int i = (int)(hi % (Dn + Dv)), h = (int)(hi / (Dn + Dv));
+    float val;
+    if constexpr (Q8) {
+        const uint8_t *blk = (const uint8_t *)wkv_b + hi * (int64_t)(R / 32) * 34 + (l / 32) * 34;
+        const float d = (float)__builtin_bit_cast(_Float16, *(const uint16_t *)blk);
+        val = d * (float)(int8_t)blk[2 + (l % 32)];
+    } else {
+        val = ld_f((const T *)wkv_b + x);
+    }
+    if (i < Dn)
+        st_f(wk_b + ((int64_t)h * R + l) * Dn + i, val);
+    else
+        st_f(wv_b + ((int64_t)h * Dv + (i - Dn)) * R + l, val);
+}
+
+template <typename T>
+hipError_t launch_wkv_merge(const T *wk_b, const T *wv_b, void *wkv_b, bool q8, int H, int R,
+                            int Dn, int Dv, hipStream_t st) {
+    const int64_t n = (int64_t)H * (Dn + Dv) * (q8 ? R / 32 : R);
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (q8)
+        hipLaunchKernelGGL(wkv_merge_q8_kernel<T>, grid, dim3(256), 0, st, wk_b, wv_b,
+                           (uint8_t *)wkv_b, H, R, Dn, Dv);
+    else
+        hipLaunchKernelGGL(wkv_merge_kernel<T>, grid, dim3(256), 0, st, wk_b, wv_b, (T *)wkv_b, H,
+                           R, Dn, Dv);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_wkv_split(const void *wkv_b, bool q8, T *wk_b, T *wv_b, int H, int R, int Dn,
+                            int Dv, hipStream_t st) {
+    const int64_t n = (int64_t)H * (Dn + Dv) * R;
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (q8)
+        hipLaunchKernelGGL((wkv_split_kernel<T, true>), grid, dim3(256), 0, st, wkv_b, wk_b, wv_b,
+                           H, R, Dn, Dv);
+    else
+        hipLaunchKernelGGL((wkv_split_kernel<T, false>), grid, dim3(256), 0, st, wkv_b, wk_b, wv_b,
+                           H, R, Dn, Dv);
+    return hipGetLastError();
+}
+template hipError_t launch_wkv_merge<float>(const float *, const float *, void *, bool, int, int,
+                                            int, int, hipStream_t);
+template hipError_t launch_wkv_merge<bf16>(const bf16 *, const bf16 *, void *, bool, int, int, int,
+                                           int, hipStream_t);
+template hipError_t launch_wkv_split<float>(const void *, bool, float *, float *, int, int, int,
+                                            int, hipStream_t);
+template hipError_t launch_wkv_split<bf16>(const void *, bool, bf16 *, bf16 *, int, int, int, int,
+                                           hipStream_t);
+
 // ------------------------------------------------------------ Walsh-Hadamard rotation
 // H (n = 2^k) is the normalised Sylvester matrix of the page "llama.cpp KV cache", section
 // 3.1: H[i][j] = (-1)^popcount(i & j) / sqrt(n), symmetric and orthonormal (H H = I).

@@ -21,7 +21,8 @@ EXPORTS = ("mla_absorb_q", "mla_attn_prefill", "mla_prefill_workspace_bytes",
            "mla_heads_per_chunk", "mla_decode_workspace_bytes",
            "mla_decode_auto_splits", "mla_attn_decode", "mla_out_proj", "mla_prefill_materialized",
            "mla_materialized_workspace_bytes", "mla_cache_append",
-           "mla_cache_append_hadamard", "mla_hadamard_weights",
+           "mla_cache_append_hadamard", "mla_hadamard_weights", "mla_wkv_b_merge",
+           "mla_wkv_b_split",
            "mla_quantize_q8_0", "mla_dequant_q8_0", "mla_q8_0_row_bytes", "mla_status_str")
 
 
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
             "mla_cache_append_hadamard": ([D, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i32, vp,
                                            i64, vp], ctypes.c_int),
             "mla_hadamard_weights": ([D, ctypes.c_int, vp, vp, vp, vp, vp], ctypes.c_int),
+            "mla_wkv_b_merge": ([D, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp], ctypes.c_int),
+            "mla_wkv_b_split": ([D, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp], ctypes.c_int),
             "mla_cache_append": ([D, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i32, vp, i64,
                                   vp], ctypes.c_int),
             "mla_quantize_q8_0": ([vp, vp, i64, i32, vp], ctypes.c_int),
@@ -215,6 +218,16 @@ def mla_cache_append_hadamard(dims, act, kv, c_kv, k_rope, pos, T, cache, n_rows
 def mla_hadamard_weights(dims, act, wk_b, wv_b, wk_b_rot, wv_b_rot, stream=None):
     _check(lib().mla_hadamard_weights(_d(dims), act, _p(wk_b), _p(wv_b), _p(wk_b_rot),
                                       _p(wv_b_rot), _s(stream)), "mla_hadamard_weights")
+
+
+def mla_wkv_b_merge(dims, act, out, wk_b, wv_b, wkv_b, stream=None):
+    _check(lib().mla_wkv_b_merge(_d(dims), act, out, _p(wk_b), _p(wv_b), _p(wkv_b), _s(stream)),
+           "mla_wkv_b_merge")
+
+
+def mla_wkv_b_split(dims, inp, act, wkv_b, wk_b, wv_b, stream=None):
+    _check(lib().mla_wkv_b_split(_d(dims), inp, act, _p(wkv_b), _p(wk_b), _p(wv_b), _s(stream)),
+           "mla_wkv_b_split")
 
 
 def mla_quantize_q8_0(x, rows, n_rows, width, stream=None):

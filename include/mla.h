@@ -248,6 +248,22 @@ int mla_cache_append_hadamard(const mla_dims *dims, mla_dtype act, mla_dtype kv,
 int mla_hadamard_weights(const mla_dims *dims, mla_dtype act, const void *wk_b, const void *wv_b,
                          void *wk_b_rot, void *wv_b_rot, void *stream);
 
+/* Merged and split weight layouts (the page "ik_llama.cpp PR #394": section 2.1 names the
+ * merged attn_kv_b tensor of ggml shape {R, H*(Dn+Dv)}, section 3.3 rebuilds it from the
+ * split pair, with BF16 sources giving BF16 and other sources Q8_0).  Row-major:
+ *   wkv_b[h][i][l] = wk_b[h][l][i]        for i <  Dn   (k_nope row i of head h)
+ *   wkv_b[h][Dn+e][l] = wv_b[h][e][l]     for e <  Dv   (v row e of head h)
+ * so that [k_nope | v] of head h = wkv_b[h] . c_kv.  wkv_b is [H][Dn+Dv][R] of type `out`
+ * (act, an exact copy, or MLA_Q8_0: each R-wide row quantised as by mla_quantize_q8_0);
+ * wk_b [H][R][Dn], wv_b [H][Dv][R] of type act (MLA_F32 or MLA_BF16).
+ * mla_wkv_b_merge: split -> merged.  mla_wkv_b_split: merged (type `in`: act, or MLA_Q8_0
+ * dequantised to d*q and rounded to act) -> split.
+ * Errors: INVALID_ARG (nulls, dtype not act or Q8_0, Q8_0 with R % 32 != 0). */
+int mla_wkv_b_merge(const mla_dims *dims, mla_dtype act, mla_dtype out, const void *wk_b,
+                    const void *wv_b, void *wkv_b, void *stream);
+int mla_wkv_b_split(const mla_dims *dims, mla_dtype in, mla_dtype act, const void *wkv_b,
+                    void *wk_b, void *wv_b, void *stream);
+
 /* Bytes of one Q8_0 row of `width` values (width/32*34), or -1 if width is not a
  * positive multiple of 32.  Host-only. */
 int32_t mla_q8_0_row_bytes(int32_t width);

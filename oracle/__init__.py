@@ -235,6 +235,23 @@ def cache_rows_new_hadamard(dims, c_kv, k_rope, pos):
     return rows
 
 
+def wkv_b_merge(dims, wk_b, wv_b):
+    """The merged attn_kv_b layout of the PR #394 page (section 2.1; rebuilt from the split
+    pair as in its section 3.3): per head, the transposed wk_b ([Dn][R]) stacked over
+    wv_b ([Dv][R]).  [H][Dn+Dv][R] float32."""
+    wk_b = np.asarray(wk_b, np.float32)
+    wv_b = np.asarray(wv_b, np.float32)
+    return np.ascontiguousarray(np.concatenate([wk_b.transpose(0, 2, 1), wv_b], axis=1))
+
+
+def wkv_b_split(dims, wkv_b):
+    """Inverse of wkv_b_merge: (wk_b [H][R][Dn], wv_b [H][Dv][R])."""
+    wkv_b = np.asarray(wkv_b, np.float32)
+    Dn = dims.qk_nope
+    return (np.ascontiguousarray(wkv_b[:, :Dn, :].transpose(0, 2, 1)),
+            np.ascontiguousarray(wkv_b[:, Dn:, :]))
+
+
 def heads_per_chunk(n_head: int, size_mib: float, cap_mib: int) -> int:
     return int(lib().orc_heads_per_chunk(int(n_head), float(size_mib), int(cap_mib)))
 

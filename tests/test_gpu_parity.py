@@ -922,3 +922,43 @@ def test_hadamard_q8_0_decode_layer(dev, outliers):
               flush=True)
     if outliers:
         assert acc[True] < acc[False]
+
+
+# ------------------------------------------------------ merged wkv_b layout ---
+
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+def test_wkv_b_merge_split(dev, mode):
+    """Merge (as act and as Q8_0) and split (from both) against the oracle's layout, bit
+    for bit: pure data movement, the Q8_0 rows by the shared quantiser rule, the Q8_0
+    split as d*q rounded to act."""
+    from deepseek_mla_amd import mla
+    d = synth.TINY if mode == "f32" else synth.deepseek_dims(16, 2048)
+    x = synth.generate(d, 1, 4, seed=102, mode=mode)
+    tdt = torch.float32 if mode == "f32" else torch.bfloat16
+    act = mla.F32 if mode == "f32" else mla.BF16
+    cd = mla.make_dims(d)
+    H, R, Dn, Dv = d.n_head, d.kv_lora_rank, d.qk_nope, d.v_head
+    wk = torch.from_numpy(x["wk_b"]).to(dev).to(tdt)
+    wv = torch.from_numpy(x["wv_b"]).to(dev).to(tdt)
+    ref = oracle.wkv_b_merge(d, x["wk_b"], x["wv_b"])
+    merged = torch.empty((H, Dn + Dv, R), dtype=tdt, device=dev)
+    mla.mla_wkv_b_merge(cd, act, act, wk, wv, merged)
+    merged_q8 = torch.empty((H, Dn + Dv, R // 32 * 34), dtype=torch.uint8, device=dev)
+    mla.mla_wkv_b_merge(cd, act, mla.Q8_0, wk, wv, merged_q8)
+    torch.cuda.synchronize()
+    assert np.array_equal(merged.float().cpu().numpy(), ref)
+    ref_q8 = oracle.q8_0_quantize(ref)
+    assert np.array_equal(merged_q8.cpu().numpy(), ref_q8)
+    for src, kind in ((merged, act), (merged_q8, mla.Q8_0)):
+        gk, gv = torch.empty_like(wk), torch.empty_like(wv)
+        mla.mla_wkv_b_split(cd, kind, act, src, gk, gv)
+        torch.cuda.synchronize()
+        if kind == mla.Q8_0:
+            deq = oracle.q8_0_dequantize(ref_q8, R)
+            if mode == "bf16":
+                deq = oracle.bf16_round(deq)
+            want_k, want_v = oracle.wkv_b_split(d, deq)
+        else:
+            want_k, want_v = x["wk_b"], x["wv_b"]
+        assert np.array_equal(gk.float().cpu().numpy(), want_k)
+        assert np.array_equal(gv.float().cpu().numpy(), want_v)

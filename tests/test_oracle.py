@@ -562,3 +562,26 @@ def test_hadamard_q8_0_spreads_outlier_channels():
                                   x["wo"])["out"]
     e_plain, e_rot = rel_err(out_plain, exact), rel_err(out_rot, exact)
     assert e_rot < 0.5 * e_plain, (e_rot, e_plain)
+
+
+# ------------------------------------------------------ merged wkv_b layout ---
+
+def test_wkv_b_merged_rows_match_absorption_and_late_projection():
+    """The merged rows' orientation pinned against the oracle's own absorption and late
+    projection (separate C code): q_lat = wkv_b[h][:Dn]^T q_nope (the K rows seen from the
+    query side) and v = wkv_b[h][Dn:] o_lat (the V rows); the split of the merge gives the
+    pair back exactly."""
+    d = small_dims(H=3, R=64, Dn=32, Dr=16, Dv=24, D=40)
+    x = inputs(d, 4, 20, seed=101, pos=np.array([3, 9, 15, 19]))
+    m = oracle.wkv_b_merge(d, x["wk_b"], x["wv_b"])
+    assert m.shape == (3, 32 + 24, 64)
+    q_cat = oracle.absorb_q(d, x["q_nope"], x["q_rope"], x["pos"], x["wk_b"])
+    want_q = np.einsum("hdl,thd->thl", m[:, :32, :].astype(np.float64),
+                       x["q_nope"].astype(np.float64))
+    assert rel_err(q_cat[:, :, :64], want_q) <= 1e-6
+    o_lat, _ = oracle.attention(d, q_cat, x["pos"], x["rows"])
+    v, _ = oracle.out_proj(d, o_lat, x["wv_b"], x["wo"])
+    want_v = np.einsum("hel,thl->the", m[:, 32:, :].astype(np.float64), o_lat.astype(np.float64))
+    assert rel_err(v.reshape(4, 3, 24), want_v) <= 1e-6
+    wk, wv = oracle.wkv_b_split(d, m)
+    assert np.array_equal(wk, x["wk_b"]) and np.array_equal(wv, x["wv_b"])
