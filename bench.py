@@ -41,11 +41,13 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 TRAFFIC = {
     "src": (("deepseek_mla_amd/csrc/flash_mfma.hip", "deepseek_mla_amd/csrc/decode_mfma.hip",
              "deepseek_mla_amd/csrc/latent_tile.h", "deepseek_mla_amd/csrc/lds_dma.h",
-             "deepseek_mla_amd/csrc/simt.hip", "deepseek_mla_amd/csrc/common.h"), "0b61018a92ec56da"),
-    "lite_prefill": (71.40e6 + 82.25e6) + (61.83e6 + 15.32e6),      # prefill kernel + merge
-    "v3_long_prefill": 9804.56e6 + 1195.38e6,
+             "deepseek_mla_amd/csrc/simt.hip", "deepseek_mla_amd/csrc/common.h",
+             "deepseek_mla_amd/csrc/flash_mha.hip"), "9f64317baa84c09c"),
+    "lite_prefill": (71.35e6 + 82.26e6) + (61.83e6 + 15.32e6),      # prefill kernel + merge
+    "v3_long_prefill": 9804.50e6 + 1195.38e6,
     "v3_decode": (39.24e6 + 16.84e6) + (17.43e6 + 0.14e6),          # partial kernel + combine
-    "v3_decode_q8": (245.73e6 + 16.84e6) + (17.43e6 + 0.54e6),      # partial kernel + combine
+    "v3_decode_q8": (245.72e6 + 16.84e6) + (17.43e6 + 0.54e6),      # partial kernel + combine
+    "v3_long_prefill@materialized": 193.52e6 + 18.87e6,             # one 8-head chunk launch
 }
 
 
@@ -251,7 +253,15 @@ def run_materialized(name, steps, warmup):
     decomp = 2 * w.n_kv * d.kv_lora_rank * d.n_head * (d.qk_nope + d.v_head)
     wo = 2 * len(pos) * d.d_model * d.n_head * d.v_head
     absorbed = sum(step_flops(w, pos).values())
-    return {"workload": name, "path": "materialized (decompress k_nope / v, then 192/128 "
+    att = attn / (ms * 1e-3) / 1e12
+    return {"workload": name,
+            "roofline": {"kernel": "flash_mha_kernel (all head chunks of the call)",
+                         "bound": "mfma", "achieved": att, "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": att / BF16_PEAK_TFLOPS,
+                         "traffic": measured_traffic(name),
+                         "per_launch": "attention FLOP = visible pairs x 640 x heads, over the "
+                                       "whole call (decompression GEMMs, wo and launch gaps "
+                                       "included: a lower bound for the kernel)"}, "path": "materialized (decompress k_nope / v, then 192/128 "
                                       "causal attention)",
             "ms_per_step": wall * 1e3, "call_ms": ms,
             "flops_performed": {"attention": attn, "decompression": decomp, "wo": wo},
