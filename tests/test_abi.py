@@ -85,3 +85,49 @@ def test_host_helpers():
     s = mla.mla_decode_auto_splits(v3, mla.BF16, 1, 32768)
     assert s >= 1
     assert mla.mla_decode_workspace_bytes(v3, 1, 32768, s) >= s * 128 * 513 * 4
+
+
+def test_new_entry_points_validate_without_gpu():
+    """Cache append, the materialised prefill, the Hadamard rotation and the wkv_b layout
+    reject bad arguments before any launch (pointers are never dereferenced)."""
+    L = mla.lib()
+    d = tiny()  # R 64, Dr 16: W 80 (not a multiple of 32)
+    p = ctypes.c_void_p(16)
+    D = ctypes.byref(d)
+    # cache append: Q8_0 needs W % 32 == 0; act/kv mix; T < 0; nulls; T == 0 is a no-op
+    assert L.mla_cache_append(D, 0, 2, p, p, p, None, 3, p, 10, None) == mla.ERR_INVALID_ARG
+    assert L.mla_cache_append(D, 0, 1, p, p, p, None, 3, p, 10, None) == mla.ERR_INVALID_ARG
+    assert L.mla_cache_append(D, 0, 0, p, p, p, None, -1, p, 10, None) == mla.ERR_INVALID_ARG
+    assert L.mla_cache_append(D, 0, 0, None, p, p, None, 3, p, 10, None) == mla.ERR_INVALID_ARG
+    assert L.mla_cache_append(D, 0, 0, None, None, None, None, 0, None, 10, None) == mla.OK
+    # Hadamard: R must be a power of two; outputs must not alias inputs
+    r48 = mla.mla_dims(4, 48, 32, 16, 32, 128, 0.1, 10000.0)
+    assert L.mla_cache_append_hadamard(ctypes.byref(r48), 0, 0, p, p, p, None, 3, p, 10,
+                                       None) == mla.ERR_INVALID_ARG
+    assert L.mla_hadamard_weights(ctypes.byref(r48), 0, p, p, ctypes.c_void_p(32),
+                                  ctypes.c_void_p(48), None) == mla.ERR_INVALID_ARG
+    assert L.mla_hadamard_weights(D, 0, p, ctypes.c_void_p(32), p, ctypes.c_void_p(48),
+                                  None) == mla.ERR_INVALID_ARG
+    # wkv_b layout: the merged type is act or Q8_0 (then R % 32 == 0)
+    assert L.mla_wkv_b_merge(D, 0, 1, p, p, p, None) == mla.ERR_INVALID_ARG
+    assert L.mla_wkv_b_merge(ctypes.byref(r48), 0, 2, p, p, p, None) == mla.ERR_INVALID_ARG
+    assert L.mla_wkv_b_split(D, 1, 0, p, p, p, None) == mla.ERR_INVALID_ARG
+    assert L.mla_wkv_b_split(D, 0, 0, p, None, p, None) == mla.ERR_INVALID_ARG
+    # materialised prefill: bf16 DeepSeek head shape only; workspace checked
+    v3 = mla.mla_dims(128, 512, 128, 64, 128, 7168, 0.0722, 10000.0)
+    V = ctypes.byref(v3)
+    args = lambda act, kv, ws, nb: (act, kv, p, p, p, 64, p, 256, p, p, None, p, None, None, 0,
+                                    ws, nb, None)
+    assert L.mla_prefill_materialized(D, *args(1, 1, p, 1 << 30)) == mla.ERR_UNSUPPORTED
+    assert L.mla_prefill_materialized(V, *args(0, 0, p, 1 << 30)) == mla.ERR_UNSUPPORTED
+    assert L.mla_prefill_materialized(V, *args(1, 2, p, 1 << 30)) == mla.ERR_UNSUPPORTED
+    need = mla.mla_materialized_workspace_bytes(v3, 64, 256, 0)
+    assert need > 0 and mla.mla_materialized_workspace_bytes(d, 64, 256, 0) == 0
+    assert L.mla_prefill_materialized(V, *args(1, 1, ctypes.c_void_p(256), need - 1)) == \
+        mla.ERR_WORKSPACE
+    assert L.mla_prefill_materialized(V, *args(1, 1, ctypes.c_void_p(272), need)) == \
+        mla.ERR_WORKSPACE  # not 256-byte aligned
+    # wo and out come together
+    a = list(args(1, 1, ctypes.c_void_p(256), need))
+    a[10] = p  # wo given, out missing
+    assert L.mla_prefill_materialized(V, *a) == mla.ERR_INVALID_ARG

@@ -1,6 +1,7 @@
 """Checks on the gfx950 assembly of the flash kernels (CPU only: hipcc cross-compiles).
 
-The bf16 tile copies are written as inline asm (LDS-direct loads through M0) that the
+The tile copies of the bf16 kernels (absorbed prefill and decode, materialised prefill) are
+written as inline asm (LDS-direct loads through M0) that the
 compiler's wait tracking does not see; their correctness rests on properties of the
 generated code that these tests pin:
 
@@ -21,8 +22,8 @@ import pytest
 
 from deepseek_mla_amd import build as B
 
-SRCS = [os.path.join(B.CSRC, f) for f in ("flash_mfma.hip", "decode_mfma.hip")]
-BF16_KERNELS = ("flash_prefill_bf16_kernel", "flash_decode_kernelILb0E")
+SRCS = [os.path.join(B.CSRC, f) for f in ("flash_mfma.hip", "decode_mfma.hip", "flash_mha.hip")]
+BF16_KERNELS = ("flash_prefill_bf16_kernel", "flash_decode_kernelILb0E", "flash_mha_kernel")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None,
                                 reason="hipcc not available")
@@ -61,7 +62,7 @@ def kernel_bodies(text):
 
 def bf16_bodies(text):
     b = {n: body for n, body in kernel_bodies(text).items() if any(k in n for k in BF16_KERNELS)}
-    assert len(b) == 2, sorted(kernel_bodies(text))
+    assert len(b) == 3, sorted(kernel_bodies(text))
     return b
 
 
@@ -98,17 +99,20 @@ def test_no_spill_access_in_copy_loops(asm):
             m = re.match(r"^\s*s_c?branch\w*\s+(\.LBB\w+)\s*$", line)
             if m and m.group(1) in labels and labels[m.group(1)] < i:
                 edges.append((labels[m.group(1)], i))
+        def instrs_of(h, e):
+            return [l.strip() for l in body[h:e + 1]
+                    if l.strip() and not l.strip().startswith((";", "."))]
+
+        # tile loops: loops that issue copies and carry matrix work; the innermost of them
+        # (an outer pass loop may spill around the tile loop)
+        tile = [(h, e) for h, e in edges
+                if any(x.startswith("global_load_lds") for x in instrs_of(h, e))
+                and sum(x.startswith("v_mfma") for x in instrs_of(h, e)) >= 32]
         loops = 0
-        for h, e in edges:
-            if any(h < h2 <= e and (h2, e2) != (h, e) for h2, e2 in edges):
-                continue  # not innermost (the outer pass loop may spill around the tile loop)
-            seg = body[h:e + 1]
-            instrs = [l.strip() for l in seg if l.strip() and not l.strip().startswith((";", "."))]
-            if not any(x.startswith("global_load_lds") for x in instrs):
+        for h, e in tile:
+            if any(h <= h2 and e2 <= e and (h2, e2) != (h, e) for h2, e2 in tile):
                 continue
-            if sum(x.startswith("v_mfma") for x in instrs) < 48:
-                continue  # only the tile loops
             loops += 1
-            spills = [x for x in instrs if x.startswith("scratch_")]
+            spills = [x for x in instrs_of(h, e) if x.startswith("scratch_")]
             assert not spills, f"{name}: spill access in the tile loop: {spills[:3]}"
         assert loops >= 1, f"{name}: tile loop not found"
