@@ -34,12 +34,6 @@
 
 #include <algorithm>
 
-#ifndef MH_NW
-#define MH_NW 8  // waves per workgroup
-#endif
-#ifndef MH_NS
-#define MH_NS 3  // LDS stages
-#endif
 
 namespace mla {
 
@@ -370,6 +364,30 @@ __global__ __launch_bounds__(256) void zero_cols_kernel(f16 *__restrict__ x, int
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// One chunk's attention launch.  8 waves (256 tokens) and 3 stages per workgroup, one
+// workgroup per CU; when that grid would leave CUs idle (few tokens per head chunk), 4 waves
+// (128 tokens) and 2 stages, two workgroups per CU.
+template <int NW, int NS>
+static hipError_t launch_mha(const bf16 *q_nope, const bf16 *qr, const int32_t *pos, int T, int H,
+                             int h0, int nh, const f16 *kn, const bf16 *cache, int W, int R,
+                             const f16 *vt, int vt_len, int n_kv, float sc, bf16 *v_out,
+                             float *lse, hipStream_t st) {
+    const size_t shm = (size_t)NS * mh::STAGE;
+    static bool attr_set = false;  // per process; every device takes the same value
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute((const void *)flash_mha_kernel<NW, NS>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)shm);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int nqb = (T + 32 * NW - 1) / (32 * NW);
+    hipLaunchKernelGGL((flash_mha_kernel<NW, NS>), dim3(nqb * nh), dim3(64 * NW), shm, st, q_nope,
+                       qr, pos, T, H, h0, nh, (const uint8_t *)kn, (const uint8_t *)cache,
+                       (int64_t)W * 2, R * 2, (const uint8_t *)vt, vt_len, n_kv, sc, v_out, lse);
+    return hipGetLastError();
+}
+
 static int vt_len_of(int n_kv) { return (n_kv + mh::NK - 1) / mh::NK * mh::NK; }
 
 size_t materialized_workspace_bytes(int T, int H, int R, int n_kv, int hc) {
@@ -399,16 +417,12 @@ hipError_t launch_prefill_materialized(const bf16 *q_nope, const bf16 *q_rope, c
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_rope_q<bf16>(q_rope, pos, qr, T, H, 0, DR, rope_base, st)) != hipSuccess)
         return e;
-    constexpr int KNW = MH_NW, KNS = MH_NS;
-    const size_t shm = (size_t)KNS * STAGE;
-    static bool attr_set = false;  // per process; every device takes the same value
-    if (!attr_set) {
-        e = hipFuncSetAttribute((const void *)flash_mha_kernel<KNW, KNS>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        if (e != hipSuccess) return e;
-        attr_set = true;
+    int n_cu = 256;
+    {
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess)
+            (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
     }
-    const int nqb = (T + 32 * KNW - 1) / (32 * KNW);
     for (int h0 = 0; h0 < H; h0 += hc) {
         const int nh = std::min(hc, H - h0);
         // k_nope[i][j][d] = sum_l c_kv[j][l] wk_b[h0+i][l][d]
@@ -425,12 +439,12 @@ hipError_t launch_prefill_materialized(const bf16 *q_nope, const bf16 *q_rope, c
                                st, vt, (int64_t)nh * DV, vt_len, n_kv);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        hipLaunchKernelGGL((flash_mha_kernel<KNW, KNS>), dim3(nqb * nh), dim3(64 * KNW), shm, st,
-                           q_nope, qr,
-                           pos, T, H, h0, nh, (const uint8_t *)kn, (const uint8_t *)cache,
-                           (int64_t)W * 2, R * 2, (const uint8_t *)vt, vt_len, n_kv,
-                           scale * LOG2E, v_out, lse);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const bool wide = (int64_t)((T + 255) / 256) * nh >= n_cu;
+        e = wide ? launch_mha<8, 3>(q_nope, qr, pos, T, H, h0, nh, kn, cache, W, R, vt, vt_len, n_kv,
+                                    scale * LOG2E, v_out, lse, st)
+                 : launch_mha<4, 2>(q_nope, qr, pos, T, H, h0, nh, kn, cache, W, R, vt, vt_len, n_kv,
+                                    scale * LOG2E, v_out, lse, st);
+        if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
