@@ -36,31 +36,42 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 # HBM bytes per launch of the dominant kernel(s), from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # passes scaled by a 512 MiB copy (fetch x2.0, write x1.0); the summaries and commands are
-# in profiles/.  Valid only for the kernel sources they were taken on (sha256 prefix over
-# the files listed, in order).
+# in profiles/.  Each figure is valid only for the kernel sources it was taken on (sha256
+# prefix over the files listed, in order).
+ABSORBED_SRC = ("deepseek_mla_amd/csrc/flash_mfma.hip", "deepseek_mla_amd/csrc/decode_mfma.hip",
+                "deepseek_mla_amd/csrc/latent_tile.h", "deepseek_mla_amd/csrc/lds_dma.h",
+                "deepseek_mla_amd/csrc/simt.hip", "deepseek_mla_amd/csrc/common.h")
+MATERIALIZED_SRC = ("deepseek_mla_amd/csrc/flash_mha.hip", "deepseek_mla_amd/csrc/latent_tile.h",
+                    "deepseek_mla_amd/csrc/lds_dma.h", "deepseek_mla_amd/csrc/common.h")
 TRAFFIC = {
-    "src": (("deepseek_mla_amd/csrc/flash_mfma.hip", "deepseek_mla_amd/csrc/decode_mfma.hip",
-             "deepseek_mla_amd/csrc/latent_tile.h", "deepseek_mla_amd/csrc/lds_dma.h",
-             "deepseek_mla_amd/csrc/simt.hip", "deepseek_mla_amd/csrc/common.h",
-             "deepseek_mla_amd/csrc/flash_mha.hip"), "9f64317baa84c09c"),
-    "lite_prefill": (71.35e6 + 82.26e6) + (61.83e6 + 15.32e6),      # prefill kernel + merge
-    "v3_long_prefill": 9804.50e6 + 1195.38e6,
-    "v3_decode": (39.24e6 + 16.84e6) + (17.43e6 + 0.14e6),          # partial kernel + combine
-    "v3_decode_q8": (245.72e6 + 16.84e6) + (17.43e6 + 0.54e6),      # partial kernel + combine
-    "v3_long_prefill@materialized": 193.52e6 + 18.87e6,             # one 8-head chunk launch
+    # workload: (bytes per launch, sources, sha256 prefix)
+    "lite_prefill": ((71.35e6 + 82.26e6) + (61.83e6 + 15.32e6), ABSORBED_SRC,
+                     "705d8b7c38267a3d"),                                         # prefill kernel + merge
+    "v3_long_prefill": (9804.50e6 + 1195.38e6, ABSORBED_SRC, "705d8b7c38267a3d"),
+    "v3_decode": ((39.24e6 + 16.84e6) + (17.43e6 + 0.14e6), ABSORBED_SRC,
+                  "705d8b7c38267a3d"),                                            # partial kernel + combine
+    "v3_decode_q8": ((245.72e6 + 16.84e6) + (17.43e6 + 0.54e6), ABSORBED_SRC, "705d8b7c38267a3d"),
+    "v3_long_prefill@materialized": (193.70e6 + 18.87e6, MATERIALIZED_SRC,
+                                     "d69295dd3c0935e8"),                         # one 8-head chunk launch
 }
 
 
-def measured_traffic(name):
+def _sources_sha(paths):
     import hashlib
-    paths, sha = TRAFFIC["src"]
     h = hashlib.sha256()
     for path in paths:
         with open(os.path.join(ROOT, path), "rb") as f:
             h.update(f.read())
-    if h.hexdigest()[:16] != sha:
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name):
+    if name not in TRAFFIC:
+        return None
+    value, paths, sha = TRAFFIC[name]
+    if _sources_sha(paths) != sha:
         return None  # kernels changed since the counters were taken
-    return TRAFFIC.get(name)
+    return value
 
 
 def log(*a):
