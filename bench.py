@@ -333,6 +333,51 @@ def run_one(name, steps, warmup, with_cpu, n_splits=0):
     return entry
 
 
+def decode_batch_sweep(batches=(1, 4, 16, 64), n_kv=32768, reps=20):
+    """mla_attn_decode (partials + combine) at V3 dims over batch sizes, random bf16 queries
+    and caches made on the device (timing only), copies rotated past the MALL.  Prints one
+    JSON line per batch size."""
+    import math
+    import torch
+    from deepseek_mla_amd import mla, synth
+    d = synth.deepseek_dims(128, 7168)
+    cd = mla.make_dims(d)
+    W, H, R = d.kv_lora_rank + d.qk_rope, d.n_head, d.kv_lora_rank
+    for B in batches:
+        per = B * n_kv * W * 2
+        copies = max(1, min(8, math.ceil(700e6 / per)))
+        caches = [torch.randn((B, n_kv, W), device="cuda").to(torch.bfloat16)
+                  for _ in range(copies)]
+        q = torch.randn((B, H, W), device="cuda").to(torch.bfloat16)
+        nkv = torch.full((B,), n_kv, dtype=torch.int32, device="cuda")
+        ns = mla.mla_decode_auto_splits(cd, mla.BF16, B, n_kv)
+        wsb = mla.mla_decode_workspace_bytes(cd, B, n_kv, 0)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        o = torch.empty((B, H, R), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+
+        def run(i):
+            mla.mla_attn_decode(cd, mla.BF16, mla.BF16, q, caches[i % copies], n_kv * W * 2, nkv,
+                                B, n_kv, 0, o, lse, ws, wsb)
+
+        for i in range(3):
+            run(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            run(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = B * (n_kv * W * 2 + H * W * 2 + H * R * 2)
+        print(json.dumps({"sweep": "v3_decode_batch", "B": B, "splits": ns, "us": ms * 1e3,
+                          "GB/s": nbytes / (ms * 1e-3) / 1e9,
+                          "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}), flush=True)
+        del caches, q, ws, o
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -345,6 +390,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0,
                     help="decode key splits per sequence (0 = the library's automatic choice)")
+    ap.add_argument("--decode-batch-sweep", action="store_true",
+                    help="only time V3 bf16 decode at B = 1, 4, 16, 64 (one JSON line each)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -354,6 +401,11 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.decode_batch_sweep:
+        from deepseek_mla_amd import mla
+        mla.lib()
+        decode_batch_sweep()
+        return
     if args.calibrate_copy:
         n = 512 << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
