@@ -161,6 +161,17 @@ int32_t mla_decode_auto_splits(const mla_dims *d, mla_dtype kv, int32_t B, int32
     return auto_splits(d, kv, B, n_kv_max);
 }
 
+// Decode of many sequences at once: with 128 heads (one row group of the prefill kernel per
+// sequence) and at least DEC_GROUPED_MIN_B sequences, the bf16 decode runs on the prefill
+// kernel over the batched caches (its key parts and their merge are the splits and their
+// combine); that kernel's tile loop sustains more of the MFMA rate than the 64-head decode
+// kernel's, and enough sequences fill the CUs.  Only with the automatic split count.
+constexpr int DEC_GROUPED_MIN_B = 16;
+static bool decode_grouped(const mla_dims *d, int kv, int B, int n_splits) {
+    return kv == MLA_BF16 && n_splits == 0 && d->n_head == 128 && bf16_attn_dims(d) &&
+           B >= DEC_GROUPED_MIN_B;
+}
+
 size_t mla_decode_workspace_bytes(const mla_dims *d, int32_t B, int32_t n_kv_max,
                                   int32_t n_splits) {
     if (!dims_ok(d) || B < 1 || n_kv_max < 1 || n_splits < 0 || n_splits > MAX_SPLITS) return 0;
@@ -173,7 +184,12 @@ size_t mla_decode_workspace_bytes(const mla_dims *d, int32_t B, int32_t n_kv_max
     if (S > n_kv_max) S = n_kv_max;
     const size_t rows = (size_t)B * S * d->n_head;
     // partial outputs: float32 on the float32 path, bfloat16 otherwise; sized for the larger
-    return align256(rows * d->kv_lora_rank * sizeof(float)) + align256(rows * sizeof(float));
+    size_t bytes = align256(rows * d->kv_lora_rank * sizeof(float)) + align256(rows * sizeof(float));
+    if (decode_grouped(d, MLA_BF16, B, n_splits)) {
+        const size_t g = prefill_workspace_bytes(B, d->n_head, n_kv_max, 128, true);
+        bytes = g > bytes ? g : bytes;
+    }
+    return bytes;
 }
 
 int mla_attn_decode(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *q_cat,
@@ -202,6 +218,13 @@ int mla_attn_decode(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *
     if (kv != MLA_F32 && !bf16_attn_dims(d)) return MLA_ERR_UNSUPPORTED;
     if (kv == MLA_F32 && d->kv_lora_rank > 1024) return MLA_ERR_UNSUPPORTED;
 
+    if (decode_grouped(d, kv, B, n_splits)) {
+        if (workspace_bytes < mla_decode_workspace_bytes(d, B, n_kv_max, 0)) return MLA_ERR_WORKSPACE;
+        if ((uintptr_t)workspace & 15) return MLA_ERR_INVALID_ARG;
+        return hip_status(launch_flash_prefill_bf16(
+            (const bf16 *)q_cat, nullptr, B, d->n_head, (const bf16 *)kv_cache, n_kv_max, 128,
+            d->scale, (bf16 *)o_lat, lse, workspace, as_stream(stream), kv_seq_stride_bytes, n_kv));
+    }
     int S = n_splits ? n_splits : auto_splits(d, kv, B, n_kv_max);
     if (S > n_kv_max) S = n_kv_max;
     int split_len, count;

@@ -96,11 +96,14 @@ hipError_t launch_gemv_nt_bf16(const bf16 *A, const bf16 *B, bf16 *C, int M, int
                                int64_t sB, int64_t sC, hipStream_t st);
 // prefill key parts: parts per row group (keys per part in *ks), and the workspace the
 // merge of parts needs (0 when every group is one part)
-int prefill_parts(int T, int H, int n_kv, int *ks);
-size_t prefill_workspace_bytes(int T, int H, int n_kv, int hc);
+// batched: one cache per token (sequence), of seq_n_kv[t] rows at cache + t * seq_stride
+// bytes, every row visible (decode of many sequences); needs hc == 128 (a group per token)
+int prefill_parts(int T, int H, int n_kv, int *ks, bool batched = false);
+size_t prefill_workspace_bytes(int T, int H, int n_kv, int hc, bool batched = false);
 hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int T, int H,
                                      const bf16 *cache, int n_kv, int hc, float scale,
-                                     bf16 *o_lat, float *lse, void *ws, hipStream_t st);
+                                     bf16 *o_lat, float *lse, void *ws, hipStream_t st,
+                                     int64_t seq_stride = 0, const int32_t *seq_n_kv = nullptr);
 // materialised (pp_opt) prefill: Dn 128, Dr 64, Dv 128; workspace bytes and the launch
 size_t materialized_workspace_bytes(int T, int H, int R, int n_kv, int hc);
 hipError_t launch_prefill_materialized(const bf16 *q_nope, const bf16 *q_rope, const int32_t *pos,

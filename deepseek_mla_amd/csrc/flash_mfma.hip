@@ -489,7 +489,7 @@ __device__ __forceinline__ float finish_f32(WaveState &st, uint8_t MLA_LDS *pbuf
 
 constexpr int PF_NW = 4, PF_NS = 4;
 constexpr int PF_ROWS = 32 * PF_NW;  // rows per workgroup
-constexpr int PF_MAX_PARTS = 4;      // key parts per row group (the merge keeps 8 weights)
+constexpr int PF_MAX_PARTS = 16;     // key parts per row group (the merge keeps one weight each)
 constexpr int PF_MAX_ITEMS = 1024;   // (row group, part) items when groups are cut
 // Block order of a cut prefill (a kernel argument: 2 KB, within the argument limit).
 constexpr int PF_LISTS = 256;       // workgroups of a cut prefill: one per CU, each with a list
@@ -497,7 +497,7 @@ struct PrefillOrder {
     uint16_t item[PF_MAX_ITEMS];  // unit * nparts + part, grouped by workgroup
     uint16_t start[PF_LISTS + 1];  // workgroup b takes item[start[b] .. start[b + 1])
 };
-static_assert(PF_MAX_PARTS <= 8, "the merge holds one log-sum-exp per part in lp[8]");
+static_assert(PF_MAX_PARTS <= 16, "the merge holds every part's log-sum-exp and row at once");
 
 // Prefill.  Rows are the flattened (token, head-in-chunk) pairs of all head chunks; a
 // group of 128 rows attends to its keys in parts of ks keys (part p: keys [p*ks,
@@ -513,7 +513,8 @@ __device__ __forceinline__ void prefill_item(
     int unit, int part, const bf16 *__restrict__ q_cat, const int32_t *__restrict__ pos, int T,
     int H, const uint8_t *__restrict__ cache, int n_kv, int hc, int n_groups, int n_chunks,
     float sc, bf16 *__restrict__ o_lat, float *__restrict__ lse, int ks, int nparts,
-    float *__restrict__ ws_o, float *__restrict__ ws_lse, int *__restrict__ ws_np) {
+    float *__restrict__ ws_o, float *__restrict__ ws_lse, int *__restrict__ ws_np,
+    int64_t seq_stride, const int32_t *__restrict__ seq_n_kv) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     uint8_t MLA_LDS *lds = (uint8_t MLA_LDS *)lds_raw;
     uint8_t MLA_LDS *pbuf = lds + PF_NS * fl::TILE_BYTES;
@@ -532,8 +533,16 @@ __device__ __forceinline__ void prefill_item(
     };
     int t, h;
     const bool valid = row_of(threadIdx.x & 63, w, t, h);
+    // Batched caches (seq_n_kv given; one token per group): the group's token is a sequence
+    // with its own rows at cache + t * seq_stride, all of its seq_n_kv[t] rows visible.
+    int n_rows = n_kv;
+    if (seq_n_kv) {
+        const int sq = __builtin_amdgcn_readfirstlane(grp);
+        n_rows = min(seq_n_kv[sq], n_kv);
+        cache += (int64_t)sq * seq_stride;
+    }
     int lim = -1;
-    if (valid) lim = min(pos[t], n_kv - 1);
+    if (valid) lim = seq_n_kv ? n_rows - 1 : min(pos[t], n_kv - 1);
 
     // key range of the group (max) and of each wave (min of the rows' last visible key)
     // Butterfly reductions within the wave, one barrier for the group (atomics on one LDS
@@ -550,8 +559,10 @@ __device__ __forceinline__ void prefill_item(
     }
     __syncthreads();
     const int kend = max(max(misc->wmax[0], misc->wmax[1]), max(misc->wmax[2], misc->wmax[3])) + 1;
-    const int np = (kend + ks - 1) / ks;  // parts holding keys of this group
-    if (part >= np) return;               // uniform: nothing to attend to
+    // parts holding keys of this group; a group whose rows see no key at all still has
+    // part 0, which writes its rows (zeros, lse -inf) after an empty key range
+    const int np = max(1, (kend + ks - 1) / ks);
+    if (part >= np) return;  // uniform: nothing to attend to
     WaveState st;
     load_q(st, q_cat + ((int64_t)t * H + h) * fl::W);
     const int wlim = misc->wmin[w];
@@ -559,7 +570,7 @@ __device__ __forceinline__ void prefill_item(
     // values live across the tile loop, which then spills.
     int kbeg = part * ks;
     asm volatile("" : "+s"(kbeg));
-    attend_range<PF_NW, PF_NS>(st, lds, pbuf, &misc->flag, cache, n_kv, kbeg,
+    attend_range<PF_NW, PF_NS>(st, lds, pbuf, &misc->flag, cache, n_rows, kbeg,
                                min(kbeg + ks, kend), lim, wlim, sc);
     // Output rows are recomputed here from the thread index: values kept from before the
     // key stream would stay live across it, crowd out the tile loop's registers and come
@@ -569,6 +580,9 @@ __device__ __forceinline__ void prefill_item(
     asm volatile("" : "+v"(tid));
     const int l = tid & 63;
     if (np == 1) {
+        // the group's part count tells the merge that these rows are final (the workspace
+        // is not initialised by the caller)
+        if (nparts > 1 && threadIdx.x == 0) ws_np[chunk * n_groups + grp] = 1;
         const float ls = finish(st, lds, pbuf, [&](int r) -> bf16 * {
             const int rr = grp * PF_ROWS + r;
             if (rr >= rows_total) return nullptr;
@@ -598,17 +612,18 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
     const uint8_t *__restrict__ cache, int n_kv, int hc, int n_groups, int n_chunks, float sc,
     bf16 *__restrict__ o_lat, float *__restrict__ lse, int ks, int nparts,
     float *__restrict__ ws_o, float *__restrict__ ws_lse, int *__restrict__ ws_np,
-    const PrefillOrder order) {
+    int64_t seq_stride, const int32_t *__restrict__ seq_n_kv, const PrefillOrder order) {
     if (nparts == 1) {
         prefill_item(blockIdx.x, 0, q_cat, pos, T, H, cache, n_kv, hc, n_groups, n_chunks, sc,
-                     o_lat, lse, ks, nparts, ws_o, ws_lse, ws_np);
+                     o_lat, lse, ks, nparts, ws_o, ws_lse, ws_np, seq_stride, seq_n_kv);
         return;
     }
     const int k1 = order.start[blockIdx.x + 1];
     for (int k = order.start[blockIdx.x]; k < k1; ++k) {
         const int it = order.item[k];
         prefill_item(it / nparts, it % nparts, q_cat, pos, T, H, cache, n_kv, hc, n_groups,
-                     n_chunks, sc, o_lat, lse, ks, nparts, ws_o, ws_lse, ws_np);
+                     n_chunks, sc, o_lat, lse, ks, nparts, ws_o, ws_lse, ws_np, seq_stride,
+                     seq_n_kv);
         __syncthreads();  // the item's output staging and exchange areas are free again
     }
 }
@@ -646,10 +661,17 @@ __global__ __launch_bounds__(64 * MG_ROWS) void prefill_merge_kernel(
 #pragma unroll
     for (int p = 0; p < PF_MAX_PARTS; ++p)
         if (p < np) m = fmaxf(m, lp[p]);
+    const int64_t orow = (int64_t)(rr / hc) * H + chunk * hc + rr % hc;
+    if (m == -INFINITY) {  // a row that sees no key (a negative position): zeros, lse -inf
+        const bf16x8 z = {};
+        *(bf16x8 *)(o_lat + orow * fl::R + l * 8) = z;
+        if (lse && l == 0) lse[orow] = -INFINITY;
+        return;
+    }
     float ssum = 0.0f;
 #pragma unroll
     for (int p = 0; p < PF_MAX_PARTS; ++p)
-        if (p < np) ssum += expf(lp[p] - m);  // m finite: part 0 holds key 0
+        if (p < np) ssum += expf(lp[p] - m);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < PF_MAX_PARTS; ++p) {
@@ -665,7 +687,6 @@ __global__ __launch_bounds__(64 * MG_ROWS) void prefill_merge_kernel(
     bf16x8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = f2bf(acc[e]);
-    const int64_t orow = (int64_t)(rr / hc) * H + chunk * hc + rr % hc;
     *(bf16x8 *)(o_lat + orow * fl::R + l * 8) = o;
     if (lse && l == 0) lse[orow] = m + logf(ssum);
 }
@@ -720,19 +741,22 @@ static double lpt_assign(const double *c, int n, int nb, uint16_t *sorted, uint1
 // depends on (T, H, n_kv) only: the part boundaries, hence the results, do not depend on
 // the head-chunk cap.  Part counts leave room for the extra groups of a chunked grouping
 // within the work-list capacity.
-int prefill_parts(int T, int H, int n_kv, int *ks) {
+int prefill_parts(int T, int H, int n_kv, int *ks, bool batched) {
     constexpr int NUM_CUS = 256;
     *ks = n_kv;
     const int64_t groups = ((int64_t)T * H + PF_ROWS - 1) / PF_ROWS;
     if (groups >= 2 * NUM_CUS || n_kv <= fl::NK) return 1;
-    static int64_t cache_key[3] = {-1, -1, -1};
+    static int64_t cache_key[4] = {-1, -1, -1, -1};
     static int cache_ks = 0;
-    const int64_t key[3] = {T, H, n_kv};
-    if (std::equal(key, key + 3, cache_key)) {
+    const int64_t key[4] = {T, H, n_kv, batched};
+    if (std::equal(key, key + 4, cache_key)) {
         *ks = cache_ks;
         return (n_kv + cache_ks - 1) / cache_ks;
     }
-    const int pmax = (int)std::min<int64_t>(PF_MAX_PARTS, PF_MAX_ITEMS / (groups + H));
+    // items G * P must fit the work lists; G <= groups + H over every head chunking (one
+    // chunk, G = groups, for batched caches)
+    const int pmax =
+        (int)std::min<int64_t>(PF_MAX_PARTS, PF_MAX_ITEMS / (batched ? groups : groups + H));
     double best = 1e30;
     int best_ks = n_kv;
     std::vector<double> c;
@@ -759,15 +783,15 @@ int prefill_parts(int T, int H, int n_kv, int *ks) {
             if (P == 1) break;
         }
     }
-    std::copy(key, key + 3, cache_key);
+    std::copy(key, key + 4, cache_key);
     cache_ks = best_ks;
     *ks = best_ks;
     return (n_kv + best_ks - 1) / best_ks;
 }
 
-size_t prefill_workspace_bytes(int T, int H, int n_kv, int hc) {
+size_t prefill_workspace_bytes(int T, int H, int n_kv, int hc, bool batched) {
     int ks;
-    const int P = prefill_parts(T, H, n_kv, &ks);
+    const int P = prefill_parts(T, H, n_kv, &ks, batched);
     if (P == 1) return 0;
     const int64_t G = (int64_t)(H / hc) * (((int64_t)T * hc + PF_ROWS - 1) / PF_ROWS);
     const size_t cnt = ((size_t)G * 4 + 255) & ~(size_t)255;  // part count per group
@@ -777,13 +801,16 @@ size_t prefill_workspace_bytes(int T, int H, int n_kv, int hc) {
 
 hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int T, int H,
                                      const bf16 *cache, int n_kv, int hc, float scale,
-                                     bf16 *o_lat, float *lse, void *ws, hipStream_t st) {
+                                     bf16 *o_lat, float *lse, void *ws, hipStream_t st,
+                                     int64_t seq_stride, const int32_t *seq_n_kv) {
     if (T <= 0) return hipSuccess;
     const int rows = T * hc;
     const int n_groups = (rows + PF_ROWS - 1) / PF_ROWS;
     const int n_chunks = H / hc;
     int ks;
-    const int P = prefill_parts(T, H, n_kv, &ks);
+    const bool batched = seq_n_kv != nullptr;
+    if (batched && hc != PF_ROWS) return hipErrorInvalidValue;  // one sequence per group
+    const int P = prefill_parts(T, H, n_kv, &ks, batched);
     const int64_t G = (int64_t)n_chunks * n_groups;
     int *ws_np = (int *)ws;
     float *ws_lse = (float *)((char *)ws + (((size_t)G * 4 + 255) & ~(size_t)255));
@@ -804,11 +831,11 @@ hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int 
     // never the results (every item is listed; one without keys returns at once).  The
     // lists depend only on (T, H, n_kv, hc); they are kept for the next call.
     static PrefillOrder order;
-    static int64_t order_key[4] = {-1, -1, -1, -1};
+    static int64_t order_key[5] = {-1, -1, -1, -1, -1};
     static int n_lists = 0;
-    const int64_t key[4] = {T, H, n_kv, hc};
+    const int64_t key[5] = {T, H, n_kv, hc, batched};
     if (P > 1 && G * P > PF_MAX_ITEMS) return hipErrorInvalidValue;  // prefill_parts leaves room
-    if (P > 1 && !std::equal(key, key + 4, order_key)) {
+    if (P > 1 && !std::equal(key, key + 5, order_key)) {
         const int n_items = (int)G * P;
         double cost[PF_MAX_ITEMS];
         for (int it = 0; it < n_items; ++it) {
@@ -828,12 +855,13 @@ hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int 
         int fillp[PF_LISTS];
         for (int b = 0; b < n_lists; ++b) fillp[b] = order.start[b];
         for (int k = 0; k < n_items; ++k) order.item[fillp[owner[k]]++] = sorted[k];
-        std::copy(key, key + 4, order_key);
+        std::copy(key, key + 5, order_key);
     }
     const unsigned nblocks = P > 1 ? (unsigned)n_lists : (unsigned)G;
     hipLaunchKernelGGL(flash_prefill_bf16_kernel, dim3(nblocks), dim3(64 * PF_NW), shm,
                        st, q_cat, pos, T, H, (const uint8_t *)cache, n_kv, hc, n_groups, n_chunks,
-                       scale * fl::LOG2E, o_lat, lse, ks, P, ws_o, ws_lse, ws_np, order);
+                       scale * fl::LOG2E, o_lat, lse, ks, P, ws_o, ws_lse, ws_np, seq_stride,
+                       seq_n_kv, order);
     if (P > 1) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
