@@ -133,6 +133,10 @@ int32_t mla_decode_auto_splits(const mla_dims *dims, mla_dtype kv, int32_t B, in
  * partial (o_s, lse_s) of the attention above over its rows, and a combine step
  * merges them:  lse = log sum_s exp(lse_s),  o_lat = sum_s exp(lse_s - lse) o_s.
  * Splits with no row contribute nothing (lse_s = -inf).
+ * With n_splits == 0, a bf16 cache, H == 128 and B >= 16 the same computation runs on the
+ * prefill kernel instead (one row group per sequence; its key parts, chosen by the
+ * library, are the splits and merge by the same rule); the workspace size function
+ * accounts for it.
  * q_cat [B][H][W] (act); kv_cache: sequence b's rows start at byte offset
  * b * kv_seq_stride_bytes (rows of W values for F32/BF16, of W/32*34 bytes for
  * Q8_0), the stride a multiple of 16 bytes (a Q8_0 sequence of N rows therefore takes
