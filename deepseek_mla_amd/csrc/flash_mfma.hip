@@ -631,7 +631,10 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
 // Merge of the key parts of the row groups that were cut (flash_prefill_bf16_kernel):
 // lse = log sum_p exp(lse_p), o = sum_p exp(lse_p - lse) o_p, the split-KV combine.
 // Block (group, slab of 4 rows); wave w takes one row, lane l columns 8l .. 8l+7.
+// MAXP: the largest part count the kernel handles (each thread holds every part's row piece
+// and lse at once, so fewer slots keep more waves resident).
 constexpr int MG_ROWS = 4;
+template <int MAXP>
 __global__ __launch_bounds__(64 * MG_ROWS) void prefill_merge_kernel(
     int T, int H, int hc, int n_groups, int nparts, const int *__restrict__ ws_np,
     const float *__restrict__ ws_o, const float *__restrict__ ws_lse, bf16 *__restrict__ o_lat,
@@ -646,10 +649,10 @@ __global__ __launch_bounds__(64 * MG_ROWS) void prefill_merge_kernel(
     const int l = threadIdx.x & 63;
     const int64_t slot0 = (int64_t)gid * nparts;
     // the lse and the rows of every part are requested together (one memory latency)
-    float lp[PF_MAX_PARTS];
-    f32x4 va[PF_MAX_PARTS], vb[PF_MAX_PARTS];
+    float lp[MAXP];
+    f32x4 va[MAXP], vb[MAXP];
 #pragma unroll
-    for (int p = 0; p < PF_MAX_PARTS; ++p) {
+    for (int p = 0; p < MAXP; ++p) {
         if (p < np) {
             lp[p] = ws_lse[(slot0 + p) * PF_ROWS + r];
             const float *src = ws_o + ((slot0 + p) * PF_ROWS + r) * fl::R + l * 8;
@@ -659,7 +662,7 @@ __global__ __launch_bounds__(64 * MG_ROWS) void prefill_merge_kernel(
     }
     float m = -INFINITY;
 #pragma unroll
-    for (int p = 0; p < PF_MAX_PARTS; ++p)
+    for (int p = 0; p < MAXP; ++p)
         if (p < np) m = fmaxf(m, lp[p]);
     const int64_t orow = (int64_t)(rr / hc) * H + chunk * hc + rr % hc;
     if (m == -INFINITY) {  // a row that sees no key (a negative position): zeros, lse -inf
@@ -670,11 +673,11 @@ __global__ __launch_bounds__(64 * MG_ROWS) void prefill_merge_kernel(
     }
     float ssum = 0.0f;
 #pragma unroll
-    for (int p = 0; p < PF_MAX_PARTS; ++p)
+    for (int p = 0; p < MAXP; ++p)
         if (p < np) ssum += expf(lp[p] - m);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int p = 0; p < PF_MAX_PARTS; ++p) {
+    for (int p = 0; p < MAXP; ++p) {
         if (p < np) {
             const float wt = expf(lp[p] - m) / ssum;
 #pragma unroll
@@ -865,9 +868,14 @@ hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int 
     if (P > 1) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(prefill_merge_kernel, dim3((unsigned)(G * (PF_ROWS / MG_ROWS))),
-                           dim3(64 * MG_ROWS), 0, st, T, H, hc, n_groups, P, ws_np, ws_o, ws_lse,
-                           o_lat, lse);
+        if (P <= 4)
+            hipLaunchKernelGGL(prefill_merge_kernel<4>, dim3((unsigned)(G * (PF_ROWS / MG_ROWS))),
+                               dim3(64 * MG_ROWS), 0, st, T, H, hc, n_groups, P, ws_np, ws_o,
+                               ws_lse, o_lat, lse);
+        else
+            hipLaunchKernelGGL(prefill_merge_kernel<PF_MAX_PARTS>,
+                               dim3((unsigned)(G * (PF_ROWS / MG_ROWS))), dim3(64 * MG_ROWS), 0, st,
+                               T, H, hc, n_groups, P, ws_np, ws_o, ws_lse, o_lat, lse);
     }
     return hipGetLastError();
 }
