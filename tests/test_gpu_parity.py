@@ -1035,3 +1035,32 @@ def test_decode_many_sequences(dev, B):
     # two GPU results, each within TOL of the exact one (the split kernel's parity is tested
     # on its own above): they may differ by the sum
     report("o_lat vs split kernel", rel_err_stored(outs[0][0], outs[1][0], "bf16"), 2 * TOL["bf16"])
+
+
+def test_decode_many_sequences_full_size(dev):
+    """16 V3 sequences of 32768 bf16 rows (the batched-cache decode at the size the decode
+    sweep times): every sequence against the oracle on 4 sampled heads."""
+    from deepseek_mla_amd import mla
+    d = synth.deepseek_dims(128, 7168)
+    B, N, W = 16, 32768, 576
+    g = torch.Generator(device="cpu").manual_seed(113)
+    cache_f = synth.round_bf16(torch.randn((B, N, W), generator=g).numpy())
+    q = synth.round_bf16(torch.randn((B, 128, W), generator=g).numpy())
+    lens = np.full(B, N, np.int32)
+    lens[3], lens[9] = 17, 20000
+    cd = mla.make_dims(d)
+    cache = torch.from_numpy(cache_f).to(dev).to(torch.bfloat16)
+    wsb = mla.mla_decode_workspace_bytes(cd, B, N, 0)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    o = torch.empty((B, 128, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, 128), dtype=torch.float32, device=dev)
+    mla.mla_attn_decode(cd, mla.BF16, mla.BF16, torch.from_numpy(q).to(dev).to(torch.bfloat16),
+                        cache, N * W * 2, torch.from_numpy(lens).to(dev), B, N, 0, o, lse, ws, wsb)
+    torch.cuda.synchronize()
+    got_o, got_l = o.float().cpu().numpy(), lse.cpu().numpy()
+    heads = np.array([0, 37, 90, 127])
+    for b in range(B):
+        ro, rl = oracle.attention(d, q[b:b + 1][:, heads], np.array([lens[b] - 1], np.int32),
+                                  cache_f[b, :lens[b]])
+        report(f"o_lat seq {b}", rel_err_stored(got_o[b][heads], ro[0], "bf16"), TOL["bf16"])
+        assert np.abs(got_l[b][heads] - rl[0]).max() <= TOL["bf16"]
