@@ -45,12 +45,12 @@ MATERIALIZED_SRC = ("deepseek_mla_amd/csrc/flash_mha.hip", "deepseek_mla_amd/csr
                     "deepseek_mla_amd/csrc/lds_dma.h", "deepseek_mla_amd/csrc/common.h")
 TRAFFIC = {
     # workload: (bytes per launch, sources, sha256 prefix)
-    "lite_prefill": ((71.37e6 + 82.25e6) + (61.82e6 + 15.32e6), ABSORBED_SRC,
-                     "e8ea48a278ff89da"),                                         # prefill kernel + merge
-    "v3_long_prefill": (9804.62e6 + 1195.38e6, ABSORBED_SRC, "e8ea48a278ff89da"),
-    "v3_decode": ((39.24e6 + 16.84e6) + (17.43e6 + 0.14e6), ABSORBED_SRC,
-                  "e8ea48a278ff89da"),                                            # partial kernel + combine
-    "v3_decode_q8": ((245.73e6 + 16.84e6) + (17.43e6 + 0.54e6), ABSORBED_SRC, "e8ea48a278ff89da"),
+    "lite_prefill": ((71.32e6 + 82.26e6) + (61.82e6 + 15.32e6), ABSORBED_SRC,
+                     "be9298de0b078631"),                                         # prefill kernel + merge
+    "v3_long_prefill": (9804.58e6 + 1195.38e6, ABSORBED_SRC, "be9298de0b078631"),
+    "v3_decode": ((39.25e6 + 16.84e6) + (17.43e6 + 0.14e6), ABSORBED_SRC,
+                  "be9298de0b078631"),                                            # partial kernel + combine
+    "v3_decode_q8": ((245.75e6 + 16.84e6) + (17.43e6 + 0.54e6), ABSORBED_SRC, "be9298de0b078631"),
     "v3_long_prefill@materialized": (193.71e6 + 18.87e6, MATERIALIZED_SRC,
                                      "8bb3e0163161f07e"),                         # one 8-head chunk launch
 }

@@ -297,20 +297,29 @@ __device__ __forceinline__ void softmax_tile(DqState &st, f32x4 (&s)[2], int key
     for (int i = 1; i < 8; ++i) sq.piece(i);
 }
 
-// Copies of the workgroup's 64 query rows into the query staging area (chunk-major: chunk
-// c of head h at (c*64 + h)*16, so that the fragment reads of 16 consecutive heads are
-// conflict-free).  Wave w issues chunks 18w .. 18w+17, one instruction each; heads past
-// H re-read head H-1 (their outputs are discarded).
+// Query staging layout: 16-byte chunk c (of 72) of head h (of 64) at slot
+// (c/8)*512 + h*8 + ((c%8) ^ (h%8)): blocks of 8 chunks (128 contiguous bytes of a row) per
+// head, so that one copy instruction moves 8 heads x 128 B (8 lanes per row: 8 cache lines
+// instead of 64 for a chunk of 64 heads), and the fragment reads of 16 consecutive heads
+// meet at most 2 per bank group.
+__device__ __forceinline__ int qslot(int c, int h) {
+    return (c >> 3) * 512 + h * 8 + ((c & 7) ^ (h & 7));
+}
+// Copies of the workgroup's 64 query rows into the staging area: instruction i (wave w
+// issues 18w .. 18w+17) fills slots 64i .. 64i+63, i.e. heads 8(i%8) .. +7 of chunk block
+// i/8; heads past H re-read head H-1 (their outputs are discarded).
 __device__ __forceinline__ void issue_query_copies(const bf16 *__restrict__ qb, int hbase, int H,
                                                    uint8_t MLA_LDS *qs) {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int l = threadIdx.x & 63;
     asm volatile("" : "+v"(l));
-    const uint32_t row = (uint32_t)min(hbase + l, H - 1) * (uint32_t)fl::RB;
 #pragma unroll
-    for (int i = 0; i < dq::QCOPY_PER; ++i) {
-        const int c = w * dq::QCOPY_PER + i;
-        lds_copy16((const uint8_t *)qb, row + (uint32_t)(c * 16), lds_u32(qs + c * 1024));
+    for (int i0 = 0; i0 < dq::QCOPY_PER; ++i0) {
+        const int i = w * dq::QCOPY_PER + i0;
+        const int h = (i & 7) * 8 + (l >> 3);
+        const int c = (i >> 3) * 8 + ((l & 7) ^ (h & 7));
+        const uint32_t off = (uint32_t)min(hbase + h, H - 1) * (uint32_t)fl::RB + (uint32_t)(c * 16);
+        lds_copy16((const uint8_t *)qb, off, lds_u32(qs + i * 1024));
     }
 }
 
@@ -324,7 +333,7 @@ __device__ __forceinline__ void read_query(DqState &st, const uint8_t MLA_LDS *q
         const int h = hh * 32 + hb * 16 + (l & 15);
 #pragma unroll
         for (int kk = 0; kk < dq::KSTEPS; ++kk)
-            st.q[hb][kk] = *(const bf16x8 MLA_LDS *)(qs + ((kk * 4 + g) * 64 + h) * 16);
+            st.q[hb][kk] = *(const bf16x8 MLA_LDS *)(qs + qslot(kk * 4 + g, h) * 16);
     }
 }
 
