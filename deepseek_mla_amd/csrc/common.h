@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/mla.h"
 
 namespace mla {
@@ -37,6 +39,20 @@ template <> __device__ __forceinline__ void st_f<bf16>(bf16 *p, float v) { *p = 
 // lgkmcnt[11:8] | vmcnt_hi[15:14]).
 #define MLA_WAIT_VMCNT(n)                                                                      \
     __builtin_amdgcn_s_waitcnt((((n)&0xF) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (0xF << 8)))
+
+// Raises a kernel's dynamic LDS limit to `bytes` on the current device, once per device
+// (the attribute is held per device).  `done` is the kernel's own bit mask of devices
+// already set; concurrent callers may both set it, which is harmless.
+inline hipError_t ensure_lds_limit(const void *fn, int bytes, std::atomic<uint64_t> &done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = 1ull << (dev & 63);
+    if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
 
 // ---- launchers (implemented in the .hip sources; all return hipError_t of launch)
 

@@ -655,25 +655,17 @@ hipError_t launch_flash_decode_bf16(const bf16 *q_cat, const void *cache, int ca
     const float sc = scale * fl::LOG2E;
     if (cache_q8) {
         const int shm = dq::lds_bytes(true);
-        static bool attr_set = false;
-        if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute((const void *)flash_decode_kernel<true>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, shm);
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
+        static std::atomic<uint64_t> lds_set{0};
+        const hipError_t e = ensure_lds_limit((const void *)flash_decode_kernel<true>, shm, lds_set);
+        if (e != hipSuccess) return e;
         hipLaunchKernelGGL(flash_decode_kernel<true>, dim3(nblocks), dim3(64 * dq::NW), shm, st,
                            q_cat, H, (const uint8_t *)cache, seq_stride_bytes, n_kv, n_kv_max,
                            n_splits, split_len, hgroups, units, sc, part_o, part_lse);
     } else {
         const int shm = dq::lds_bytes(false);
-        static bool attr_set = false;
-        if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute((const void *)flash_decode_kernel<false>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, shm);
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
+        static std::atomic<uint64_t> lds_set{0};
+        const hipError_t e = ensure_lds_limit((const void *)flash_decode_kernel<false>, shm, lds_set);
+        if (e != hipSuccess) return e;
         hipLaunchKernelGGL(flash_decode_kernel<false>, dim3(nblocks), dim3(64 * dq::NW), shm, st,
                            q_cat, H, (const uint8_t *)cache, seq_stride_bytes, n_kv, n_kv_max,
                            n_splits, split_len, hgroups, units, sc, part_o, part_lse);

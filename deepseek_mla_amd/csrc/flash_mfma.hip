@@ -33,6 +33,7 @@
 #include "latent_tile.h"
 
 #include <algorithm>
+#include <mutex>
 #include <utility>
 #include <vector>
 
@@ -619,8 +620,10 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
         return;
     }
     const int k1 = order.start[blockIdx.x + 1];
+    const int units = n_groups * n_chunks;
     for (int k = order.start[blockIdx.x]; k < k1; ++k) {
         const int it = order.item[k];
+        if (it / nparts >= units) continue;  // not an item of this launch (uniform)
         prefill_item(it / nparts, it % nparts, q_cat, pos, T, H, cache, n_kv, hc, n_groups,
                      n_chunks, sc, o_lat, lse, ks, nparts, ws_o, ws_lse, ws_np, seq_stride,
                      seq_n_kv);
@@ -737,6 +740,10 @@ static double lpt_assign(const double *c, int n, int nb, uint16_t *sorted, uint1
     return worst;
 }
 
+// The host-side plans below (key-part size, work lists) are kept for the next call with
+// the same shape; this lock guards them, so calls from several host threads are safe.
+static std::mutex plan_lock;
+
 // Parts per row group and keys per part.  Few row groups (fewer than two per CU) leave
 // the longest groups setting the time; their keys are then cut into up to 4 parts of a
 // fixed size ks (a multiple of the 32-key tile).  ks is chosen to minimise the estimated
@@ -749,6 +756,7 @@ int prefill_parts(int T, int H, int n_kv, int *ks, bool batched) {
     *ks = n_kv;
     const int64_t groups = ((int64_t)T * H + PF_ROWS - 1) / PF_ROWS;
     if (groups >= 2 * NUM_CUS || n_kv <= fl::NK) return 1;
+    std::lock_guard<std::mutex> guard(plan_lock);
     static int64_t cache_key[4] = {-1, -1, -1, -1};
     static int cache_ks = 0;
     const int64_t key[4] = {T, H, n_kv, batched};
@@ -802,6 +810,32 @@ size_t prefill_workspace_bytes(int T, int H, int n_kv, int hc, bool batched) {
     return cnt + ls + (size_t)G * P * PF_ROWS * fl::R * 4;
 }
 
+// Work lists of a cut prefill (G units x P parts) into `order`; returns the number of
+// lists (workgroups).
+static int build_order(int64_t G, int P, int ks, int T, int hc, int n_kv, int n_groups,
+                       int n_chunks, PrefillOrder &order) {
+    const int n_items = (int)G * P;
+    double cost[PF_MAX_ITEMS];
+    for (int it = 0; it < n_items; ++it) {
+        const int u = it / P, p = it % P;
+        bool cut;
+        const int t = est_tiles(n_groups - 1 - u / n_chunks, p, ks, T, hc, n_kv, &cut);
+        cost[it] = est_cost(t, cut);
+    }
+    uint16_t sorted[PF_MAX_ITEMS], owner[PF_MAX_ITEMS];
+    const int n_lists = std::min(PF_LISTS, n_items);
+    lpt_assign(cost, n_items, n_lists, sorted, owner);
+    int count[PF_LISTS];
+    std::fill(count, count + n_lists, 0);
+    for (int k = 0; k < n_items; ++k) ++count[owner[k]];
+    order.start[0] = 0;
+    for (int b = 0; b < n_lists; ++b) order.start[b + 1] = (uint16_t)(order.start[b] + count[b]);
+    int fillp[PF_LISTS];
+    for (int b = 0; b < n_lists; ++b) fillp[b] = order.start[b];
+    for (int k = 0; k < n_items; ++k) order.item[fillp[owner[k]]++] = sorted[k];
+    return n_lists;
+}
+
 hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int T, int H,
                                      const bf16 *cache, int n_kv, int hc, float scale,
                                      bf16 *o_lat, float *lse, void *ws, hipStream_t st,
@@ -820,45 +854,31 @@ hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int 
     float *ws_o = (float *)((char *)ws_lse + (((size_t)G * P * PF_ROWS * 4 + 255) & ~(size_t)255));
     if (P == 1) ws_np = nullptr, ws_lse = nullptr, ws_o = nullptr;
     const size_t shm = (size_t)PF_NS * fl::TILE_BYTES + PBUF_BYTES;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)flash_prefill_bf16_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t ea = ensure_lds_limit((const void *)flash_prefill_bf16_kernel, (int)shm, lds_set);
+    if (ea != hipSuccess) return ea;
     // Work lists of a cut prefill: items by decreasing estimated cost (tiles plus a fixed
     // per-item cost), each assigned to the least loaded of the PF_LISTS workgroups (longest
     // processing time first).  Estimated with the usual prefill positions (the T tokens
     // are the last T of the n_kv cached rows): only the schedule depends on this estimate,
     // never the results (every item is listed; one without keys returns at once).  The
-    // lists depend only on (T, H, n_kv, hc); they are kept for the next call.
-    static PrefillOrder order;
-    static int64_t order_key[5] = {-1, -1, -1, -1, -1};
-    static int n_lists = 0;
-    const int64_t key[5] = {T, H, n_kv, hc, batched};
+    // lists depend only on (T, H, n_kv, hc); they are kept for the next call, and each
+    // launch takes its own copy (made under the plan lock).
     if (P > 1 && G * P > PF_MAX_ITEMS) return hipErrorInvalidValue;  // prefill_parts leaves room
-    if (P > 1 && !std::equal(key, key + 5, order_key)) {
-        const int n_items = (int)G * P;
-        double cost[PF_MAX_ITEMS];
-        for (int it = 0; it < n_items; ++it) {
-            const int u = it / P, p = it % P;
-            bool cut;
-            const int t = est_tiles(n_groups - 1 - u / n_chunks, p, ks, T, hc, n_kv, &cut);
-            cost[it] = est_cost(t, cut);
+    PrefillOrder order;
+    int n_lists = 0;
+    if (P > 1) {
+        std::lock_guard<std::mutex> guard(plan_lock);
+        static PrefillOrder cached;
+        static int64_t cached_key[5] = {-1, -1, -1, -1, -1};
+        static int cached_lists = 0;
+        const int64_t key[5] = {T, H, n_kv, hc, batched};
+        if (!std::equal(key, key + 5, cached_key)) {
+            cached_lists = build_order(G, P, ks, T, hc, n_kv, n_groups, n_chunks, cached);
+            std::copy(key, key + 5, cached_key);
         }
-        uint16_t sorted[PF_MAX_ITEMS], owner[PF_MAX_ITEMS];
-        n_lists = std::min(PF_LISTS, n_items);
-        lpt_assign(cost, n_items, n_lists, sorted, owner);
-        int count[PF_LISTS];
-        std::fill(count, count + n_lists, 0);
-        for (int k = 0; k < n_items; ++k) ++count[owner[k]];
-        order.start[0] = 0;
-        for (int b = 0; b < n_lists; ++b) order.start[b + 1] = (uint16_t)(order.start[b] + count[b]);
-        int fillp[PF_LISTS];
-        for (int b = 0; b < n_lists; ++b) fillp[b] = order.start[b];
-        for (int k = 0; k < n_items; ++k) order.item[fillp[owner[k]]++] = sorted[k];
-        std::copy(key, key + 5, order_key);
+        order = cached;
+        n_lists = cached_lists;
     }
     const unsigned nblocks = P > 1 ? (unsigned)n_lists : (unsigned)G;
     hipLaunchKernelGGL(flash_prefill_bf16_kernel, dim3(nblocks), dim3(64 * PF_NW), shm,

@@ -373,14 +373,9 @@ static hipError_t launch_mha(const bf16 *q_nope, const bf16 *qr, const int32_t *
                              const f16 *vt, int vt_len, int n_kv, float sc, bf16 *v_out,
                              float *lse, hipStream_t st) {
     const size_t shm = (size_t)NS * mh::STAGE;
-    static bool attr_set = false;  // per process; every device takes the same value
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void *)flash_mha_kernel<NW, NS>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)shm);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = ensure_lds_limit((const void *)flash_mha_kernel<NW, NS>, (int)shm, lds_set);
+    if (e != hipSuccess) return e;
     const int nqb = (T + 32 * NW - 1) / (32 * NW);
     hipLaunchKernelGGL((flash_mha_kernel<NW, NS>), dim3(nqb * nh), dim3(64 * NW), shm, st, q_nope,
                        qr, pos, T, H, h0, nh, (const uint8_t *)kn, (const uint8_t *)cache,

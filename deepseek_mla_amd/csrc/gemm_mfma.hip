@@ -334,13 +334,10 @@ static hipError_t launch_lds_gemm(const bf16 *A, const bf16 *B, TO *C, int M, in
                                   int64_t sB, int64_t sC, const RopeTail &rope, hipStream_t st) {
     static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
     const int shm = NS * gl_stage_bytes(BM);
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)gemm_nt_bf16_lds_kernel<BM, NS, TO>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, shm);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e =
+        ensure_lds_limit((const void *)gemm_nt_bf16_lds_kernel<BM, NS, TO>, shm, lds_set);
+    if (e != hipSuccess) return e;
     dim3 grid((N + GL_BN - 1) / GL_BN, (M + BM - 1) / BM, batch);
     hipLaunchKernelGGL((gemm_nt_bf16_lds_kernel<BM, NS, TO>), grid, dim3(256), shm, st, A, B, C, M, N, K,
                        lda, ldb, ldc, sA, sB, sC, rope);

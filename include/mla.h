@@ -15,6 +15,10 @@
  *     by the mla_dtype arguments.  Device pointers must be 16-byte aligned.
  *   - Launches are asynchronous on `stream` (a hipStream_t; NULL = default stream).
  *     Nothing synchronises.
+ *   - Calls may come from several host threads at once.  The host-side plans the library
+ *     keeps between calls (prefill work lists, kernel attributes) are guarded by a lock.
+ *     Calls whose output or workspace buffers overlap must not run concurrently, on any
+ *     stream.
  *   - Every call validates its arguments before launching anything and returns an
  *     mla_status; nothing aborts or exits.  A shape or dtype a kernel does not
  *     implement returns MLA_ERR_UNSUPPORTED: no call silently switches to another
@@ -191,6 +195,12 @@ int mla_dequant_q8_0(const void *rows, float *out, int64_t n_rows, int32_t width
  * bytes of device memory, 256-byte aligned, contents need not be initialised; it holds
  * the transposed wk_b, the rotated query rope and one head chunk's keys and values.
  * Supported: act == kv == MLA_BF16, Dn 128, Dr 64, Dv 128, R % 8 == 0, scale > 0.
+ * Domain: q_nope and the decompressed k_nope and v are held in binary16 (IEEE half), so
+ * every q_nope value and every k_nope[h][j], v[h][j] component must lie within +-65504;
+ * the rope parts and all stored inputs and outputs stay bfloat16.  Outside that domain the
+ * half conversion gives +-inf and the affected rows come out inf or NaN (or lose those
+ * keys' contributions); the library does not scan the inputs to reject them.  The absorbed
+ * chain (mla_absorb_q, mla_attn_prefill, mla_out_proj) has no such limit.
  * Errors: INVALID_ARG (nulls, T < 0, n_kv < 1), UNSUPPORTED (other dtypes or dims),
  * WORKSPACE (missing, too small or misaligned). */
 int mla_prefill_materialized(const mla_dims *dims, mla_dtype act, mla_dtype kv,
