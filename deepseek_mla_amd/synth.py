@@ -162,6 +162,22 @@ def generate_workload(w: Workload) -> dict:
                     n_seq=(w.n_seq if w.kind == "decode" else None), mode=w.mode, pos=pos)
 
 
+def sample_tokens(T: int, k: int, seed: int) -> np.ndarray:
+    """Sorted indices of k seeded draws from range(T) (without replacement) together with
+    the first and the last token."""
+    rng = np.random.default_rng(seed)
+    s = set(rng.choice(T, size=min(k, T), replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(s))
+
+
+def long_prefill_sample(T: int = 8192) -> np.ndarray:
+    """The 64 query tokens of the long prefill that the CPU oracle computes (parity tests
+    and the CPU baseline): 62 seeded draws plus the first and the last token."""
+    sel = sample_tokens(T, 62, 62)
+    assert len(sel) == 64 and sel[0] == 0 and sel[-1] == T - 1
+    return sel
+
+
 def cache_rows(c_kv: np.ndarray, k_rope: np.ndarray) -> np.ndarray:
     """Lay out latent cache rows [c_kv | k_rope] along the last axis (float32)."""
     return np.ascontiguousarray(np.concatenate([c_kv, k_rope], axis=-1), dtype=np.float32)

@@ -56,6 +56,9 @@ def oracle_chain(dims, x, rows, qsel=None):
     return oracle.mla_absorbed(dims, q_nope, q_rope, pos, rows, x["wk_b"], x["wv_b"], x["wo"])
 
 
+ALL_STAGES = ("q_cat", "o_lat", "lse", "v", "out")
+
+
 def check_stages(got, ref, mode, sel=None, stages=("q_cat", "o_lat", "lse", "out")):
     tol = TOL[mode]
     for k in stages:
@@ -386,9 +389,7 @@ def test_decode_partial_head_groups(dev, H):
 # ------------------------------------------------------- full-size configs ---
 
 def _sample(T, k, seed):
-    rng = np.random.default_rng(seed)
-    s = set(rng.choice(T, size=min(k, T), replace=False).tolist()) | {0, T - 1}
-    return np.array(sorted(s))
+    return synth.sample_tokens(T, k, seed)
 
 
 def test_lite_prefill_full(dev):
@@ -402,7 +403,7 @@ def test_lite_prefill_full(dev):
     rows = synth.cache_rows(x["c_kv"][0], x["k_rope"][0])
     sel = _sample(w.T, 24, 61)
     ref = oracle_chain(w.dims, x, rows, qsel=sel)
-    check_stages(L.outputs(), ref, "bf16", sel=sel)
+    check_stages(L.outputs(), ref, "bf16", sel=sel, stages=ALL_STAGES)
 
 
 def test_v3_decode_full(dev):
@@ -414,12 +415,16 @@ def test_v3_decode_full(dev):
     torch.cuda.synchronize()
     rows = synth.cache_rows(x["c_kv"][0], x["k_rope"][0])
     ref = oracle_chain(w.dims, x, rows)
-    check_stages(L.outputs(), ref, "bf16")
+    check_stages(L.outputs(), ref, "bf16", stages=ALL_STAGES)
+
+
+long_prefill_sample = synth.long_prefill_sample
 
 
 def test_v3_long_prefill_sampled(dev):
     """8192 queries at 24576..32767 over 32768 rows with the 8192 MiB cap (8-head chunks);
-    the oracle checks 6 sampled queries (all 128 heads)."""
+    the oracle checks 64 queries (tokens 0 and 8191 among them), all 128 heads, every
+    stage."""
     from deepseek_mla_amd import layer
     w = synth.WORKLOADS["v3_long_prefill"]
     x = synth.generate_workload(w)
@@ -427,13 +432,14 @@ def test_v3_long_prefill_sampled(dev):
     L.step()
     torch.cuda.synchronize()
     rows = synth.cache_rows(x["c_kv"][0], x["k_rope"][0])
-    sel = _sample(w.T, 4, 62)
+    sel = long_prefill_sample(w.T)
     ref = oracle_chain(w.dims, x, rows, qsel=sel)
-    check_stages(L.outputs(), ref, "bf16", sel=sel)
+    check_stages(L.outputs(), ref, "bf16", sel=sel, stages=ALL_STAGES)
 
 
-def test_v3_decode_q8_sampled_heads(dev):
-    """4 sequences x 98304 Q8_0 rows; the oracle checks every sequence on 16 heads."""
+def test_v3_decode_q8_full(dev):
+    """4 sequences x 98304 Q8_0 rows: every stage of every sequence against the oracle
+    chain over the oracle's own dequantised rows (all 128 heads)."""
     from deepseek_mla_amd import layer
     w = synth.WORKLOADS["v3_decode_q8"]
     x = synth.generate_workload(w)
@@ -442,15 +448,13 @@ def test_v3_decode_q8_sampled_heads(dev):
     torch.cuda.synchronize()
     got = L.outputs()
     d = w.dims
-    heads = np.arange(0, 128, 8)
-    qc = oracle.absorb_q(d, x["q_nope"], x["q_rope"], x["pos"], x["wk_b"])
-    report("q_cat", rel_err_stored(got["q_cat"], qc, "q8_0"), 2e-2)
     for b in range(w.n_seq):
         rows = synth.cache_rows(x["c_kv"][b], x["k_rope"][b])
         rows = oracle.q8_0_dequantize(oracle.q8_0_quantize(rows), 576)
-        ro, rl = oracle.attention(d, qc[b:b + 1][:, heads], x["pos"][b:b + 1], rows)
-        report(f"o_lat seq {b}", rel_err_stored(got["o_lat"][b][heads], ro[0], "q8_0"), 2e-2)
-        report(f"lse seq {b} (abs)", float(np.abs(got["lse"][b][heads] - rl[0]).max()), 2e-2)
+        xb = {k: (v[b:b + 1] if k in ("q_nope", "q_rope", "pos") else v) for k, v in x.items()}
+        ref = oracle_chain(d, xb, rows)
+        print(f" seq {b}", flush=True)
+        check_stages({k: v[b:b + 1] for k, v in got.items()}, ref, "q8_0", stages=ALL_STAGES)
 
 
 @pytest.mark.parametrize("T", [1, 3, 8, 9])
@@ -761,7 +765,8 @@ def test_materialized_lite_full(dev):
 
 def test_materialized_v3_long_sampled(dev):
     """The V3 long prefill (8192 tokens at 24576..32767 over 32768 rows, 8192 MiB cap:
-    16 chunks of 8 heads) on the materialised path; 4 sampled tokens, all 128 heads."""
+    16 chunks of 8 heads) on the materialised path; 64 tokens (0 and 8191 among them), all
+    128 heads."""
     from deepseek_mla_amd import layer
     w = synth.WORKLOADS["v3_long_prefill"]
     x = synth.generate_workload(w)
@@ -769,7 +774,7 @@ def test_materialized_v3_long_sampled(dev):
     L.step()
     torch.cuda.synchronize()
     rows = synth.cache_rows(x["c_kv"][0], x["k_rope"][0])
-    sel = _sample(w.T, 4, 77)
+    sel = long_prefill_sample(w.T)
     ref = oracle_chain(w.dims, x, rows, qsel=sel)
     check_stages(L.outputs(), ref, "bf16", sel=sel, stages=MAT_STAGES)
 
