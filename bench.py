@@ -3,20 +3,26 @@
 A step is the whole path on one batch of synthetic input already resident in HBM:
 mla_absorb_q -> mla_attn_prefill (or mla_attn_decode) -> mla_out_proj.
 
-Default workload (the headline line): the DeepSeek-Lite-shaped prefill layer
-(16 heads, kv_lora_rank 512, rope 64, nope 128, v 128, d_model 2048; 2048 causal
-tokens over a 2048-row bf16 latent cache).  `value` is the step's algorithmic FLOP
-count (absorption GEMM + two-term attention + latent weighted sum + wv_b + wo, a
-multiply-add counted as 2 FLOP; attention priced per visible (query, key) pair as
-in the absorption page's section 7 table) divided by the step's wall time.
+Default workload (the headline line): the DeepSeek-V3-shaped long prefill (128 heads,
+kv_lora_rank 512, rope 64, nope 128, v 128, d_model 7168; 8192 query tokens at positions
+24576..32767, causal over a 32768-row bf16 latent cache, heads in -amb chunks under an
+8192 MiB cap), the largest single-GPU configuration.  `value` is the metric's attention
+TFLOP/s: the two-term score and the latent weighted sum priced per visible (query, key)
+pair as in the absorption page's section 7 table (2 * (576 + 512) FLOP per head, a
+multiply-add counted as 2), divided by the attention call's median duration (HIP events
+on the launch stream).  The whole step's rate (absorption GEMM + attention + wv_b + wo
+over the step's wall time) is reported beside it as `step_tflops`.
 
-The V3-shaped configurations run as extra entries under "workloads" (decode ones
-report latent-cache GB/s of the attention kernels, prefill ones TFLOP/s); each entry
-carries its own roofline object.  Decode timing rotates through several copies of
-the latent cache so that the 256 MB last-level cache cannot hold it between steps.
+The other workloads run as entries under "workloads" (decode ones report latent-cache
+GB/s of the attention kernels, prefill ones TFLOP/s); each entry carries its own roofline
+object and the median / p10 / p90 of its per-iteration attention times.  Decode timing
+rotates through several copies of the latent cache so that the 256 MB last-level cache
+cannot hold it between steps.
 
-`cpu_baseline` times the CPU oracle (test infrastructure) on a bounded sample of the
-same workload on this host's cores.
+`cpu_baseline` times the CPU oracle (test infrastructure) on this host's cores, threads
+pinned, on the same workload: in full where it finishes in seconds, else on a fixed sample
+whose time is extrapolated by visible-pair count (labelled so); a single-thread time on a
+smaller sample is reported beside it.
 """
 from __future__ import annotations
 
@@ -32,7 +38,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+MFMA_FLOP_PER_CLK = 256 * 4096  # chip-wide dense bf16 FLOP per clock
 
 # HBM bytes per launch of the dominant kernel(s), from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # passes scaled by a 512 MiB copy (fetch x2.0, write x1.0); the summaries and commands are
@@ -45,14 +52,11 @@ MATERIALIZED_SRC = ("deepseek_mla_amd/csrc/flash_mha.hip", "deepseek_mla_amd/csr
                     "deepseek_mla_amd/csrc/lds_dma.h", "deepseek_mla_amd/csrc/common.h")
 TRAFFIC = {
     # workload: (bytes per launch, sources, sha256 prefix)
-    "lite_prefill": ((71.32e6 + 82.26e6) + (61.82e6 + 15.32e6), ABSORBED_SRC,
-                     "be9298de0b078631"),                                         # prefill kernel + merge
-    "v3_long_prefill": (9804.58e6 + 1195.38e6, ABSORBED_SRC, "be9298de0b078631"),
-    "v3_decode": ((39.25e6 + 16.84e6) + (17.43e6 + 0.14e6), ABSORBED_SRC,
-                  "be9298de0b078631"),                                            # partial kernel + combine
-    "v3_decode_q8": ((245.75e6 + 16.84e6) + (17.43e6 + 0.54e6), ABSORBED_SRC, "be9298de0b078631"),
-    "v3_long_prefill@materialized": (193.71e6 + 18.87e6, MATERIALIZED_SRC,
-                                     "8bb3e0163161f07e"),                         # one 8-head chunk launch
+}
+# Sustained shader clock under each kernel's load (GHz): GRBM_GUI_ACTIVE cycles per
+# dispatch over the dispatch's duration, from the counter summaries in profiles/; keyed
+# like TRAFFIC.
+CLOCK_GHZ = {
 }
 
 
@@ -65,17 +69,32 @@ def _sources_sha(paths):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(name):
-    if name not in TRAFFIC:
+def _keyed(table, name):
+    if name not in table:
         return None
-    value, paths, sha = TRAFFIC[name]
+    value, paths, sha = table[name]
     if _sources_sha(paths) != sha:
         return None  # kernels changed since the counters were taken
     return value
 
 
+def measured_traffic(name):
+    return _keyed(TRAFFIC, name)
+
+
+def measured_clock(name):
+    return _keyed(CLOCK_GHZ, name)
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def stats(ms):
+    ms = np.asarray(ms, np.float64)
+    return {"median_ms": float(np.median(ms)), "p10_ms": float(np.percentile(ms, 10)),
+            "p90_ms": float(np.percentile(ms, 90)), "mean_ms": float(ms.mean()),
+            "iterations": int(ms.size)}
 
 
 def step_flops(w, pos) -> dict:
@@ -99,6 +118,26 @@ def attention_bytes(w) -> int:
     W = d.kv_lora_rank + d.qk_rope
     row = accounting.q8_0_row_bytes(W) if w.mode == "q8_0" else W * 2
     return accounting.decode_bytes(d, w.n_kv, w.n_seq, row)
+
+
+def copy_bandwidth(nbytes=1 << 30, reps=10):
+    """Measured device-to-device copy rate (read + write bytes per second, GB/s)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / s / 1e9
 
 
 def time_workload(w, steps, warmup, copies=1, n_splits=0):
@@ -127,9 +166,9 @@ def time_workload(w, steps, warmup, copies=1, n_splits=0):
     wall = (time.perf_counter() - t0) / steps
     parts = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
                       for e in ev])
-    res = {"ms_per_step": wall * 1e3, "absorb_ms": float(parts[:, 0].mean()),
-           "attention_ms": float(parts[:, 1].mean()), "out_proj_ms": float(parts[:, 2].mean()),
-           "attention_ms_min": float(parts[:, 1].min())}
+    res = {"ms_per_step": wall * 1e3, "absorb_ms": float(np.median(parts[:, 0])),
+           "attention_ms": float(np.median(parts[:, 1])),
+           "out_proj_ms": float(np.median(parts[:, 2])), "attention_stats": stats(parts[:, 1])}
     res["cache_append"] = time_append(w, L, steps)
     pos = L.pos.cpu().numpy()
     del L
@@ -164,13 +203,11 @@ def time_append(w, L, reps):
         mla.mla_cache_append(L.cdims, L.act, L.kv, c_kv, k_rope, pos, n_new, cache, n_rows,
                              dst_row=dst, stream=stream)
 
-    for _ in range(3):
-        run()
     def run_had():
         mla.mla_cache_append_hadamard(L.cdims, L.act, L.kv, c_kv, k_rope, pos, n_new, cache,
                                       n_rows, dst_row=dst, stream=stream)
 
-    reps = max(reps, 20)
+    reps = max(min(reps, 50), 20)
     in_b = 4 if w.mode == "f32" else 2
     nbytes = n_new * (W * in_b + 4 + (8 if dst is not None else 0) + L.row_bytes)
     res = {"kernel": "cache_append_kernel", "tokens": n_new, "bytes_per_launch": nbytes,
@@ -192,27 +229,37 @@ def time_append(w, L, reps):
     return res
 
 
-def cpu_baseline(w, max_queries):
-    """Oracle (absorb + attention + out_proj) on a bounded sample of the workload."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# Oracle coverage of each workload: prefill query-token sample (None = all tokens) for
+# the multi-thread timing, and the smaller sample of the single-thread timing.
+CPU_PLAN = {
+    "tiny_f32": (None, None),
+    "lite_prefill": (None, 64),
+    "v3_long_prefill": ("long64", 2),
+    "v3_decode": (None, None),
+    "v3_decode_q8": (None, 1),
+}
+
+
+def _oracle_run(w, x, rows_of, seqs):
+    """Runs the oracle chain over (sequence, query selection) pairs; returns seconds,
+    the algorithmic FLOP and the visible pairs covered."""
     import oracle
-    from deepseek_mla_amd import accounting, synth
-    x = synth.generate_workload(w)
+    from deepseek_mla_amd import accounting
     d = w.dims
-    if w.kind == "prefill":
-        sel = np.unique(np.linspace(0, w.T - 1, min(max_queries, w.T)).astype(int))
-        seqs = [(0, sel)]
-        sample = f"{len(sel)} of {w.T} query tokens (evenly spaced), all {d.n_head} heads"
-    else:
-        nseq = min(w.n_seq, max(1, max_queries))
-        seqs = [(b, np.array([b])) for b in range(nseq)]
-        sample = f"{nseq} of {w.n_seq} sequences, all {d.n_head} heads, all {w.n_kv} rows"
-    fl = 0
-    dt = 0.0
-    nbytes = 0
+    dt, fl, pairs = 0.0, 0, 0
     for b, sel in seqs:
-        rows = synth.cache_rows(x["c_kv"][b], x["k_rope"][b])
-        if w.mode == "q8_0":
-            rows = oracle.q8_0_dequantize(oracle.q8_0_quantize(rows), rows.shape[-1])
+        rows = rows_of(b)
         t0 = time.perf_counter()
         oracle.mla_absorbed(d, x["q_nope"][sel], x["q_rope"][sel], x["pos"][sel], rows,
                             x["wk_b"], x["wv_b"], x["wo"])
@@ -220,14 +267,80 @@ def cpu_baseline(w, max_queries):
         f = step_flops(w, x["pos"][sel])
         if w.kind == "decode":
             f["attention"] = accounting.absorbed_flops_per_pair(d) * w.n_kv
-        fl += f["attention"] if w.kind == "decode" else sum(f.values())
-        nbytes += attention_bytes(w) // w.n_seq
-    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
+            pairs += w.n_kv
+        else:
+            pairs += accounting.visible_pairs(x["pos"][sel], w.n_kv)
+        fl += sum(f.values())
+    return dt, fl, pairs
+
+
+def cpu_baseline(w):
+    """The oracle (absorb + attention + out_proj, test infrastructure) on this host's cores
+    with pinned threads, on the plan of CPU_PLAN; see the module docstring."""
+    import oracle
+    from deepseek_mla_amd import accounting, synth
+    x = synth.generate_workload(w)
+    d = w.dims
+    threads = oracle.max_threads()  # OMP_NUM_THREADS, or every core the process may use
+    multi, single = CPU_PLAN[w.name]
+    cache = {}
+
+    def rows_of(b):
+        if b not in cache:
+            cache.clear()
+            r = synth.cache_rows(x["c_kv"][b], x["k_rope"][b])
+            if w.mode == "q8_0":
+                r = oracle.q8_0_dequantize(oracle.q8_0_quantize(r), r.shape[-1])
+            cache[b] = r
+        return cache[b]
+
     if w.kind == "prefill":
-        return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-                "sample": sample + "; full step (absorb, attention, out_proj)", "seconds": dt}
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": sample + "; full step, bytes = latent rows + q_cat + o_lat", "seconds": dt}
+        all_tok = np.arange(w.T)
+        sel = synth.long_prefill_sample(w.T) if multi == "long64" else all_tok
+        seqs = [(0, sel)]
+        sample = (f"{len(sel)} of {w.T} query tokens (tokens 0 and {w.T - 1} among them), "
+                  f"all {d.n_head} heads" if multi == "long64" else
+                  f"all {w.T} query tokens, all {d.n_head} heads")
+        ssel = all_tok if single is None else sel[np.linspace(0, len(sel) - 1, single).astype(int)]
+        sseqs = [(0, ssel)]
+        total_pairs = accounting.visible_pairs(x["pos"], w.n_kv)
+        total_flops = sum(step_flops(w, x["pos"]).values())
+    else:
+        seqs = [(b, np.array([b])) for b in range(w.n_seq)]
+        sample = f"all {w.n_seq} sequences, all {d.n_head} heads, all {w.n_kv} rows"
+        sseqs = seqs if single is None else seqs[:single]
+        total_pairs = w.n_seq * w.n_kv
+        total_flops = None
+    dt, fl, pairs = _oracle_run(w, x, rows_of, seqs)
+    oracle.set_threads(1)
+    try:
+        dt1, fl1, pairs1 = _oracle_run(w, x, rows_of, sseqs)
+    finally:
+        oracle.set_threads(threads)
+    extrap = pairs < total_pairs
+    full_s = dt * total_pairs / pairs
+    full_s1 = dt1 * total_pairs / pairs1
+    res = {"cores": threads, "kind": "oracle", "cpu": cpu_model(),
+           "threads_pinned": os.environ.get("OMP_PROC_BIND", ""),
+           "places": os.environ.get("OMP_PLACES", ""),
+           "seconds": dt, "extrapolated": bool(extrap),
+           "full_workload_seconds": full_s,
+           "single_thread": {"seconds": dt1, "full_workload_seconds": full_s1,
+                             "sample": (f"{len(sseqs[0][1])} query tokens" if w.kind == "prefill"
+                                        else f"{len(sseqs)} of {w.n_seq} sequences")}}
+    label = " (extrapolated by visible-pair count)" if extrap else ""
+    if w.kind == "prefill":
+        res.update({"value": fl / dt / 1e12, "unit": "TFLOP/s",
+                    "sample": sample + "; full step (absorb, attention, out_proj)" + label})
+        res["single_thread"]["value"] = fl1 / dt1 / 1e12
+        if extrap:
+            res["full_workload_flops"] = total_flops
+    else:
+        nbytes = attention_bytes(w)
+        res.update({"value": nbytes / full_s / 1e9, "unit": "GB/s",
+                    "sample": sample + "; full step, bytes = latent rows + q_cat + o_lat"})
+        res["single_thread"]["value"] = nbytes / full_s1 / 1e9
+    return res
 
 
 def run_materialized(name, steps, warmup):
@@ -254,7 +367,8 @@ def run_materialized(name, steps, warmup):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    calls = [e[0].elapsed_time(e[1]) for e in ev]
+    ms = float(np.median(calls))
     pos = L.pos.cpu().numpy()
     del L
     torch.cuda.empty_cache()
@@ -263,7 +377,6 @@ def run_materialized(name, steps, warmup):
     attn = pairs * accounting.decompressed_flops_per_pair(d)
     decomp = 2 * w.n_kv * d.kv_lora_rank * d.n_head * (d.qk_nope + d.v_head)
     wo = 2 * len(pos) * d.d_model * d.n_head * d.v_head
-    absorbed = sum(step_flops(w, pos).values())
     att = attn / (ms * 1e-3) / 1e12
     return {"workload": name,
             "roofline": {"kernel": "flash_mha_kernel (all head chunks of the call)",
@@ -272,14 +385,11 @@ def run_materialized(name, steps, warmup):
                          "traffic": measured_traffic(name),
                          "per_launch": "attention FLOP = visible pairs x 640 x heads, over the "
                                        "whole call (decompression GEMMs, wo and launch gaps "
-                                       "included: a lower bound for the kernel)"}, "path": "materialized (decompress k_nope / v, then 192/128 "
-                                      "causal attention)",
-            "ms_per_step": wall * 1e3, "call_ms": ms,
+                                       "included: a lower bound for the kernel)"},
+            "path": "materialized (decompress k_nope / v, then 192/128 causal attention)",
+            "ms_per_step": wall * 1e3, "call_ms": ms, "call_stats": stats(calls),
             "flops_performed": {"attention": attn, "decompression": decomp, "wo": wo},
-            "performed_tflops": (attn + decomp + wo) / (ms * 1e-3) / 1e12,
-            "absorbed_equivalent_tflops": absorbed / (ms * 1e-3) / 1e12,
-            "note": "absorbed_equivalent_tflops prices the step with the absorbed path's "
-                    "FLOP count (the same result, 3.4x more attention FLOPs per pair)"}
+            "performed_tflops": (attn + decomp + wo) / (ms * 1e-3) / 1e12}
 
 
 def run_one(name, steps, warmup, with_cpu, n_splits=0):
@@ -298,19 +408,26 @@ def run_one(name, steps, warmup, with_cpu, n_splits=0):
     total = sum(fl.values())
     entry = {"workload": name, "ms_per_step": res["ms_per_step"],
              "kernel_ms": {k: res[k] for k in ("absorb_ms", "attention_ms", "out_proj_ms")},
+             "attention_stats": res["attention_stats"],
              "step_tflops": total / (res["ms_per_step"] * 1e-3) / 1e12,
              "cache_append": res["cache_append"]}
+    clk = measured_clock(name)
     if w.kind == "prefill":
         ach = fl["attention"] / (res["attention_ms"] * 1e-3) / 1e12
-        entry["value"] = entry["step_tflops"]
+        entry["value"] = ach
         entry["unit"] = "TFLOP/s"
         entry["attention_tflops"] = ach
-        entry["roofline"] = {"kernel": "flash_prefill_bf16_kernel (+ prefill_merge_kernel for cut row groups)", "bound": "mfma",
+        entry["roofline"] = {"kernel": "flash_prefill_bf16_kernel (+ prefill_merge_kernel for cut "
+                                       "row groups)", "bound": "mfma",
                              "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": ach / BF16_PEAK_TFLOPS, "traffic": measured_traffic(name),
                              "per_launch": f"{fl['attention']} FLOP = visible pairs x "
                                            f"{2 * (2 * w.dims.kv_lora_rank + w.dims.qk_rope)}"
                                            f" x {w.dims.n_head} heads"}
+        if clk:
+            pk = MFMA_FLOP_PER_CLK * clk * 1e9 / 1e12
+            entry["roofline"].update({"clock_ghz_measured": clk, "peak_at_measured_clock": pk,
+                                      "frac_at_measured_clock": ach / pk})
     else:
         nbytes = attention_bytes(w)
         ach = nbytes / (res["attention_ms"] * 1e-3) / 1e9
@@ -323,11 +440,11 @@ def run_one(name, steps, warmup, with_cpu, n_splits=0):
                              "mfma_frac": entry["attention_tflops"] / BF16_PEAK_TFLOPS,
                              "per_launch": f"{nbytes} B = {w.n_seq} x ({w.n_kv} latent rows + "
                                            f"q_cat + o_lat of {w.dims.n_head} heads)"}
+        if clk:
+            entry["roofline"]["clock_ghz_measured"] = clk
     if with_cpu:
         t0 = time.perf_counter()
-        mq = {"lite_prefill": 2048, "v3_long_prefill": 8, "v3_decode": 1, "v3_decode_q8": 1,
-              "tiny_f32": 16}[name]
-        entry["cpu_baseline"] = cpu_baseline(w, mq)
+        entry["cpu_baseline"] = cpu_baseline(w)
         log(f"[bench] {name}: cpu baseline {time.perf_counter() - t0:.1f}s")
     log(f"[bench] {name}: {json.dumps(entry)}")
     return entry
@@ -378,13 +495,17 @@ def decode_batch_sweep(batches=(1, 4, 16, 64), n_kv=32768, reps=20):
         torch.cuda.empty_cache()
 
 
+# Iterations per workload entry (the measurement protocol: 50 prefill, 200 decode).
+PROTOCOL_STEPS = {"prefill": 50, "decode": 200}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="lite_prefill")
-    ap.add_argument("--extra", default="v3_decode,v3_long_prefill,v3_decode_q8,"
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v3_long_prefill")
+    ap.add_argument("--extra", default="v3_decode,v3_decode_q8,lite_prefill,"
                                        "lite_prefill@materialized,v3_long_prefill@materialized",
                     help="comma-separated extra workloads reported under 'workloads' ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -399,6 +520,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the design for sharding is described in DESIGN.md).", file=sys.stderr)
         sys.exit(2)
+    # the CPU oracle's OpenMP threads are pinned to cores (read when its runtime loads)
+    os.environ.setdefault("OMP_PROC_BIND", "close")
+    os.environ.setdefault("OMP_PLACES", "cores")
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.decode_batch_sweep:
@@ -416,15 +540,29 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
         return
-    from deepseek_mla_amd import mla
+    from deepseek_mla_amd import mla, synth
     mla.lib()
+    copy_gbs = copy_bandwidth()
+    log(f"[bench] device copy: {copy_gbs:.0f} GB/s (read + write)")
     main_entry = run_one(args.workload, args.steps, args.warmup, not args.no_cpu_baseline,
                          args.splits)
     extras = []
     for name in [n for n in args.extra.split(",") if n and n != args.workload]:
-        steps = max(3, args.steps // 2) if "long" in name else args.steps
+        kind = synth.WORKLOADS[name.split("@")[0]].kind
+        steps = PROTOCOL_STEPS[kind]
         extras.append(run_one(name, steps, args.warmup, not args.no_cpu_baseline, args.splits))
-    from deepseek_mla_amd import synth
+    # the materialised path against the absorbed step of the same workload
+    absorbed = {e["workload"]: e["ms_per_step"] for e in [main_entry] + extras
+                if "@" not in e["workload"]}
+    for e in extras:
+        base = e["workload"].split("@")[0]
+        if "@materialized" in e["workload"] and base in absorbed:
+            e["speedup_vs_absorbed"] = absorbed[base] / e["ms_per_step"]
+            e["speedup_note"] = "absorbed step ms (absorb + attention + out_proj) / this step ms"
+    for e in [main_entry] + extras:
+        if e["roofline"]["bound"] == "hbm":
+            e["roofline"]["copy_gbs_measured"] = copy_gbs
+            e["roofline"]["frac_of_measured_copy"] = e["roofline"]["achieved"] / copy_gbs
     w = synth.WORKLOADS[args.workload]
     line = {
         "metric": "MLA attention TFLOP/s (prefill) and latent-cache GB/s (decode), 1 MI355X",
@@ -436,10 +574,14 @@ def main():
                    "kv_lora_rank": w.dims.kv_lora_rank, "qk_rope": w.dims.qk_rope,
                    "qk_nope": w.dims.qk_nope, "v_head": w.dims.v_head,
                    "d_model": w.dims.d_model, "query_tokens": w.n_query, "n_kv": w.n_kv,
-                   "cache": w.mode, "flop_count": "absorb + attention + out_proj per step"},
+                   "cache": w.mode, "scratch_cap_mib": w.scratch_cap_mib,
+                   "value": "attention FLOP (visible pairs x 2176 x heads) / median attention "
+                            "call time"},
         "roofline": main_entry["roofline"],
+        "attention_stats": main_entry["attention_stats"],
         "kernel_ms": main_entry["kernel_ms"],
-        "attention_tflops": main_entry.get("attention_tflops"),
+        "step_tflops": main_entry["step_tflops"],
+        "copy_gbs_measured": copy_gbs,
         "cache_append": main_entry["cache_append"],
         "workloads": extras,
     }

@@ -172,6 +172,13 @@ static bool decode_grouped(const mla_dims *d, int kv, int B, int n_splits) {
            B >= DEC_GROUPED_MIN_B;
 }
 
+// Workspace bytes the decode of these arguments uses with a cache of type kv: the split
+// partials (float32 on the float32 path, bfloat16 otherwise) and their lse, or the batched
+// prefill's part buffers.  mla_decode_workspace_bytes reports the largest of these over the
+// cache types.
+static size_t decode_need_bytes(const mla_dims *d, int kv, int32_t B, int32_t n_kv_max,
+                                int32_t n_splits);
+
 size_t mla_decode_workspace_bytes(const mla_dims *d, int32_t B, int32_t n_kv_max,
                                   int32_t n_splits) {
     if (!dims_ok(d) || B < 1 || n_kv_max < 1 || n_splits < 0 || n_splits > MAX_SPLITS) return 0;
@@ -192,10 +199,28 @@ size_t mla_decode_workspace_bytes(const mla_dims *d, int32_t B, int32_t n_kv_max
     return bytes;
 }
 
+// mla_attn_decode with the workspace checked against the exact need of this cache type
+// (mla_attn_decode's own check is against the larger size its callers are told).
+static int decode_impl(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *q_cat,
+                       const void *kv_cache, int64_t kv_seq_stride_bytes, const int32_t *n_kv,
+                       int32_t B, int32_t n_kv_max, int32_t n_splits, void *o_lat, float *lse,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
 int mla_attn_decode(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *q_cat,
                     const void *kv_cache, int64_t kv_seq_stride_bytes, const int32_t *n_kv,
                     int32_t B, int32_t n_kv_max, int32_t n_splits, void *o_lat, float *lse,
                     void *workspace, size_t workspace_bytes, void *stream) {
+    if (dims_ok(d) && B > 0 && n_kv_max > 0 && n_splits >= 0 && n_splits <= MAX_SPLITS &&
+        workspace_bytes < mla_decode_workspace_bytes(d, B, n_kv_max, n_splits))
+        workspace_bytes = 0;  // smaller than this call's documented size: rejected below
+    return decode_impl(d, act, kv, q_cat, kv_cache, kv_seq_stride_bytes, n_kv, B, n_kv_max,
+                       n_splits, o_lat, lse, workspace, workspace_bytes, stream);
+}
+
+static int decode_impl(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *q_cat,
+                       const void *kv_cache, int64_t kv_seq_stride_bytes, const int32_t *n_kv,
+                       int32_t B, int32_t n_kv_max, int32_t n_splits, void *o_lat, float *lse,
+                       void *workspace, size_t workspace_bytes, void *stream) {
     if (!dims_ok(d) || !act_ok(act) || B < 0 || n_kv_max < 1 || n_splits < 0 ||
         n_splits > MAX_SPLITS)
         return MLA_ERR_INVALID_ARG;
@@ -218,8 +243,8 @@ int mla_attn_decode(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *
     if (kv != MLA_F32 && !bf16_attn_dims(d)) return MLA_ERR_UNSUPPORTED;
     if (kv == MLA_F32 && d->kv_lora_rank > 1024) return MLA_ERR_UNSUPPORTED;
 
+    if (workspace_bytes < decode_need_bytes(d, kv, B, n_kv_max, n_splits)) return MLA_ERR_WORKSPACE;
     if (decode_grouped(d, kv, B, n_splits)) {
-        if (workspace_bytes < mla_decode_workspace_bytes(d, B, n_kv_max, 0)) return MLA_ERR_WORKSPACE;
         if ((uintptr_t)workspace & 15) return MLA_ERR_INVALID_ARG;
         return hip_status(launch_flash_prefill_bf16(
             (const bf16 *)q_cat, nullptr, B, d->n_head, (const bf16 *)kv_cache, n_kv_max, 128,
@@ -229,7 +254,6 @@ int mla_attn_decode(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *
     if (S > n_kv_max) S = n_kv_max;
     int split_len, count;
     split_plan(kv, n_kv_max, S, &split_len, &count);
-    if (workspace_bytes < mla_decode_workspace_bytes(d, B, n_kv_max, S)) return MLA_ERR_WORKSPACE;
     const size_t rows = (size_t)B * count * d->n_head;
     const size_t po_elem = kv == MLA_F32 ? sizeof(float) : sizeof(bf16);
     void *part_o = workspace;
@@ -252,6 +276,19 @@ int mla_attn_decode(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *
                                            d->kv_lora_rank, count, (bf16 *)o_lat, lse, st);
     }
     return hip_status(e);
+}
+
+static size_t decode_need_bytes(const mla_dims *d, int kv, int32_t B, int32_t n_kv_max,
+                                int32_t n_splits) {
+    if (decode_grouped(d, kv, B, n_splits))
+        return prefill_workspace_bytes(B, d->n_head, n_kv_max, 128, true);
+    int S = n_splits ? n_splits : auto_splits(d, kv, B, n_kv_max);
+    if (S > n_kv_max) S = n_kv_max;
+    int split_len, count;
+    split_plan(kv, n_kv_max, S, &split_len, &count);
+    const size_t rows = (size_t)B * count * d->n_head;
+    const size_t po_elem = kv == MLA_F32 ? sizeof(float) : sizeof(bf16);
+    return align256(rows * d->kv_lora_rank * po_elem) + align256(rows * sizeof(float));
 }
 
 int mla_out_proj(const mla_dims *d, mla_dtype act, const void *o_lat, const void *wv_b,

@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.orc_q8_0_dequantize.argtypes = [_u8p, ctypes.c_int64, i, _f32p]
         L.orc_heads_per_chunk.argtypes = [i, d, i]
         L.orc_heads_per_chunk.restype = i
+        L.orc_set_threads.argtypes = [i]
+        L.orc_max_threads.restype = i
         _lib = L
     return _lib
 
@@ -250,6 +252,15 @@ def wkv_b_split(dims, wkv_b):
     Dn = dims.qk_nope
     return (np.ascontiguousarray(wkv_b[:, :Dn, :].transpose(0, 2, 1)),
             np.ascontiguousarray(wkv_b[:, Dn:, :]))
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of the oracle's loops (timing only; results do not depend on it)."""
+    lib().orc_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
 
 
 def heads_per_chunk(n_head: int, size_mib: float, cap_mib: int) -> int:

@@ -22,9 +22,15 @@
  * "ik_llama.cpp PR #394" section 3.2 (ggml {Dn,R,H} and {R,Dv,H}).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Thread count of the parallel loops below (the timing of the CPU baseline sets it;
+ * results do not depend on it: every output element is summed by one thread). */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int orc_max_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- RoPE ---
  * Rotary position embedding of one vector of even length dr at position pos.
