@@ -2,6 +2,8 @@
 // Every check happens before the first launch; no call allocates device memory.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 
 using namespace mla;
@@ -289,6 +291,47 @@ static size_t decode_need_bytes(const mla_dims *d, int kv, int32_t B, int32_t n_
     const size_t rows = (size_t)B * count * d->n_head;
     const size_t po_elem = kv == MLA_F32 ? sizeof(float) : sizeof(bf16);
     return align256(rows * d->kv_lora_rank * po_elem) + align256(rows * sizeof(float));
+}
+
+// The allocation-free decode: the workspace is a file-scope device array of
+// MLA_DECODE_STATIC_BYTES, one copy per device (the runtime creates it when the library's
+// code is loaded onto that device).  Host code never passes the array's name to a kernel:
+// its device address, taken once per device with hipGetSymbolAddress, is kept in
+// static_scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[MLA_DECODE_STATIC_BYTES];
+
+static std::mutex static_scratch_lock;
+static void *static_scratch_ptr[64];
+
+static int static_scratch(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MLA_ERR_HIP;
+    std::lock_guard<std::mutex> guard(static_scratch_lock);
+    if (!static_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_ERR_HIP;
+        static_scratch_ptr[dev] = p;
+    }
+    *out = static_scratch_ptr[dev];
+    return MLA_OK;
+}
+
+int mla_attn_decode_static(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *q_cat,
+                           const void *kv_cache, int64_t kv_seq_stride_bytes,
+                           const int32_t *n_kv, int32_t B, int32_t n_kv_max, int32_t n_splits,
+                           void *o_lat, float *lse, void *stream) {
+    if (!dims_ok(d) || B < 0 || n_kv_max < 1 || n_splits < 0 || n_splits > MAX_SPLITS)
+        return MLA_ERR_INVALID_ARG;
+    if (kv != MLA_F32 && kv != MLA_BF16 && kv != MLA_Q8_0) return MLA_ERR_INVALID_ARG;
+    if (B == 0) return MLA_OK;
+    if (decode_need_bytes(d, kv, B, n_kv_max, n_splits) > MLA_DECODE_STATIC_BYTES)
+        return MLA_ERR_WORKSPACE;
+    if (!q_cat || !kv_cache || !n_kv || !o_lat) return MLA_ERR_INVALID_ARG;
+    void *ws = nullptr;
+    const int s = static_scratch(&ws);
+    if (s != MLA_OK) return s;
+    return decode_impl(d, act, kv, q_cat, kv_cache, kv_seq_stride_bytes, n_kv, B, n_kv_max,
+                       n_splits, o_lat, lse, ws, MLA_DECODE_STATIC_BYTES, stream);
 }
 
 int mla_out_proj(const mla_dims *d, mla_dtype act, const void *o_lat, const void *wv_b,

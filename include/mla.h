@@ -157,6 +157,27 @@ int mla_attn_decode(const mla_dims *dims, mla_dtype act, mla_dtype kv, const voi
                     int32_t B, int32_t n_kv_max, int32_t n_splits, void *o_lat, float *lse,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* Size of the device scratch array behind mla_attn_decode_static (bytes, per device). */
+#define MLA_DECODE_STATIC_BYTES (64u << 20)
+
+/* mla_attn_decode without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The partial results live in a file-scope device array of
+ * MLA_DECODE_STATIC_BYTES bytes, one per device, held from the library's load onto the
+ * device until the process ends; the call allocates nothing (its first call on a device
+ * looks up that device's array address once).  Same arguments, semantics, kernels and
+ * results as mla_attn_decode.  The array needs no initialisation and keeps the last call's
+ * partials.  All calls on one device share the one array: calls that may overlap in time
+ * on one device (different streams, or host threads racing on one stream) race on it and
+ * must be serialised by the caller.
+ * Errors: as mla_attn_decode; WORKSPACE when this call's partials would need more than
+ * MLA_DECODE_STATIC_BYTES (V3 dims: one or four sequences of up to 98304 rows with the
+ * automatic split count fit; use mla_attn_decode with a workspace beyond that). */
+int mla_attn_decode_static(const mla_dims *dims, mla_dtype act, mla_dtype kv, const void *q_cat,
+                           const void *kv_cache, int64_t kv_seq_stride_bytes,
+                           const int32_t *n_kv, int32_t B, int32_t n_kv_max, int32_t n_splits,
+                           void *o_lat, float *lse, void *stream);
+
 /* Late V decompression and output projection (absorption page, section 4):
  *   v[t][h*Dv + d] = sum_l wv_b[h][d][l] * o_lat[t][h][l]     (einsum bhqc,hdc->bhqd)
  *   out[t][e]      = sum_k wo[e][k] * v[t][k]                  (einsum hdD,bhqd->bqD)

@@ -131,3 +131,22 @@ def test_new_entry_points_validate_without_gpu():
     a = list(args(1, 1, ctypes.c_void_p(256), need))
     a[10] = p  # wo given, out missing
     assert L.mla_prefill_materialized(V, *a) == mla.ERR_INVALID_ARG
+
+
+def test_static_decode_validates_without_gpu():
+    """The allocation-free decode rejects a call whose partials exceed its device array
+    (and invalid arguments) before touching the GPU."""
+    L = mla.lib()
+    v3 = mla.mla_dims(128, 512, 128, 64, 128, 7168, 0.0722, 10000.0)
+    V = ctypes.byref(v3)
+    p = ctypes.c_void_p(16)
+    # 64 sequences x 98304 rows, 10 splits each: 64 * 10 * 128 partial rows of 1 KB > 64 MiB
+    assert L.mla_attn_decode_static(V, 1, 1, p, p, 98304 * 1152, p, 64, 98304, 10, p, None,
+                                    None) == mla.ERR_WORKSPACE
+    assert L.mla_attn_decode_static(None, 1, 1, p, p, 1152, p, 1, 1, 0, p, None,
+                                    None) == mla.ERR_INVALID_ARG
+    assert L.mla_attn_decode_static(V, 1, 1, None, p, 1152, p, 1, 1, 0, p, None,
+                                    None) == mla.ERR_INVALID_ARG
+    assert L.mla_attn_decode_static(V, 1, 1, None, None, 0, None, 0, 1, 0, None, None,
+                                    None) == mla.OK
+    assert mla.MLA_DECODE_STATIC_BYTES == 64 << 20
