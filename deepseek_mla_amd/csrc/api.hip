@@ -31,12 +31,19 @@ constexpr int SIMT_SPLIT_GRAIN = 64;
 constexpr int MAX_SPLITS = 4096;  // largest split count accepted
 constexpr int MFMA_SPLIT_GRAIN = 32;
 
+// A Q8_0 cache with whole groups of 128 heads decodes on the wide kernel (128 heads per
+// workgroup, every raw tile dequantised once for all of them).
+bool decode_q8_wide(const mla_dims *d, int kv) {
+    return kv == MLA_Q8_0 && d->n_head % decode_wide_heads() == 0;
+}
+
 int auto_splits(const mla_dims *d, int kv, int B, int n_kv_max) {
     if (kv == MLA_F32) {
         int s = (n_kv_max + 255) / 256;
         return s < 1 ? 1 : (s > 64 ? 64 : s);
     }
-    const int hgroups = (d->n_head + decode_heads_per_block() - 1) / decode_heads_per_block();
+    const int hpb = decode_q8_wide(d, kv) ? decode_wide_heads() : decode_heads_per_block();
+    const int hgroups = (d->n_head + hpb - 1) / hpb;
     const int per_seq = (B * hgroups);
     int s = (NUM_CUS + per_seq - 1) / per_seq;
     // at least 4 tiles of 32 keys per split
@@ -187,8 +194,10 @@ size_t mla_decode_workspace_bytes(const mla_dims *d, int32_t B, int32_t n_kv_max
     int S = n_splits;
     if (S == 0) {
         // the largest automatic choice over cache types
-        int a = auto_splits(d, MLA_F32, B, n_kv_max), b = auto_splits(d, MLA_BF16, B, n_kv_max);
+        const int a = auto_splits(d, MLA_F32, B, n_kv_max), b = auto_splits(d, MLA_BF16, B, n_kv_max),
+                  c = auto_splits(d, MLA_Q8_0, B, n_kv_max);
         S = a > b ? a : b;
+        S = S > c ? S : c;
     }
     if (S > n_kv_max) S = n_kv_max;
     const size_t rows = (size_t)B * S * d->n_head;
@@ -270,9 +279,14 @@ static int decode_impl(const mla_dims *d, mla_dtype act, mla_dtype kv, const voi
             e = launch_combine<float, float>((const float *)part_o, part_lse, B, d->n_head,
                                              d->kv_lora_rank, count, (float *)o_lat, lse, st);
     } else {
-        e = launch_flash_decode_bf16((const bf16 *)q_cat, kv_cache, kv == MLA_Q8_0,
-                                     kv_seq_stride_bytes, n_kv, n_kv_max, B, d->n_head, count,
-                                     split_len, d->scale, (bf16 *)part_o, part_lse, st);
+        if (decode_q8_wide(d, kv))
+            e = launch_flash_decode_q8_wide((const bf16 *)q_cat, kv_cache, kv_seq_stride_bytes, n_kv,
+                                            n_kv_max, B, d->n_head, count, split_len, d->scale,
+                                            (bf16 *)part_o, part_lse, st);
+        else
+            e = launch_flash_decode_bf16((const bf16 *)q_cat, kv_cache, kv == MLA_Q8_0,
+                                         kv_seq_stride_bytes, n_kv, n_kv_max, B, d->n_head, count,
+                                         split_len, d->scale, (bf16 *)part_o, part_lse, st);
         if (e == hipSuccess)
             e = launch_combine<bf16, bf16>((const bf16 *)part_o, part_lse, B, d->n_head,
                                            d->kv_lora_rank, count, (bf16 *)o_lat, lse, st);

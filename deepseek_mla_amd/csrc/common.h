@@ -15,6 +15,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -129,6 +130,14 @@ hipError_t launch_prefill_materialized(const bf16 *q_nope, const bf16 *q_rope, c
                                        hipStream_t st);
 // heads per workgroup of the decode kernel (the split planner fills the CUs with it)
 int decode_heads_per_block();
+// decode over a Q8_0 cache with 128 heads per workgroup (every raw tile dequantised once
+// for all of them); same partial layout as launch_flash_decode_bf16
+int decode_wide_heads();
+hipError_t launch_flash_decode_q8_wide(const bf16 *q_cat, const void *cache,
+                                       int64_t seq_stride_bytes, const int32_t *n_kv,
+                                       int n_kv_max, int B, int H, int n_splits, int split_len,
+                                       float scale, bf16 *part_o, float *part_lse,
+                                       hipStream_t st);
 hipError_t launch_flash_decode_bf16(const bf16 *q_cat, const void *cache, int cache_q8,
                                     int64_t seq_stride_bytes, const int32_t *n_kv, int n_kv_max,
                                     int B, int H,

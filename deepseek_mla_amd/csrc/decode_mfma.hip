@@ -350,19 +350,6 @@ __device__ __forceinline__ void wait_groups(int n) {
     }
 }
 
-// Waits until at most n of this wave's copy instructions are outstanding, n a sum of up
-// to three Q8_0 tile counts (5 each, the last possibly 20): 0, 5, 10, 15, 20, 25 or 30.
-__device__ __forceinline__ void wait_vm_q8(int n) {
-    switch (n) {
-    case 0: MLA_WAIT_VMCNT(0); break;
-    case 5: MLA_WAIT_VMCNT(5); break;
-    case 10: MLA_WAIT_VMCNT(10); break;
-    case 15: MLA_WAIT_VMCNT(15); break;
-    case 20: MLA_WAIT_VMCNT(20); break;
-    case 25: MLA_WAIT_VMCNT(25); break;
-    default: MLA_WAIT_VMCNT(30); break;
-    }
-}
 static_assert(Q8_X4_INST / dq::NW == 5 && q8_inst_per_wave<dq::NW>() == 20,
               "wait_vm_q8 enumerates sums of 5 and 20");
 

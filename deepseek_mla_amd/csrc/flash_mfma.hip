@@ -900,4 +900,178 @@ hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int 
     return hipGetLastError();
 }
 
+
+// ------------------------------------------------------ decode over a Q8_0 cache (wide)
+//
+// Token generation over Q8_0 latent rows (absorption page, section 8: a separate decode
+// kernel; section 8.1: the 8-bit latent cache), one workgroup per (sequence, key split,
+// group of 128 heads), with the prefill's wave structure: wave w owns heads 32w .. 32w+31
+// of the group, each wave scores all 32 keys of a tile for its own heads, and a wave pair
+// swaps its weights so that each wave accumulates O for the pair's 64 heads over half of
+// the latent columns.  Every raw tile is dequantised once into the bf16 tile layout and
+// serves all 128 heads (a 64-head workgroup would dequantise each tile twice per head
+// group pair).
+//
+// Per tile t: the scores of tile t (K from bf16 stage t % 2) with the dequantisation of
+// raw tile t+1 into the other bf16 stage interleaved between the score MFMAs, the softmax,
+// the weight exchange, then O += P V over tile t.  Raw tiles land in 3 stages, two tiles
+// ahead.  Partials are written exactly as the split decode kernel writes them (normalised
+// bf16 rows and their lse), so the split-KV combine merges them.
+constexpr int DW_NS = 2;  // bf16 tile stages
+constexpr int DW_NR = 3;  // raw Q8_0 stages
+constexpr int DW_STAGES = DW_NS * fl::TILE_BYTES + DW_NR * Q8_RAW_STAGE;  // 139264 B
+constexpr int DW_HEADS = PF_ROWS;                                        // 128 heads
+static_assert(DW_STAGES + PBUF_BYTES <= 163840, "LDS budget");
+static_assert(OSTAGE_BYTES <= DW_STAGES, "output staging fits the stages");
+
+// Keys [kbeg, kend) of the Q8_0 rows of one sequence (nk rows); lim = nk - 1 is every
+// row's last visible key.
+__device__ __forceinline__ void stream_keys_q8(WaveState &st, uint8_t MLA_LDS *lds,
+                                               uint8_t MLA_LDS *pbuf,
+                                               const uint8_t *__restrict__ rows, int nk,
+                                               int kbeg, int kend, float sc) {
+    constexpr int NW = PF_NW;
+    if (kend <= kbeg) return;
+    const int ntiles = (kend - kbeg + fl::NK - 1) / fl::NK;
+    const int lim = nk - 1;
+    uint8_t MLA_LDS *raw = lds + DW_NS * fl::TILE_BYTES;
+    const int ch = (threadIdx.x >> 6) & 1;  // column half of this wave
+    constexpr int PX = Q8_X4_INST / NW, PD = q8_inst_per_wave<NW>();
+    // only the sequence's last tile can reach past its end: that one takes dword copies
+    auto tail = [&](int j) { return kbeg + (j + 1) * fl::NK > nk; };
+    auto cnt = [&](int j) { return j < ntiles ? (tail(j) ? PD : PX) : 0; };
+    auto issue_raw = [&](int j) {
+        uint8_t MLA_LDS *dst = raw + (j % DW_NR) * Q8_RAW_STAGE;
+        if (tail(j))
+            issue_tile_q8<NW>(rows, kbeg + j * fl::NK, nk, dst);
+        else
+            issue_tile_q8_full<NW>(rows, kbeg + j * fl::NK, dst);
+    };
+    // Every earlier vector-memory load (queries, the sequence length) completes before the
+    // first copy: the compiler does not see the copies (see lds_copy16).
+    MLA_WAIT_VMCNT(0);
+    for (int j = 0; j < DW_NR; ++j)
+        if (j < ntiles) issue_raw(j);
+    wait_vm_q8(cnt(1) + cnt(2));  // raw tile 0 landed
+    __syncthreads();
+    DequantQ8{raw, lds, kbeg, nk}.all();
+    for (int t = 0; t < ntiles; ++t) {
+        // raw tile t+1 landed (only raw tile t+2 may be in flight); the barrier also
+        // orders the dequantisation of tile t, the O update of tile t-1 (whose stage the
+        // dequantisation of tile t+1 overwrites) and the reads of raw tile t (whose stage
+        // takes raw tile t+3)
+        wait_vm_q8(cnt(t + 2));
+        __syncthreads();
+        if (t + 3 < ntiles) issue_raw(t + 3);
+        const uint8_t MLA_LDS *tile = lds + (t & 1) * fl::TILE_BYTES;
+        const bool next = t + 1 < ntiles;
+        const DequantQ8 dqz{raw + ((t + 1) % DW_NR) * Q8_RAW_STAGE,
+                            lds + ((t + 1) & 1) * fl::TILE_BYTES, kbeg + (t + 1) * fl::NK, nk};
+        DequantQ8::Words dw;
+        const int key0 = kbeg + t * fl::NK;
+        int lim_t = lim;
+        asm volatile("" : "+v"(lim_t));
+        // Dequantisation of raw tile t+1 between the MFMAs: task m (0 .. 4) is fetched after
+        // score step 7m and converted after step 7m + 4; tasks 5 .. 8 are fetched after the
+        // O-update steps 8(m - 5) and converted after steps 8(m - 5) + 6.
+        f32x16 s = score_tile(st, tile, key0 + fl::NK - 1 > lim, key0, lim_t, [&](auto kc) {
+            constexpr int kk = decltype(kc)::value;
+            if (next) {
+                if constexpr (kk % 7 == 0 && kk / 7 < 5) dw = dqz.load(kk / 7);
+                if constexpr (kk % 7 == 4 && kk / 7 < 5) dqz.convert(kk / 7, dw);
+            }
+        });
+        static_assert(7 * 4 + 4 < 36, "five tasks in the score steps");
+        float nmu = 0.0f, psum = 0.0f;
+        bf16x8 pcur[2];
+        const SoftFill soft{st, s, pcur, psum, nmu, key0, lim_t, sc};
+        static_for<32>(soft);
+        st.lsum += psum;
+        put_p(pbuf, pcur);
+        __syncthreads();  // the pair's weights visible
+        bf16x8 poth[2];
+        get_partner_p(pbuf, poth);
+        const VAddr vt(tile, ch);
+        bf16x8 va[PV_AHEAD];
+#pragma unroll
+        for (int i = 0; i < PV_AHEAD; ++i) va[i] = vt.load(i);
+        pv_tile(st, vt, va, pcur, poth, [&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if (next) {
+                if constexpr (j % 8 == 0) dw = dqz.load(5 + j / 8);
+                if constexpr (j % 8 == 6) dqz.convert(5 + j / 8, dw);
+            }
+        });
+        static_assert(5 + 3 == DequantQ8::TASKS - 1, "four tasks in the O-update steps");
+    }
+    __syncthreads();
+}
+
+// Block (unit u = (b * n_splits + split) * hgroups + head group): blocks go round-robin
+// over the XCDs; no two blocks share a tile, so no placement matters.
+__global__ __launch_bounds__(64 * PF_NW, 1) void flash_decode_q8w_kernel(
+    const bf16 *__restrict__ q_cat, int H, const uint8_t *__restrict__ cache, int64_t seq_stride,
+    const int32_t *__restrict__ n_kv, int n_kv_max, int n_splits, int split_len, int hgroups,
+    float sc, bf16 *__restrict__ part_o, float *__restrict__ part_lse) {
+    const int u = blockIdx.x;
+    const int hg = u % hgroups;
+    const int b = u / hgroups / n_splits, sp = (u / hgroups) % n_splits;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+    uint8_t MLA_LDS *lds = (uint8_t MLA_LDS *)lds_raw;
+    uint8_t MLA_LDS *pbuf = lds + DW_STAGES;
+    Misc *misc = misc_of(lds_raw + DW_STAGES);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nk = min(n_kv[b], n_kv_max);  // rows past n_kv_max are never read
+    const int k0 = sp * split_len;
+    const int k1 = min(k0 + split_len, nk);
+    // heads past H load head H-1's query; their rows are never written
+    const int h = min(hg * DW_HEADS + w * 32 + (int)(threadIdx.x & 31), H - 1);
+    WaveState st;
+    load_q(st, q_cat + ((int64_t)b * H + h) * fl::W);
+    const uint8_t *rows = cache + b * seq_stride;
+    float m0 = -INFINITY;
+    for (int pass = 0; pass < 2; ++pass) {
+        init_acc(st, m0);
+        stream_keys_q8(st, lds, pbuf, rows, nk, k0, k1, sc);
+        if (threadIdx.x == 0) misc->flag = 0;
+        __syncthreads();
+        if (__builtin_amdgcn_ballot_w64(st.bad) && (threadIdx.x & 63) == 0) atomicOr(&misc->flag, 1);
+        __syncthreads();
+        const int again = misc->flag;
+        __syncthreads();
+        if (!again) break;
+        m0 = st.m;  // marked rows: their true max; others: unchanged reference
+    }
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));  // recomputed, not kept across the key stream
+    const int l = tid & 63;
+    const int64_t pi = ((int64_t)b * n_splits + sp) * H + hg * DW_HEADS;
+    const int hmax = H - hg * DW_HEADS;  // heads of this group
+    const float ls = finish(st, lds, pbuf, [&](int r) -> bf16 * {
+        return r < hmax ? part_o + (pi + r) * fl::R : nullptr;
+    });
+    const int r = __builtin_amdgcn_readfirstlane(tid >> 6) * 32 + (l & 31);
+    if (l < 32 && r < hmax) part_lse[pi + r] = ls;
+}
+
+int decode_wide_heads() { return DW_HEADS; }
+
+hipError_t launch_flash_decode_q8_wide(const bf16 *q_cat, const void *cache,
+                                       int64_t seq_stride_bytes, const int32_t *n_kv,
+                                       int n_kv_max, int B, int H, int n_splits, int split_len,
+                                       float scale, bf16 *part_o, float *part_lse,
+                                       hipStream_t st) {
+    const int hgroups = (H + DW_HEADS - 1) / DW_HEADS;
+    const int64_t nblocks = (int64_t)B * n_splits * hgroups;
+    if (nblocks <= 0 || nblocks > INT32_MAX) return hipErrorInvalidValue;
+    const int shm = DW_STAGES + PBUF_BYTES;
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = ensure_lds_limit((const void *)flash_decode_q8w_kernel, shm, lds_set);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(flash_decode_q8w_kernel, dim3((unsigned)nblocks), dim3(64 * PF_NW), shm, st,
+                       q_cat, H, (const uint8_t *)cache, seq_stride_bytes, n_kv, n_kv_max,
+                       n_splits, split_len, hgroups, scale * fl::LOG2E, part_o, part_lse);
+    return hipGetLastError();
+}
+
 }  // namespace mla

@@ -213,6 +213,21 @@ template <int NW> __host__ __device__ constexpr int q8_inst_per_wave() {
     return Q8_RAW_INST / NW;
 }
 
+// Waits until at most n of this wave's copy instructions are outstanding, n a sum of up
+// to three Q8_0 tile counts of a 4-wave workgroup (5 each for whole tiles, 20 for the one
+// tile that reaches past the sequence end): 0, 5, 10, 15, 20, 25 or 30.
+__device__ __forceinline__ void wait_vm_q8(int n) {
+    switch (n) {
+    case 0: MLA_WAIT_VMCNT(0); break;
+    case 5: MLA_WAIT_VMCNT(5); break;
+    case 10: MLA_WAIT_VMCNT(10); break;
+    case 15: MLA_WAIT_VMCNT(15); break;
+    case 20: MLA_WAIT_VMCNT(20); break;
+    case 25: MLA_WAIT_VMCNT(25); break;
+    default: MLA_WAIT_VMCNT(30); break;
+    }
+}
+
 // Dequantisation of a raw Q8_0 tile (LDS, the global byte image) into the bf16 tile
 // layout (LDS), in tasks of one 16-byte output chunk: 8 values of one 32-value block.
 // Thread x of the 256-thread workgroup takes row k = x / 8 and chunks c = x % 8 + 8 i,
@@ -222,9 +237,12 @@ template <int NW> __host__ __device__ constexpr int q8_inst_per_wave() {
 // (the row mask only permutes the low two chunk bits).  load(i) fetches the task's scale
 // and the 2-3 dwords holding its 8 codes; convert(i) forms the values and writes the
 // chunk, so that the two can sit between other work.  Value = float(d) * q, exact in
-// float32 (an 11-bit by 8-bit product), computed as fma(q + 128, d, -128 d) on the code
-// with its sign bit flipped (an unsigned byte); rows with key0 + k >= n_rows are written
-// as zeros.
+// float32 (an 11-bit by 8-bit product), then rounded to bf16.  The code with its sign bit
+// flipped is the unsigned byte u = q + 128; two of them at a time become the binary16
+// values 1024 + u (the byte placed under the exponent bits 0x64), and one mixed-precision
+// fma per value forms d (1024 + u) - 1152 d = d q: the product of two binary16 values is
+// exact in float32 and the sum is exact because the result is representable.  Rows with
+// key0 + k >= n_rows are written as zeros.
 struct DequantQ8 {
     const uint8_t MLA_LDS *raw;
     uint8_t MLA_LDS *dst;
@@ -261,13 +279,19 @@ struct DequantQ8 {
         const uint32_t lo = __builtin_amdgcn_alignbyte(r.w1, r.w0, sh) ^ 0x80808080u;
         const uint32_t hi = __builtin_amdgcn_alignbyte(r.w2, r.w1, sh) ^ 0x80808080u;
         const bool valid = key0 + k < n_rows;
-        const float d = valid ? (float)__builtin_bit_cast(_Float16, r.d) : 0.0f;
-        const float nd = -128.0f * d;  // exact: a power-of-two multiple
+        const _Float16 dh = valid ? __builtin_bit_cast(_Float16, r.d) : (_Float16)0.0f;
+        const float c = -1152.0f * (float)dh;  // exact: 9 * 2^7 times an 11-bit value
+        constexpr uint32_t EXP = 0x64646464u;  // binary16 exponent byte of 1024
+        const uint32_t h[4] = {__builtin_amdgcn_perm(EXP, lo, 0x05010400u),
+                               __builtin_amdgcn_perm(EXP, lo, 0x05030402u),
+                               __builtin_amdgcn_perm(EXP, hi, 0x05010400u),
+                               __builtin_amdgcn_perm(EXP, hi, 0x05030402u)};
         bf16x8 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            v[e] = f2bf(fmaf((float)((lo >> (8 * e)) & 0xFF), d, nd));
-            v[4 + e] = f2bf(fmaf((float)((hi >> (8 * e)) & 0xFF), d, nd));
+            const f16x2 x = __builtin_bit_cast(f16x2, h[e]);
+            v[2 * e] = f2bf(fmaf((float)x[0], (float)dh, c));
+            v[2 * e + 1] = f2bf(fmaf((float)x[1], (float)dh, c));
         }
         const int c0 = x & 7;
         const int off = i < 8 ? k * fl::PA + ((c0 ^ mask_a(k)) << 4) + 128 * i
@@ -280,5 +304,6 @@ struct DequantQ8 {
     }
 };
 static_assert(fl::Q8_TILE_BYTES + 8 <= Q8_RAW_STAGE, "the last task's third word stays in the stage");
+
 
 }  // namespace mla
