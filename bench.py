@@ -140,11 +140,11 @@ def copy_bandwidth(nbytes=1 << 30, reps=10):
     return 2 * nbytes / s / 1e9
 
 
-def time_workload(w, steps, warmup, copies=1, n_splits=0):
+def time_workload(w, steps, warmup, copies=1, n_splits=0, path="absorbed"):
     import torch
     from deepseek_mla_amd import layer, synth
     x = synth.generate_workload(w)
-    L = layer.for_workload(w, x, cache_copies=copies, n_splits=n_splits)
+    L = layer.for_workload(w, x, cache_copies=copies, n_splits=n_splits, path=path)
     del x
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -170,6 +170,8 @@ def time_workload(w, steps, warmup, copies=1, n_splits=0):
            "attention_ms": float(np.median(parts[:, 1])),
            "out_proj_ms": float(np.median(parts[:, 2])), "attention_stats": stats(parts[:, 1])}
     res["cache_append"] = time_append(w, L, steps)
+    if path == "vt":
+        res["transpose_v_append"] = time_transpose_append(w, L, steps)
     pos = L.pos.cpu().numpy()
     del L
     torch.cuda.empty_cache()
@@ -227,6 +229,32 @@ def time_append(w, L, reps):
         res[key + "GB/s"] = nbytes / (us * 1e-6) / 1e9
     res["frac_hbm"] = res["GB/s"] / HBM_PEAK_GBS
     return res
+
+
+def time_transpose_append(w, L, reps):
+    """mla_cache_transpose_v of one new row per sequence (its last row), the V^T upkeep
+    that follows each cache append on the K + V^T path."""
+    import torch
+    from deepseek_mla_amd import mla
+    R = w.dims.kv_lora_rank
+    stream = torch.cuda.current_stream()
+
+    def run():
+        mla.mla_cache_transpose_v(L.cdims, L.kv, L.caches[0], L.seq_stride, L.n_seq, w.n_kv - 1,
+                                  w.n_kv, L.vts[0], R * L.vt_ld * 2, L.vt_ld, stream=stream)
+
+    for _ in range(3):
+        run()
+    reps = max(min(reps, 50), 20)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return {"kernel": "transpose_v_kernel", "rows": L.n_seq,
+            "us_per_launch": e0.elapsed_time(e1) * 1e3 / reps}
 
 
 def cpu_model():
@@ -396,14 +424,15 @@ def run_one(name, steps, warmup, with_cpu, n_splits=0):
     from deepseek_mla_amd import synth
     if name.endswith("@materialized"):
         return run_materialized(name, steps, warmup)
-    w = synth.WORKLOADS[name]
+    path = "vt" if name.endswith("@vt") else "absorbed"
+    w = synth.WORKLOADS[name.split("@")[0]]
     copies = 1
     if w.kind == "decode":
         # rotate caches so that the 256 MB last-level cache holds none of them between steps
         per = attention_bytes(w)
         copies = max(1, min(16, int(np.ceil(600e6 / per))))
     log(f"[bench] {name}: {steps} steps after {warmup} warmup, cache copies {copies}")
-    res, pos = time_workload(w, steps, warmup, copies, n_splits)
+    res, pos = time_workload(w, steps, warmup, copies, n_splits, path)
     fl = step_flops(w, pos)
     total = sum(fl.values())
     entry = {"workload": name, "ms_per_step": res["ms_per_step"],
@@ -411,6 +440,10 @@ def run_one(name, steps, warmup, with_cpu, n_splits=0):
              "attention_stats": res["attention_stats"],
              "step_tflops": total / (res["ms_per_step"] * 1e-3) / 1e12,
              "cache_append": res["cache_append"]}
+    if path == "vt":
+        entry["path"] = ("K + V^T cache (absorption page, section 8.2, mode 1): "
+                         "mla_attn_decode_vt over the bf16 rows and their transposed latent copy")
+        entry["transpose_v_append"] = res["transpose_v_append"]
     clk = measured_clock(name)
     if w.kind == "prefill":
         ach = fl["attention"] / (res["attention_ms"] * 1e-3) / 1e12
@@ -430,19 +463,28 @@ def run_one(name, steps, warmup, with_cpu, n_splits=0):
                                       "frac_at_measured_clock": ach / pk})
     else:
         nbytes = attention_bytes(w)
+        # the K + V^T form also reads the transposed latent rows (R bf16 per key)
+        vt_bytes = w.n_seq * w.n_kv * w.dims.kv_lora_rank * 2 if path == "vt" else 0
+        if path == "vt":
+            entry["row_cache_gbs"] = nbytes / (res["attention_ms"] * 1e-3) / 1e9
+        nbytes += vt_bytes
         ach = nbytes / (res["attention_ms"] * 1e-3) / 1e9
         entry["value"] = ach
         entry["unit"] = "GB/s"
         entry["attention_tflops"] = fl["attention"] / (res["attention_ms"] * 1e-3) / 1e12
-        entry["roofline"] = {"kernel": "flash_decode_kernel + combine_kernel", "bound": "hbm",
+        kern = ("flash_decode_w_kernel<VT> + combine_kernel" if path == "vt" else
+                "flash_decode_w_kernel<Q8> + combine_kernel" if w.mode == "q8_0" else
+                "flash_decode_kernel + combine_kernel")
+        entry["roofline"] = {"kernel": kern, "bound": "hbm",
                              "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(name),
                              "mfma_frac": entry["attention_tflops"] / BF16_PEAK_TFLOPS,
-                             "per_launch": f"{nbytes} B = {w.n_seq} x ({w.n_kv} latent rows + "
+                             "per_launch": f"{nbytes} B = {w.n_seq} x ({w.n_kv} latent rows "
+                                           f"{'+ their V^T copy ' if vt_bytes else ''}+ "
                                            f"q_cat + o_lat of {w.dims.n_head} heads)"}
         if clk:
             entry["roofline"]["clock_ghz_measured"] = clk
-    if with_cpu:
+    if with_cpu and path == "absorbed":
         t0 = time.perf_counter()
         entry["cpu_baseline"] = cpu_baseline(w)
         log(f"[bench] {name}: cpu baseline {time.perf_counter() - t0:.1f}s")
@@ -505,7 +547,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_long_prefill")
-    ap.add_argument("--extra", default="v3_decode,v3_decode_q8,lite_prefill,"
+    ap.add_argument("--extra", default="v3_decode,v3_decode@vt,v3_decode_q8,lite_prefill,"
                                        "lite_prefill@materialized,v3_long_prefill@materialized",
                     help="comma-separated extra workloads reported under 'workloads' ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -554,11 +596,15 @@ def main():
     # the materialised path against the absorbed step of the same workload
     absorbed = {e["workload"]: e["ms_per_step"] for e in [main_entry] + extras
                 if "@" not in e["workload"]}
+    attn_ms = {e["workload"]: e["kernel_ms"]["attention_ms"] for e in [main_entry] + extras
+               if "@" not in e["workload"]}
     for e in extras:
         base = e["workload"].split("@")[0]
         if "@materialized" in e["workload"] and base in absorbed:
             e["speedup_vs_absorbed"] = absorbed[base] / e["ms_per_step"]
             e["speedup_note"] = "absorbed step ms (absorb + attention + out_proj) / this step ms"
+        if "@vt" in e["workload"] and base in attn_ms:
+            e["attention_speedup_vs_row_cache"] = attn_ms[base] / e["kernel_ms"]["attention_ms"]
     for e in [main_entry] + extras:
         if e["roofline"]["bound"] == "hbm":
             e["roofline"]["copy_gbs_measured"] = copy_gbs

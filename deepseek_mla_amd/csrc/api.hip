@@ -30,6 +30,8 @@ hipStream_t as_stream(void *s) { return (hipStream_t)s; }
 constexpr int SIMT_SPLIT_GRAIN = 64;
 constexpr int MAX_SPLITS = 4096;  // largest split count accepted
 constexpr int MFMA_SPLIT_GRAIN = 32;
+// V^T row length limit: a 16-row copy's lane offsets (15 rows of 2 vt_ld bytes) stay 32-bit
+constexpr int32_t MAX_VT_LD = 1 << 26;
 
 // A Q8_0 cache with whole groups of 128 heads decodes on the wide kernel (128 heads per
 // workgroup, every raw tile dequantised once for all of them).
@@ -37,12 +39,8 @@ bool decode_q8_wide(const mla_dims *d, int kv) {
     return kv == MLA_Q8_0 && d->n_head % decode_wide_heads() == 0;
 }
 
-int auto_splits(const mla_dims *d, int kv, int B, int n_kv_max) {
-    if (kv == MLA_F32) {
-        int s = (n_kv_max + 255) / 256;
-        return s < 1 ? 1 : (s > 64 ? 64 : s);
-    }
-    const int hpb = decode_q8_wide(d, kv) ? decode_wide_heads() : decode_heads_per_block();
+// Splits that fill the CUs with workgroups of hpb heads (at least 4 tiles per split).
+int splits_for(const mla_dims *d, int hpb, int B, int n_kv_max) {
     const int hgroups = (d->n_head + hpb - 1) / hpb;
     const int per_seq = (B * hgroups);
     int s = (NUM_CUS + per_seq - 1) / per_seq;
@@ -50,6 +48,15 @@ int auto_splits(const mla_dims *d, int kv, int B, int n_kv_max) {
     const int max_s = (n_kv_max + 127) / 128;
     if (s > max_s) s = max_s;
     return s < 1 ? 1 : s;
+}
+
+int auto_splits(const mla_dims *d, int kv, int B, int n_kv_max) {
+    if (kv == MLA_F32) {
+        int s = (n_kv_max + 255) / 256;
+        return s < 1 ? 1 : (s > 64 ? 64 : s);
+    }
+    return splits_for(d, decode_q8_wide(d, kv) ? decode_wide_heads() : decode_heads_per_block(),
+                      B, n_kv_max);
 }
 
 // split length (multiple of the kernel's key grain) and the resulting split count
@@ -194,10 +201,13 @@ size_t mla_decode_workspace_bytes(const mla_dims *d, int32_t B, int32_t n_kv_max
     int S = n_splits;
     if (S == 0) {
         // the largest automatic choice over cache types
+        // (and the transposed-V decode, on 128-head workgroups)
         const int a = auto_splits(d, MLA_F32, B, n_kv_max), b = auto_splits(d, MLA_BF16, B, n_kv_max),
-                  c = auto_splits(d, MLA_Q8_0, B, n_kv_max);
+                  c = auto_splits(d, MLA_Q8_0, B, n_kv_max),
+                  v = splits_for(d, decode_wide_heads(), B, n_kv_max);
         S = a > b ? a : b;
         S = S > c ? S : c;
+        S = S > v ? S : v;
     }
     if (S > n_kv_max) S = n_kv_max;
     const size_t rows = (size_t)B * S * d->n_head;
@@ -346,6 +356,70 @@ int mla_attn_decode_static(const mla_dims *d, mla_dtype act, mla_dtype kv, const
     if (s != MLA_OK) return s;
     return decode_impl(d, act, kv, q_cat, kv_cache, kv_seq_stride_bytes, n_kv, B, n_kv_max,
                        n_splits, o_lat, lse, ws, MLA_DECODE_STATIC_BYTES, stream);
+}
+
+int mla_cache_transpose_v(const mla_dims *d, mla_dtype kv, const void *kv_cache,
+                          int64_t kv_seq_stride_bytes, int32_t B, int32_t row0, int32_t row1,
+                          void *v_t, int64_t vt_seq_stride_bytes, int32_t vt_ld, void *stream) {
+    if (!dims_ok(d) || B < 0 || B > 65535 || row0 < 0 || row1 < row0 || vt_ld < 1 ||
+        vt_ld > MAX_VT_LD)
+        return MLA_ERR_INVALID_ARG;
+    if (kv != MLA_BF16) return kv == MLA_F32 || kv == MLA_Q8_0 ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+    if (!bf16_attn_dims(d)) return MLA_ERR_UNSUPPORTED;
+    if (B == 0 || row1 == row0) return MLA_OK;
+    if (!kv_cache || !v_t) return MLA_ERR_INVALID_ARG;
+    const int64_t row_bytes = (int64_t)(d->kv_lora_rank + d->qk_rope) * 2;
+    const int64_t rows_need = ((int64_t)row1 + 31) / 32 * 32;  // whole 32-key groups
+    if (vt_ld < rows_need || kv_seq_stride_bytes % 2 || vt_seq_stride_bytes % 2) return MLA_ERR_INVALID_ARG;
+    if (B > 1 && (kv_seq_stride_bytes < row_bytes * row1 ||
+                  vt_seq_stride_bytes < (int64_t)d->kv_lora_rank * vt_ld * 2))
+        return MLA_ERR_INVALID_ARG;
+    return hip_status(launch_transpose_v((const bf16 *)kv_cache, kv_seq_stride_bytes, B, row0, row1,
+                                         (bf16 *)v_t, vt_seq_stride_bytes, vt_ld, as_stream(stream)));
+}
+
+int mla_attn_decode_vt(const mla_dims *d, mla_dtype act, mla_dtype kv, const void *q_cat,
+                       const void *kv_cache, int64_t kv_seq_stride_bytes, const void *v_t,
+                       int64_t vt_seq_stride_bytes, int32_t vt_ld, const int32_t *n_kv, int32_t B,
+                       int32_t n_kv_max, int32_t n_splits, void *o_lat, float *lse,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    if (!dims_ok(d) || B < 0 || n_kv_max < 1 || n_splits < 0 || n_splits > MAX_SPLITS ||
+        vt_ld < 1 || vt_ld > MAX_VT_LD)
+        return MLA_ERR_INVALID_ARG;
+    if (act != MLA_BF16 || kv != MLA_BF16)
+        return (act == MLA_F32 || act == MLA_BF16) && (kv == MLA_F32 || kv == MLA_Q8_0)
+                   ? MLA_ERR_UNSUPPORTED
+                   : MLA_ERR_INVALID_ARG;
+    if (!bf16_attn_dims(d)) return MLA_ERR_UNSUPPORTED;
+    if (B == 0) return MLA_OK;
+    if (!q_cat || !kv_cache || !v_t || !n_kv || !o_lat || !workspace) return MLA_ERR_INVALID_ARG;
+    const int64_t row_bytes = (int64_t)(d->kv_lora_rank + d->qk_rope) * 2;
+    const int64_t rows_need = ((int64_t)n_kv_max + 31) / 32 * 32;
+    if (kv_seq_stride_bytes < 0 || kv_seq_stride_bytes % 16 || vt_seq_stride_bytes < 0 ||
+        vt_seq_stride_bytes % 16 || vt_ld % 8 || vt_ld < rows_need || ((uintptr_t)v_t & 15))
+        return MLA_ERR_INVALID_ARG;
+    if (B > 1 && (kv_seq_stride_bytes < row_bytes * n_kv_max ||
+                  vt_seq_stride_bytes < (int64_t)d->kv_lora_rank * vt_ld * 2))
+        return MLA_ERR_INVALID_ARG;
+    int S = n_splits ? n_splits : splits_for(d, decode_wide_heads(), B, n_kv_max);
+    if (S > n_kv_max) S = n_kv_max;
+    int split_len, count;
+    split_plan(MLA_BF16, n_kv_max, S, &split_len, &count);
+    const size_t rows = (size_t)B * count * d->n_head;
+    const size_t need = align256(rows * d->kv_lora_rank * sizeof(bf16)) + align256(rows * sizeof(float));
+    if (workspace_bytes < need || workspace_bytes < mla_decode_workspace_bytes(d, B, n_kv_max, n_splits))
+        return MLA_ERR_WORKSPACE;
+    bf16 *part_o = (bf16 *)workspace;
+    float *part_lse = (float *)((char *)workspace + align256(rows * d->kv_lora_rank * sizeof(bf16)));
+    hipStream_t st = as_stream(stream);
+    hipError_t e = launch_flash_decode_bf16_wide((const bf16 *)q_cat, kv_cache, kv_seq_stride_bytes,
+                                                 v_t, vt_seq_stride_bytes, vt_ld, n_kv, n_kv_max, B,
+                                                 d->n_head, count, split_len, d->scale, part_o,
+                                                 part_lse, st);
+    if (e == hipSuccess)
+        e = launch_combine<bf16, bf16>(part_o, part_lse, B, d->n_head, d->kv_lora_rank, count,
+                                       (bf16 *)o_lat, lse, st);
+    return hip_status(e);
 }
 
 int mla_out_proj(const mla_dims *d, mla_dtype act, const void *o_lat, const void *wv_b,

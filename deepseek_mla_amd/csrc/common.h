@@ -138,6 +138,21 @@ hipError_t launch_flash_decode_q8_wide(const bf16 *q_cat, const void *cache,
                                        int n_kv_max, int B, int H, int n_splits, int split_len,
                                        float scale, bf16 *part_o, float *part_lse,
                                        hipStream_t st);
+// the same over a bf16 cache; with vt (the transposed latent rows of each sequence, vt_ld
+// keys apart, keys in score-slot order within each 32-key group) the O update reads V^T from
+// there instead of transposing the cache rows
+hipError_t launch_flash_decode_bf16_wide(const bf16 *q_cat, const void *cache,
+                                         int64_t seq_stride_bytes, const void *vt,
+                                         int64_t vt_seq_stride_bytes, int64_t vt_ld,
+                                         const int32_t *n_kv, int n_kv_max, int B, int H,
+                                         int n_splits, int split_len, float scale, bf16 *part_o,
+                                         float *part_lse, hipStream_t st);
+// transposed latent rows (the V^T cache) from a bf16 cache: rows [row0, row1) of each of B
+// sequences; keys in score-slot order (bits 2 and 3 of the index swapped) within each
+// aligned 32-key group
+hipError_t launch_transpose_v(const bf16 *cache, int64_t seq_stride_bytes, int B, int row0,
+                              int row1, bf16 *vt, int64_t vt_seq_stride_bytes, int64_t vt_ld,
+                              hipStream_t st);
 hipError_t launch_flash_decode_bf16(const bf16 *q_cat, const void *cache, int cache_q8,
                                     int64_t seq_stride_bytes, const int32_t *n_kv, int n_kv_max,
                                     int B, int H,

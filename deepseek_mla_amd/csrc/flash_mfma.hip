@@ -185,8 +185,8 @@ __device__ __forceinline__ void soft_piece(const f32x16 &s, int e, float sc, flo
 // O^T += V^T P^T over the 32 keys of a tile for both row blocks: 16 steps (ks, nb), each
 // one V^T fragment and two MFMAs (own weights pown, partner's weights poth), with a
 // read-ahead ring whose first PV_AHEAD entries the caller loaded; fill(j) follows MFMA j.
-template <typename Fill>
-__device__ __forceinline__ void pv_tile(WaveState &st, const VAddr &va_addr,
+template <typename VA, typename Fill>
+__device__ __forceinline__ void pv_tile(WaveState &st, const VA &va_addr,
                                         bf16x8 (&va)[PV_AHEAD], const bf16x8 (&pown)[2],
                                         const bf16x8 (&poth)[2], Fill fill) {
     static_for<16>([&](auto ic) {
@@ -901,87 +901,197 @@ hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int 
 }
 
 
-// ------------------------------------------------------ decode over a Q8_0 cache (wide)
+// ------------------------------------------------------------- wide decode kernels
 //
-// Token generation over Q8_0 latent rows (absorption page, section 8: a separate decode
-// kernel; section 8.1: the 8-bit latent cache), one workgroup per (sequence, key split,
-// group of 128 heads), with the prefill's wave structure: wave w owns heads 32w .. 32w+31
-// of the group, each wave scores all 32 keys of a tile for its own heads, and a wave pair
-// swaps its weights so that each wave accumulates O for the pair's 64 heads over half of
-// the latent columns.  Every raw tile is dequantised once into the bf16 tile layout and
-// serves all 128 heads (a 64-head workgroup would dequantise each tile twice per head
-// group pair).
-//
-// Per tile t: the scores of tile t (K from bf16 stage t % 2) with the dequantisation of
-// raw tile t+1 into the other bf16 stage interleaved between the score MFMAs, the softmax,
-// the weight exchange, then O += P V over tile t.  Raw tiles land in 3 stages, two tiles
-// ahead.  Partials are written exactly as the split decode kernel writes them (normalised
-// bf16 rows and their lse), so the split-KV combine merges them.
-constexpr int DW_NS = 2;  // bf16 tile stages
+// Token generation (absorption page, section 8: a separate decode kernel), one workgroup
+// per (sequence, key split, group of 128 heads), with the prefill's wave structure: wave w
+// owns heads 32w .. 32w+31 of the group, each wave scores all 32 keys of a tile for its own
+// heads, and a wave pair swaps its weights so that each wave accumulates O for the pair's
+// 64 heads over half of the latent columns.  Every tile serves all 128 heads.  Partials are
+// written exactly as the split decode kernel writes them (normalised bf16 rows and their
+// lse), so the split-KV combine merges them.  Three cache forms:
+//   DW_Q8   Q8_0 rows (section 8.1): every raw tile is dequantised once into the bf16 tile
+//           layout, its tasks interleaved with the score and O-update MFMAs of the previous
+//           tile; raw tiles land in 3 stages, two tiles ahead, bf16 tiles in 2.
+//   DW_BF16 bf16 rows; V^T fragments read from the row-major tile (ds_read_b64_tr_b16), as
+//           in prefill; 2 stages, one tile ahead.
+//   DW_VT   bf16 rows for the scores and a separate transposed copy of their latent part
+//           for the O update: section 8.2's mode 1, a K cache and a V^T cache.  The V^T
+//           tile [512 columns][32 keys] is read with ds_read_b128 (one instruction per
+//           fragment instead of two transposing ones) at the cost of 1 KB more per key;
+//           2 stages, one tile ahead.
+// Per tile t: the scores of tile t, the softmax, the weight exchange, then O += P V over
+// tile t.
+enum { DW_Q8 = 0, DW_BF16 = 1, DW_VT = 2 };
+constexpr int DW_NS = 2;  // tile stages
 constexpr int DW_NR = 3;  // raw Q8_0 stages
-constexpr int DW_STAGES = DW_NS * fl::TILE_BYTES + DW_NR * Q8_RAW_STAGE;  // 139264 B
-constexpr int DW_HEADS = PF_ROWS;                                        // 128 heads
-static_assert(DW_STAGES + PBUF_BYTES <= 163840, "LDS budget");
-static_assert(OSTAGE_BYTES <= DW_STAGES, "output staging fits the stages");
+constexpr int VT_TILE = fl::R * fl::NK * 2;  // 32768 B: [512 columns][32 keys] bf16
+constexpr int DW_HEADS = PF_ROWS;            // 128 heads
+__host__ __device__ constexpr int dw_stage(int mode) {
+    return mode == DW_VT ? fl::TILE_BYTES + VT_TILE : fl::TILE_BYTES;
+}
+__host__ __device__ constexpr int dw_stages(int mode) {
+    return mode == DW_Q8 ? DW_NS * fl::TILE_BYTES + DW_NR * Q8_RAW_STAGE : DW_NS * dw_stage(mode);
+}
+// the stages, or the output staging of finish() once the key stream ended
+__host__ __device__ constexpr int dw_front(int mode) {
+    return dw_stages(mode) > OSTAGE_BYTES ? dw_stages(mode) : OSTAGE_BYTES;
+}
+static_assert(dw_front(DW_Q8) + PBUF_BYTES <= 163840 && dw_front(DW_VT) + PBUF_BYTES <= 163840,
+              "LDS budget");
 
-// Keys [kbeg, kend) of the Q8_0 rows of one sequence (nk rows); lim = nk - 1 is every
-// row's last visible key.
-__device__ __forceinline__ void stream_keys_q8(WaveState &st, uint8_t MLA_LDS *lds,
-                                               uint8_t MLA_LDS *pbuf,
-                                               const uint8_t *__restrict__ rows, int nk,
-                                               int kbeg, int kend, float sc) {
+// V^T fragments from the transposed tile (A operand of 32x32x16: lane l holds column l & 31
+// of a 32-column block and the 8 keys 16 ks + 8 (l >> 5) .. +7 of key step ks).  Column c's
+// 64 bytes hold its 32 keys in the order of the score slots (bits 2 and 3 of the key index
+// swapped, as the V^T cache stores them), so those 8 keys are 16 contiguous bytes; 16-byte
+// chunk q of column c sits at q ^ ((c >> 2) & 3), which spreads the 16 columns a
+// 16-lane read touches over the 16 bank groups.
+struct VAddrT {
+    const uint8_t MLA_LDS *b[2];
+    __device__ __forceinline__ VAddrT(const uint8_t MLA_LDS *vt, int ch) {
+        const int l = threadIdx.x & 63;
+        const int col = ch * 256 + (l & 31);     // plus 32 nb, a multiple of 16
+        const int swz = ((l & 31) >> 2) & 3;     // (col >> 2) & 3
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) b[ks] = vt + col * 64 + (((2 * ks + (l >> 5)) ^ swz) << 4);
+    }
+    __device__ __forceinline__ bf16x8 load(int i) const {  // step i = (ks, nb) = (i/8, i%8)
+        return *(const bf16x8 MLA_LDS *)(b[i >> 3] + (i & 7) * 32 * 64);
+    }
+};
+
+// Copy of the V^T tile of keys key0 .. key0+31 (32 instructions, 8 per wave): instruction i
+// moves columns 16i .. 16i+15, lane l column 16i + (l >> 2), stored chunk l & 3 (logical
+// chunk (l & 3) ^ ((l >> 4) & 3), the swizzle of that column).  vt: the sequence's V^T rows
+// (ld keys apart, bf16); the 32 keys of the tile must lie inside the rows.
+__device__ __forceinline__ void issue_part_vt(const uint8_t *vt, int64_t ld_bytes, int key0,
+                                              uint32_t dst, int i) {
+    const int l = threadIdx.x & 63;
+    const uint32_t voff = (uint32_t)((l >> 2) * ld_bytes) + ((((l & 3) ^ ((l >> 4) & 3))) << 4);
+    lds_copy16(vt + (int64_t)key0 * 2 + (int64_t)16 * i * ld_bytes, voff, dst + (uint32_t)(i * 1024));
+}
+
+// Zeroes the V^T tile entries of keys past the sequence end (nk rows; the tile starts at
+// key0): their weights are 0, but the transposed rows hold whatever the caller left there.
+__device__ __forceinline__ void zero_vt_tail(uint8_t MLA_LDS *vt, int key0, int nk) {
+    for (int e = threadIdx.x; e < fl::R * 4; e += 64 * PF_NW) {
+        const int c = e >> 2, q = e & 3;          // column, logical chunk
+        uint8_t MLA_LDS *p = vt + c * 64 + ((q ^ ((c >> 2) & 3)) << 4);
+        bf16x8 v = *(bf16x8 MLA_LDS *)p;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            const int pos = q * 8 + x;  // slot order: key = pos with bits 2 and 3 swapped
+            const int key = (pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1);
+            if (key0 + key >= nk) v[x] = (bf16)0.0f;
+        }
+        *(bf16x8 MLA_LDS *)p = v;
+    }
+}
+
+// Keys [kbeg, kend) of one sequence (nk rows; lim = nk - 1 is every row's last visible
+// key).  rows: the sequence's cache rows; vt, vt_ld: its V^T rows (DW_VT).
+template <int MODE>
+__device__ __forceinline__ void stream_keys_w(WaveState &st, uint8_t MLA_LDS *lds,
+                                              uint8_t MLA_LDS *pbuf,
+                                              const uint8_t *__restrict__ rows,
+                                              const uint8_t *__restrict__ vt, int64_t vt_ld,
+                                              int nk, int kbeg, int kend, float sc) {
     constexpr int NW = PF_NW;
     if (kend <= kbeg) return;
     const int ntiles = (kend - kbeg + fl::NK - 1) / fl::NK;
     const int lim = nk - 1;
-    uint8_t MLA_LDS *raw = lds + DW_NS * fl::TILE_BYTES;
     const int ch = (threadIdx.x >> 6) & 1;  // column half of this wave
-    constexpr int PX = Q8_X4_INST / NW, PD = q8_inst_per_wave<NW>();
-    // only the sequence's last tile can reach past its end: that one takes dword copies
+    const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // only the sequence's last tile can reach past its end
     auto tail = [&](int j) { return kbeg + (j + 1) * fl::NK > nk; };
-    auto cnt = [&](int j) { return j < ntiles ? (tail(j) ? PD : PX) : 0; };
-    auto issue_raw = [&](int j) {
+    auto stage = [&](int j) { return lds + (j & 1) * dw_stage(MODE); };
+    [[maybe_unused]] uint8_t MLA_LDS *raw = lds + DW_NS * fl::TILE_BYTES;
+    [[maybe_unused]] constexpr int PX = Q8_X4_INST / NW, PD = q8_inst_per_wave<NW>();
+    [[maybe_unused]] auto cnt = [&](int j) { return j < ntiles ? (tail(j) ? PD : PX) : 0; };
+    [[maybe_unused]] auto issue_raw = [&](int j) {
         uint8_t MLA_LDS *dst = raw + (j % DW_NR) * Q8_RAW_STAGE;
         if (tail(j))
             issue_tile_q8<NW>(rows, kbeg + j * fl::NK, nk, dst);
         else
             issue_tile_q8_full<NW>(rows, kbeg + j * fl::NK, dst);
     };
+    // a whole tile's copies at once (bf16 forms: the first tile and the tail tile)
+    [[maybe_unused]] auto issue_all = [&](int j) {
+        const int key0 = kbeg + j * fl::NK;
+        issue_tile_bf16<NW>(rows, key0, nk - 1, stage(j));
+        if constexpr (MODE == DW_VT) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                issue_part_vt(vt, 2 * vt_ld, key0, lds_u32(stage(j) + fl::TILE_BYTES), 8 * wu + i);
+        }
+    };
     // Every earlier vector-memory load (queries, the sequence length) completes before the
     // first copy: the compiler does not see the copies (see lds_copy16).
     MLA_WAIT_VMCNT(0);
-    for (int j = 0; j < DW_NR; ++j)
-        if (j < ntiles) issue_raw(j);
-    wait_vm_q8(cnt(1) + cnt(2));  // raw tile 0 landed
-    __syncthreads();
-    DequantQ8{raw, lds, kbeg, nk}.all();
-    for (int t = 0; t < ntiles; ++t) {
-        // raw tile t+1 landed (only raw tile t+2 may be in flight); the barrier also
-        // orders the dequantisation of tile t, the O update of tile t-1 (whose stage the
-        // dequantisation of tile t+1 overwrites) and the reads of raw tile t (whose stage
-        // takes raw tile t+3)
-        wait_vm_q8(cnt(t + 2));
+    if constexpr (MODE == DW_Q8) {
+        for (int j = 0; j < DW_NR; ++j)
+            if (j < ntiles) issue_raw(j);
+        wait_vm_q8(cnt(1) + cnt(2));  // raw tile 0 landed
         __syncthreads();
-        if (t + 3 < ntiles) issue_raw(t + 3);
-        const uint8_t MLA_LDS *tile = lds + (t & 1) * fl::TILE_BYTES;
+        DequantQ8{raw, lds, kbeg, nk}.all();
+    } else {
+        issue_all(0);
+    }
+    for (int t = 0; t < ntiles; ++t) {
+        if constexpr (MODE == DW_Q8) {
+            // raw tile t+1 landed (only raw tile t+2 may be in flight); the barrier also
+            // orders the dequantisation of tile t, the O update of tile t-1 (whose stage
+            // the dequantisation of tile t+1 overwrites) and the reads of raw tile t (whose
+            // stage takes raw tile t+3)
+            wait_vm_q8(cnt(t + 2));
+            __syncthreads();
+            if (t + 3 < ntiles) issue_raw(t + 3);
+        } else {
+            // tile t landed; the barrier also orders the O update of tile t-1, whose stage
+            // takes tile t+1
+            MLA_WAIT_VMCNT(0);
+            __syncthreads();
+            if constexpr (MODE == DW_VT) {
+                // (ordered before the O update by the exchange barrier below)
+                if (tail(t)) zero_vt_tail(stage(t) + fl::TILE_BYTES, kbeg + t * fl::NK, nk);
+            }
+            if (t + 1 < ntiles && tail(t + 1)) issue_all(t + 1);
+        }
+        const uint8_t MLA_LDS *tile = stage(t);
         const bool next = t + 1 < ntiles;
-        const DequantQ8 dqz{raw + ((t + 1) % DW_NR) * Q8_RAW_STAGE,
-                            lds + ((t + 1) & 1) * fl::TILE_BYTES, kbeg + (t + 1) * fl::NK, nk};
-        DequantQ8::Words dw;
+        // the next bf16 tile's copies when it lies inside the sequence, spread over the
+        // score steps (a copy instruction blocks its wave while the address unit is backed
+        // up): K parts after steps 0, 4, .., 32, V^T parts after steps 2, 6, .., 30
+        [[maybe_unused]] const bool fast = next && !tail(t + 1);
+        [[maybe_unused]] const int nkey0 = kbeg + (t + 1) * fl::NK;
+        [[maybe_unused]] const uint8_t *sbase = rows + (int64_t)(nkey0 + 8 * wu) * fl::RB;
+        [[maybe_unused]] const uint32_t ndst = lds_u32(stage(t + 1));
+        [[maybe_unused]] const CopyPlan plan = make_copy_plan();
+        [[maybe_unused]] const DequantQ8 dqz{raw + ((t + 1) % DW_NR) * Q8_RAW_STAGE,
+                                             lds + ((t + 1) & 1) * fl::TILE_BYTES, nkey0, nk};
+        [[maybe_unused]] DequantQ8::Words dw;
         const int key0 = kbeg + t * fl::NK;
         int lim_t = lim;
         asm volatile("" : "+v"(lim_t));
-        // Dequantisation of raw tile t+1 between the MFMAs: task m (0 .. 4) is fetched after
-        // score step 7m and converted after step 7m + 4; tasks 5 .. 8 are fetched after the
-        // O-update steps 8(m - 5) and converted after steps 8(m - 5) + 6.
+        // Q8_0: the dequantisation of raw tile t+1 between the MFMAs: task m (0 .. 4) is
+        // fetched after score step 7m and converted after step 7m + 4; tasks 5 .. 8 are
+        // fetched after the O-update steps 8(m - 5) and converted after steps 8(m - 5) + 6.
         f32x16 s = score_tile(st, tile, key0 + fl::NK - 1 > lim, key0, lim_t, [&](auto kc) {
             constexpr int kk = decltype(kc)::value;
-            if (next) {
-                if constexpr (kk % 7 == 0 && kk / 7 < 5) dw = dqz.load(kk / 7);
-                if constexpr (kk % 7 == 4 && kk / 7 < 5) dqz.convert(kk / 7, dw);
+            if constexpr (MODE == DW_Q8) {
+                if (next) {
+                    if constexpr (kk % 7 == 0 && kk / 7 < 5) dw = dqz.load(kk / 7);
+                    if constexpr (kk % 7 == 4 && kk / 7 < 5) dqz.convert(kk / 7, dw);
+                }
+            } else {
+                if (fast) {
+                    if constexpr (kk % 4 == 0) issue_part_full<kk / 4>(sbase, plan, ndst, wu);
+                    if constexpr (MODE == DW_VT && kk % 4 == 2 && kk / 4 < 8)
+                        issue_part_vt(vt, 2 * vt_ld, nkey0, ndst + fl::TILE_BYTES, 8 * wu + kk / 4);
+                }
             }
         });
-        static_assert(7 * 4 + 4 < 36, "five tasks in the score steps");
+        static_assert(7 * 4 + 4 < 36 && 4 * 8 < 36, "every task and copy inside the score steps");
         float nmu = 0.0f, psum = 0.0f;
         bf16x8 pcur[2];
         const SoftFill soft{st, s, pcur, psum, nmu, key0, lim_t, sc};
@@ -991,17 +1101,24 @@ __device__ __forceinline__ void stream_keys_q8(WaveState &st, uint8_t MLA_LDS *l
         __syncthreads();  // the pair's weights visible
         bf16x8 poth[2];
         get_partner_p(pbuf, poth);
-        const VAddr vt(tile, ch);
-        bf16x8 va[PV_AHEAD];
+        auto o_update = [&](const auto &va_addr) {
+            bf16x8 va[PV_AHEAD];
 #pragma unroll
-        for (int i = 0; i < PV_AHEAD; ++i) va[i] = vt.load(i);
-        pv_tile(st, vt, va, pcur, poth, [&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            if (next) {
-                if constexpr (j % 8 == 0) dw = dqz.load(5 + j / 8);
-                if constexpr (j % 8 == 6) dqz.convert(5 + j / 8, dw);
-            }
-        });
+            for (int i = 0; i < PV_AHEAD; ++i) va[i] = va_addr.load(i);
+            pv_tile(st, va_addr, va, pcur, poth, [&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                if constexpr (MODE == DW_Q8) {
+                    if (next) {
+                        if constexpr (j % 8 == 0) dw = dqz.load(5 + j / 8);
+                        if constexpr (j % 8 == 6) dqz.convert(5 + j / 8, dw);
+                    }
+                }
+            });
+        };
+        if constexpr (MODE == DW_VT)
+            o_update(VAddrT(tile + fl::TILE_BYTES, ch));
+        else
+            o_update(VAddr(tile, ch));
         static_assert(5 + 3 == DequantQ8::TASKS - 1, "four tasks in the O-update steps");
     }
     __syncthreads();
@@ -1009,8 +1126,10 @@ __device__ __forceinline__ void stream_keys_q8(WaveState &st, uint8_t MLA_LDS *l
 
 // Block (unit u = (b * n_splits + split) * hgroups + head group): blocks go round-robin
 // over the XCDs; no two blocks share a tile, so no placement matters.
-__global__ __launch_bounds__(64 * PF_NW, 1) void flash_decode_q8w_kernel(
+template <int MODE>
+__global__ __launch_bounds__(64 * PF_NW, 1) void flash_decode_w_kernel(
     const bf16 *__restrict__ q_cat, int H, const uint8_t *__restrict__ cache, int64_t seq_stride,
+    const uint8_t *__restrict__ vt, int64_t vt_seq_stride, int64_t vt_ld,
     const int32_t *__restrict__ n_kv, int n_kv_max, int n_splits, int split_len, int hgroups,
     float sc, bf16 *__restrict__ part_o, float *__restrict__ part_lse) {
     const int u = blockIdx.x;
@@ -1018,8 +1137,8 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_decode_q8w_kernel(
     const int b = u / hgroups / n_splits, sp = (u / hgroups) % n_splits;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     uint8_t MLA_LDS *lds = (uint8_t MLA_LDS *)lds_raw;
-    uint8_t MLA_LDS *pbuf = lds + DW_STAGES;
-    Misc *misc = misc_of(lds_raw + DW_STAGES);
+    uint8_t MLA_LDS *pbuf = lds + dw_front(MODE);
+    Misc *misc = misc_of(lds_raw + dw_front(MODE));
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nk = min(n_kv[b], n_kv_max);  // rows past n_kv_max are never read
     const int k0 = sp * split_len;
@@ -1029,10 +1148,11 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_decode_q8w_kernel(
     WaveState st;
     load_q(st, q_cat + ((int64_t)b * H + h) * fl::W);
     const uint8_t *rows = cache + b * seq_stride;
+    const uint8_t *vts = MODE == DW_VT ? vt + b * vt_seq_stride : nullptr;
     float m0 = -INFINITY;
     for (int pass = 0; pass < 2; ++pass) {
         init_acc(st, m0);
-        stream_keys_q8(st, lds, pbuf, rows, nk, k0, k1, sc);
+        stream_keys_w<MODE>(st, lds, pbuf, rows, vts, vt_ld, nk, k0, k1, sc);
         if (threadIdx.x == 0) misc->flag = 0;
         __syncthreads();
         if (__builtin_amdgcn_ballot_w64(st.bad) && (threadIdx.x & 63) == 0) atomicOr(&misc->flag, 1);
@@ -1056,21 +1176,83 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_decode_q8w_kernel(
 
 int decode_wide_heads() { return DW_HEADS; }
 
+template <int MODE>
+static hipError_t launch_w(const bf16 *q_cat, const void *cache, int64_t seq_stride_bytes,
+                           const void *vt, int64_t vt_seq_stride_bytes, int64_t vt_ld,
+                           const int32_t *n_kv, int n_kv_max, int B, int H, int n_splits,
+                           int split_len, float scale, bf16 *part_o, float *part_lse,
+                           hipStream_t st) {
+    const int hgroups = (H + DW_HEADS - 1) / DW_HEADS;
+    const int64_t nblocks = (int64_t)B * n_splits * hgroups;
+    if (nblocks <= 0 || nblocks > INT32_MAX) return hipErrorInvalidValue;
+    const int shm = dw_front(MODE) + PBUF_BYTES;
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = ensure_lds_limit((const void *)flash_decode_w_kernel<MODE>, shm, lds_set);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(flash_decode_w_kernel<MODE>, dim3((unsigned)nblocks), dim3(64 * PF_NW), shm,
+                       st, q_cat, H, (const uint8_t *)cache, seq_stride_bytes,
+                       (const uint8_t *)vt, vt_seq_stride_bytes, vt_ld, n_kv, n_kv_max, n_splits,
+                       split_len, hgroups, scale * fl::LOG2E, part_o, part_lse);
+    return hipGetLastError();
+}
+
 hipError_t launch_flash_decode_q8_wide(const bf16 *q_cat, const void *cache,
                                        int64_t seq_stride_bytes, const int32_t *n_kv,
                                        int n_kv_max, int B, int H, int n_splits, int split_len,
                                        float scale, bf16 *part_o, float *part_lse,
                                        hipStream_t st) {
-    const int hgroups = (H + DW_HEADS - 1) / DW_HEADS;
-    const int64_t nblocks = (int64_t)B * n_splits * hgroups;
-    if (nblocks <= 0 || nblocks > INT32_MAX) return hipErrorInvalidValue;
-    const int shm = DW_STAGES + PBUF_BYTES;
-    static std::atomic<uint64_t> lds_set{0};
-    const hipError_t e = ensure_lds_limit((const void *)flash_decode_q8w_kernel, shm, lds_set);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(flash_decode_q8w_kernel, dim3((unsigned)nblocks), dim3(64 * PF_NW), shm, st,
-                       q_cat, H, (const uint8_t *)cache, seq_stride_bytes, n_kv, n_kv_max,
-                       n_splits, split_len, hgroups, scale * fl::LOG2E, part_o, part_lse);
+    return launch_w<DW_Q8>(q_cat, cache, seq_stride_bytes, nullptr, 0, 0, n_kv, n_kv_max, B, H,
+                           n_splits, split_len, scale, part_o, part_lse, st);
+}
+
+hipError_t launch_flash_decode_bf16_wide(const bf16 *q_cat, const void *cache,
+                                         int64_t seq_stride_bytes, const void *vt,
+                                         int64_t vt_seq_stride_bytes, int64_t vt_ld,
+                                         const int32_t *n_kv, int n_kv_max, int B, int H,
+                                         int n_splits, int split_len, float scale, bf16 *part_o,
+                                         float *part_lse, hipStream_t st) {
+    if (vt)
+        return launch_w<DW_VT>(q_cat, cache, seq_stride_bytes, vt, vt_seq_stride_bytes, vt_ld,
+                               n_kv, n_kv_max, B, H, n_splits, split_len, scale, part_o, part_lse,
+                               st);
+    return launch_w<DW_BF16>(q_cat, cache, seq_stride_bytes, nullptr, 0, 0, n_kv, n_kv_max, B, H,
+                             n_splits, split_len, scale, part_o, part_lse, st);
+}
+
+// Transposed latent rows for the K + V^T cache form (absorption page, section 8.2, mode 1):
+// vt[c][32 g + p] = cache[32 g + pi(p)][c] for the 512 latent columns c, pi swapping bits 2
+// and 3 of the in-group index (an involution), so that a 16-byte run of a column holds the
+// 8 keys one lane's score slots cover.  Block (32-key group, 64-column chunk, sequence);
+// keys outside [row0, row1) are neither read nor written.
+__global__ __launch_bounds__(256) void transpose_v_kernel(const bf16 *__restrict__ cache,
+                                                          int64_t seq_stride, int row0, int row1,
+                                                          bf16 *__restrict__ vt,
+                                                          int64_t vt_seq_stride, int64_t vt_ld) {
+    __shared__ bf16 t[fl::NK][64 + 2];
+    const int kb = (row0 / fl::NK + (int)blockIdx.x) * fl::NK, c0 = (int)blockIdx.y * 64;
+    const bf16 *src = cache + (int64_t)blockIdx.z * seq_stride;
+    bf16 *dst = vt + (int64_t)blockIdx.z * vt_seq_stride;
+    for (int i = threadIdx.x; i < fl::NK * 64; i += 256) {
+        const int k = i >> 6, c = i & 63, key = kb + k;
+        t[k][c] = (key >= row0 && key < row1) ? src[(int64_t)key * fl::W + c0 + c] : (bf16)0.0f;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * fl::NK; i += 256) {
+        const int c = i >> 5, p = i & 31;
+        const int k = (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
+        const int key = kb + k;
+        if (key >= row0 && key < row1) dst[(int64_t)(c0 + c) * vt_ld + kb + p] = t[k][c];
+    }
+}
+
+hipError_t launch_transpose_v(const bf16 *cache, int64_t seq_stride_bytes, int B, int row0,
+                              int row1, bf16 *vt, int64_t vt_seq_stride_bytes, int64_t vt_ld,
+                              hipStream_t st) {
+    if (row1 <= row0 || B <= 0) return hipSuccess;
+    const int groups = (row1 - 1) / fl::NK - row0 / fl::NK + 1;
+    hipLaunchKernelGGL(transpose_v_kernel, dim3((unsigned)groups, fl::R / 64, (unsigned)B),
+                       dim3(256), 0, st, cache, seq_stride_bytes / 2, row0, row1, vt,
+                       vt_seq_stride_bytes / 2, vt_ld);
     return hipGetLastError();
 }
 

@@ -3,7 +3,9 @@
 A step is the whole path in the order of the absorption page, section 4:
 mla_absorb_q -> mla_attn_prefill (or mla_attn_decode) -> mla_out_proj.  A prefill step
 on the materialised path (section 8.4) is the single call mla_prefill_materialized
-(decompression, attention and wo).
+(decompression, attention and wo).  A decode step on the K + V^T path (section 8.2, the
+-mla switch's mode 1) calls mla_attn_decode_vt on the row cache and its transposed latent
+copy, built once by mla_cache_transpose_v.
 Buffers are allocated once with torch (device memory only); every computation runs
 in libmla.so.
 """
@@ -32,8 +34,9 @@ class LayerStep:
     def __init__(self, dims: synth.Dims, mode: str, kind: str, inputs: dict, n_kv: int,
                  scratch_cap_mib: int = 0, n_splits: int = 0, cache_copies: int = 1,
                  device="cuda", path: str = "absorbed"):
-        assert path in ("absorbed", "materialized")
-        assert path == "absorbed" or kind == "prefill"
+        assert path in ("absorbed", "materialized", "vt")
+        assert path != "materialized" or kind == "prefill"
+        assert path != "vt" or (kind == "decode" and mode == "bf16")
         self.path = path
         self.dims, self.mode, self.kind = dims, mode, kind
         self.act, self.kv = _MODE[mode]
@@ -91,6 +94,15 @@ class LayerStep:
             wsb = mla.mla_decode_workspace_bytes(self.cdims, S, n_kv, n_splits)
             self.workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=device)
             self.ws_bytes = wsb
+        if path == "vt":
+            # each cache copy's V^T rows: [S][R][vt_ld], vt_ld = n_kv rounded up to 32
+            self.vt_ld = (n_kv + 31) // 32 * 32
+            self.vts = []
+            for c in self.caches:
+                vt = torch.empty((S, R, self.vt_ld), dtype=tdt, device=device)
+                mla.mla_cache_transpose_v(self.cdims, self.kv, c, self.seq_stride, S, 0, n_kv, vt,
+                                          R * self.vt_ld * 2, self.vt_ld)
+                self.vts.append(vt)
 
     def absorb(self, stream=None):
         mla.mla_absorb_q(self.cdims, self.act, self.q_nope, self.q_rope, self.pos, self.wk_b,
@@ -98,8 +110,15 @@ class LayerStep:
 
     def attend(self, stream=None):
         self.cache = self.caches[self._ci]
+        ci = self._ci
         self._ci = (self._ci + 1) % len(self.caches)
-        if self.kind == "prefill":
+        if self.path == "vt":
+            mla.mla_attn_decode_vt(self.cdims, self.act, self.kv, self.q_cat, self.cache,
+                                   self.seq_stride, self.vts[ci], self.dims.kv_lora_rank *
+                                   self.vt_ld * 2, self.vt_ld, self.n_kv_dev, self.n_seq,
+                                   self.n_kv, self.n_splits, self.o_lat, self.lse,
+                                   self.workspace, self.ws_bytes, stream)
+        elif self.kind == "prefill":
             mla.mla_attn_prefill(self.cdims, self.act, self.kv, self.q_cat, self.pos, self.T,
                                  self.cache, self.n_kv, self.o_lat, self.lse,
                                  self.scratch_cap_mib, self.prefill_ws, stream)

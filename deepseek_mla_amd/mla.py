@@ -19,7 +19,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 # Every symbol include/mla.h declares.
 EXPORTS = ("mla_absorb_q", "mla_attn_prefill", "mla_prefill_workspace_bytes",
            "mla_heads_per_chunk", "mla_decode_workspace_bytes",
-           "mla_decode_auto_splits", "mla_attn_decode", "mla_attn_decode_static", "mla_out_proj",
+           "mla_decode_auto_splits", "mla_attn_decode", "mla_attn_decode_static",
+           "mla_cache_transpose_v", "mla_attn_decode_vt", "mla_out_proj",
            "mla_prefill_materialized",
            "mla_materialized_workspace_bytes", "mla_cache_append",
            "mla_cache_append_hadamard", "mla_hadamard_weights", "mla_wkv_b_merge",
@@ -70,6 +71,10 @@ def lib() -> ctypes.CDLL:
                                  vp, vp, vp, sz, vp], ctypes.c_int),
             "mla_attn_decode_static": ([D, ctypes.c_int, ctypes.c_int, vp, vp, i64, vp, i32, i32,
                                         i32, vp, vp, vp], ctypes.c_int),
+            "mla_cache_transpose_v": ([D, ctypes.c_int, vp, i64, i32, i32, i32, vp, i64, i32, vp],
+                                      ctypes.c_int),
+            "mla_attn_decode_vt": ([D, ctypes.c_int, ctypes.c_int, vp, vp, i64, vp, i64, i32, vp,
+                                    i32, i32, i32, vp, vp, vp, sz, vp], ctypes.c_int),
             "mla_out_proj": ([D, ctypes.c_int, vp, vp, vp, vp, vp, i32, vp], ctypes.c_int),
             "mla_prefill_materialized": ([D, ctypes.c_int, ctypes.c_int, vp, vp, vp, i32, vp, i32,
                                           vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, sz, vp],
@@ -173,6 +178,23 @@ def mla_attn_decode(dims, act, kv, q_cat, kv_cache, kv_seq_stride_bytes, n_kv, B
     _check(lib().mla_attn_decode(_d(dims), act, kv, _p(q_cat), _p(kv_cache), kv_seq_stride_bytes,
                                  _p(n_kv), B, n_kv_max, n_splits, _p(o_lat), _p(lse),
                                  _p(workspace), workspace_bytes, _s(stream)), "mla_attn_decode")
+
+
+def mla_cache_transpose_v(dims, kv, kv_cache, kv_seq_stride_bytes, B, row0, row1, v_t,
+                          vt_seq_stride_bytes, vt_ld, stream=None):
+    _check(lib().mla_cache_transpose_v(_d(dims), kv, _p(kv_cache), kv_seq_stride_bytes, B, row0,
+                                       row1, _p(v_t), vt_seq_stride_bytes, vt_ld, _s(stream)),
+           "mla_cache_transpose_v")
+
+
+def mla_attn_decode_vt(dims, act, kv, q_cat, kv_cache, kv_seq_stride_bytes, v_t,
+                       vt_seq_stride_bytes, vt_ld, n_kv, B, n_kv_max, n_splits, o_lat, lse,
+                       workspace, workspace_bytes, stream=None):
+    _check(lib().mla_attn_decode_vt(_d(dims), act, kv, _p(q_cat), _p(kv_cache),
+                                    kv_seq_stride_bytes, _p(v_t), vt_seq_stride_bytes, vt_ld,
+                                    _p(n_kv), B, n_kv_max, n_splits, _p(o_lat), _p(lse),
+                                    _p(workspace), workspace_bytes, _s(stream)),
+           "mla_attn_decode_vt")
 
 
 MLA_DECODE_STATIC_BYTES = 64 << 20  # include/mla.h

@@ -157,6 +157,34 @@ int mla_attn_decode(const mla_dims *dims, mla_dtype act, mla_dtype kv, const voi
                     int32_t B, int32_t n_kv_max, int32_t n_splits, void *o_lat, float *lse,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* The K + V^T cache form (absorption page, section 8.2: the -mla switch's mode 1 keeps a
+ * K cache and a cache of V transposed).  Beside the row cache [c_kv | k_rope]
+ * (bf16), each sequence holds the transpose of its latent part: v_t[c][p] for the R = 512
+ * columns c, vt_ld positions p per column, bf16.  Within every aligned group of 32 keys
+ * the position of key 32g + i is 32g + pi(i), pi swapping bits 2 and 3 of i (the order of
+ * the decode kernel's score slots; pi is its own inverse).
+ * mla_cache_transpose_v: writes v_t from the row cache for rows [row0, row1) of each of B
+ *   sequences (sequence b's rows at b * kv_seq_stride_bytes, its v_t at
+ *   b * vt_seq_stride_bytes); other positions are left as they are, so new rows can be
+ *   added as they are appended.  vt_ld >= row1 rounded up to 32 and <= 2^26; B <= 65535.
+ *   bf16 only.
+ * mla_attn_decode_vt: mla_attn_decode (bf16 cache, same arguments, semantics and
+ *   workspace size, mla_decode_workspace_bytes) with the O update reading V^T from v_t
+ *   (rows [0, n_kv[b]) of v_t must have been written; positions up to n_kv_max rounded up
+ *   to 32 are read and those past n_kv[b] ignored).  Workgroups of 128 heads; vt_ld a
+ *   multiple of 8, >= n_kv_max rounded up to 32 and <= 2^26; strides multiples of 16
+ *   bytes; v_t 16-byte aligned.
+ * Errors: INVALID_ARG (nulls, sizes, strides, alignment), UNSUPPORTED (other dtypes or
+ * dims: R 512 and Dr 64 as for the bf16 kernels), WORKSPACE. */
+int mla_cache_transpose_v(const mla_dims *dims, mla_dtype kv, const void *kv_cache,
+                          int64_t kv_seq_stride_bytes, int32_t B, int32_t row0, int32_t row1,
+                          void *v_t, int64_t vt_seq_stride_bytes, int32_t vt_ld, void *stream);
+int mla_attn_decode_vt(const mla_dims *dims, mla_dtype act, mla_dtype kv, const void *q_cat,
+                       const void *kv_cache, int64_t kv_seq_stride_bytes, const void *v_t,
+                       int64_t vt_seq_stride_bytes, int32_t vt_ld, const int32_t *n_kv,
+                       int32_t B, int32_t n_kv_max, int32_t n_splits, void *o_lat, float *lse,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
 /* Size of the device scratch array behind mla_attn_decode_static (bytes, per device). */
 #define MLA_DECODE_STATIC_BYTES (64u << 20)
 

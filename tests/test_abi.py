@@ -150,3 +150,48 @@ def test_static_decode_validates_without_gpu():
     assert L.mla_attn_decode_static(V, 1, 1, None, None, 0, None, 0, 1, 0, None, None,
                                     None) == mla.OK
     assert mla.MLA_DECODE_STATIC_BYTES == 64 << 20
+
+
+def test_vt_entry_points_validate_without_gpu():
+    """The K + V^T cache entry points reject bad arguments before any launch."""
+    L = mla.lib()
+    v3 = mla.mla_dims(128, 512, 128, 64, 128, 7168, 0.0722, 10000.0)
+    V = ctypes.byref(v3)
+    D = ctypes.byref(tiny())
+    p = ctypes.c_void_p(16)
+    # transpose: bf16 and R 512 / Dr 64 only; vt_ld covers row1 rounded up to 32
+    assert L.mla_cache_transpose_v(V, 1, p, 1152 * 100, 2, 0, 100, p, 512 * 64 * 2, 128,
+                                   None) == mla.ERR_INVALID_ARG  # V^T rows overlap
+    assert L.mla_cache_transpose_v(V, 1, p, 1152 * 99, 2, 0, 100, p, 512 * 128 * 2, 128,
+                                   None) == mla.ERR_INVALID_ARG  # cache rows overlap
+    assert L.mla_cache_transpose_v(V, 1, p, 1152 * 100, 1, 0, 100, p, 0, 96,
+                                   None) == mla.ERR_INVALID_ARG  # vt_ld < 128
+    assert L.mla_cache_transpose_v(V, 2, p, 612 * 100, 1, 0, 100, p, 0, 128,
+                                   None) == mla.ERR_UNSUPPORTED
+    assert L.mla_cache_transpose_v(D, 1, p, 160 * 100, 1, 0, 100, p, 0, 128,
+                                   None) == mla.ERR_UNSUPPORTED
+    assert L.mla_cache_transpose_v(V, 1, p, 1152, 1, 5, 4, p, 0, 128, None) == mla.ERR_INVALID_ARG
+    assert L.mla_cache_transpose_v(V, 1, p, 1152, 1, 0, 1, p, 0, (1 << 26) + 8,
+                                   None) == mla.ERR_INVALID_ARG
+    assert L.mla_cache_transpose_v(V, 1, None, 1152, 1, 0, 1, p, 0, 32,
+                                   None) == mla.ERR_INVALID_ARG
+    assert L.mla_cache_transpose_v(V, 1, None, 0, 1, 7, 7, None, 0, 32, None) == mla.OK
+    # decode: dtypes, vt_ld (multiple of 8, >= n_kv_max rounded up to 32), strides, workspace
+    def dec(act=1, kv=1, kvs=1152 * 100, vts=512 * 128 * 2, ld=128, B=1, nmax=100, ws=p,
+            wsb=1 << 30, dims=V, vt=p):
+        return L.mla_attn_decode_vt(dims, act, kv, p, p, kvs, vt, vts, ld, p, B, nmax, 0, p,
+                                    None, ws, wsb, None)
+    assert dec(kv=2) == mla.ERR_UNSUPPORTED
+    assert dec(act=0, kv=0) == mla.ERR_UNSUPPORTED
+    assert dec(act=3) == mla.ERR_INVALID_ARG
+    assert dec(dims=D) == mla.ERR_UNSUPPORTED
+    assert dec(ld=96) == mla.ERR_INVALID_ARG
+    assert dec(ld=132) == mla.ERR_INVALID_ARG
+    assert dec(kvs=1152 * 100 + 8) == mla.ERR_INVALID_ARG
+    assert dec(B=2, vts=512 * 64 * 2) == mla.ERR_INVALID_ARG
+    assert dec(vt=ctypes.c_void_p(24)) == mla.ERR_INVALID_ARG
+    assert dec(ws=None) == mla.ERR_INVALID_ARG
+    need = mla.mla_decode_workspace_bytes(v3, 1, 100, 0)
+    assert dec(wsb=need - 1) == mla.ERR_WORKSPACE
+    assert L.mla_attn_decode_vt(V, 1, 1, None, None, 0, None, 0, 32, None, 0, 1, 0, None, None,
+                                None, 0, None) == mla.OK
