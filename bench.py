@@ -52,11 +52,20 @@ MATERIALIZED_SRC = ("deepseek_mla_amd/csrc/flash_mha.hip", "deepseek_mla_amd/csr
                     "deepseek_mla_amd/csrc/lds_dma.h", "deepseek_mla_amd/csrc/common.h")
 TRAFFIC = {
     # workload: (bytes per launch, sources, sha256 prefix)
+    "v3_long_prefill": (18188329433, ABSORBED_SRC, "b395ee7ecdc23bfa"),
+    "lite_prefill": (228379384, ABSORBED_SRC, "b395ee7ecdc23bfa"),
+    "v3_decode": (73664603, ABSORBED_SRC, "b395ee7ecdc23bfa"),
+    "v3_decode@vt": (141551574, ABSORBED_SRC, "b395ee7ecdc23bfa"),
+    "v3_decode_q8": (314777499, ABSORBED_SRC, "b395ee7ecdc23bfa"),
+    "v3_long_prefill@materialized": (3401222750, MATERIALIZED_SRC, "dc2fec14b793305f"),
 }
 # Sustained shader clock under each kernel's load (GHz): GRBM_GUI_ACTIVE cycles per
 # dispatch over the dispatch's duration, from the counter summaries in profiles/; keyed
 # like TRAFFIC.
 CLOCK_GHZ = {
+    "v3_long_prefill": (2.157, ABSORBED_SRC, "b395ee7ecdc23bfa"),
+    "v3_decode_q8": (2.145, ABSORBED_SRC, "b395ee7ecdc23bfa"),
+    "v3_long_prefill@materialized": (1.927, MATERIALIZED_SRC, "dc2fec14b793305f"),
 }
 
 
@@ -609,7 +618,7 @@ def main():
         if e["roofline"]["bound"] == "hbm":
             e["roofline"]["copy_gbs_measured"] = copy_gbs
             e["roofline"]["frac_of_measured_copy"] = e["roofline"]["achieved"] / copy_gbs
-    w = synth.WORKLOADS[args.workload]
+    w = synth.WORKLOADS[args.workload.split("@")[0]]
     line = {
         "metric": "MLA attention TFLOP/s (prefill) and latent-cache GB/s (decode), 1 MI355X",
         "value": main_entry["value"], "unit": main_entry["unit"], "n_gpus": 1,
