@@ -41,16 +41,16 @@ namespace mla {
 
 // Per-wave attention state and the tile computation.
 //
-// Waves 2p and 2p+1 of a workgroup form a pair over 64 rows.  Each wave computes the
-// scores and the softmax of its own 32 rows; the pair swaps the bf16 weights P through
-// LDS, and each wave accumulates O for all 64 rows over its half of the latent columns.
-// Every V^T fragment read from LDS then feeds two MFMAs (one per row block), halving
-// the V reads, while the score MFMAs are not duplicated.
+// Each wave computes the scores and the softmax of its own 32 rows; the four waves share
+// their bf16 weights P through LDS, and wave w accumulates O for all 128 rows of the
+// workgroup over its quarter of the latent columns (128 columns).  Every V^T fragment
+// read from LDS then feeds four MFMAs (one per row block): each tile's V is read from
+// LDS once per workgroup, while the score MFMAs are not duplicated.
 struct WaveState {
     bf16x8 q[36];     // Q^T fragments of the own rows: lane l holds row l%32,
                       // dims kk*16 + (l/32)*8 .. +7
-    f32x16 o[8][2];   // O^T: column block nb of this wave's half (columns
-                      // half*256 + nb*32 ..), row block rb (0: own rows, 1: partner's)
+    f32x16 o[4][4];   // O^T: column block nb of this wave's quarter (columns
+                      // 128w + nb*32 ..), row block rb (the rows of wave rb)
     float m;          // frozen reference max of the own row (scaled, log2 domain)
     float lsum;       // this lane's share of the own row's softmax denominator
     bool bad;         // a score exceeded m + FREEZE_LIMIT: this pass is discarded
@@ -150,13 +150,13 @@ __device__ __forceinline__ void softmax_check(WaveState &st, const f32x16 &s, fl
 static_assert(fl::FREEZE_LIMIT == 64.0f, "softmax_check compares against 2^64");
 
 // V^T fragment addressing of the tile in stage t for O^T += V^T P^T, over the column
-// half `ch` (uniform).  Lane: key kin + 8*h (+16 ks) and 4 columns at colb of each
+// quarter `cq` (uniform).  Lane: key kin + 8*h (+16 ks) and 4 columns at colb of each
 // 32-column block.  Row ks*16 + h*8 + kin has mask mask_a(h*8 + kin); chunk 4nb + c3
 // (c3 < 4) is stored at 4nb + (c3 ^ mask): one base per row half plus compile-time
 // offsets.
 struct VAddr {
     const uint8_t MLA_LDS *vb[2];
-    __device__ __forceinline__ VAddr(const uint8_t MLA_LDS *t, int ch) {
+    __device__ __forceinline__ VAddr(const uint8_t MLA_LDS *t, int cq) {
         const int l = threadIdx.x & 63;
         const int G = l >> 4, lam = l & 15;
         const int kin = (G >> 1) * 4 + (lam >> 2);     // key within an 8-key group
@@ -164,15 +164,15 @@ struct VAddr {
         const int c3 = colb >> 3, cb = (colb & 7) * 2;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-            vb[h] = t + ch * 512 + (h * 8 + kin) * fl::PA + ((c3 ^ mask_a(h * 8 + kin)) * 16) + cb;
+            vb[h] = t + cq * 256 + (h * 8 + kin) * fl::PA + ((c3 ^ mask_a(h * 8 + kin)) * 16) + cb;
     }
-    __device__ __forceinline__ bf16x8 load(int i) const {  // step i = (ks, nb) = (i/8, i%8)
-        const int off = (i >> 3) * 16 * fl::PA + (i & 7) * 64;
+    __device__ __forceinline__ bf16x8 load(int i) const {  // step i = (ks, nb) = (i/4, i%4)
+        const int off = (i >> 2) * 16 * fl::PA + (i & 3) * 64;
         return tr_pair(vb[0] + off, vb[1] + off);
     }
 };
 
-constexpr int PV_AHEAD = 2;  // V^T read-ahead in PV steps (two MFMAs each)
+constexpr int PV_AHEAD = 2;  // V^T read-ahead in PV steps (four MFMAs each)
 
 // Weight of key slot e (e < 16) of this lane: exp2(s*sc - m); masked keys give 0.
 __device__ __forceinline__ void soft_piece(const f32x16 &s, int e, float sc, float nmu,
@@ -182,26 +182,36 @@ __device__ __forceinline__ void soft_piece(const f32x16 &s, int e, float sc, flo
     p[e >> 3][e & 7] = f2bf(pe);
 }
 
-// O^T += V^T P^T over the 32 keys of a tile for both row blocks: 16 steps (ks, nb), each
-// one V^T fragment and two MFMAs (own weights pown, partner's weights poth), with a
-// read-ahead ring whose first PV_AHEAD entries the caller loaded; fill(j) follows MFMA j.
+// P^T fragment (B operand of 32x32x16) of wave rb's weights for key step ks, from the
+// exchange buffer: lane l holds row l & 31 of wave rb, keys 16 ks + 8 (l >> 5) .. +7.
+__device__ __forceinline__ bf16x8 get_p(const uint8_t MLA_LDS *pbuf, int rb, int ks) {
+    return ((const bf16x8 MLA_LDS *)(pbuf + rb * 2048))[ks * 64 + (threadIdx.x & 63)];
+}
+
+// O^T += V^T P^T over the 32 keys of a tile for all four row blocks: 8 steps (ks, nb),
+// each one V^T fragment and four MFMAs (the weights of wave rb's rows), with a read-ahead
+// ring whose first PV_AHEAD entries the caller loaded; fill(j) follows MFMA j (32 MFMAs).
+// pk[rb] holds the weights of key step 0 (loaded by the caller from pbuf); each is
+// replaced by key step 1's right after its last use, so the weights take 16 registers.
 template <typename VA, typename Fill>
 __device__ __forceinline__ void pv_tile(WaveState &st, const VA &va_addr,
-                                        bf16x8 (&va)[PV_AHEAD], const bf16x8 (&pown)[2],
-                                        const bf16x8 (&poth)[2], Fill fill) {
-    static_for<16>([&](auto ic) {
+                                        bf16x8 (&va)[PV_AHEAD], const uint8_t MLA_LDS *pbuf,
+                                        bf16x8 (&pk)[4], Fill fill) {
+    static_for<8>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        constexpr int ks = i >> 3, nb = i & 7;
-        st.o[nb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % PV_AHEAD], pown[ks],
-                                                              st.o[nb][0], 0, 0, 0);
-        fill(std::integral_constant<int, 2 * i>{});
-        __builtin_amdgcn_sched_barrier(0);
-        st.o[nb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % PV_AHEAD], poth[ks],
-                                                              st.o[nb][1], 0, 0, 0);
-        constexpr int ni = i + PV_AHEAD;
-        if constexpr (ni < 16) va[i % PV_AHEAD] = va_addr.load(ni);
-        fill(std::integral_constant<int, 2 * i + 1>{});
-        __builtin_amdgcn_sched_barrier(0);
+        constexpr int nb = i & 3;
+        static_for<4>([&](auto rc) {
+            constexpr int rb = decltype(rc)::value;
+            st.o[nb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % PV_AHEAD], pk[rb],
+                                                                   st.o[nb][rb], 0, 0, 0);
+            if constexpr (i == 3) pk[rb] = get_p(pbuf, rb, 1);
+            if constexpr (rb == 3) {
+                constexpr int ni = i + PV_AHEAD;
+                if constexpr (ni < 8) va[i % PV_AHEAD] = va_addr.load(ni);
+            }
+            fill(std::integral_constant<int, 4 * i + rb>{});
+            __builtin_amdgcn_sched_barrier(0);
+        });
     });
 }
 
@@ -232,16 +242,10 @@ __device__ __forceinline__ void put_p(uint8_t MLA_LDS *pbuf, const bf16x8 (&p)[2
     slot[l] = p[0];
     slot[64 + l] = p[1];
 }
-// Weights of wave (w ^ flip) from the exchange buffer: flip 1 reads the partner's, flip 0
-// reads back this wave's own (so they need not stay in registers across the score MFMAs).
-__device__ __forceinline__ void get_p(const uint8_t MLA_LDS *pbuf, int flip, bf16x8 (&p)[2]) {
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const bf16x8 MLA_LDS *slot = (const bf16x8 MLA_LDS *)(pbuf + (w ^ flip) * 2048);
-    p[0] = slot[l];
-    p[1] = slot[64 + l];
-}
-__device__ __forceinline__ void get_partner_p(const uint8_t MLA_LDS *pbuf, bf16x8 (&p)[2]) {
-    get_p(pbuf, 1, p);
+// Key step 0's weights of all four waves (pv_tile loads step 1's).
+__device__ __forceinline__ void get_p0(const uint8_t MLA_LDS *pbuf, bf16x8 (&pk)[4]) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) pk[rb] = get_p(pbuf, rb, 0);
 }
 
 // Rows that are not valid load a valid row's query instead (their keys are all masked,
@@ -255,9 +259,9 @@ __device__ __forceinline__ void load_q(WaveState &st, const bf16 *__restrict__ q
 
 __device__ __forceinline__ void init_acc(WaveState &st, float m0) {
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) st.o[nb][rb][e] = 0.0f;
     st.m = m0;
@@ -272,10 +276,10 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
                                             uint8_t MLA_LDS *pbuf,
                                             const uint8_t *__restrict__ rows, int n_rows,
                                             int kbeg, int kend, int lim, int wlim, float sc) {
-    static_assert(NW == 4, "two wave pairs per workgroup");
+    static_assert(NW == 4, "four row blocks and four column quarters per workgroup");
     if (kend <= kbeg) return;
     const int ntiles = (kend - kbeg + fl::NK - 1) / fl::NK;
-    const int ch = (threadIdx.x >> 6) & 1;  // column half of this wave
+    const int cq = threadIdx.x >> 6;  // column quarter of this wave
     // Finish every earlier vector-memory load (queries, row bounds) before the first tile
     // copy.  The compiler cannot see the copies; a load it still counted as pending would
     // get a wait for all outstanding vector-memory operations inside the tile loop, which
@@ -290,10 +294,14 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
         // Iteration t: wait for tile t, scores of tile t (with the copy of tile t+2 into
         // the stage tile t-2 used, free since the barrier), then the O update of tile t-1
         // carrying the softmax of tile t.  Tile t-1 stays resident for its V reads.  The
-        // weights of tile t go to the exchange buffer at the end of iteration t; the
-        // partner reads them in iteration t+1 before the middle barrier, which orders
-        // those reads before the buffer is overwritten.
+        // weights of tile t stay in registers until the top barrier of iteration t+1, which
+        // follows every wave's last read of the exchange buffer (the O update of tile t-1
+        // reads key step 1's weights while it runs); they are written right after it, and
+        // a second barrier after score step 2 makes all four waves' weights visible.
         static_assert(NS == 4, "tiles t-1 .. t+2 resident or in flight");
+        constexpr int P_SYNC = 2, P_READ = 28;
+        static_assert(P_SYNC < P_READ && P_READ + 4 <= 36 - PV_AHEAD, "score steps");
+        bf16x8 pprev[2];  // the own rows' weights of tile t-1
         for (int ti = 0; ti < ntiles; ++ti) {
             if (ti + 1 < ntiles) {
                 MLA_WAIT_VMCNT(PER);
@@ -301,6 +309,7 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
                 MLA_WAIT_VMCNT(0);
             }
             __syncthreads();
+            if (ti > 0) put_p(pbuf, pprev);
             const int nx = ti + 2;
             uint8_t MLA_LDS *ndst = lds + (nx % NS) * fl::TILE_BYTES;
             const int nkey0 = kbeg + nx * fl::NK;
@@ -316,8 +325,8 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             // The copy's 9 instructions are spread over the score MFMAs: issued together,
             // the four waves' 36 instructions queue behind each other in the CU's memory
             // address unit.
-            const VAddr vprev(lds + ((ti + NS - 1) % NS) * fl::TILE_BYTES, ch);
-            bf16x8 va[PV_AHEAD];
+            const VAddr vprev(lds + ((ti + NS - 1) % NS) * fl::TILE_BYTES, cq);
+            bf16x8 va[PV_AHEAD], pk[4];
             const int key0 = kbeg + ti * fl::NK;
             // The row bound is made opaque per tile: values the compiler would derive from
             // it once and keep across the loop end up spilled, and a spill reload pending at
@@ -327,6 +336,12 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             f32x16 s = score_tile(st, lds + (ti % NS) * fl::TILE_BYTES, key0 + fl::NK - 1 > wlim, key0,
                                   lim_t, [&](auto kc) {
                 constexpr int kk = decltype(kc)::value;
+                if constexpr (kk == P_SYNC) {
+                    if (ti > 0) __syncthreads();  // every wave's weights of tile t-1 written
+                }
+                if constexpr (kk >= P_READ && kk < P_READ + 4) {
+                    if (ti > 0) pk[kk - P_READ] = get_p(pbuf, kk - P_READ, 0);
+                }
                 if (ti > 0 && kk >= 36 - PV_AHEAD)
                     va[kk - (36 - PV_AHEAD)] = vprev.load(kk - (36 - PV_AHEAD));
             });
@@ -344,26 +359,24 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
                 }
             };
             if (ti > 0) {
-                bf16x8 pown[2], poth[2];
-                get_p(pbuf, 0, pown);
-                get_partner_p(pbuf, poth);
-                __syncthreads();
-                pv_tile(st, vprev, va, pown, poth, fill);
+                pv_tile(st, vprev, va, pbuf, pk, fill);
             } else {
                 static_for<32>(fill);
             }
             st.lsum += psum;
-            put_p(pbuf, pcur);
+            pprev[0] = pcur[0];
+            pprev[1] = pcur[1];
         }
+        __syncthreads();  // every wave's last O update done
+        put_p(pbuf, pprev);
         __syncthreads();
         {
-            const VAddr vlast(lds + ((ntiles - 1) % NS) * fl::TILE_BYTES, ch);
-            bf16x8 va[PV_AHEAD], pown[2], poth[2];
+            const VAddr vlast(lds + ((ntiles - 1) % NS) * fl::TILE_BYTES, cq);
+            bf16x8 va[PV_AHEAD], pk[4];
 #pragma unroll
             for (int i = 0; i < PV_AHEAD; ++i) va[i] = vlast.load(i);
-            get_p(pbuf, 0, pown);
-            get_partner_p(pbuf, poth);
-            pv_tile(st, vlast, va, pown, poth, [](int) {});
+            get_p0(pbuf, pk);
+            pv_tile(st, vlast, va, pbuf, pk, [](int) {});
         }
         __syncthreads();
     }
@@ -404,8 +417,8 @@ __device__ __forceinline__ void attend_range(WaveState &st, uint8_t MLA_LDS *lds
     }
 }
 
-// Final normalisation and output.  Each wave holds O for its own rows (rb 0) and its
-// partner's (rb 1) over its column half; the pair swaps the row denominators through
+// Final normalisation and output.  Each wave holds O for all 128 rows (row block rb: the
+// rows of wave rb) over its column quarter; the waves share the row denominators through
 // LDS.  The normalised bf16 rows are staged in LDS (the tile stages are free once the key
 // stream ended) and written out one 1 KB row per instruction: stores straight from the
 // MFMA layout would scatter 8 bytes per lane over 32 rows.  row_dst(r) gives the output
@@ -423,17 +436,20 @@ __device__ __forceinline__ float finish(WaveState &st, uint8_t MLA_LDS *stage,
     float MLA_LDS *den = (float MLA_LDS *)pbuf;  // buffer free: the key stream ended on a barrier
     if (l < 32) den[w * 32 + l] = lt;
     __syncthreads();
-    const float lo = den[(w ^ 1) * 32 + (l & 31)];
-    const float inv[2] = {lt > 0.0f ? 1.0f / lt : 0.0f, lo > 0.0f ? 1.0f / lo : 0.0f};
-    const int ch = w & 1;
+    float inv[4];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int r = (w ^ rb) * 32 + (l & 31);
+    for (int rb = 0; rb < 4; ++rb) {
+        const float x = den[rb * 32 + (l & 31)];
+        inv[rb] = x > 0.0f ? 1.0f / x : 0.0f;
+    }
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
+    for (int rb = 0; rb < 4; ++rb) {
+        const int r = rb * 32 + (l & 31);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int col = ch * 256 + nb * 32 + g * 8 + hi * 4;
+                const int col = w * 128 + nb * 32 + g * 8 + hi * 4;
                 const f32x16 &o = st.o[nb][rb];
                 const bf16x4 v = {f2bf(o[g * 4 + 0] * inv[rb]), f2bf(o[g * 4 + 1] * inv[rb]),
                                   f2bf(o[g * 4 + 2] * inv[rb]), f2bf(o[g * 4 + 3] * inv[rb])};
@@ -469,14 +485,17 @@ __device__ __forceinline__ float finish_f32(WaveState &st, uint8_t MLA_LDS *pbuf
     float MLA_LDS *den = (float MLA_LDS *)pbuf;  // buffer free: the key stream ended on a barrier
     if (l < 32) den[w * 32 + l] = lt;
     __syncthreads();
-    const float lo = den[(w ^ 1) * 32 + (l & 31)];
-    const float inv[2] = {lt > 0.0f ? 1.0f / lt : 0.0f, lo > 0.0f ? 1.0f / lo : 0.0f};
-    const int ch = w & 1;
+    float inv[4];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        float *row = dst + (int64_t)((w ^ rb) * 32 + (l & 31)) * fl::R + ch * 256 + hi * 4;
+    for (int rb = 0; rb < 4; ++rb) {
+        const float x = den[rb * 32 + (l & 31)];
+        inv[rb] = x > 0.0f ? 1.0f / x : 0.0f;
+    }
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
+    for (int rb = 0; rb < 4; ++rb) {
+        float *row = dst + (int64_t)(rb * 32 + (l & 31)) * fl::R + w * 128 + hi * 4;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const f32x16 &o = st.o[nb][rb];
@@ -906,8 +925,8 @@ hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int 
 // Token generation (absorption page, section 8: a separate decode kernel), one workgroup
 // per (sequence, key split, group of 128 heads), with the prefill's wave structure: wave w
 // owns heads 32w .. 32w+31 of the group, each wave scores all 32 keys of a tile for its own
-// heads, and a wave pair swaps its weights so that each wave accumulates O for the pair's
-// 64 heads over half of the latent columns.  Every tile serves all 128 heads.  Partials are
+// heads, and the four waves share their weights so that each wave accumulates O for all
+// 128 heads over a quarter of the latent columns.  Every tile serves all 128 heads.  Partials are
 // written exactly as the split decode kernel writes them (normalised bf16 rows and their
 // lse), so the split-KV combine merges them.  Three cache forms:
 //   DW_Q8   Q8_0 rows (section 8.1): every raw tile is dequantised once into the bf16 tile
@@ -948,15 +967,15 @@ static_assert(dw_front(DW_Q8) + PBUF_BYTES <= 163840 && dw_front(DW_VT) + PBUF_B
 // 16-lane read touches over the 16 bank groups.
 struct VAddrT {
     const uint8_t MLA_LDS *b[2];
-    __device__ __forceinline__ VAddrT(const uint8_t MLA_LDS *vt, int ch) {
+    __device__ __forceinline__ VAddrT(const uint8_t MLA_LDS *vt, int cq) {
         const int l = threadIdx.x & 63;
-        const int col = ch * 256 + (l & 31);     // plus 32 nb, a multiple of 16
+        const int col = cq * 128 + (l & 31);     // plus 32 nb, a multiple of 16
         const int swz = ((l & 31) >> 2) & 3;     // (col >> 2) & 3
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) b[ks] = vt + col * 64 + (((2 * ks + (l >> 5)) ^ swz) << 4);
     }
-    __device__ __forceinline__ bf16x8 load(int i) const {  // step i = (ks, nb) = (i/8, i%8)
-        return *(const bf16x8 MLA_LDS *)(b[i >> 3] + (i & 7) * 32 * 64);
+    __device__ __forceinline__ bf16x8 load(int i) const {  // step i = (ks, nb) = (i/4, i%4)
+        return *(const bf16x8 MLA_LDS *)(b[i >> 2] + (i & 3) * 32 * 64);
     }
 };
 
@@ -1000,7 +1019,7 @@ __device__ __forceinline__ void stream_keys_w(WaveState &st, uint8_t MLA_LDS *ld
     if (kend <= kbeg) return;
     const int ntiles = (kend - kbeg + fl::NK - 1) / fl::NK;
     const int lim = nk - 1;
-    const int ch = (threadIdx.x >> 6) & 1;  // column half of this wave
+    const int cq = threadIdx.x >> 6;  // column quarter of this wave
     const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // only the sequence's last tile can reach past its end
     auto tail = [&](int j) { return kbeg + (j + 1) * fl::NK > nk; };
@@ -1098,14 +1117,14 @@ __device__ __forceinline__ void stream_keys_w(WaveState &st, uint8_t MLA_LDS *ld
         static_for<32>(soft);
         st.lsum += psum;
         put_p(pbuf, pcur);
-        __syncthreads();  // the pair's weights visible
-        bf16x8 poth[2];
-        get_partner_p(pbuf, poth);
+        __syncthreads();  // every wave's weights visible
+        bf16x8 pk[4];
+        get_p0(pbuf, pk);
         auto o_update = [&](const auto &va_addr) {
             bf16x8 va[PV_AHEAD];
 #pragma unroll
             for (int i = 0; i < PV_AHEAD; ++i) va[i] = va_addr.load(i);
-            pv_tile(st, va_addr, va, pcur, poth, [&](auto jc) {
+            pv_tile(st, va_addr, va, pbuf, pk, [&](auto jc) {
                 constexpr int j = decltype(jc)::value;
                 if constexpr (MODE == DW_Q8) {
                     if (next) {
@@ -1116,9 +1135,9 @@ __device__ __forceinline__ void stream_keys_w(WaveState &st, uint8_t MLA_LDS *ld
             });
         };
         if constexpr (MODE == DW_VT)
-            o_update(VAddrT(tile + fl::TILE_BYTES, ch));
+            o_update(VAddrT(tile + fl::TILE_BYTES, cq));
         else
-            o_update(VAddr(tile, ch));
+            o_update(VAddr(tile, cq));
         static_assert(5 + 3 == DequantQ8::TASKS - 1, "four tasks in the O-update steps");
     }
     __syncthreads();
