@@ -82,7 +82,7 @@ __device__ __forceinline__ f32x16 score_tile(const WaveState &st, const uint8_t 
         return kk < 32 ? kb[kk & 1] + (kk >> 1) * 64 : rowb + (((2 * (kk - 32) + hi) ^ mb) * 16);
     };
     f32x16 s;
-    constexpr int QK_AHEAD = 4;
+    constexpr int QK_AHEAD = 6;
     bf16x8 a[QK_AHEAD];
 #pragma unroll
     for (int kk = 0; kk < QK_AHEAD; ++kk) a[kk] = *(const bf16x8 MLA_LDS *)kaddr(kk);
