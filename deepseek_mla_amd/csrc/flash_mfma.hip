@@ -178,6 +178,7 @@ constexpr int PV_AHEAD = 2;  // V^T read-ahead in PV steps (four MFMAs each)
 __device__ __forceinline__ void soft_piece(const f32x16 &s, int e, float sc, float nmu,
                                            float &psum, bf16x8 (&p)[2]) {
     const float pe = __builtin_amdgcn_exp2f(fmaf(s[e], sc, nmu));
+    asm volatile("" ::"v"(pe));  // computed here, between the MFMAs (not sunk to its use)
     psum += pe;
     p[e >> 3][e & 7] = f2bf(pe);
 }
@@ -219,6 +220,18 @@ __device__ __forceinline__ void pv_tile(WaveState &st, const VA &va_addr,
 // step per MFMA, 32 steps): step 0 masks and sets the reference, odd step 2e+1 computes
 // weight e (about two VALU operations per MFMA, which issue in the MFMA's shadow), step
 // 31 also tests for overflow.  The weights land in p, their sum in psum.
+// The weights alone (step 2e+1 computes weight e), for an O update whose softmax set-up
+// and overflow test run outside it.
+struct SoftPieces {
+    const f32x16 &s;
+    bf16x8 (&p)[2];
+    float &psum;
+    const float nmu, sc;
+    __device__ __forceinline__ void operator()(int i) const {
+        if (i & 1) soft_piece(s, i >> 1, sc, nmu, psum, p);
+    }
+};
+
 struct SoftFill {
     WaveState &st;
     f32x16 &s;
@@ -345,9 +358,12 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
                 if (ti > 0 && kk >= 36 - PV_AHEAD)
                     va[kk - (36 - PV_AHEAD)] = vprev.load(kk - (36 - PV_AHEAD));
             });
-            float nmu = 0.0f, psum = 0.0f;
+            float psum = 0.0f;
+            // the reference (its wave-uniform branch runs before the O update: a branch
+            // among the MFMAs would split the block and the weights would sink to its end)
+            float nmu = softmax_prep(st, s, key0, lim_t, sc);
             bf16x8 pcur[2];
-            const SoftFill soft{st, s, pcur, psum, nmu, key0, lim_t, sc};
+            const SoftPieces soft{s, pcur, psum, nmu, sc};
             // Copy parts go between the O-update MFMAs (even steps; the softmax takes the
             // odd ones): that phase leaves LDS bandwidth for the copies' writes, while the
             // score MFMAs already keep LDS busy with K-fragment reads.
@@ -363,6 +379,7 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             } else {
                 static_for<32>(fill);
             }
+            softmax_check(st, s, psum, sc);
             st.lsum += psum;
             pprev[0] = pcur[0];
             pprev[1] = pcur[1];
