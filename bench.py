@@ -52,20 +52,19 @@ MATERIALIZED_SRC = ("deepseek_mla_amd/csrc/flash_mha.hip", "deepseek_mla_amd/csr
                     "deepseek_mla_amd/csrc/lds_dma.h", "deepseek_mla_amd/csrc/common.h")
 TRAFFIC = {
     # workload: (bytes per launch, sources, sha256 prefix)
-    "v3_long_prefill": (18188329433, ABSORBED_SRC, "b395ee7ecdc23bfa"),
-    "lite_prefill": (228379384, ABSORBED_SRC, "b395ee7ecdc23bfa"),
-    "v3_decode": (73664603, ABSORBED_SRC, "b395ee7ecdc23bfa"),
-    "v3_decode@vt": (141551574, ABSORBED_SRC, "b395ee7ecdc23bfa"),
-    "v3_decode_q8": (314777499, ABSORBED_SRC, "b395ee7ecdc23bfa"),
-    "v3_long_prefill@materialized": (3401222750, MATERIALIZED_SRC, "dc2fec14b793305f"),
+    "v3_long_prefill": (10917061297, ABSORBED_SRC, "1f42f3fff257ac9d"),
+    "lite_prefill": (227765411, ABSORBED_SRC, "1f42f3fff257ac9d"),
+    "v3_decode": (73664650, ABSORBED_SRC, "1f42f3fff257ac9d"),
+    "v3_decode@vt": (141546325, ABSORBED_SRC, "1f42f3fff257ac9d"),
+    "v3_decode_q8": (315308532, ABSORBED_SRC, "1f42f3fff257ac9d"),
+    "v3_long_prefill@materialized": (3401259541, MATERIALIZED_SRC, "dc2fec14b793305f"),
 }
 # Sustained shader clock under each kernel's load (GHz): GRBM_GUI_ACTIVE cycles per
 # dispatch over the dispatch's duration, from the counter summaries in profiles/; keyed
 # like TRAFFIC.
 CLOCK_GHZ = {
-    "v3_long_prefill": (2.157, ABSORBED_SRC, "b395ee7ecdc23bfa"),
-    "v3_decode_q8": (2.145, ABSORBED_SRC, "b395ee7ecdc23bfa"),
-    "v3_long_prefill@materialized": (1.927, MATERIALIZED_SRC, "dc2fec14b793305f"),
+    "v3_long_prefill": (2.043, ABSORBED_SRC, "1f42f3fff257ac9d"),
+    "v3_long_prefill@materialized": (1.920, MATERIALIZED_SRC, "dc2fec14b793305f"),
 }
 
 
