@@ -45,25 +45,31 @@ MFMA_FLOP_PER_CLK = 256 * 4096  # chip-wide dense bf16 FLOP per clock
 # passes scaled by a 512 MiB copy (fetch x2.0, write x1.0); the summaries and commands are
 # in profiles/.  Each figure is valid only for the kernel sources it was taken on (sha256
 # prefix over the files listed, in order).
-ABSORBED_SRC = ("deepseek_mla_amd/csrc/flash_mfma.hip", "deepseek_mla_amd/csrc/decode_mfma.hip",
-                "deepseek_mla_amd/csrc/latent_tile.h", "deepseek_mla_amd/csrc/lds_dma.h",
-                "deepseek_mla_amd/csrc/simt.hip", "deepseek_mla_amd/csrc/common.h")
-MATERIALIZED_SRC = ("deepseek_mla_amd/csrc/flash_mha.hip", "deepseek_mla_amd/csrc/latent_tile.h",
-                    "deepseek_mla_amd/csrc/lds_dma.h", "deepseek_mla_amd/csrc/common.h")
+_CSRC = "deepseek_mla_amd/csrc/"
+# the prefill kernel and its merge
+PREFILL_SRC = tuple(_CSRC + f for f in ("flash_mfma.hip", "latent_tile.h", "lds_dma.h", "common.h"))
+# the 64-head split decode and the combine
+DECODE_SRC = tuple(_CSRC + f for f in ("decode_mfma.hip", "simt.hip", "latent_tile.h", "lds_dma.h",
+                                       "common.h"))
+# the 128-head split decode (Q8_0, K + V^T) and the combine
+WIDE_DECODE_SRC = tuple(_CSRC + f for f in ("flash_mfma.hip", "simt.hip", "latent_tile.h",
+                                            "lds_dma.h", "common.h"))
+MATERIALIZED_SRC = tuple(_CSRC + f for f in ("flash_mha.hip", "latent_tile.h", "lds_dma.h",
+                                             "common.h"))
 TRAFFIC = {
     # workload: (bytes per launch, sources, sha256 prefix)
-    "v3_long_prefill": (10917061297, ABSORBED_SRC, "1f42f3fff257ac9d"),
-    "lite_prefill": (227765411, ABSORBED_SRC, "1f42f3fff257ac9d"),
-    "v3_decode": (73664650, ABSORBED_SRC, "1f42f3fff257ac9d"),
-    "v3_decode@vt": (141546325, ABSORBED_SRC, "1f42f3fff257ac9d"),
-    "v3_decode_q8": (315308532, ABSORBED_SRC, "1f42f3fff257ac9d"),
+    "v3_long_prefill": (10917061297, PREFILL_SRC, "a366e71f165c98e2"),
+    "lite_prefill": (227765411, PREFILL_SRC, "a366e71f165c98e2"),
+    "v3_decode": (73664650, DECODE_SRC, "4c8d37b98d6313b5"),
+    "v3_decode@vt": (141546325, WIDE_DECODE_SRC, "33bd3954592c5db6"),
+    "v3_decode_q8": (315308532, WIDE_DECODE_SRC, "33bd3954592c5db6"),
     "v3_long_prefill@materialized": (3401259541, MATERIALIZED_SRC, "dc2fec14b793305f"),
 }
 # Sustained shader clock under each kernel's load (GHz): GRBM_GUI_ACTIVE cycles per
 # dispatch over the dispatch's duration, from the counter summaries in profiles/; keyed
 # like TRAFFIC.
 CLOCK_GHZ = {
-    "v3_long_prefill": (2.043, ABSORBED_SRC, "1f42f3fff257ac9d"),
+    "v3_long_prefill": (2.043, PREFILL_SRC, "a366e71f165c98e2"),
     "v3_long_prefill@materialized": (1.920, MATERIALIZED_SRC, "dc2fec14b793305f"),
 }
 

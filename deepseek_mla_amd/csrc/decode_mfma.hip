@@ -147,16 +147,17 @@ __device__ __forceinline__ void load_pt(const uint8_t MLA_LDS *pb, bf16x8 (&pt)[
 // Scores of one tile (stage t) for both head blocks: 18 steps, each one K fragment (read
 // four steps ahead) feeding two 16x16x32 MFMAs.  Even and odd steps accumulate into
 // separate chains (four in flight), summed at the end.  fill(kk) follows step kk.
+//
+// The score MFMAs are asm statements with VGPR accumulators: given the choice, the
+// register allocator puts the chains into the AGPRs of O blocks and moves those blocks
+// to VGPRs and back on every tile (112 extra instructions per tile, in a loop that is
+// bound by instruction issue).  The chains start from a literal zero (no VALU write feeds
+// an MFMA source), and since the compiler does not count wait states after an MFMA it
+// cannot see, 20 of them separate the last MFMAs from the reads of their results.
 template <typename Fill>
 __device__ __forceinline__ void score_tile_q(const DqState &st, const uint8_t MLA_LDS *t,
                                              const KAddr &ka, f32x4 (&s)[2], Fill fill) {
     f32x4 c[2][2];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int par = 0; par < 2; ++par)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) c[hb][par][e] = 0.0f;
     constexpr int AH = 4;
     bf16x8 a[AH];
 #pragma unroll
@@ -164,13 +165,24 @@ __device__ __forceinline__ void score_tile_q(const DqState &st, const uint8_t ML
     static_for<dq::KSTEPS>([&](auto kc) {
         constexpr int kk = decltype(kc)::value;
         constexpr int par = kk & 1;
-        c[0][par] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk % AH], st.q[0][kk], c[0][par], 0, 0, 0);
-        c[1][par] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk % AH], st.q[1][kk], c[1][par], 0, 0, 0);
+        if constexpr (kk < 2) {
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+                asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0"
+                             : "=&v"(c[hb][par]) : "v"(a[kk % AH]), "v"(st.q[hb][kk]));
+        } else {
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+                asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                             : "+v"(c[hb][par]) : "v"(a[kk % AH]), "v"(st.q[hb][kk]));
+        }
         if constexpr (kk + AH < dq::KSTEPS)
             a[kk % AH] = *(const bf16x8 MLA_LDS *)(t + ka.at(kk + AH));
         fill(kc);
         __builtin_amdgcn_sched_barrier(0);
     });
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                 : "+v"(c[0][0]), "+v"(c[0][1]), "+v"(c[1][0]), "+v"(c[1][1]));
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
