@@ -1063,6 +1063,7 @@ __device__ __forceinline__ void stream_keys_w(WaveState &st, uint8_t MLA_LDS *ld
     };
     // Every earlier vector-memory load (queries, the sequence length) completes before the
     // first copy: the compiler does not see the copies (see lds_copy16).
+    [[maybe_unused]] const Q8CopyParts<NW> qparts;
     MLA_WAIT_VMCNT(0);
     if constexpr (MODE == DW_Q8) {
         for (int j = 0; j < DW_NR; ++j)
@@ -1081,7 +1082,9 @@ __device__ __forceinline__ void stream_keys_w(WaveState &st, uint8_t MLA_LDS *ld
             // stage takes raw tile t+3)
             wait_vm_q8(cnt(t + 2));
             __syncthreads();
-            if (t + 3 < ntiles) issue_raw(t + 3);
+            // raw tile t+3 (into the stage raw tile t left): the tail tile's copies here, a
+            // whole tile's spread over the score steps below
+            if (t + 3 < ntiles && tail(t + 3)) issue_raw(t + 3);
         } else {
             // tile t landed; the barrier also orders the O update of tile t-1, whose stage
             // takes tile t+1
@@ -1103,21 +1106,40 @@ __device__ __forceinline__ void stream_keys_w(WaveState &st, uint8_t MLA_LDS *ld
         [[maybe_unused]] const uint8_t *sbase = rows + (int64_t)(nkey0 + 8 * wu) * fl::RB;
         [[maybe_unused]] const uint32_t ndst = lds_u32(stage(t + 1));
         [[maybe_unused]] const CopyPlan plan = make_copy_plan();
-        [[maybe_unused]] const DequantQ8 dqz{raw + ((t + 1) % DW_NR) * Q8_RAW_STAGE,
-                                             lds + ((t + 1) & 1) * fl::TILE_BYTES, nkey0, nk};
+        // Q8_0: the dequantisation of raw tile t+1, also after the split's last tile (it
+        // then converts a stale raw stage into the free bf16 stage: both lie inside LDS, and
+        // nothing reads the result), which keeps the tile loop free of branches around it
+        [[maybe_unused]] const DequantQ8Pieces dqp(raw + ((t + 1) % DW_NR) * Q8_RAW_STAGE,
+                                                   lds + ((t + 1) & 1) * fl::TILE_BYTES, nkey0, nk);
+        [[maybe_unused]] const bool raw_fast = t + 3 < ntiles && !tail(t + 3);
+        [[maybe_unused]] const uint8_t *rbase = rows + (int64_t)(kbeg + (t + 3) * fl::NK) * fl::Q8_RB;
+        [[maybe_unused]] const uint32_t rstage = lds_u32(raw + ((t + 3) % DW_NR) * Q8_RAW_STAGE);
         [[maybe_unused]] DequantQ8::Words dw;
+        [[maybe_unused]] DequantQ8Pieces::Mid mid;
+        [[maybe_unused]] bf16x4 h0, h1;
         const int key0 = kbeg + t * fl::NK;
         int lim_t = lim;
         asm volatile("" : "+v"(lim_t));
-        // Q8_0: the dequantisation of raw tile t+1 between the MFMAs: task m (0 .. 4) is
-        // fetched after score step 7m and converted after step 7m + 4; tasks 5 .. 8 are
-        // fetched after the O-update steps 8(m - 5) and converted after steps 8(m - 5) + 6.
+        // Q8_0: the dequantisation of raw tile t+1 between the MFMAs, one piece per step:
+        // task m (0 .. 4) is fetched after score step 7m, prepared after step 7m + 3 and
+        // converted and stored after steps 7m + 4 and 7m + 5; raw copy instruction m of
+        // tile t+3 follows step 7m + 1.  Tasks 5 .. 8 take the O-update steps 8(m - 5) + 0,
+        // 3, 4 and 5 the same way.
         f32x16 s = score_tile(st, tile, key0 + fl::NK - 1 > lim, key0, lim_t, [&](auto kc) {
             constexpr int kk = decltype(kc)::value;
             if constexpr (MODE == DW_Q8) {
-                if (next) {
-                    if constexpr (kk % 7 == 0 && kk / 7 < 5) dw = dqz.load(kk / 7);
-                    if constexpr (kk % 7 == 4 && kk / 7 < 5) dqz.convert(kk / 7, dw);
+                constexpr int m = kk / 7, r = kk % 7;
+                if constexpr (m < 5) {
+                    if constexpr (r == 0) dqp.fetch(m, dw);
+                    if constexpr (r == 1) {
+                        if (raw_fast) qparts.issue(rbase, rstage, m);
+                    }
+                    if constexpr (r == 3) dqp.prep(dw, mid);
+                    if constexpr (r == 4) dqp.half(mid, 0, h0);
+                    if constexpr (r == 5) {
+                        dqp.half(mid, 1, h1);
+                        dqp.store(m, h0, h1);
+                    }
                 }
             } else {
                 if (fast) {
@@ -1127,7 +1149,8 @@ __device__ __forceinline__ void stream_keys_w(WaveState &st, uint8_t MLA_LDS *ld
                 }
             }
         });
-        static_assert(7 * 4 + 4 < 36 && 4 * 8 < 36, "every task and copy inside the score steps");
+        static_assert(7 * 4 + 5 < 36 && 4 * 8 < 36 && Q8_X4_INST / NW == 5,
+                      "every task, raw copy and bf16 copy inside the score steps");
         float nmu = 0.0f, psum = 0.0f;
         bf16x8 pcur[2];
         const SoftFill soft{st, s, pcur, psum, nmu, key0, lim_t, sc};
@@ -1144,9 +1167,13 @@ __device__ __forceinline__ void stream_keys_w(WaveState &st, uint8_t MLA_LDS *ld
             pv_tile(st, va_addr, va, pbuf, pk, [&](auto jc) {
                 constexpr int j = decltype(jc)::value;
                 if constexpr (MODE == DW_Q8) {
-                    if (next) {
-                        if constexpr (j % 8 == 0) dw = dqz.load(5 + j / 8);
-                        if constexpr (j % 8 == 6) dqz.convert(5 + j / 8, dw);
+                    constexpr int m = 5 + j / 8, r = j % 8;
+                    if constexpr (r == 0) dqp.fetch(m, dw);
+                    if constexpr (r == 3) dqp.prep(dw, mid);
+                    if constexpr (r == 4) dqp.half(mid, 0, h0);
+                    if constexpr (r == 5) {
+                        dqp.half(mid, 1, h1);
+                        dqp.store(m, h0, h1);
                     }
                 }
             });

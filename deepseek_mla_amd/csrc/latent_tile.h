@@ -206,6 +206,28 @@ __device__ __forceinline__ void issue_tile_q8_full(const uint8_t *__restrict__ r
         lds_copy16(gbase, (uint32_t)min(inst * 64 + l, LAST) * 16u, lds_u32(dst + inst * 1024));
     }
 }
+// The same copy one instruction at a time, with the per-lane offsets formed once for a
+// whole stream: instruction i of wave w moves pieces 64 (w NI + i) .. +63.
+template <int NW>
+struct Q8CopyParts {
+    static constexpr int NI = Q8_X4_INST / NW;
+    uint32_t off[NI];  // source byte offsets inside the tile (clamped to its last piece)
+    uint32_t dst0;     // LDS offset of the wave's first instruction inside a stage
+    __device__ __forceinline__ Q8CopyParts() {
+        static_assert(Q8_X4_INST % NW == 0, "raw copies must split evenly over waves");
+        constexpr int LAST = fl::Q8_TILE_BYTES / 16 - 1;
+        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int l = threadIdx.x & 63;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) off[i] = (uint32_t)min((w * NI + i) * 64 + l, LAST) * 16u;
+        dst0 = (uint32_t)(w * NI * 1024);
+    }
+    // instruction i of the copy of the tile at gbase (the global image of its first row)
+    // into the stage at LDS offset stage
+    __device__ __forceinline__ void issue(const uint8_t *gbase, uint32_t stage, int i) const {
+        lds_copy16(gbase, off[i], stage + dst0 + (uint32_t)(i * 1024));
+    }
+};
 static_assert(fl::Q8_TILE_BYTES % 16 == 0, "a tile is a whole number of 16-byte pieces");
 
 // Number of async-copy instructions a wave issues per Q8_0 tile (for vmcnt waits).
@@ -304,6 +326,76 @@ struct DequantQ8 {
     }
 };
 static_assert(fl::Q8_TILE_BYTES + 8 <= Q8_RAW_STAGE, "the last task's third word stays in the stage");
+
+// The same dequantisation (same tasks, same arithmetic) cut into pieces of a few
+// instructions, for a loop that places one piece after each of its MFMAs: fetch (the
+// task's four LDS reads), prep (align the 8 codes, flip their sign bits, the block scale),
+// then half 0 and half 1 (four values each: byte placement, mixed-precision fmas, bf16
+// rounding), and store.  The per-thread LDS addresses are formed once per tile, so every
+// task reads and writes at constant offsets from them.  Each piece pins its inputs and
+// outputs with empty asm statements so that the compiler keeps it where it is placed.
+struct DequantQ8Pieces {
+    const uint8_t MLA_LDS *rw;  // first code dword of task 0 (task i: + 68 i)
+    const uint8_t MLA_LDS *rs;  // scale of task 0's block
+    uint8_t MLA_LDS *wa;        // latent output chunk of task 0 (task i < 8: + 128 i)
+    uint8_t MLA_LDS *wb;        // rope output chunk (task 8)
+    uint32_t sh;                // byte offset of the codes in their first dword (0 or 2)
+    bool valid;                 // the thread's row lies inside the sequence
+
+    struct Mid {
+        uint32_t lo, hi;  // codes 0..3 and 4..7 with the sign bit flipped (u = q + 128)
+        _Float16 d;       // block scale (0 for rows past the sequence end)
+        float c;          // -1152 d
+    };
+
+    __device__ __forceinline__ DequantQ8Pieces(const uint8_t MLA_LDS *raw, uint8_t MLA_LDS *dst,
+                                               int key0, int n_rows) {
+        const int x = (int)threadIdx.x, k = x >> 3, c0 = x & 7;
+        const int blk = k * fl::Q8_RB + ((x >> 2) & 1) * 34;
+        const int o = blk + 2 + (x & 3) * 8;
+        rw = raw + (o & ~3);
+        rs = raw + blk;
+        sh = (uint32_t)(o & 3);
+        wa = dst + k * fl::PA + ((c0 ^ mask_a(k)) << 4);
+        wb = dst + fl::A_BYTES + k * fl::PB + ((c0 ^ mask_b(k)) << 4);
+        valid = key0 + k < n_rows;
+    }
+    __device__ __forceinline__ void fetch(int i, DequantQ8::Words &r) const {
+        r.w0 = *(const uint32_t MLA_LDS *)(rw + 68 * i);
+        r.w1 = *(const uint32_t MLA_LDS *)(rw + 68 * i + 4);
+        r.w2 = *(const uint32_t MLA_LDS *)(rw + 68 * i + 8);
+        r.d = *(const uint16_t MLA_LDS *)(rs + 68 * i);
+    }
+    __device__ __forceinline__ void prep(DequantQ8::Words &r, Mid &m) const {
+        asm volatile("" : "+v"(r.w0), "+v"(r.w1), "+v"(r.w2), "+v"(r.d));
+        m.lo = __builtin_amdgcn_alignbyte(r.w1, r.w0, sh) ^ 0x80808080u;
+        m.hi = __builtin_amdgcn_alignbyte(r.w2, r.w1, sh) ^ 0x80808080u;
+        m.d = valid ? __builtin_bit_cast(_Float16, r.d) : (_Float16)0.0f;
+        m.c = -1152.0f * (float)m.d;  // exact: 9 * 2^7 times an 11-bit value
+        asm volatile("" : "+v"(m.lo), "+v"(m.hi), "+v"(m.d), "+v"(m.c));
+    }
+    __device__ __forceinline__ void half(Mid &m, int hf, bf16x4 &v) const {
+        asm volatile("" : "+v"(m.lo), "+v"(m.hi), "+v"(m.d), "+v"(m.c));
+        constexpr uint32_t EXP = 0x64646464u;  // binary16 exponent byte of 1024
+        const uint32_t src = hf ? m.hi : m.lo;
+        const uint32_t h[2] = {__builtin_amdgcn_perm(EXP, src, 0x05010400u),
+                               __builtin_amdgcn_perm(EXP, src, 0x05030402u)};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const f16x2 x = __builtin_bit_cast(f16x2, h[e]);
+            v[2 * e] = f2bf(fmaf((float)x[0], (float)m.d, m.c));
+            v[2 * e + 1] = f2bf(fmaf((float)x[1], (float)m.d, m.c));
+        }
+        asm volatile("" : "+v"(v));
+    }
+    __device__ __forceinline__ void store(int i, bf16x4 a, bf16x4 b) const {
+        const bf16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        if (i < 8)
+            *(bf16x8 MLA_LDS *)(wa + 128 * i) = v;
+        else
+            *(bf16x8 MLA_LDS *)wb = v;
+    }
+};
 
 
 }  // namespace mla
