@@ -11,7 +11,9 @@
 
 Paths: the Lite-shaped prefill with cut row groups (work lists and the merge), the bf16
 split decode, the Q8_0 decode (128 heads per workgroup), the batched decode that runs on
-the prefill kernel, the K + V^T decode, the float32 decode and the materialised prefill.
+the prefill kernel, the K + V^T decode, the float32 decode and the materialised prefill;
+then the projections (absorb and out-proj, few-token and GEMM kernels), the cache append
+(bf16, Q8_0, Hadamard-rotated Q8_0: only the target rows may change) and the Q8_0 helpers.
 """
 import numpy as np
 import pytest
@@ -236,3 +238,77 @@ def test_materialized_repeat(dev):
                                      scratch_cap_mib=cap, workspace=ws.t[:wsb])
 
     repeat_check("materialised prefill", run, [v, out, lse], ws)
+
+
+@pytest.mark.parametrize("T", [5, 300])
+def test_projections_repeat(dev, T):
+    """mla_absorb_q and mla_out_proj (Lite dims; T = 5 takes the few-token kernels):
+    q_cat, v and out bitwise repeatable, fully written, guards intact."""
+    from deepseek_mla_amd import mla
+    d = synth.deepseek_dims(16, 2048)
+    x = synth.generate(d, T, T, seed=451 + T, mode="bf16")
+    q_nope, q_rope, wk_b = bf16_dev(x["q_nope"]), bf16_dev(x["q_rope"]), bf16_dev(x["wk_b"])
+    wv_b, wo = bf16_dev(x["wv_b"]), bf16_dev(x["wo"])
+    pos = torch.from_numpy(x["pos"]).to("cuda")
+    o_lat = bf16_dev(np.random.default_rng(452).standard_normal((T, 16, R)) * 0.2)
+    cd = mla.make_dims(d)
+    q_cat = Guarded((T, 16, W), torch.bfloat16)
+    v = Guarded((T, 16 * 128), torch.bfloat16)
+    out = Guarded((T, 2048), torch.bfloat16)
+    repeat_check(f"absorb T={T}",
+                 lambda: mla.mla_absorb_q(cd, mla.BF16, q_nope, q_rope, pos, wk_b, q_cat.t, T),
+                 [q_cat], None)
+    repeat_check(f"out_proj T={T}",
+                 lambda: mla.mla_out_proj(cd, mla.BF16, o_lat, wv_b, wo, v.t, out.t, T),
+                 [v, out], None)
+
+
+@pytest.mark.parametrize("mode,hadamard", [("bf16", False), ("q8_0", False), ("q8_0", True)])
+def test_cache_append_bounds(dev, mode, hadamard):
+    """mla_cache_append (and the Hadamard-rotated form) into a cache of random bytes: only
+    the target rows change, the guards around the cache stay intact, and a second append of
+    the same tokens writes the same bits."""
+    from deepseek_mla_amd import mla
+    d = synth.deepseek_dims(16, 2048)
+    rng = np.random.default_rng(461)
+    T, n_rows = 37, 300
+    pos = rng.choice(n_rows, size=T, replace=False).astype(np.int32)
+    c_kv = bf16_dev(rng.standard_normal((T, R)))
+    k_rope = bf16_dev(rng.standard_normal((T, 64)))
+    pt = torch.from_numpy(pos).to("cuda")
+    row_bytes = 612 if mode == "q8_0" else W * 2
+    cache = Guarded((n_rows, row_bytes), torch.uint8)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(462)
+    cache.poison(gen)
+    before = cache.t.cpu().numpy().copy()
+    kv = mla.Q8_0 if mode == "q8_0" else mla.BF16
+    call = mla.mla_cache_append_hadamard if hadamard else mla.mla_cache_append
+    target = np.zeros(n_rows, bool)
+    target[pos] = True
+    first = None
+    for rep in range(2):
+        call(mla.make_dims(d), mla.BF16, kv, c_kv, k_rope, pt, T, cache.t, n_rows)
+        torch.cuda.synchronize()
+        after = cache.t.cpu().numpy()
+        changed_other = int((after[~target] != before[~target]).sum())
+        diff = 0 if first is None else int((after[target] != first).sum())
+        print(f"  append {mode}{' hadamard' if hadamard else ''} rep {rep}: other rows' bytes "
+              f"changed {changed_other}, guard bytes changed {cache.intact()}, target bytes "
+              f"differing from rep 0 {diff}", flush=True)
+        assert changed_other == 0 and cache.intact() == 0 and diff == 0
+        if first is None:
+            first = after[target].copy()
+
+
+def test_q8_0_helpers_bounds(dev):
+    """mla_quantize_q8_0 and mla_dequant_q8_0 on 333 rows: outputs fully written and
+    repeatable, guards intact."""
+    from deepseek_mla_amd import mla
+    rng = np.random.default_rng(471)
+    n = 333
+    x = torch.from_numpy(rng.standard_normal((n, W)).astype(np.float32)).to("cuda")
+    rows = Guarded((n, 612), torch.uint8)
+    repeat_check("quantize", lambda: mla.mla_quantize_q8_0(x, rows.t, n, W), [rows], None)
+    out = Guarded((n, W), torch.float32)
+    repeat_check("dequant", lambda: mla.mla_dequant_q8_0(rows.t, out.t, n, W), [out], None)
