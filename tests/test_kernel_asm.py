@@ -12,6 +12,11 @@ generated code that these tests pin:
 * no scratch (spill) access sits inside a tile loop that issues copies: the loop's hand
   placed vmcnt waits count only copies, and a spill reload there would also stall on
   every copy in flight.
+
+The same copy properties are pinned for the Q8_0 decodes and the K + V^T decode.  The
+split decode's score MFMAs are inline asm with VGPR accumulators, whose wait states the
+compiler does not manage; the generated code must keep VALU writes away from their
+sources and their results unread for 20 wait states after the last one.
 """
 import os
 import re
@@ -24,6 +29,9 @@ from deepseek_mla_amd import build as B
 
 SRCS = [os.path.join(B.CSRC, f) for f in ("flash_mfma.hip", "decode_mfma.hip", "flash_mha.hip")]
 BF16_KERNELS = ("flash_prefill_bf16_kernel", "flash_decode_kernelILb0E", "flash_mha_kernel")
+# every kernel with LDS-direct tile copies: the bf16 ones, the Q8_0 split decode and the
+# 128-head decodes (Q8_0, bf16, K + V^T)
+COPY_KERNELS = BF16_KERNELS + ("flash_decode_kernelILb1E", "flash_decode_w_kernel")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None,
                                 reason="hipcc not available")
@@ -66,8 +74,14 @@ def bf16_bodies(text):
     return b
 
 
+def copy_bodies(text):
+    b = {n: body for n, body in kernel_bodies(text).items() if any(k in n for k in COPY_KERNELS)}
+    assert len(b) == 8, sorted(kernel_bodies(text))
+    return b
+
+
 def test_m0_written_only_by_copy_asm(asm):
-    for name, body in bf16_bodies(asm).items():
+    for name, body in copy_bodies(asm).items():
         in_asm = False
         for line in body:
             s = line.strip()
@@ -88,7 +102,7 @@ def test_lds_loads_have_no_immediate_offset(asm):
 
 
 def test_no_spill_access_in_copy_loops(asm):
-    for name, body in bf16_bodies(asm).items():
+    for name, body in copy_bodies(asm).items():
         labels = {}
         for i, line in enumerate(body):
             m = re.match(r"^(\.LBB\w+):", line)
@@ -116,3 +130,59 @@ def test_no_spill_access_in_copy_loops(asm):
             spills = [x for x in instrs_of(h, e) if x.startswith("scratch_")]
             assert not spills, f"{name}: spill access in the tile loop: {spills[:3]}"
         assert loops >= 1, f"{name}: tile loop not found"
+
+
+def _vregs(tok):
+    m = re.match(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def test_vgpr_accumulator_mfma_wait_states(asm):
+    """In the split decode, around every MFMA that accumulates in VGPRs (the asm score
+    MFMAs): no VALU instruction writes one of its sources in the 4 instructions before it,
+    and no instruction other than an MFMA accumulating into the same registers reads or
+    writes its result within 20 wait states after it (s_nop n counts n + 1)."""
+    bodies = {n: b for n, b in kernel_bodies(asm).items() if "flash_decode_kernel" in n}
+    assert len(bodies) == 2, sorted(bodies)
+    for name, body in bodies.items():
+        ins = []
+        for line in body:
+            t = line.split(";")[0].strip()
+            if t and not t.startswith(".") and not t.endswith(":"):
+                ins.append(t)
+        found = 0
+        for i, t in enumerate(ins):
+            parts = t.split(None, 1)
+            ops = [x.strip() for x in parts[1].split(",")] if len(parts) > 1 else []
+            if not parts[0].startswith("v_mfma") or not ops or not ops[0].startswith("v"):
+                continue
+            found += 1
+            dst = _vregs(ops[0])
+            srcs = set().union(*[_vregs(x) for x in ops[1:4]])
+            for j in range(max(0, i - 4), i):
+                p = ins[j].split(None, 1)
+                if p[0].startswith("v_") and not p[0].startswith("v_mfma") and len(p) > 1:
+                    w = _vregs(p[1].split(",")[0].strip())
+                    assert not (w & srcs), f"{name}: VALU write feeds an MFMA: {ins[j]} | {t}"
+            ws = 0
+            for j in range(i + 1, min(len(ins), i + 40)):
+                p = ins[j].split(None, 1)
+                if p[0] == "s_nop":
+                    ws += int(p[1], 0) + 1
+                    continue
+                if ws >= 20:
+                    break
+                q = [x.strip() for x in p[1].split(",")] if len(p) > 1 else []
+                used = set().union(*[_vregs(x) for x in q]) if q else set()
+                if p[0].startswith("v_mfma"):
+                    # a later MFMA may accumulate into exactly these registers (srcC = dst)
+                    assert not (set().union(*[_vregs(x) for x in q[1:3]]) & dst), \
+                        f"{name}: MFMA result used as a multiplicand: {t} | {ins[j]}"
+                else:
+                    assert not (used & dst), f"{name}: MFMA result touched after {ws} wait " \
+                                             f"states: {t} | {ins[j]}"
+                ws += 1
+        assert found >= 36, f"{name}: {found} VGPR-accumulator MFMAs"
