@@ -78,61 +78,6 @@ struct DqState {
     bool bad;                 // a score exceeded m + FREEZE_LIMIT in this pass
 };
 
-// Byte offsets (within a tile stage) of the K fragment of score step kk for this lane:
-// key kh*16 + (l & 15), logical chunk kk*4 + (l >> 4).  Latent chunks (kk < 16) are
-// stored at kk*4 + ((l >> 4) ^ mask_a(key)): one base plus kk*64.
-struct KAddr {
-    uint32_t a, r0, r1;
-    __device__ __forceinline__ KAddr(int kh) {
-        const int l = threadIdx.x & 63, g = l >> 4;
-        const int k = kh * 16 + (l & 15);
-        a = (uint32_t)(k * fl::PA + ((g ^ mask_a(k)) << 4));
-        r0 = (uint32_t)(fl::A_BYTES + k * fl::PB + ((g ^ mask_b(k)) << 4));
-        r1 = (uint32_t)(fl::A_BYTES + k * fl::PB + (((4 + g) ^ mask_b(k)) << 4));
-    }
-    __device__ __forceinline__ uint32_t at(int kk) const {
-        return kk < 16 ? a + (uint32_t)(kk * 64) : (kk == 16 ? r0 : r1);
-    }
-};
-
-// Byte offsets of the V^T fragments (A operand of 32x32x16: lane l holds column l & 31
-// of a 32-column block and keys (l >> 5)*8 .. +7 of a 16-key step).  Two transposing
-// reads of 4 keys each: in its 16-lane group G, lane 4r + c addresses key
-// (G >> 1)*8 + 4s + r and columns (G & 1)*16 + 4c .. +3 of the block; lane i of the group
-// receives column (G & 1)*16 + i of those 4 keys.  The row mask mask_a depends only on
-// (G >> 1, s), so step (cb, ks) adds a compile-time offset.
-struct VAddrQ {
-    uint32_t b[2];
-    __device__ __forceinline__ VAddrQ() {
-        const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-        const int G = l >> 4, i = l & 15, r = i >> 2, c = i & 3;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int krow = (G >> 1) * 8 + s * 4 + r;
-            const int mk = ((G >> 1) * 2 + s) & 3;  // == mask_a(ks*16 + krow)
-            b[s] = (uint32_t)(krow * fl::PA + w * 256 + ((((G & 1) * 2 + (c >> 1)) ^ mk) << 4) +
-                              ((c & 1) << 3));
-        }
-    }
-    // fragment of column block cb, key step ks
-    __device__ __forceinline__ bf16x8 load(const uint8_t MLA_LDS *t, int cb, int ks) const {
-        const int off = ks * 16 * fl::PA + cb * 64;
-        return tr_pair(t + b[0] + off, t + b[1] + off);
-    }
-};
-
-// Weight buffer [64 heads][32 keys] bf16, 64 B per head, 16-byte chunk c of head h stored
-// at c ^ ((h >> 2) & 3): the P^T reads (16 consecutive heads at one chunk) and the
-// 8-byte weight writes are conflict-free.
-__device__ __forceinline__ uint32_t pbuf_w_off(int hd, int kh, int g) {
-    const int chunk = 2 * kh + (g >> 1);
-    return (uint32_t)(hd * 64 + ((chunk ^ ((hd >> 2) & 3)) << 4) + ((g & 1) << 3));
-}
-__device__ __forceinline__ uint32_t pbuf_r_off(int hd, int ks, int half) {
-    const int chunk = 2 * ks + half;
-    return (uint32_t)(hd * 64 + ((chunk ^ ((hd >> 2) & 3)) << 4));
-}
-
 // P^T fragments of the previous tile's weights (B operand of 32x32x16: lane l holds head
 // hb2*32 + (l & 31), keys ks*16 + (l >> 5)*8 .. +7).
 __device__ __forceinline__ void load_pt(const uint8_t MLA_LDS *pb, bf16x8 (&pt)[2][2]) {
@@ -154,9 +99,9 @@ __device__ __forceinline__ void load_pt(const uint8_t MLA_LDS *pb, bf16x8 (&pt)[
 // bound by instruction issue).  The chains start from a literal zero (no VALU write feeds
 // an MFMA source), and since the compiler does not count wait states after an MFMA it
 // cannot see, 20 of them separate the last MFMAs from the reads of their results.
-template <typename Fill>
+template <typename KA, typename Fill>
 __device__ __forceinline__ void score_tile_q(const DqState &st, const uint8_t MLA_LDS *t,
-                                             const KAddr &ka, f32x4 (&s)[2], Fill fill) {
+                                             const KA &ka, f32x4 (&s)[2], Fill fill) {
     f32x4 c[2][2];
     constexpr int AH = 4;
     bf16x8 a[AH];
@@ -191,9 +136,9 @@ __device__ __forceinline__ void score_tile_q(const DqState &st, const uint8_t ML
 
 // O^T += V^T P^T over the tile's 32 keys: 8 V^T fragments (two reads ahead), each
 // feeding two 32x32x16 MFMAs (head blocks); fill(i) follows step i.
-template <typename Fill>
+template <typename VA, typename Fill>
 __device__ __forceinline__ void update_tile_q(DqState &st, const uint8_t MLA_LDS *t,
-                                              const VAddrQ &va, const bf16x8 (&pt)[2][2],
+                                              const VA &va, const bf16x8 (&pt)[2][2],
                                               Fill fill) {
     bf16x8 v[2];
     v[0] = va.load(t, 0, 0);
@@ -207,20 +152,6 @@ __device__ __forceinline__ void update_tile_q(DqState &st, const uint8_t MLA_LDS
         fill(ic);
         __builtin_amdgcn_sched_barrier(0);
     });
-}
-
-// Max over the four lanes (l & 15) + 16g that hold the same head; all four get the
-// result of the same fixed-order combination.
-__device__ __forceinline__ float quad_max(float x) {
-    const float a = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(a, __shfl_xor(a, 32));
-}
-__device__ __forceinline__ float quad_sum(float x) {
-    const int l = threadIdx.x & 63;
-    const float y = __shfl_xor(x, 16);
-    const float a = (l & 16) ? y + x : x + y;
-    const float z = __shfl_xor(a, 32);
-    return (l & 32) ? z + a : a + z;
 }
 
 // Softmax of one tile's scores s (keys key0 + kh*16 + (l >> 4)*4 + e; keys >= kend are
@@ -376,11 +307,14 @@ __device__ __forceinline__ void dq_stream(DqState &st, uint8_t MLA_LDS *lds,
                                           const uint8_t *__restrict__ rows, int nk, int k0,
                                           int k1, float sc, bool have_m, bool first,
                                           const bf16 *__restrict__ qb, int hbase, int H) {
+    // bf16 tiles take the masks of 16-row fragment reads; Q8_0 tiles keep those of the
+    // dequantisation's writes
+    using Masks = std::conditional_t<Q8, TileMasks, TileMasks16>;
     uint8_t MLA_LDS *pbuf = lds + dq::stage_bytes(Q8);
     uint8_t MLA_LDS *qs = lds + dq::qstage_off(Q8);
     const int w = threadIdx.x >> 6;
-    const KAddr ka(w & 1);
-    const VAddrQ va;
+    const KAddr<Masks> ka(w & 1);
+    const VAddrQ<Masks> va(w);
     const int ntiles = (k1 - k0 + fl::NK - 1) / fl::NK;
     // Every earlier vector-memory load (the sequence length) must be complete before the
     // first copy: the compiler does not see the copies, and a load it still counted as
@@ -391,7 +325,8 @@ __device__ __forceinline__ void dq_stream(DqState &st, uint8_t MLA_LDS *lds,
         const int last = nk - 1;
         // tiles 0 and 1 now (stages 2-3 hold the query rows until they are read)
         for (int i = 0; i < 2; ++i)
-            if (i < ntiles) issue_tile_bf16<dq::NW>(rows, k0 + i * fl::NK, last, lds + i * fl::TILE_BYTES);
+            if (i < ntiles)
+                issue_tile_bf16<dq::NW, Masks>(rows, k0 + i * fl::NK, last, lds + i * fl::TILE_BYTES);
         if (first) {
             wait_groups<dq::COPY_PER>(min(2, ntiles));  // the query copies (issued first)
             __syncthreads();
@@ -410,10 +345,10 @@ __device__ __forceinline__ void dq_stream(DqState &st, uint8_t MLA_LDS *lds,
             const int nkey0 = k0 + nx * fl::NK;
             const bool full = nkey0 + fl::NK - 1 <= last;
             uint8_t MLA_LDS *ndst = lds + (nx % dq::NS_BF16) * fl::TILE_BYTES;
-            if (more && !full) issue_tile_bf16<dq::NW>(rows, nkey0, last, ndst);  // the tail tile
+            if (more && !full) issue_tile_bf16<dq::NW, Masks>(rows, nkey0, last, ndst);  // the tail tile
             const uint8_t *sbase = rows + (int64_t)(nkey0 + 8 * wu) * fl::RB;
             const uint32_t dsts = lds_u32(ndst);
-            const CopyPlan plan = make_copy_plan();
+            const CopyPlan plan = make_copy_plan<Masks>();
             f32x4 s[2];
             // Copy parts 0..5 follow score steps 0, 3, .. 15 and parts 6..8 the O-update
             // steps 1, 3, 5: a copy instruction blocks its wave while the CU's address

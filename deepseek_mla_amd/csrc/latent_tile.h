@@ -89,24 +89,52 @@ __device__ __forceinline__ bf16x8 tr_pair(const uint8_t MLA_LDS *p0, const uint8
 // they are masked out of the softmax) into LDS stage `dst`.  Part i (0 .. 8) of wave w:
 // parts 0..7 copy the latent row 8w + i (one instruction, uniform source row), part 8
 // copies the rope rows 8w .. 8w+7 (one instruction).
-template <int NW>
-__device__ __forceinline__ void issue_chunk_bf16(const uint8_t *__restrict__ rows, int key0,
-                                                 int last, uint8_t MLA_LDS *dst, int i) {
-    static_assert(NW == 4, "one latent row per instruction: 8 rows and one rope part per wave");
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+// The chunk masks of the tile layout above, as a policy for the copies and the fragment
+// addressing.
+struct TileMasks {
+    __device__ __forceinline__ static int a(int k) { return mask_a(k); }
+    __device__ __forceinline__ static int b(int k) { return mask_b(k); }
+};
+// Masks for tiles whose K fragments are read 16 rows at a time (v_mfma_f32_16x16x32_bf16:
+// lane l reads row l & 15 at chunk 4kk + (l >> 4)).  Measured on gfx950 (an in-bounds probe
+// of each access form under the bank-conflict counter): ds_read_b128 serves a wave in four
+// passes of 16 lanes, lanes with equal bit 5 and equal parity of bits 2..4 together, and a
+// pass is conflict-free when its lanes hit distinct 16-byte groups of a 256-byte bank row.
+// A pass of the 16-row fragment read holds rows k, k + 12 at chunk c and rows k + 4, k + 8
+// at chunk c ^ 1 (k = 0..3); with mask_a the second pair lands on the first pair's groups
+// (two passes per group of lanes).  Here a(k) = -(k >> 2) mod 4 gives the four rows of each
+// k & 3 four different groups, and b(k) = k & 6 spreads the even and the odd rope rows of
+// a pass over eight chunks each.  Rows k and k + 16 keep equal masks, and the transposing
+// V reads (32 lanes per pass, four consecutive rows at four chunks) stay conflict-free with
+// any row mask.
+struct TileMasks16 {
+    __device__ __forceinline__ static int a(int k) { return (4 - ((k >> 2) & 3)) & 3; }
+    __device__ __forceinline__ static int b(int k) { return k & 6; }
+};
+// cw: the copying wave's index among the four that share the tile (uniform); Masks: the
+// layout's chunk masks.
+template <typename Masks = TileMasks>
+__device__ __forceinline__ void issue_chunk_bf16_cw(const uint8_t *__restrict__ rows, int key0,
+                                                    int last, uint8_t MLA_LDS *dst, int i, int w) {
     const int l = threadIdx.x & 63;
     if (i < 8) {
         const int k = w * 8 + i;
         const uint8_t *src = rows + (int64_t)min(key0 + k, last) * fl::RB;
-        lds_copy16(src, (uint32_t)((l ^ mask_a(k)) * 16), lds_u32(dst + k * fl::PA));
+        lds_copy16(src, (uint32_t)((l ^ Masks::a(k)) * 16), lds_u32(dst + k * fl::PA));
     } else {
         // rows past `last` are clamped per lane; offsets stay below 32 rows
         const int k = w * 8 + (l >> 3);
         const int kr = min(k, last - key0);
         lds_copy16(rows + (int64_t)key0 * fl::RB,
-                   (uint32_t)(kr * fl::RB + fl::R * 2 + (((l & 7) ^ mask_b(k)) * 16)),
+                   (uint32_t)(kr * fl::RB + fl::R * 2 + (((l & 7) ^ Masks::b(k)) * 16)),
                    lds_u32(dst + fl::A_BYTES + w * 1024));
     }
+}
+template <int NW>
+__device__ __forceinline__ void issue_chunk_bf16(const uint8_t *__restrict__ rows, int key0,
+                                                 int last, uint8_t MLA_LDS *dst, int i) {
+    static_assert(NW == 4, "one latent row per instruction: 8 rows and one rope part per wave");
+    issue_chunk_bf16_cw(rows, key0, last, dst, i, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
 }
 
 // Copy plan of a full tile (all 32 keys inside the cache) for wave w: one uniform source
@@ -118,14 +146,15 @@ __device__ __forceinline__ void issue_chunk_bf16(const uint8_t *__restrict__ row
 struct CopyPlan {
     uint32_t va0, va1, vb;
 };
+template <typename Masks = TileMasks>
 __device__ __forceinline__ CopyPlan make_copy_plan() {
     const int w = threadIdx.x >> 6;
     int l = threadIdx.x & 63;
     asm volatile("" : "+v"(l));  // recomputed where used, not kept live across the loop
     CopyPlan c;
-    c.va0 = (uint32_t)((l ^ mask_a(8 * w)) * 16);
-    c.va1 = (uint32_t)((l ^ mask_a(8 * w + 4)) * 16);
-    c.vb = (uint32_t)((l >> 3) * fl::RB + fl::R * 2 + (((l & 7) ^ mask_b(8 * w + (l >> 3))) * 16));
+    c.va0 = (uint32_t)((l ^ Masks::a(8 * w)) * 16);
+    c.va1 = (uint32_t)((l ^ Masks::a(8 * w + 4)) * 16);
+    c.vb = (uint32_t)((l >> 3) * fl::RB + fl::R * 2 + (((l & 7) ^ Masks::b(8 * w + (l >> 3))) * 16));
     return c;
 }
 
@@ -142,11 +171,13 @@ __device__ __forceinline__ void issue_part_full(const uint8_t *sbase, const Copy
     }
 }
 
-template <int NW>
+template <int NW, typename Masks = TileMasks>
 __device__ __forceinline__ void issue_tile_bf16(const uint8_t *__restrict__ rows, int key0,
                                                 int last, uint8_t MLA_LDS *dst) {
+    static_assert(NW == 4, "one latent row per instruction: 8 rows and one rope part per wave");
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-    for (int i = 0; i < 9; ++i) issue_chunk_bf16<NW>(rows, key0, last, dst, i);
+    for (int i = 0; i < 9; ++i) issue_chunk_bf16_cw<Masks>(rows, key0, last, dst, i, w);
 }
 
 // Issue the async copy of the raw Q8_0 bytes of a 32-row tile into LDS, one dword per
@@ -397,5 +428,83 @@ struct DequantQ8Pieces {
     }
 };
 
+
+// ------------------------------------------------- 16-row score and weight-buffer layouts
+// Shared by the attention kernels whose waves score 16 query rows (or heads) at a time
+// with v_mfma_f32_16x16x32_bf16 and exchange their weights through a [64 rows][32 keys]
+// LDS buffer.
+
+// Byte offsets (within a tile stage) of the K fragment of score step kk for this lane:
+// key kh*16 + (l & 15), logical chunk kk*4 + (l >> 4).  Latent chunks (kk < 16) are
+// stored at kk*4 + ((l >> 4) ^ mask_a(key)): one base plus kk*64.  Keys k and k + 16 have
+// the same masks, so key half 1 is key half 0 moved by 16 rows (compile-time offsets).
+template <typename Masks = TileMasks>
+struct KAddr {
+    uint32_t a, r0, r1;
+    __device__ __forceinline__ KAddr(int kh) {
+        const int l = threadIdx.x & 63, g = l >> 4;
+        const int k = kh * 16 + (l & 15);
+        a = (uint32_t)(k * fl::PA + ((g ^ Masks::a(k)) << 4));
+        r0 = (uint32_t)(fl::A_BYTES + k * fl::PB + ((g ^ Masks::b(k)) << 4));
+        r1 = (uint32_t)(fl::A_BYTES + k * fl::PB + (((4 + g) ^ Masks::b(k)) << 4));
+    }
+    __device__ __forceinline__ uint32_t at(int kk) const {
+        return kk < 16 ? a + (uint32_t)(kk * 64) : (kk == 16 ? r0 : r1);
+    }
+};
+
+// Byte offsets of the V^T fragments (A operand of 32x32x16: lane l holds column l & 31
+// of a 32-column block and keys (l >> 5)*8 .. +7 of a 16-key step) over the 128 latent
+// columns of quarter cq.  Two transposing reads of 4 keys each: in its 16-lane group G,
+// lane 4r + c addresses key (G >> 1)*8 + 4s + r and columns (G & 1)*16 + 4c .. +3 of the
+// block; lane i of the group receives column (G & 1)*16 + i of those 4 keys.  The row
+// mask mask_a depends only on (G >> 1, s), so step (cb, ks) adds a compile-time offset.
+template <typename Masks = TileMasks>
+struct VAddrQ {
+    uint32_t b[2];
+    __device__ __forceinline__ explicit VAddrQ(int cq) {
+        const int l = threadIdx.x & 63;
+        const int G = l >> 4, i = l & 15, r = i >> 2, c = i & 3;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int krow = (G >> 1) * 8 + s * 4 + r;
+            const int mk = Masks::a(krow);  // the same for the 4 rows (krow >> 2 fixed) and at krow + 16
+            b[s] = (uint32_t)(krow * fl::PA + cq * 256 + ((((G & 1) * 2 + (c >> 1)) ^ mk) << 4) +
+                              ((c & 1) << 3));
+        }
+    }
+    // fragment of column block cb, key step ks
+    __device__ __forceinline__ bf16x8 load(const uint8_t MLA_LDS *t, int cb, int ks) const {
+        const int off = ks * 16 * fl::PA + cb * 64;
+        return tr_pair(t + b[0] + off, t + b[1] + off);
+    }
+};
+
+// Weight buffer [64 rows][32 keys] bf16, 64 B per row, 16-byte chunk c of row h stored
+// at c ^ ((h >> 2) & 3): the P^T reads (16 consecutive rows at one chunk) and the
+// 8-byte weight writes are conflict-free.  pbuf_w_off: the 4 weights of keys
+// kh*16 + g*4 .. +3; pbuf_r_off: the 8 weights of keys ks*16 + half*8 .. +7.
+__device__ __forceinline__ uint32_t pbuf_w_off(int hd, int kh, int g) {
+    const int chunk = 2 * kh + (g >> 1);
+    return (uint32_t)(hd * 64 + ((chunk ^ ((hd >> 2) & 3)) << 4) + ((g & 1) << 3));
+}
+__device__ __forceinline__ uint32_t pbuf_r_off(int hd, int ks, int half) {
+    const int chunk = 2 * ks + half;
+    return (uint32_t)(hd * 64 + ((chunk ^ ((hd >> 2) & 3)) << 4));
+}
+
+// Max over the four lanes (l & 15) + 16g that hold the same row; all four get the
+// result of the same fixed-order combination.
+__device__ __forceinline__ float quad_max(float x) {
+    const float a = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(a, __shfl_xor(a, 32));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+    const int l = threadIdx.x & 63;
+    const float y = __shfl_xor(x, 16);
+    const float a = (l & 16) ? y + x : x + y;
+    const float z = __shfl_xor(a, 32);
+    return (l & 32) ? z + a : a + z;
+}
 
 }  // namespace mla
