@@ -58,19 +58,19 @@ MATERIALIZED_SRC = tuple(_CSRC + f for f in ("flash_mha.hip", "latent_tile.h", "
                                              "common.h"))
 TRAFFIC = {
     # workload: (bytes per launch, sources, sha256 prefix)
-    "v3_long_prefill": (10916048582, PREFILL_SRC, "95af0a8d6b93183c"),
-    "lite_prefill": (227714663, PREFILL_SRC, "95af0a8d6b93183c"),
-    "v3_decode": (73657596, DECODE_SRC, "5366107a5f962f00"),
-    "v3_decode@vt": (141552400, WIDE_DECODE_SRC, "b7674e77dc0c9d27"),
-    "v3_decode_q8": (318310681, WIDE_DECODE_SRC, "b7674e77dc0c9d27"),
-    "v3_long_prefill@materialized": (3401259541, MATERIALIZED_SRC, "2d5adc30f0a8af4b"),
+    "v3_long_prefill": (10916048582, PREFILL_SRC, "cf78866709404e22"),
+    "lite_prefill": (227714663, PREFILL_SRC, "cf78866709404e22"),
+    "v3_decode": (73657596, DECODE_SRC, "d3648251bb2fc5f5"),
+    "v3_decode@vt": (141552400, WIDE_DECODE_SRC, "ddc6d27a88794adf"),
+    "v3_decode_q8": (318310681, WIDE_DECODE_SRC, "ddc6d27a88794adf"),
+    "v3_long_prefill@materialized": (3401259541, MATERIALIZED_SRC, "b55cdceb7076f3ef"),
 }
 # Sustained shader clock under each kernel's load (GHz): GRBM_GUI_ACTIVE cycles per
 # dispatch over the dispatch's duration, from the counter summaries in profiles/; keyed
 # like TRAFFIC.
 CLOCK_GHZ = {
-    "v3_long_prefill": (2.029, PREFILL_SRC, "95af0a8d6b93183c"),
-    "v3_long_prefill@materialized": (1.920, MATERIALIZED_SRC, "2d5adc30f0a8af4b"),
+    "v3_long_prefill": (2.029, PREFILL_SRC, "cf78866709404e22"),
+    "v3_long_prefill@materialized": (1.920, MATERIALIZED_SRC, "b55cdceb7076f3ef"),
 }
 
 

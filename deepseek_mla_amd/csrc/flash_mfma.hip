@@ -299,7 +299,7 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
     // would also drain the tile copies in flight on every tile.
     MLA_WAIT_VMCNT(0);
     {
-        constexpr int PER = 9;  // copy instructions per wave per tile (issue_chunk_bf16)
+        constexpr int PER = 9;  // copy instructions per wave per tile (issue_tile_bf16)
         const int last = n_rows - 1;
 #pragma unroll
         for (int s = 0; s < 2; ++s)

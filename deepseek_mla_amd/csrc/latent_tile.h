@@ -134,12 +134,6 @@ __device__ __forceinline__ void issue_chunk_bf16_cw(const uint8_t *__restrict__ 
                    lds_u32(dst + fl::A_BYTES + w * 1024));
     }
 }
-template <int NW>
-__device__ __forceinline__ void issue_chunk_bf16(const uint8_t *__restrict__ rows, int key0,
-                                                 int last, uint8_t MLA_LDS *dst, int i) {
-    static_assert(NW == 4, "one latent row per instruction: 8 rows and one rope part per wave");
-    issue_chunk_bf16_cw(rows, key0, last, dst, i, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
-}
 
 // Copy plan of a full tile (all 32 keys inside the cache) for wave w: one uniform source
 // address per tile (key0 + 8w) plus a compile-time row step per instruction, and lane
