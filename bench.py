@@ -69,7 +69,7 @@ TRAFFIC = {
 # dispatch over the dispatch's duration, from the counter summaries in profiles/; keyed
 # like TRAFFIC.
 CLOCK_GHZ = {
-    "v3_long_prefill": (2.029, PREFILL_SRC, "cf78866709404e22"),
+    "v3_long_prefill": (2.068, PREFILL_SRC, "cf78866709404e22"),
     "v3_long_prefill@materialized": (1.920, MATERIALIZED_SRC, "b55cdceb7076f3ef"),
 }
 
