@@ -154,6 +154,17 @@ struct GlPlan {
             b[j] = (uint32_t)((int64_t)rr * ldb * 2 + (((l & 7) ^ gl_swz(r)) << 4));
         }
     }
+    // copy instruction c (0 .. BM/32 + 3; A rows first, then B rows) of k-tile [k0, k0 + 64)
+    // into the stage at LDS address dst
+    __device__ __forceinline__ void issue_one(const uint8_t *abase, const uint8_t *bbase, int k0,
+                                              uint32_t dst, int c) const {
+        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        if (c < BM / 32)
+            lds_copy16(abase + 2 * k0, a[c], dst + (w * (BM / 4) + 8 * c) * GL_ROWB);
+        else
+            lds_copy16(bbase + 2 * k0, b[c - BM / 32],
+                       dst + BM * GL_ROWB + (w * 32 + 8 * (c - BM / 32)) * GL_ROWB);
+    }
     // copies of k-tile [k0, k0 + 64) into the stage at LDS address dst
     __device__ __forceinline__ void issue(const uint8_t *abase, const uint8_t *bbase, int k0,
                                           uint32_t dst) const {
@@ -290,9 +301,16 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_lds_kernel(
             MLA_WAIT_VMCNT(0);
         }
         __syncthreads();  // k-tile kt landed everywhere; k-tile kt-1 no longer read
-        if (kt + NS - 1 < nk)
-            plan.issue(abase, bbase, (kt + NS - 1) * GL_BK, lbase + ((kt + NS - 1) % NS) * SB);
+        // k-tile kt + NS - 1 goes into the stage k-tile kt-1 left.  With three or more stages,
+        // one copy instruction after every other MFMA: issued together, the four waves' copies
+        // queue in the CU's address unit and hold back the first MFMAs of the k-tile.  With
+        // two (K of two k-tiles), all at once: the second k-tile is the last.
+        constexpr bool SPREAD = NS > 2;
+        const bool more = kt + NS - 1 < nk;
+        const int nk0 = (kt + NS - 1) * GL_BK;
+        const uint32_t ndst = lbase + ((kt + NS - 1) % NS) * SB;
         const uint8_t MLA_LDS *st = lds + (kt % NS) * SB;
+        if (!SPREAD && more) plan.issue(abase, bbase, nk0, ndst);
         // fragments of k step ks+1 are read while the MFMAs of step ks run
         bf16x8 bf[2][2], af[2][MB];
         auto fetch = [&](int ks, int b) {
@@ -309,12 +327,19 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_lds_kernel(
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int i = 0; i < MB; ++i)
+                for (int i = 0; i < MB; ++i) {
                     acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[ks & 1][j], af[ks & 1][i],
                                                                         acc[j][i], 0, 0, 0);
+                    const int q = (ks * 2 + j) * MB + i;  // MFMA index within the k-tile
+                    if (SPREAD && q % 2 == 0 && q / 2 < CP) {
+                        if (more) plan.issue_one(abase, bbase, nk0, ndst, q / 2);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    static_assert(2 * CP <= GL_BK / 16 * 2 * MB, "every copy instruction inside the k-tile's MFMAs");
     __syncthreads();  // stages free: staging of the output tile
     // lane: output row m = wm + 32i + (l & 31); columns n = wn + 32j + 8g + 4*hi + 0..3
 #pragma unroll
