@@ -139,6 +139,7 @@ __device__ __forceinline__ int gl_swz(int r) { return (r >> 1) & 7; }
 template <int BM>
 struct GlPlan {
     uint32_t a[BM / 32], b[4];
+    uint32_t wa, wb;  // LDS offsets of this wave's first A row and first B row in a stage
     __device__ __forceinline__ GlPlan(int M, int N, int64_t lda, int64_t ldb, int m0, int n0) {
         const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
 #pragma unroll
@@ -153,28 +154,23 @@ struct GlPlan {
             const int rr = min(n0 + r, N - 1) - n0;
             b[j] = (uint32_t)((int64_t)rr * ldb * 2 + (((l & 7) ^ gl_swz(r)) << 4));
         }
+        wa = (uint32_t)(w * (BM / 4) * GL_ROWB);
+        wb = (uint32_t)(BM * GL_ROWB + w * 32 * GL_ROWB);
     }
-    // copy instruction c (0 .. BM/32 + 3; A rows first, then B rows) of k-tile [k0, k0 + 64)
-    // into the stage at LDS address dst
-    __device__ __forceinline__ void issue_one(const uint8_t *abase, const uint8_t *bbase, int k0,
+    // copy instruction c (0 .. BM/32 + 3; A rows first, then B rows) of the k-tile whose
+    // first elements are at asrc (A) and bsrc (B), into the stage at LDS address dst
+    __device__ __forceinline__ void issue_one(const uint8_t *asrc, const uint8_t *bsrc,
                                               uint32_t dst, int c) const {
-        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         if (c < BM / 32)
-            lds_copy16(abase + 2 * k0, a[c], dst + (w * (BM / 4) + 8 * c) * GL_ROWB);
+            lds_copy16(asrc, a[c], dst + wa + 8 * c * GL_ROWB);
         else
-            lds_copy16(bbase + 2 * k0, b[c - BM / 32],
-                       dst + BM * GL_ROWB + (w * 32 + 8 * (c - BM / 32)) * GL_ROWB);
+            lds_copy16(bsrc, b[c - BM / 32], dst + wb + 8 * (c - BM / 32) * GL_ROWB);
     }
     // copies of k-tile [k0, k0 + 64) into the stage at LDS address dst
     __device__ __forceinline__ void issue(const uint8_t *abase, const uint8_t *bbase, int k0,
                                           uint32_t dst) const {
-        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-        for (int j = 0; j < BM / 32; ++j)
-            lds_copy16(abase + 2 * k0, a[j], dst + (w * (BM / 4) + 8 * j) * GL_ROWB);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            lds_copy16(bbase + 2 * k0, b[j], dst + BM * GL_ROWB + (w * 32 + 8 * j) * GL_ROWB);
+        for (int c = 0; c < BM / 32 + 4; ++c) issue_one(abase + 2 * k0, bbase + 2 * k0, dst, c);
     }
 };
 
@@ -287,30 +283,27 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_lds_kernel(
     };
 
     const int nk = K / GL_BK;
+    // With three or more stages, every stage receives a copy in the prologue and every
+    // k-tile issues one, also past the last k-tile (the last one again, into the stage the
+    // previous k-tile left, which nothing reads any more): the count of copy groups in flight
+    // is then the same at every wait, and the copies need no branches.
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-        if (s < nk) plan.issue(abase, bbase, s * GL_BK, lbase + s * SB);
+    for (int s = 0; s < NS - 1; ++s) plan.issue(abase, bbase, min(s, nk - 1) * GL_BK, lbase + s * SB);
     for (int kt = 0; kt < nk; ++kt) {
-        // k-tile kt landed (later ones may still be in flight: at most NS - 2 of them)
-        const int ahead = min(nk - 1 - kt, NS - 2);
-        if (ahead >= 2) {
-            MLA_WAIT_VMCNT(2 * CP);
-        } else if (ahead == 1) {
-            MLA_WAIT_VMCNT(CP);
-        } else {
-            MLA_WAIT_VMCNT(0);
-        }
+        // k-tile kt landed (the NS - 2 copy groups issued after its own may be in flight)
+        MLA_WAIT_VMCNT((NS - 2) * CP);
         __syncthreads();  // k-tile kt landed everywhere; k-tile kt-1 no longer read
         // k-tile kt + NS - 1 goes into the stage k-tile kt-1 left.  With three or more stages,
         // one copy instruction after every other MFMA: issued together, the four waves' copies
         // queue in the CU's address unit and hold back the first MFMAs of the k-tile.  With
-        // two (K of two k-tiles), all at once: the second k-tile is the last.
+        // two (K of two k-tiles), all at once, and none past the last k-tile (the wait is for
+        // every copy in flight there).
         constexpr bool SPREAD = NS > 2;
-        const bool more = kt + NS - 1 < nk;
-        const int nk0 = (kt + NS - 1) * GL_BK;
+        const int nk0 = min(kt + NS - 1, nk - 1) * GL_BK;
+        const uint8_t *asrc = abase + 2 * nk0, *bsrc = bbase + 2 * nk0;
         const uint32_t ndst = lbase + ((kt + NS - 1) % NS) * SB;
         const uint8_t MLA_LDS *st = lds + (kt % NS) * SB;
-        if (!SPREAD && more) plan.issue(abase, bbase, nk0, ndst);
+        if (!SPREAD && kt + 1 < nk) plan.issue(abase, bbase, nk0, ndst);
         // fragments of k step ks+1 are read while the MFMAs of step ks run
         bf16x8 bf[2][2], af[2][MB];
         auto fetch = [&](int ks, int b) {
@@ -332,7 +325,7 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_lds_kernel(
                                                                         acc[j][i], 0, 0, 0);
                     const int q = (ks * 2 + j) * MB + i;  // MFMA index within the k-tile
                     if (SPREAD && q % 2 == 0 && q / 2 < CP) {
-                        if (more) plan.issue_one(abase, bbase, nk0, ndst, q / 2);
+                        plan.issue_one(asrc, bsrc, ndst, q / 2);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -340,7 +333,8 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_lds_kernel(
         }
     }
     static_assert(2 * CP <= GL_BK / 16 * 2 * MB, "every copy instruction inside the k-tile's MFMAs");
-    __syncthreads();  // stages free: staging of the output tile
+    MLA_WAIT_VMCNT(0);  // the copies issued past the last k-tile land before the staging
+    __syncthreads();    // stages free: staging of the output tile
     // lane: output row m = wm + 32i + (l & 31); columns n = wn + 32j + 8g + 4*hi + 0..3
 #pragma unroll
     for (int j = 0; j < 2; ++j)
