@@ -69,8 +69,8 @@ TRAFFIC = {
 # dispatch over the dispatch's duration, from the counter summaries in profiles/; keyed
 # like TRAFFIC.
 CLOCK_GHZ = {
-    "v3_long_prefill": (2.068, PREFILL_SRC, "cf78866709404e22"),
-    "v3_long_prefill@materialized": (1.920, MATERIALIZED_SRC, "b55cdceb7076f3ef"),
+    "v3_long_prefill": (2.089, PREFILL_SRC, "cf78866709404e22"),
+    "v3_long_prefill@materialized": (1.921, MATERIALIZED_SRC, "b55cdceb7076f3ef"),
 }
 
 
