@@ -283,8 +283,12 @@ __device__ __forceinline__ void init_acc(WaveState &st, float m0) {
 }
 
 // Stream keys [kbeg, kend) of the bf16 `rows` through LDS and attend every tile.
-// pbuf: the weight exchange buffer (PBUF_BYTES of LDS).
-template <int NW, int NS>
+// pbuf: the weight exchange buffer (PBUF_BYTES of LDS).  AF: every tile of the stream lies
+// inside the cache (a multiple of 32 rows, kbeg a multiple of 32).  The copies of the tile
+// two ahead then go out in every iteration, past the stream's end as well (the cache's last
+// 32 rows, into the stage the tile two back left, which nothing reads again): they need no
+// branches, and every wait allows the same count of copies in flight.
+template <int NW, int NS, bool AF>
 __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
                                             uint8_t MLA_LDS *pbuf,
                                             const uint8_t *__restrict__ rows, int n_rows,
@@ -303,7 +307,9 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
         const int last = n_rows - 1;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-            if (s < ntiles) issue_tile_bf16<NW>(rows, kbeg + s * fl::NK, last, lds + s * fl::TILE_BYTES);
+            if (AF || s < ntiles)
+                issue_tile_bf16<NW>(rows, kbeg + min(s, ntiles - 1) * fl::NK, last,
+                                    lds + s * fl::TILE_BYTES);
         // Iteration t: wait for tile t, scores of tile t (with the copy of tile t+2 into
         // the stage tile t-2 used, free since the barrier), then the O update of tile t-1
         // carrying the softmax of tile t.  Tile t-1 stays resident for its V reads.  The
@@ -316,7 +322,7 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
         static_assert(P_SYNC < P_READ && P_READ + 4 <= 36 - PV_AHEAD, "score steps");
         bf16x8 pprev[2];  // the own rows' weights of tile t-1
         for (int ti = 0; ti < ntiles; ++ti) {
-            if (ti + 1 < ntiles) {
+            if (AF || ti + 1 < ntiles) {
                 MLA_WAIT_VMCNT(PER);
             } else {
                 MLA_WAIT_VMCNT(0);
@@ -329,12 +335,13 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             const bool more = nx < ntiles;
             // Full tiles take the fast copy path spread over the score MFMAs; the one tile
             // reaching past the cache's last row clamps per row and is issued at once.
-            const bool full = nkey0 + fl::NK - 1 <= last;
+            const bool full = AF || nkey0 + fl::NK - 1 <= last;
             const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-            const uint8_t *sbase = rows + (int64_t)(nkey0 + 8 * wu) * fl::RB;
+            const int skey = AF ? min(nkey0, last - (fl::NK - 1)) : nkey0;
+            const uint8_t *sbase = rows + (int64_t)(skey + 8 * wu) * fl::RB;
             const uint32_t dsts = lds_u32(ndst);
             const CopyPlan plan = make_copy_plan();
-            if (more && !full) issue_tile_bf16<NW>(rows, nkey0, last, ndst);  // once per stream
+            if (!AF && more && !full) issue_tile_bf16<NW>(rows, nkey0, last, ndst);  // once per stream
             // The copy's 9 instructions are spread over the score MFMAs: issued together,
             // the four waves' 36 instructions queue behind each other in the CU's memory
             // address unit.
@@ -371,7 +378,8 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
                 constexpr int j = decltype(jc)::value;
                 soft(j);
                 if constexpr ((j & 3) == 2 || j == 16) {
-                    if (more && full) issue_part_full<(j == 16 ? 8 : j >> 2)>(sbase, plan, dsts, wu);
+                    if (AF || (more && full))
+                        issue_part_full<(j == 16 ? 8 : j >> 2)>(sbase, plan, dsts, wu);
                 }
             };
             if (ti > 0) {
@@ -395,6 +403,7 @@ __device__ __forceinline__ void stream_keys(WaveState &st, uint8_t MLA_LDS *lds,
             get_p0(pbuf, pk);
             pv_tile(st, vlast, va, pbuf, pk, [](int) {});
         }
+        if (AF) MLA_WAIT_VMCNT(0);  // the copies past the stream's end land before the stages are reused
         __syncthreads();
     }
 }
@@ -414,7 +423,7 @@ __device__ __forceinline__ Misc *misc_of(uint8_t *pbuf_generic) {
 static_assert(sizeof(Misc) <= 64, "misc fits the last 64 bytes");
 
 // Runs the key stream for the workgroup, repeating it once if any row was marked.
-template <int NW, int NS>
+template <int NW, int NS, bool AF>
 __device__ __forceinline__ void attend_range(WaveState &st, uint8_t MLA_LDS *lds,
                                              uint8_t MLA_LDS *pbuf, int *flag,
                                              const uint8_t *__restrict__ rows, int n_rows,
@@ -422,7 +431,7 @@ __device__ __forceinline__ void attend_range(WaveState &st, uint8_t MLA_LDS *lds
     float m0 = -INFINITY;
     for (int pass = 0; pass < 2; ++pass) {
         init_acc(st, m0);
-        stream_keys<NW, NS>(st, lds, pbuf, rows, n_rows, kbeg, kend, lim, wlim, sc);
+        stream_keys<NW, NS, AF>(st, lds, pbuf, rows, n_rows, kbeg, kend, lim, wlim, sc);
         if (threadIdx.x == 0) *flag = 0;
         __syncthreads();
         if (__builtin_amdgcn_ballot_w64(st.bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1);
@@ -545,7 +554,8 @@ static_assert(PF_MAX_PARTS <= 16, "the merge holds every part's log-sum-exp and 
 // depend only on ks, so a row's result does not depend on how rows are grouped (head
 // chunks): a row whose keys all lie in one part merges that part with weight exactly 1.
 // One (row group, head chunk, key part) item of the prefill; returns with the LDS free
-// for the next item except for a final barrier (the caller's).
+// for the next item except for a final barrier (the caller's).  AF: see stream_keys.
+template <bool AF>
 __device__ __forceinline__ void prefill_item(
     int unit, int part, const bf16 *__restrict__ q_cat, const int32_t *__restrict__ pos, int T,
     int H, const uint8_t *__restrict__ cache, int n_kv, int hc, int n_groups, int n_chunks,
@@ -607,7 +617,7 @@ __device__ __forceinline__ void prefill_item(
     // values live across the tile loop, which then spills.
     int kbeg = part * ks;
     asm volatile("" : "+s"(kbeg));
-    attend_range<PF_NW, PF_NS>(st, lds, pbuf, &misc->flag, cache, n_rows, kbeg,
+    attend_range<PF_NW, PF_NS, AF>(st, lds, pbuf, &misc->flag, cache, n_rows, kbeg,
                                min(kbeg + ks, kend), lim, wlim, sc);
     // Output rows are recomputed here from the thread index: values kept from before the
     // key stream would stay live across it, crowd out the tile loop's registers and come
@@ -644,6 +654,7 @@ __device__ __forceinline__ void prefill_item(
 // parts (small prefills), one workgroup per CU works through its own list of (unit,
 // part) items, balanced on the host by estimated work (order.start / order.item), so
 // that neither the dispatch order nor per-workgroup start-up costs decide the balance.
+template <bool AF>
 __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
     const bf16 *__restrict__ q_cat, const int32_t *__restrict__ pos, int T, int H,
     const uint8_t *__restrict__ cache, int n_kv, int hc, int n_groups, int n_chunks, float sc,
@@ -651,7 +662,7 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
     float *__restrict__ ws_o, float *__restrict__ ws_lse, int *__restrict__ ws_np,
     int64_t seq_stride, const int32_t *__restrict__ seq_n_kv, const PrefillOrder order) {
     if (nparts == 1) {
-        prefill_item(blockIdx.x, 0, q_cat, pos, T, H, cache, n_kv, hc, n_groups, n_chunks, sc,
+        prefill_item<AF>(blockIdx.x, 0, q_cat, pos, T, H, cache, n_kv, hc, n_groups, n_chunks, sc,
                      o_lat, lse, ks, nparts, ws_o, ws_lse, ws_np, seq_stride, seq_n_kv);
         return;
     }
@@ -660,7 +671,7 @@ __global__ __launch_bounds__(64 * PF_NW, 1) void flash_prefill_bf16_kernel(
     for (int k = order.start[blockIdx.x]; k < k1; ++k) {
         const int it = order.item[k];
         if (it / nparts >= units) continue;  // not an item of this launch (uniform)
-        prefill_item(it / nparts, it % nparts, q_cat, pos, T, H, cache, n_kv, hc, n_groups,
+        prefill_item<AF>(it / nparts, it % nparts, q_cat, pos, T, H, cache, n_kv, hc, n_groups,
                      n_chunks, sc, o_lat, lse, ks, nparts, ws_o, ws_lse, ws_np, seq_stride,
                      seq_n_kv);
         __syncthreads();  // the item's output staging and exchange areas are free again
@@ -890,8 +901,12 @@ hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int 
     float *ws_o = (float *)((char *)ws_lse + (((size_t)G * P * PF_ROWS * 4 + 255) & ~(size_t)255));
     if (P == 1) ws_np = nullptr, ws_lse = nullptr, ws_o = nullptr;
     const size_t shm = (size_t)PF_NS * fl::TILE_BYTES + PBUF_BYTES;
-    static std::atomic<uint64_t> lds_set{0};
-    hipError_t ea = ensure_lds_limit((const void *)flash_prefill_bf16_kernel, (int)shm, lds_set);
+    static std::atomic<uint64_t> lds_set[2];
+    // every tile inside the cache: n_kv rows in whole tiles, tiles aligned to 32 keys (key
+    // parts are multiples of 32); batched caches have their own row counts
+    const bool all_full = !seq_n_kv && n_kv >= fl::NK && n_kv % fl::NK == 0;
+    auto kern = all_full ? flash_prefill_bf16_kernel<true> : flash_prefill_bf16_kernel<false>;
+    hipError_t ea = ensure_lds_limit((const void *)kern, (int)shm, lds_set[all_full]);
     if (ea != hipSuccess) return ea;
     // Work lists of a cut prefill: items by decreasing estimated cost (tiles plus a fixed
     // per-item cost), each assigned to the least loaded of the PF_LISTS workgroups (longest
@@ -917,7 +932,7 @@ hipError_t launch_flash_prefill_bf16(const bf16 *q_cat, const int32_t *pos, int 
         n_lists = cached_lists;
     }
     const unsigned nblocks = P > 1 ? (unsigned)n_lists : (unsigned)G;
-    hipLaunchKernelGGL(flash_prefill_bf16_kernel, dim3(nblocks), dim3(64 * PF_NW), shm,
+    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(64 * PF_NW), shm,
                        st, q_cat, pos, T, H, (const uint8_t *)cache, n_kv, hc, n_groups, n_chunks,
                        scale * fl::LOG2E, o_lat, lse, ks, P, ws_o, ws_lse, ws_np, seq_stride,
                        seq_n_kv, order);
