@@ -58,18 +58,18 @@ MATERIALIZED_SRC = tuple(_CSRC + f for f in ("flash_mha.hip", "latent_tile.h", "
                                              "common.h"))
 TRAFFIC = {
     # workload: (bytes per launch, sources, sha256 prefix)
-    "v3_long_prefill": (10916048582, PREFILL_SRC, "cf78866709404e22"),
-    "lite_prefill": (227714663, PREFILL_SRC, "cf78866709404e22"),
+    "v3_long_prefill": (10849167437, PREFILL_SRC, "cf06df68df7e75e7"),
+    "lite_prefill": (228780498, PREFILL_SRC, "cf06df68df7e75e7"),
     "v3_decode": (73657596, DECODE_SRC, "d3648251bb2fc5f5"),
-    "v3_decode@vt": (141552400, WIDE_DECODE_SRC, "ddc6d27a88794adf"),
-    "v3_decode_q8": (318310681, WIDE_DECODE_SRC, "ddc6d27a88794adf"),
+    "v3_decode@vt": (141545802, WIDE_DECODE_SRC, "150288f17bf57c70"),
+    "v3_decode_q8": (317920916, WIDE_DECODE_SRC, "150288f17bf57c70"),
     "v3_long_prefill@materialized": (3401259541, MATERIALIZED_SRC, "b55cdceb7076f3ef"),
 }
 # Sustained shader clock under each kernel's load (GHz): GRBM_GUI_ACTIVE cycles per
 # dispatch over the dispatch's duration, from the counter summaries in profiles/; keyed
 # like TRAFFIC.
 CLOCK_GHZ = {
-    "v3_long_prefill": (2.089, PREFILL_SRC, "cf78866709404e22"),
+    "v3_long_prefill": (1.933, PREFILL_SRC, "cf06df68df7e75e7"),
     "v3_long_prefill@materialized": (1.921, MATERIALIZED_SRC, "b55cdceb7076f3ef"),
 }
 
