@@ -70,13 +70,15 @@ def kernel_bodies(text):
 
 def bf16_bodies(text):
     b = {n: body for n, body in kernel_bodies(text).items() if any(k in n for k in BF16_KERNELS)}
-    assert len(b) == 4, sorted(kernel_bodies(text))  # the materialised kernel in two shapes
+    # the prefill in two forms (per-copy bounds, all tiles inside the cache) and the
+    # materialised kernel in two shapes
+    assert len(b) == 5, sorted(kernel_bodies(text))
     return b
 
 
 def copy_bodies(text):
     b = {n: body for n, body in kernel_bodies(text).items() if any(k in n for k in COPY_KERNELS)}
-    assert len(b) == 8, sorted(kernel_bodies(text))
+    assert len(b) == 9, sorted(kernel_bodies(text))
     return b
 
 
