@@ -551,6 +551,27 @@ def decode_batch_sweep(batches=(1, 4, 16, 64), n_kv=32768, reps=20):
         torch.cuda.empty_cache()
 
 
+def decode_split_sweep(steps=60, warmup=5):
+    """Decode attention time against the key split count: the V3 bf16 decode (1 x 32768 rows)
+    and the V3 Q8_0 decode (4 x 98304 rows), each at a list of split counts around the
+    library's automatic choice (median of the attention call over `steps` whole steps)."""
+    from deepseek_mla_amd import mla, synth
+    for name, splits in (("v3_decode", (32, 64, 96, 128, 160, 192, 256)),
+                         ("v3_decode_q8", (16, 32, 48, 64, 96, 128))):
+        w = synth.WORKLOADS[name]
+        d = mla.make_dims(w.dims)
+        auto = mla.mla_decode_auto_splits(d, mla.Q8_0 if w.mode == "q8_0" else mla.BF16,
+                                          w.n_seq, w.n_kv)
+        for ns in splits:
+            res, _ = time_workload(w, steps, warmup, 1, ns)
+            ms = res["attention_ms"]
+            nbytes = attention_bytes(w)
+            print(json.dumps({"sweep": name + "_splits", "splits": ns, "auto": auto,
+                              "us": ms * 1e3, "p10_us": res["attention_stats"]["p10_ms"] * 1e3,
+                              "p90_us": res["attention_stats"]["p90_ms"] * 1e3,
+                              "GB/s": nbytes / (ms * 1e-3) / 1e9}), flush=True)
+
+
 # Iterations per workload entry (the measurement protocol: 50 prefill, 200 decode).
 PROTOCOL_STEPS = {"prefill": 50, "decode": 200}
 
@@ -569,6 +590,8 @@ def main():
                     help="decode key splits per sequence (0 = the library's automatic choice)")
     ap.add_argument("--decode-batch-sweep", action="store_true",
                     help="only time V3 bf16 decode at B = 1, 4, 16, 64 (one JSON line each)")
+    ap.add_argument("--decode-split-sweep", action="store_true",
+                    help="only time the V3 bf16 and Q8_0 decodes over a range of split counts")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -585,6 +608,11 @@ def main():
         from deepseek_mla_amd import mla
         mla.lib()
         decode_batch_sweep()
+        return
+    if args.decode_split_sweep:
+        from deepseek_mla_amd import mla
+        mla.lib()
+        decode_split_sweep()
         return
     if args.calibrate_copy:
         n = 512 << 20
