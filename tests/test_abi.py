@@ -87,6 +87,19 @@ def test_host_helpers():
     assert mla.mla_decode_workspace_bytes(v3, 1, 32768, s) >= s * 128 * 513 * 4
 
 
+def test_auto_split_counts_fill_the_cus_once():
+    """The automatic split counts of the two V3 decodes give one workgroup per CU (256 CUs):
+    bf16 at one sequence runs two 64-head groups per split, Q8_0 one 128-head workgroup per
+    (sequence, split).  A split-count sweep on MI355X measured these counts fastest (more
+    workgroups than CUs add a second round; fewer lengthen every workgroup's key range)."""
+    v3 = mla.mla_dims(128, 512, 128, 64, 128, 7168, 0.0722, 10000.0)
+    assert mla.mla_decode_auto_splits(v3, mla.BF16, 1, 32768) == 128
+    assert mla.mla_decode_auto_splits(v3, mla.Q8_0, 4, 98304) == 64
+    # short caches: never more splits than 32-row tiles allow work for
+    s = mla.mla_decode_auto_splits(v3, mla.BF16, 1, 100)
+    assert 1 <= s <= 100
+
+
 def test_new_entry_points_validate_without_gpu():
     """Cache append, the materialised prefill, the Hadamard rotation and the wkv_b layout
     reject bad arguments before any launch (pointers are never dereferenced)."""
